@@ -1,0 +1,253 @@
+/*
+ * CPU oracle for scaled dot-product attention and the multi-head layer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link,
+ * load or call this file; only the tests, the smoke check and the bench's
+ * CPU-baseline leg use it. It shares no code with the HIP library.
+ *
+ * Everything is computed in float64 on inputs already widened to float64,
+ * with plain loops and no blocking, fusion or reordering, so that each step
+ * can be checked against the pages by eye:
+ *
+ *   Attention(Q,K,V) = softmax(Q K^T / sqrt(d_k) + M) V
+ *
+ * as the four stages of "04. Self-Attention: Transformer 的核心计算"
+ * section 四 (scores, scaling, row softmax, weighted sum), with the mask
+ * added before the softmax as in its section 七 (causal) and the padding
+ * mask of "attention-mechanism" (page 2), section 掩码. The softmax is the
+ * stable form that subtracts the row maximum before exponentiating (page 2,
+ * section 最小实现) -- deliberately NOT the online recurrence, so that the
+ * GPU's online softmax is checked against an independent formulation.
+ *
+ * Readings of points the pages leave open (each is also listed in the design
+ * notes of the repository):
+ *  - scale is an explicit argument; the pages fix it at 1/sqrt(d_k) with d_k
+ *    the per-head width ("attention-mechanism", 工程权衡与边界).
+ *  - a masked position is excluded exactly: its weight is 0.0 (the pages'
+ *    e^{-inf} = 0), never exp(-1e9 - m).
+ *  - the padding mask removes KEY positions j >= valid_len[b] for every
+ *    query row; padded query rows are computed normally.
+ *  - causal hides keys j > i (diagonal visible); it is defined here for any
+ *    N_q, N_k with that same index rule.
+ *  - a row with no visible key has no softmax; its output is 0 (convention,
+ *    not fixed by the pages: parity unpinned for that case).
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC attn_oracle.c -o liboracle.so -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_MASK_NONE = 0, ORACLE_MASK_CAUSAL = 1, ORACLE_MASK_PADDING = 2 };
+
+/* Is key j visible to query i?  (page 1 section 七; page 2 section 掩码) */
+static int visible(int mask_kind, int64_t i, int64_t j, int64_t valid_len)
+{
+    if (mask_kind == ORACLE_MASK_CAUSAL) return j <= i;
+    if (mask_kind == ORACLE_MASK_PADDING) return j < valid_len;
+    return 1;
+}
+
+/*
+ * One query row i of one (batch, head):
+ *   q    : [d]        the query row
+ *   Kbh  : [Nk, d]    keys of this (batch, head)
+ *   Vbh  : [Nk, dv]   values of this (batch, head)
+ *   s    : [Nk]       caller's scratch for the row of scaled scores
+ *   o    : [dv]       output row
+ *   a    : [Nk]       optional attention-weight row (may be NULL)
+ */
+static void attention_row(const double *q, const double *Kbh, const double *Vbh, int64_t Nk, int64_t d,
+                          int64_t dv, int mask_kind, int64_t i, int64_t valid_len, double scale, double *s,
+                          double *o, double *a)
+{
+    /* stage 1 + 2: s_j = (q . k_j) * scale for every visible key */
+    int any = 0;
+    for (int64_t j = 0; j < Nk; ++j) {
+        if (!visible(mask_kind, i, j, valid_len)) continue;
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c) dot += q[c] * Kbh[j * d + c];
+        s[j] = dot * scale;
+        any = 1;
+    }
+
+    for (int64_t c = 0; c < dv; ++c) o[c] = 0.0;
+    if (!any) { /* no visible key: output 0, weights 0 */
+        if (a) for (int64_t j = 0; j < Nk; ++j) a[j] = 0.0;
+        return;
+    }
+
+    /* stage 3: stable softmax over the visible keys */
+    double m = -INFINITY;
+    for (int64_t j = 0; j < Nk; ++j)
+        if (visible(mask_kind, i, j, valid_len) && s[j] > m) m = s[j];
+    double z = 0.0;
+    for (int64_t j = 0; j < Nk; ++j) {
+        if (visible(mask_kind, i, j, valid_len)) {
+            s[j] = exp(s[j] - m);
+            z += s[j];
+        } else {
+            s[j] = 0.0; /* e^{-inf} = 0 exactly */
+        }
+    }
+    for (int64_t j = 0; j < Nk; ++j) s[j] = s[j] / z;
+
+    /* stage 4: weighted sum of the value rows */
+    for (int64_t j = 0; j < Nk; ++j) {
+        if (s[j] == 0.0) continue;
+        for (int64_t c = 0; c < dv; ++c) o[c] += s[j] * Vbh[j * dv + c];
+    }
+    if (a) for (int64_t j = 0; j < Nk; ++j) a[j] = s[j];
+}
+
+static int set_threads(int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+    return omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+/*
+ * Full attention. Q [B,H,Nq,d], K [B,H,Nk,d], V [B,H,Nk,dv] row-major
+ * float64; O [B,H,Nq,dv]; A optional [B,H,Nq,Nk]. valid_lens [B] is read
+ * only for the padding mask. Returns the number of threads used, or -1 on
+ * bad arguments.
+ */
+int oracle_attn(const double *Q, const double *K, const double *V, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                int64_t d, int64_t dv, int mask_kind, const int32_t *valid_lens, double scale, double *O, double *A,
+                int nthreads)
+{
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || d <= 0 || dv <= 0) return -1;
+    if (mask_kind == ORACLE_MASK_PADDING && !valid_lens) return -1;
+    int used = set_threads(nthreads);
+    int64_t rows = B * H * Nq;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < rows; ++r) {
+            int64_t i = r % Nq;
+            int64_t bh = r / Nq;
+            int64_t b = bh / H;
+            int64_t L = (mask_kind == ORACLE_MASK_PADDING) ? valid_lens[b] : Nk;
+            attention_row(Q + r * d, K + bh * Nk * d, V + bh * Nk * dv, Nk, d, dv, mask_kind, i, L, scale, s,
+                          O + r * dv, A ? A + r * Nk : NULL);
+        }
+        free(s);
+    }
+    return used;
+}
+
+/*
+ * A subset of rows of the same attention: rows[] holds flat indices
+ * r = (b*H + h)*Nq + i; O_rows is [nrows, dv]. Rows are independent, so
+ * each one is exact, not an approximation of the full computation.
+ */
+int oracle_attn_rows(const double *Q, const double *K, const double *V, int64_t B, int64_t H, int64_t Nq,
+                     int64_t Nk, int64_t d, int64_t dv, int mask_kind, const int32_t *valid_lens, double scale,
+                     const int64_t *rows, int64_t nrows, double *O_rows, int nthreads)
+{
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || d <= 0 || dv <= 0) return -1;
+    if (mask_kind == ORACLE_MASK_PADDING && !valid_lens) return -1;
+    int used = set_threads(nthreads);
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+#pragma omp for schedule(dynamic, 1) reduction(| : bad)
+        for (int64_t t = 0; t < nrows; ++t) {
+            int64_t r = rows[t];
+            if (r < 0 || r >= B * H * Nq) { bad = 1; continue; }
+            int64_t i = r % Nq;
+            int64_t bh = r / Nq;
+            int64_t b = bh / H;
+            int64_t L = (mask_kind == ORACLE_MASK_PADDING) ? valid_lens[b] : Nk;
+            attention_row(Q + r * d, K + bh * Nk * d, V + bh * Nk * dv, Nk, d, dv, mask_kind, i, L, scale, s,
+                          O_rows + t * dv, NULL);
+        }
+        free(s);
+    }
+    return bad ? -1 : used;
+}
+
+/*
+ * C[M,N] = A[M,Kd] B[Kd,N], row-major. Each output element is summed over
+ * the inner index in ascending order; the loop nest walks B by rows only so
+ * that the plain triple loop stays cache friendly.
+ */
+static void matmul_f64(const double *A, const double *Bm, double *C, int64_t M, int64_t Kd, int64_t N)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        double *c = C + m * N;
+        for (int64_t n = 0; n < N; ++n) c[n] = 0.0;
+        for (int64_t k = 0; k < Kd; ++k) {
+            const double a = A[m * Kd + k];
+            const double *b = Bm + k * N;
+            for (int64_t n = 0; n < N; ++n) c[n] += a * b[n];
+        }
+    }
+}
+
+/*
+ * Multi-head attention layer without bias ("Self-Attention 机制", page 5,
+ * sections 五步计算 and 维度全程跟踪; page 1 section 八):
+ *   P = X W_qkv with W_qkv = [W_Q | W_K | W_V]  (d_model x 3 d_model)
+ *   head i uses columns [i*d_k, (i+1)*d_k) of the Q, K and V blocks,
+ *   d_k = d_model / h, scale 1/sqrt(d_k), no mask
+ *   C[:, i*d_k:(i+1)*d_k] = head_i ;  Y = C W_o
+ * X [B,N,d_model], Y [B,N,d_model]; no intermediate rounding.
+ */
+int oracle_mha(const double *X, const double *Wqkv, const double *Wo, int64_t B, int64_t N, int64_t d_model,
+               int64_t h, double *Y, int nthreads)
+{
+    if (B < 0 || N < 0 || d_model <= 0 || h <= 0 || d_model % h) return -1;
+    int used = set_threads(nthreads);
+    const int64_t dk = d_model / h, M = B * N, W3 = 3 * d_model;
+    double *P = (double *)malloc(sizeof(double) * (size_t)(M * W3 > 0 ? M * W3 : 1));
+    double *C = (double *)malloc(sizeof(double) * (size_t)(M * d_model > 0 ? M * d_model : 1));
+    double *Qh = (double *)malloc(sizeof(double) * (size_t)(M * d_model > 0 ? M * d_model : 1));
+    double *Kh = (double *)malloc(sizeof(double) * (size_t)(M * d_model > 0 ? M * d_model : 1));
+    double *Vh = (double *)malloc(sizeof(double) * (size_t)(M * d_model > 0 ? M * d_model : 1));
+    if (!P || !C || !Qh || !Kh || !Vh) { free(P); free(C); free(Qh); free(Kh); free(Vh); return -1; }
+
+    /* step 1: one projection GEMM with the concatenated weight */
+    matmul_f64(X, Wqkv, P, M, d_model, W3);
+
+    /* split: [B,N,h,dk] -> [B,h,N,dk] for each of Q, K, V */
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t t = 0; t < N; ++t)
+            for (int64_t hh = 0; hh < h; ++hh)
+                for (int64_t c = 0; c < dk; ++c) {
+                    int64_t src = (b * N + t) * W3 + hh * dk + c;
+                    int64_t dst = ((b * h + hh) * N + t) * dk + c;
+                    Qh[dst] = P[src];
+                    Kh[dst] = P[src + d_model];
+                    Vh[dst] = P[src + 2 * d_model];
+                }
+
+    /* per-head attention, no mask, scale 1/sqrt(d_k) */
+    double *Oh = P; /* P is no longer needed; reuse its first B*h*N*dk doubles */
+    oracle_attn(Qh, Kh, Vh, B, h, N, N, dk, dk, ORACLE_MASK_NONE, NULL, 1.0 / sqrt((double)dk), Oh, NULL, nthreads);
+
+    /* concat: [B,h,N,dk] -> [B,N,h*dk] */
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t hh = 0; hh < h; ++hh)
+            for (int64_t t = 0; t < N; ++t)
+                for (int64_t c = 0; c < dk; ++c)
+                    C[(b * N + t) * d_model + hh * dk + c] = Oh[((b * h + hh) * N + t) * dk + c];
+
+    /* output projection */
+    matmul_f64(C, Wo, Y, M, d_model, d_model);
+
+    free(P); free(C); free(Qh); free(Kh); free(Vh);
+    return used;
+}

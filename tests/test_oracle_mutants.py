@@ -1,0 +1,47 @@
+"""Planted mistakes in copies of the oracle source, on the CPU: each
+plausible slip (a dropped term, a wrong sign, index or operand) must be
+caught by at least one pin. The real oracle is never modified."""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
+
+MUTANTS = {
+    "scale_dropped": ("s[j] = dot * scale;", "s[j] = dot;"),
+    "scores_use_v_not_k": ("dot += q[c] * Kbh[j * d + c];", "dot += q[c] * Vbh[j * dv + c];"),
+    "causal_hides_diagonal": ("return j <= i;", "return j < i;"),
+    "padding_off_by_one": ("return j < valid_len;", "return j <= valid_len;"),
+    "exp_sign_flipped": ("s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
+    "max_not_subtracted": ("s[j] = exp(s[j] - m);", "s[j] = exp(s[j]);"),
+    "not_normalised": ("for (int64_t j = 0; j < Nk; ++j) s[j] = s[j] / z;", ""),
+    "value_column_reversed": ("o[c] += s[j] * Vbh[j * dv + c];", "o[c] += s[j] * Vbh[j * dv + (dv - 1 - c)];"),
+    "empty_row_not_guarded": ("if (!any) {", "if (0) {"),
+    "mha_k_v_blocks_swapped": ("Kh[dst] = P[src + d_model];\n                    Vh[dst] = P[src + 2 * d_model];",
+                               "Kh[dst] = P[src + 2 * d_model];\n                    Vh[dst] = P[src + d_model];"),
+    "mha_heads_interleaved_on_split": ("int64_t src = (b * N + t) * W3 + hh * dk + c;",
+                                       "int64_t src = (b * N + t) * W3 + c * h + hh;"),
+    "mha_heads_interleaved_on_concat": ("C[(b * N + t) * d_model + hh * dk + c]",
+                                        "C[(b * N + t) * d_model + c * h + hh]"),
+    "mha_scale_by_d_model": ("1.0 / sqrt((double)dk)", "1.0 / sqrt((double)d_model)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    text = open(SRC, encoding="utf-8").read()
+    assert text.count(old) == 1, "mutation site not found exactly once: %r" % old
+    src = tmp_path / ("mutant_%s.c" % name)
+    src.write_text(text.replace(old, new), encoding="utf-8")
+    lib = oracle.compile_source(str(src), str(tmp_path / ("libmutant_%s.so" % name)))
+    caught = []
+    for pin in PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, "no pin caught the planted mistake %s" % name
