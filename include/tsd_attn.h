@@ -1,0 +1,136 @@
+/*
+ * tsd_attn.h -- C ABI of the MI355X (gfx950) scaled dot-product attention
+ * forward pass and its multi-head layer.
+ *
+ * Operations (definitions from the pages; the pages' names):
+ *
+ *   attn_fwd  O = softmax(Q K^T * scale + M) V, per (batch, head).
+ *             "04. Self-Attention：Transformer 的核心计算", section 四
+ *             (four stages: scores, scaling by 1/sqrt(d_k), row softmax,
+ *             weighted sum) and section 七 (the mask M is added before the
+ *             softmax; masked positions get weight 0). Padding mask: the
+ *             "attention-mechanism" page, section 掩码 (padded positions are
+ *             set to -inf as well).
+ *
+ *   mha_fwd   Y = Concat(head_1..head_h) W_O, head_i = Attention of the
+ *             i-th d_k-wide column block of X W_Q, X W_K, X W_V, with the
+ *             three projections fused into one GEMM against
+ *             W_QKV = [W_Q | W_K | W_V].
+ *             "Self-Attention 机制", sections 五步计算 (fused W_QKV) and
+ *             维度全程跟踪 (split into heads, transpose, concat, W_O);
+ *             "04. Self-Attention", section 八 (MultiHead formula).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The
+ *    library allocates no device memory, keeps no pointer after it
+ *    returns, and never synchronises: work is enqueued on `stream`
+ *    (a hipStream_t; NULL = the default stream) and the call returns at
+ *    once. Buffers must stay alive until the stream has passed the work.
+ *  - Tensors are dense, row-major, and 16-byte aligned. Outputs must not
+ *    overlap inputs.
+ *  - Errors are reported only through the return code; nothing aborts and
+ *    no exception crosses the ABI. Argument checks run on the host before
+ *    any HIP call, so an ATTN_EINVAL/ATTN_EUNSUPPORTED call has no side
+ *    effect. attn_last_error() gives a message for the calling thread's
+ *    last failure.
+ */
+#ifndef TSD_ATTN_H
+#define TSD_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define TSD_API __attribute__((visibility("default")))
+#else
+#define TSD_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_EINVAL = 1,       /* null pointer, bad size, misaligned pointer, non-finite scale */
+    ATTN_EUNSUPPORTED = 2, /* well-formed but outside the supported set below */
+    ATTN_EHIP = 3          /* a HIP launch failed; see attn_last_error() */
+} attn_status_t;
+
+typedef enum {
+    ATTN_MASK_NONE = 0,
+    ATTN_MASK_CAUSAL = 1,  /* key j hidden from query i when j > i (diagonal visible) */
+    ATTN_MASK_PADDING = 2  /* key j hidden from every query of batch b when j >= valid_lens[b] */
+} attn_mask_kind_t;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+
+/*
+ * attn_fwd -- scaled dot-product attention forward.
+ *
+ *   Q          [batch, heads, seq_q, head_dim]   in_dtype
+ *   K, V       [batch, heads, seq_k, head_dim]   in_dtype   (d_v = d_k = head_dim)
+ *   mask_kind  attn_mask_kind_t
+ *   valid_lens device int32 [batch]; read only for ATTN_MASK_PADDING (may be
+ *              NULL otherwise). Values are clamped to [0, seq_k] on the device.
+ *   scale      multiplies Q K^T; finite and >= 0 (the pages use 1/sqrt(d_k)).
+ *   O          [batch, heads, seq_q, head_dim]   out_dtype
+ *
+ * A query row with no visible key (valid_lens[b] == 0) gets O = 0.
+ * Masked keys get weight exactly 0: their K and V values never reach O.
+ * The [seq_q, seq_k] score matrix is never written to memory.
+ *
+ * Supported set (else ATTN_EUNSUPPORTED):
+ *   in_dtype BF16: head_dim 64 or 128; out_dtype BF16 or F32; products in
+ *                  bf16 with float32 accumulation, softmax in float32.
+ *   in_dtype F32:  head_dim 16, 32, 64 or 128; out_dtype F32; all float32.
+ *   ATTN_MASK_CAUSAL requires seq_q == seq_k.
+ *   batch*heads, seq_q, seq_k < 2^31; seq_q, seq_k may be 0 (nothing to do).
+ */
+TSD_API attn_status_t attn_fwd(const void *Q, const void *K, const void *V, int32_t mask_kind, const int32_t *valid_lens,
+                       float scale, void *O, int32_t batch, int32_t heads, int32_t seq_q, int32_t seq_k,
+                       int32_t head_dim, int32_t in_dtype, int32_t out_dtype, void *stream);
+
+/*
+ * mha_workspace_bytes -- device workspace mha_fwd needs for these sizes:
+ * Q, K, V split into heads ([3, batch, h, seq, d_model/h]) plus the
+ * concatenated head outputs ([batch, seq, d_model]), in bf16. Returns 0
+ * for sizes mha_fwd would reject.
+ */
+TSD_API size_t mha_workspace_bytes(int32_t batch, int32_t seq, int32_t d_model, int32_t h, int32_t dtype);
+
+/*
+ * mha_fwd -- multi-head self-attention layer, no bias, no mask.
+ *
+ *   X        [batch, seq, d_model]          dtype
+ *   W_qkv    [d_model, 3*d_model]           dtype; column blocks W_Q | W_K | W_V,
+ *            head i owns columns [i*d_k, (i+1)*d_k) of each block
+ *   W_o      [d_model, d_model]             dtype; Y = C W_o
+ *   h        number of heads; d_k = d_model / h; scale 1/sqrt(d_k)
+ *   O        [batch, seq, d_model]          dtype (the layer output Y)
+ *   workspace, workspace_bytes: device scratch of at least
+ *            mha_workspace_bytes(batch, seq, d_model, h, dtype) bytes,
+ *            256-byte aligned, owned by the caller.
+ *
+ * Runs three kernels on `stream`: projection GEMM (its epilogue writes the
+ * head-split layout), attention (its epilogue writes the concatenated
+ * layout), output GEMM. Intermediates are rounded to bf16.
+ *
+ * Supported set: dtype BF16; d_model % h == 0; d_k in {64, 128};
+ * d_model % 64 == 0; batch*seq < 2^31.
+ */
+TSD_API attn_status_t mha_fwd(const void *X, const void *W_qkv, const void *W_o, int32_t h, void *O, int32_t batch,
+                      int32_t seq, int32_t d_model, int32_t dtype, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* Static description of a status code. */
+TSD_API const char *attn_status_string(int32_t status);
+
+/* Message for the calling thread's most recent failed call ("" if none). */
+TSD_API const char *attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSD_ATTN_H */

@@ -18,6 +18,8 @@ valid_lens=3, X=4, W_qkv=5, W_o=6.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 GAMMA = np.uint64(0x9E3779B97F4A7C15)
@@ -52,21 +54,39 @@ def uniform01(seed: int, count: int, start: int = 0) -> np.ndarray:
     return ((x >> np.uint64(11)).astype(np.float64) + 1.0) * (1.0 / 9007199254740992.0)
 
 
+def _normal_pairs(seed: int, p0: int, n: int) -> np.ndarray:
+    u = uniform01(seed, 2 * n, start=2 * p0)
+    r = np.sqrt(-2.0 * np.log(u[0::2]))
+    t = (2.0 * np.pi) * u[1::2]
+    z = np.empty(2 * n, dtype=np.float64)
+    z[0::2] = r * np.cos(t)
+    z[1::2] = r * np.sin(t)
+    return z
+
+
 def normal_f64(seed: int, count: int) -> np.ndarray:
-    """``count`` standard normals (Box-Muller on consecutive uniform pairs)."""
+    """``count`` standard normals (Box-Muller on consecutive uniform pairs).
+    Chunks are independent slices of the stream, so they are filled by a
+    few threads (numpy releases the GIL) without changing any value."""
     out = np.empty(count, dtype=np.float64)
     pairs = (count + 1) // 2
-    for p0 in range(0, pairs, _CHUNK):
+
+    def fill(p0):
         n = min(_CHUNK, pairs - p0)
-        u = uniform01(seed, 2 * n, start=2 * p0)
-        r = np.sqrt(-2.0 * np.log(u[0::2]))
-        t = (2.0 * np.pi) * u[1::2]
-        z = np.empty(2 * n, dtype=np.float64)
-        z[0::2] = r * np.cos(t)
-        z[1::2] = r * np.sin(t)
+        z = _normal_pairs(seed, p0, n)
         lo = 2 * p0
         hi = min(count, lo + 2 * n)
         out[lo:hi] = z[: hi - lo]
+
+    starts = list(range(0, pairs, _CHUNK))
+    if len(starts) <= 1:
+        for p0 in starts:
+            fill(p0)
+    else:
+        import concurrent.futures as cf
+
+        with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1, len(starts))) as ex:
+            list(ex.map(fill, starts))
     return out
 
 

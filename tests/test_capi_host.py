@@ -1,0 +1,124 @@
+"""The C ABI library on the host (no GPU): it loads, exports every function
+include/tsd_attn.h declares, and rejects bad arguments with the documented
+status codes before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_scaled_dot_amd as tsd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tsd_attn.h")
+
+EINVAL, EUNSUP = 1, 2
+BF16, F32 = 1, 0
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    return re.findall(r"TSD_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tsd.library_path()):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return tsd.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert sorted(names) == sorted(tsd.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.attn_status_string(0) == b"ok"
+    assert lib.attn_status_string(1) == b"invalid argument"
+    assert lib.attn_status_string(2) == b"unsupported configuration"
+    assert lib.attn_status_string(3) == b"HIP error"
+    assert lib.attn_status_string(99) == b"unknown status"
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced: every call below fails validation
+
+
+def call_attn(lib, Q=FAKE, K=FAKE + (1 << 28), V=FAKE + (2 << 28), mask=0, vl=0, scale=0.125, O=FAKE + (3 << 28),
+              B=1, H=1, Nq=8, Nk=8, d=64, ind=BF16, outd=BF16):
+    P = ctypes.c_void_p
+    return lib.attn_fwd(P(Q), P(K), P(V), mask, P(vl), ctypes.c_float(scale), P(O), B, H, Nq, Nk, d, ind, outd,
+                        P(0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=0), EINVAL),
+    (dict(O=0), EINVAL),
+    (dict(K=0), EINVAL),
+    (dict(B=-1), EINVAL),
+    (dict(d=0), EINVAL),
+    (dict(mask=7), EINVAL),
+    (dict(ind=5), EINVAL),
+    (dict(scale=float("nan")), EINVAL),
+    (dict(scale=float("inf")), EINVAL),
+    (dict(mask=2, vl=0), EINVAL),
+    (dict(Q=FAKE + 2), EINVAL),
+    (dict(O=FAKE), EINVAL),                       # O aliases Q
+    (dict(scale=-1.0), EUNSUP),
+    (dict(d=32), EUNSUP),                         # bf16 needs 64 or 128
+    (dict(d=48, ind=F32, outd=F32), EUNSUP),
+    (dict(ind=F32, outd=BF16, d=64), EUNSUP),
+    (dict(mask=1, Nq=8, Nk=9), EUNSUP),
+])
+def test_attn_fwd_rejects(lib, kw, status):
+    assert call_attn(lib, **kw) == status
+    assert lib.attn_last_error() != b""
+
+
+def test_attn_fwd_empty_is_ok_without_gpu(lib):
+    # no output element: nothing is launched
+    assert call_attn(lib, Nq=0) == 0
+    assert call_attn(lib, B=0) == 0
+
+
+def call_mha(lib, X=FAKE, W=FAKE + (1 << 28), Wo=FAKE + (2 << 28), h=8, O=FAKE + (3 << 28), B=1, N=16, dm=512,
+             dt=BF16, ws=FAKE + (4 << 28), wsb=1 << 27):
+    P = ctypes.c_void_p
+    return lib.mha_fwd(P(X), P(W), P(Wo), h, P(O), B, N, dm, dt, P(ws), ctypes.c_size_t(wsb), P(0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=0), EINVAL),
+    (dict(ws=0), EINVAL),
+    (dict(h=0), EINVAL),
+    (dict(h=7), EINVAL),               # 512 % 7 != 0
+    (dict(wsb=10), EINVAL),
+    (dict(ws=FAKE + (4 << 28) + 16), EINVAL),  # workspace not 256-byte aligned
+    (dict(O=FAKE), EINVAL),             # output aliases X
+    (dict(dt=F32), EUNSUP),
+    (dict(h=16), EUNSUP),               # d_k = 32
+    (dict(dm=96, h=1), EUNSUP),         # d_k = 96
+])
+def test_mha_fwd_rejects(lib, kw, status):
+    assert call_mha(lib, **kw) == status
+
+
+def test_mha_workspace_bytes(lib):
+    assert lib.mha_workspace_bytes(4, 2048, 512, 8, BF16) == 4 * 4 * 2048 * 512 * 2
+    assert lib.mha_workspace_bytes(4, 2048, 512, 7, BF16) == 0
+    assert lib.mha_workspace_bytes(4, 2048, 512, 8, F32) == 0
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tsd.attn_fwd(q, q, q)
+    x = torch.zeros(1, 4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tsd.mha_fwd(x, torch.zeros(128, 384, dtype=torch.bfloat16), torch.zeros(128, 128, dtype=torch.bfloat16), 2)

@@ -1,0 +1,256 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the
+same seeded inputs, on an MI355X.
+
+Tolerances (max / mean absolute error against the float64 oracle):
+  float32 inputs:                       max <= 1e-5
+  bfloat16 inputs, f32 accumulation:    max <= 2e-2 and mean <= 2e-3
+Small and ragged shapes are compared element by element; the full-size
+workloads are compared on sampled query rows that the oracle computes one by
+one (rows are independent, so each sampled row is exact), plus properties
+that hold for every row at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16_MAX, TOL_BF16_MEAN = 2e-2, 2e-3
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import transformer_scaled_dot_amd as tsd
+
+    tsd.load_library()
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def gpu_attn(dev, q, k, v, mask="none", vl=None, scale=None, out_dtype=None):
+    import transformer_scaled_dot_amd as tsd
+
+    vl_t = torch.from_numpy(np.asarray(vl, dtype=np.int32)).to(dev) if vl is not None else None
+    od = {None: None, "f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
+    o = tsd.attn_fwd(q.torch(dev), k.torch(dev), v.torch(dev), mask=mask, valid_lens=vl_t, scale=scale,
+                     out_dtype=od)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64)
+
+
+def check(name, got, ref, dtype):
+    err = np.abs(got - ref)
+    mx, mean = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
+    say("%s: max abs err %.3e, mean %.3e, max|ref| %.3f" % (name, mx, mean, float(np.abs(ref).max()) if ref.size else 0))
+    assert np.all(np.isfinite(got)), "non-finite output"
+    if dtype == "f32":
+        assert mx <= TOL_F32, name
+    else:
+        assert mx <= TOL_BF16_MAX and mean <= TOL_BF16_MEAN, name
+
+
+def sample_rows(B, H, N, count, seed, tile=128):
+    """Flat row indices (b*H + h)*N + i: rows 0, 1, N-1 and both sides of
+    every tile edge of a few heads, plus seeded uniform rows."""
+    rng_rows = (synth.uniform01(seed, count) * (B * H * N)).astype(np.int64) % (B * H * N)
+    heads = (synth.uniform01(seed + 1, 4) * (B * H)).astype(np.int64) % (B * H)
+    edges = []
+    for bh in heads:
+        for e in list(range(0, N, tile)) + [1, N - 1]:
+            for i in (e - 1, e, e + 1):
+                if 0 <= i < N:
+                    edges.append(bh * N + i)
+    return np.unique(np.concatenate([rng_rows, np.asarray(edges, dtype=np.int64)]))
+
+
+# ---------------------------------------------------------------- float32 path
+
+def test_config1_f32_full(dev):
+    q, k, v, _ = synth.attn_inputs(1)
+    got = gpu_attn(dev, q, k, v)
+    check("C1 f32 [2,1,5,16]", got, oracle.attention(q.f64, k.f64, v.f64), "f32")
+
+
+def test_hand_example_f32(dev, golden_dir):
+    """The pages' 3-token example, zero-padded from d_k = 2 to 16 with the
+    scale held at 1/sqrt(2) (zeros add nothing to any product)."""
+    import json
+
+    g = json.load(open(golden_dir + "/hand_example.json", encoding="utf-8"))
+    X = np.zeros((1, 1, 3, 16), dtype=np.float32)
+    X[0, 0, :, :2] = np.asarray(g["X"], dtype=np.float32)
+    t = synth.Tensor(X.copy(), "f32", X.shape)
+    got = gpu_attn(dev, t, t, t, scale=1 / math.sqrt(2))
+    check("hand example f32", got, oracle.attention(X, X, X, scale=1 / math.sqrt(2)), "f32")
+    np.testing.assert_allclose(got[0, 0, :, :2], g["page4"]["outputs"], atol=g["page4"]["tol"])
+    np.testing.assert_allclose(got[0, 0, 2, :2], g["page1"]["row3_output"], atol=g["page1"]["tol"])
+    assert np.all(got[0, 0, :, 2:] == 0.0)
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("mask", ["none", "causal", "padding"])
+def test_f32_ragged(dev, d, mask):
+    N = 37 if d >= 64 else 70
+    q, k, v, _ = synth.attn_inputs(1, B=2, H=2, N=N, d=d)
+    vl = np.asarray([N // 3, N], dtype=np.int32)
+    got = gpu_attn(dev, q, k, v, mask=mask, vl=vl)
+    check("f32 d%d %s N%d" % (d, mask, N), got, oracle.attention(q.f64, k.f64, v.f64, mask=mask, valid_lens=vl), "f32")
+
+
+# ---------------------------------------------------------------- bf16 path
+
+SMALL = [(1, 1), (5, 5), (64, 64), (200, 200), (333, 333), (130, 77), (77, 300)]
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", ["none", "causal", "padding"])
+@pytest.mark.parametrize("nq,nk", SMALL)
+def test_bf16_ragged(dev, nq, nk, mask, d, out):
+    if mask == "causal" and nq != nk:
+        pytest.skip("causal is defined for seq_q == seq_k")
+    q, k, v, _ = synth.attn_inputs(2, B=2, H=3, N=nq, Nk=nk, d=d)
+    vl = np.asarray([max(1, nk // 2), nk + 5], dtype=np.int32)  # second one past the end: clamped
+    got = gpu_attn(dev, q, k, v, mask=mask, vl=vl, out_dtype=out)
+    ref = oracle.attention(q.f64, k.f64, v.f64, mask=mask, valid_lens=np.minimum(vl, nk))
+    check("bf16 [2,3,%d,%d] d%d %s out %s" % (nq, nk, d, mask, out), got, ref, "bf16")
+
+
+def test_config2_padding_full(dev):
+    q, k, v, vl = synth.attn_inputs(2)
+    say("C2 valid_lens", vl.tolist())
+    got = gpu_attn(dev, q, k, v, mask="padding", vl=vl)
+    check("C2 bf16 [8,8,512,64] padding", got, oracle.attention(q.f64, k.f64, v.f64, mask="padding", valid_lens=vl),
+          "bf16")
+
+
+def test_padding_masked_keys_never_reach_output(dev):
+    """Keys at or past valid_len may hold anything: the output is
+    bit-for-bit the same (weight exactly 0; the pages' e^{-inf} = 0)."""
+    q, k, v, vl = synth.attn_inputs(2, B=8, H=2, N=512)
+    o1 = gpu_attn(dev, q, k, v, mask="padding", vl=vl)
+    kr, vr = k.raw.copy(), v.raw.copy()
+    for b in range(8):
+        kr[b, :, vl[b]:] = synth.f32_to_bf16_bits(np.full(kr[b, :, vl[b]:].shape, 1e4, np.float32))
+        vr[b, :, vl[b]:] = synth.f32_to_bf16_bits(np.full(vr[b, :, vl[b]:].shape, -3e4, np.float32))
+    o2 = gpu_attn(dev, q, synth.Tensor(kr, "bf16", k.shape), synth.Tensor(vr, "bf16", v.shape), mask="padding", vl=vl)
+    assert np.array_equal(o1, o2)
+
+
+def test_causal_future_keys_never_reach_output(dev):
+    N = 700
+    q, k, v, _ = synth.attn_inputs(3, B=1, H=2, N=N, d=128)
+    o1 = gpu_attn(dev, q, k, v, mask="causal")
+    cut = 333
+    kr, vr = k.raw.copy(), v.raw.copy()
+    kr[:, :, cut:] = synth.f32_to_bf16_bits(np.full(kr[:, :, cut:].shape, 1e4, np.float32))
+    vr[:, :, cut:] = synth.f32_to_bf16_bits(np.full(vr[:, :, cut:].shape, -3e4, np.float32))
+    o2 = gpu_attn(dev, q, synth.Tensor(kr, "bf16", k.shape), synth.Tensor(vr, "bf16", v.shape), mask="causal")
+    assert np.array_equal(o1[:, :, :cut], o2[:, :, :cut])
+    # query 0 sees only key 0: its output is V[0] exactly
+    assert np.array_equal(o1[:, :, 0], v.f64[:, :, 0])
+
+
+def test_empty_and_degenerate(dev):
+    import transformer_scaled_dot_amd as tsd
+
+    # valid_len 0: no visible key, output exactly 0
+    q, k, v, _ = synth.attn_inputs(2, B=2, H=1, N=70, d=64)
+    got = gpu_attn(dev, q, k, v, mask="padding", vl=[0, 70])
+    assert np.all(got[0] == 0.0)
+    check("bf16 valid_len 0/70 other batch", got[1:], oracle.attention(q.f64[1:], k.f64[1:], v.f64[1:]), "bf16")
+    # scale 0: uniform weights over visible keys -> mean of those V rows
+    got = gpu_attn(dev, q, k, v, mask="causal", scale=0.0)
+    ref = np.cumsum(v.f64, axis=2) / np.arange(1, 71)[None, None, :, None]
+    check("bf16 causal scale 0 (prefix means)", got, ref, "bf16")
+    # seq_q = 0: nothing to do
+    z = torch.zeros(1, 1, 0, 64, dtype=torch.bfloat16, device=dev)
+    kk = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16, device=dev)
+    assert tsd.attn_fwd(z, kk, kk).shape == (1, 1, 0, 64)
+
+
+def test_config3_causal_full_size(dev):
+    """B4 H16 N4096 d128 causal, the launch the bench times: sampled rows
+    against the oracle, and every row's weights summing to one (V = 1)."""
+    q, k, v, _ = synth.attn_inputs(3)
+    B, H, N, d = q.shape
+    got = gpu_attn(dev, q, k, v, mask="causal").reshape(-1, d)
+    rows = sample_rows(B, H, N, 4096, seed=30)
+    say("C3: %d sampled rows" % rows.size)
+    ref = oracle.attention_rows_per_head(q.f32, k.f32, v.f32, rows, mask="causal")
+    check("C3 bf16 [4,16,4096,128] causal (sampled rows)", got[rows], ref, "bf16")
+    ones = synth.Tensor(synth.f32_to_bf16_bits(np.ones(v.shape, np.float32)), "bf16", v.shape)
+    o1 = gpu_attn(dev, q, k, ones, mask="causal", out_dtype="f32")
+    err = np.abs(o1 - 1.0)
+    say("C3 V=1: max |O-1| %.3e" % err.max())
+    assert err.max() <= 4e-3
+
+
+def test_config4_mha_full(dev):
+    import transformer_scaled_dot_amd as tsd
+
+    x, wqkv, wo = synth.mha_inputs(4)
+    y = tsd.mha_fwd(x.torch(dev), wqkv.torch(dev), wo.torch(dev), 8)
+    torch.cuda.synchronize()
+    got = y.float().cpu().numpy().astype(np.float64)
+    check("C4 mha bf16 [4,2048,512] h8", got, oracle.mha(x.f64, wqkv.f64, wo.f64, 8), "bf16")
+
+
+@pytest.mark.parametrize("B,N,dm,h", [(1, 96, 128, 2), (2, 77, 256, 2), (1, 130, 512, 8), (3, 33, 256, 4),
+                                      (1, 300, 768, 6)])
+def test_mha_shapes(dev, B, N, dm, h):
+    import transformer_scaled_dot_amd as tsd
+
+    x, wqkv, wo = synth.mha_inputs(4, B=B, N=N, d_model=dm)
+    y = tsd.mha_fwd(x.torch(dev), wqkv.torch(dev), wo.torch(dev), h)
+    torch.cuda.synchronize()
+    got = y.float().cpu().numpy().astype(np.float64)
+    check("mha bf16 [%d,%d,%d] h%d" % (B, N, dm, h), got, oracle.mha(x.f64, wqkv.f64, wo.f64, h), "bf16")
+
+
+def test_mha_identity_projection_hand_example(dev, golden_dir):
+    """W_QKV = [I | I | I], W_O = I: every head is attention on its own
+    64-column block of X (the split/concat order of the layer)."""
+    import transformer_scaled_dot_amd as tsd
+
+    B, N, h, dk = 1, 40, 2, 64
+    dm = h * dk
+    x = synth.normal_tensor(77, (B, N, dm), "bf16")
+    I = np.eye(dm, dtype=np.float32)
+    wqkv = synth.Tensor(synth.f32_to_bf16_bits(np.concatenate([I, I, I], axis=1)), "bf16", (dm, 3 * dm))
+    wo = synth.Tensor(synth.f32_to_bf16_bits(I), "bf16", (dm, dm))
+    y = tsd.mha_fwd(x.torch(dev), wqkv.torch(dev), wo.torch(dev), h)
+    torch.cuda.synchronize()
+    got = y.float().cpu().numpy().astype(np.float64)
+    check("mha identity projections", got, oracle.mha(x.f64, wqkv.f64, wo.f64, h), "bf16")
+
+
+def test_config5_long_context(dev):
+    """B1 H32 N32768 d128 causal, inputs x2: sampled rows. With a float32
+    output the full tolerance applies to every sampled element; with a bf16
+    output, elements with |O| >= 8 carry up to 2^-5 of output rounding alone,
+    so they are reported separately."""
+    q, k, v, _ = synth.attn_inputs(5)
+    B, H, N, d = q.shape
+    rows = sample_rows(B, H, N, 4096, seed=50)
+    say("C5: %d sampled rows" % rows.size)
+    ref = oracle.attention_rows_per_head(q.f32, k.f32, v.f32, rows, mask="causal")
+    got = gpu_attn(dev, q, k, v, mask="causal", out_dtype="f32").reshape(-1, d)
+    check("C5 bf16 [1,32,32768,128] x2 causal, f32 out (sampled rows)", got[rows], ref, "bf16")
+    del got
+    gotb = gpu_attn(dev, q, k, v, mask="causal").reshape(-1, d)[rows]
+    small = np.abs(ref) < 8
+    say("C5 bf16 out: %d of %d sampled elements have |O| >= 8" % ((~small).sum(), small.size))
+    check("C5 bf16 out, |O| < 8", gotb[small], ref[small], "bf16")
+    assert np.abs(gotb - ref).max() <= 2 ** -5 + TOL_BF16_MAX

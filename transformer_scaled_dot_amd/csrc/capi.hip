@@ -1,0 +1,170 @@
+// C ABI of the library (declared in include/tsd_attn.h): argument checks on
+// the host, then dispatch to the kernels' launchers. No device memory is
+// allocated here and no call synchronises.
+#include "tsd_attn.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+attn_status_t fail(attn_status_t st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+attn_status_t from_hip(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return ATTN_OK;
+    return fail(ATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return na && nb && x < y + nb && y < x + na;
+}
+
+size_t dtype_bytes(int32_t dt) { return dt == ATTN_F32 ? 4 : 2; }
+
+constexpr long long kI32Max = 0x7fffffffLL;
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_fwd(const void *Q, const void *K, const void *V, int32_t mask_kind, const int32_t *valid_lens,
+                       float scale, void *O, int32_t batch, int32_t heads, int32_t seq_q, int32_t seq_k,
+                       int32_t head_dim, int32_t in_dtype, int32_t out_dtype, void *stream)
+{
+    g_last_error[0] = '\0';
+    if (batch < 0 || heads < 0 || seq_q < 0 || seq_k < 0 || head_dim <= 0)
+        return fail(ATTN_EINVAL, "attn_fwd: negative size or head_dim <= 0 (batch=%d heads=%d seq_q=%d seq_k=%d "
+                                 "head_dim=%d)", batch, heads, seq_q, seq_k, head_dim);
+    if (mask_kind != ATTN_MASK_NONE && mask_kind != ATTN_MASK_CAUSAL && mask_kind != ATTN_MASK_PADDING)
+        return fail(ATTN_EINVAL, "attn_fwd: unknown mask_kind %d", mask_kind);
+    if ((in_dtype != ATTN_F32 && in_dtype != ATTN_BF16) || (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16))
+        return fail(ATTN_EINVAL, "attn_fwd: unknown dtype (in %d, out %d)", in_dtype, out_dtype);
+    if (!isfinite(scale)) return fail(ATTN_EINVAL, "attn_fwd: scale is not finite");
+    if (scale < 0.f) return fail(ATTN_EUNSUPPORTED, "attn_fwd: negative scale");
+    if (in_dtype == ATTN_BF16 && head_dim != 64 && head_dim != 128)
+        return fail(ATTN_EUNSUPPORTED, "attn_fwd: bf16 supports head_dim 64 or 128, got %d", head_dim);
+    if (in_dtype == ATTN_F32 && head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
+        return fail(ATTN_EUNSUPPORTED, "attn_fwd: f32 supports head_dim 16, 32, 64 or 128, got %d", head_dim);
+    if (in_dtype == ATTN_F32 && out_dtype != ATTN_F32)
+        return fail(ATTN_EUNSUPPORTED, "attn_fwd: f32 inputs need an f32 output");
+    if (mask_kind == ATTN_MASK_CAUSAL && seq_q != seq_k)
+        return fail(ATTN_EUNSUPPORTED, "attn_fwd: causal mask needs seq_q == seq_k (%d != %d)", seq_q, seq_k);
+    const long long bh = (long long)batch * heads;
+    if (bh > kI32Max) return fail(ATTN_EINVAL, "attn_fwd: batch*heads too large");
+
+    const size_t ib = dtype_bytes(in_dtype), ob = dtype_bytes(out_dtype);
+    const size_t nq = (size_t)bh * seq_q * head_dim, nk = (size_t)bh * seq_k * head_dim;
+    if (nq == 0) return ATTN_OK;  // no output element
+    if (!Q || !O) return fail(ATTN_EINVAL, "attn_fwd: null Q or O");
+    if (nk && (!K || !V)) return fail(ATTN_EINVAL, "attn_fwd: null K or V");
+    if (mask_kind == ATTN_MASK_PADDING && !valid_lens)
+        return fail(ATTN_EINVAL, "attn_fwd: padding mask needs valid_lens");
+    if (!aligned(Q, 16) || !aligned(O, 16) || (nk && (!aligned(K, 16) || !aligned(V, 16))))
+        return fail(ATTN_EINVAL, "attn_fwd: Q, K, V and O must be 16-byte aligned");
+    if (valid_lens && mask_kind == ATTN_MASK_PADDING && !aligned(valid_lens, 4))
+        return fail(ATTN_EINVAL, "attn_fwd: valid_lens must be 4-byte aligned");
+    if (overlaps(O, nq * ob, Q, nq * ib) || overlaps(O, nq * ob, K, nk * ib) || overlaps(O, nq * ob, V, nk * ib))
+        return fail(ATTN_EINVAL, "attn_fwd: O overlaps an input");
+
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (in_dtype == ATTN_BF16)
+        e = tsd::launch_attn_bf16(Q, K, V, mask_kind, valid_lens, scale, O, out_dtype == ATTN_F32, tsd::kOutBHND,
+                                  batch, heads, seq_q, seq_k, head_dim, s);
+    else
+        e = tsd::launch_attn_f32((const float *)Q, (const float *)K, (const float *)V, mask_kind, valid_lens, scale,
+                                 (float *)O, batch, heads, seq_q, seq_k, head_dim, s);
+    return from_hip(e, "attn_fwd launch");
+}
+
+static attn_status_t mha_check(int32_t batch, int32_t seq, int32_t d_model, int32_t h, int32_t dtype)
+{
+    if (batch < 0 || seq < 0 || d_model <= 0 || h <= 0)
+        return fail(ATTN_EINVAL, "mha_fwd: bad sizes (batch=%d seq=%d d_model=%d h=%d)", batch, seq, d_model, h);
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_EINVAL, "mha_fwd: unknown dtype %d", dtype);
+    if (d_model % h != 0) return fail(ATTN_EINVAL, "mha_fwd: d_model %% h != 0 (%d, %d)", d_model, h);
+    if (dtype != ATTN_BF16) return fail(ATTN_EUNSUPPORTED, "mha_fwd: only bf16 is supported");
+    const int dk = d_model / h;
+    if (dk != 64 && dk != 128) return fail(ATTN_EUNSUPPORTED, "mha_fwd: d_model/h must be 64 or 128, got %d", dk);
+    if (d_model % 64 != 0) return fail(ATTN_EUNSUPPORTED, "mha_fwd: d_model must be a multiple of 64");
+    if ((long long)batch * seq > kI32Max || (long long)batch * h > kI32Max)
+        return fail(ATTN_EINVAL, "mha_fwd: batch*seq too large");
+    return ATTN_OK;
+}
+
+size_t mha_workspace_bytes(int32_t batch, int32_t seq, int32_t d_model, int32_t h, int32_t dtype)
+{
+    char saved[sizeof g_last_error];
+    snprintf(saved, sizeof saved, "%s", g_last_error);
+    const attn_status_t st = mha_check(batch, seq, d_model, h, dtype);
+    snprintf(g_last_error, sizeof g_last_error, "%s", saved);
+    if (st != ATTN_OK) return 0;
+    const size_t tok = (size_t)batch * seq * d_model;
+    return (3 * tok + tok) * 2;  // q, k, v split into heads + concatenated head outputs, bf16
+}
+
+attn_status_t mha_fwd(const void *X, const void *W_qkv, const void *W_o, int32_t h, void *O, int32_t batch,
+                      int32_t seq, int32_t d_model, int32_t dtype, void *workspace, size_t workspace_bytes,
+                      void *stream)
+{
+    g_last_error[0] = '\0';
+    const attn_status_t st = mha_check(batch, seq, d_model, h, dtype);
+    if (st != ATTN_OK) return st;
+    const size_t tok = (size_t)batch * seq * d_model;
+    if (tok == 0) return ATTN_OK;
+    if (!X || !W_qkv || !W_o || !O || !workspace) return fail(ATTN_EINVAL, "mha_fwd: null pointer");
+    const size_t need = mha_workspace_bytes(batch, seq, d_model, h, dtype);
+    if (workspace_bytes < need)
+        return fail(ATTN_EINVAL, "mha_fwd: workspace of %zu bytes, need %zu", workspace_bytes, need);
+    if (!aligned(X, 16) || !aligned(W_qkv, 16) || !aligned(W_o, 16) || !aligned(O, 16) || !aligned(workspace, 256))
+        return fail(ATTN_EINVAL, "mha_fwd: tensors must be 16-byte aligned, workspace 256-byte aligned");
+    const size_t wb = (size_t)d_model * d_model * 2;
+    if (overlaps(O, tok * 2, X, tok * 2) || overlaps(O, tok * 2, W_qkv, 3 * wb) || overlaps(O, tok * 2, W_o, wb) ||
+        overlaps(workspace, need, X, tok * 2) || overlaps(workspace, need, O, tok * 2) ||
+        overlaps(workspace, need, W_qkv, 3 * wb) || overlaps(workspace, need, W_o, wb))
+        return fail(ATTN_EINVAL, "mha_fwd: output or workspace overlaps another buffer");
+
+    hipStream_t s = (hipStream_t)stream;
+    uint16_t *qkv = (uint16_t *)workspace;  // [3][batch][h][seq][dk]
+    uint16_t *ctx = qkv + 3 * tok;          // [batch][seq][h*dk]
+    const int dk = d_model / h;
+    hipError_t e = tsd::launch_gemm_bf16_qkv_split(X, W_qkv, qkv, batch, seq, d_model, h, s);
+    if (e != hipSuccess) return from_hip(e, "mha_fwd projection GEMM");
+    e = tsd::launch_attn_bf16(qkv, qkv + tok, qkv + 2 * tok, tsd::kMaskNone, nullptr, 1.0f / sqrtf((float)dk), ctx,
+                              0, tsd::kOutBNHD, batch, h, seq, seq, dk, s);
+    if (e != hipSuccess) return from_hip(e, "mha_fwd attention");
+    e = tsd::launch_gemm_bf16(ctx, W_o, O, batch * seq, d_model, d_model, s);
+    return from_hip(e, "mha_fwd output GEMM");
+}
+
+const char *attn_status_string(int32_t status)
+{
+    switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_EINVAL: return "invalid argument";
+    case ATTN_EUNSUPPORTED: return "unsupported configuration";
+    case ATTN_EHIP: return "HIP error";
+    default: return "unknown status";
+    }
+}
+
+const char *attn_last_error(void) { return g_last_error; }
+
+}  // extern "C"

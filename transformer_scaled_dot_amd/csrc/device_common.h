@@ -1,0 +1,69 @@
+// Device-side building blocks for gfx950 (CDNA4): vector types, bf16 MFMA,
+// LDS transpose reads and cross-half wavefront exchange.
+//
+// Lane layouts used throughout (wave64, l = lane, l32 = l % 32, hf = l / 32):
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//     A operand: lane holds A[l32][hf*8 + t], t = 0..7
+//     B operand: lane holds B[hf*8 + t][l32]
+//     D (16 f32): lane holds D[(r/4)*8 + hf*4 + r%4][l32], r = 0..15
+//   ds_read_b64_tr_b16 (per group of 16 lanes, i = l % 16):
+//     element t of lane i = the 16-bit word at (address of lane 4t + i/4) + (i%4)
+//     so 16 lanes that address a 4-row x 16-column block (4 words each) get
+//     one column each: lane i <- column i, rows 0..3.
+//   v_permlane32_swap(x, x): lanes < 32 get (x[l], x[l+32]), lanes >= 32 get
+//     (x[l-32], x[l]); max/sum of the pair combines a value with the same
+//     lane of the other half.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two transposed 4x4 reads make one 8-element MFMA operand.
+__device__ __forceinline__ bf16x8 lds_tr_pair(const uint16_t *lo, const uint16_t *hi)
+{
+    i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)lo);
+    i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)hi);
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    i16x8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, c);
+}
+
+// max / sum of a value with the same lane of the other 32-lane half
+__device__ __forceinline__ float half_swap_max(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float half_swap_sum(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace tsd

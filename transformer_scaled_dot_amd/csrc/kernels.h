@@ -1,0 +1,33 @@
+// Host-side launchers shared between the kernels and the C ABI layer.
+// Every launcher assumes its arguments were validated by the C ABI layer
+// (shapes, alignment, supported set) and only enqueues work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsd {
+
+enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskPadding = 2 };
+enum OutLayout { kOutBHND = 0, kOutBNHD = 1 };  // [B,H,N,D] or concatenated heads [B,N,H*D]
+
+// bf16 attention, head_dim 64 or 128, output bf16 (out_f32 = 0) or f32.
+hipError_t launch_attn_bf16(const void *Q, const void *K, const void *V, int mask, const int32_t *valid_lens,
+                            float scale, void *O, int out_f32, int out_layout, int B, int H, int Nq, int Nk, int D,
+                            hipStream_t stream);
+
+// f32 attention, head_dim 16, 32, 64 or 128, output f32, layout [B,H,N,D].
+hipError_t launch_attn_f32(const float *Q, const float *K, const float *V, int mask, const int32_t *valid_lens,
+                           float scale, float *O, int B, int H, int Nq, int Nk, int D, hipStream_t stream);
+
+// C = A[M,K] * B[K,N] in bf16 with f32 accumulation, bf16 output.
+// Plain epilogue: C row-major [M,N].
+hipError_t launch_gemm_bf16(const void *A, const void *Bm, void *C, int M, int N, int K, hipStream_t stream);
+
+// Projection epilogue: column n of the [M = batch*seq, 3*d_model] product is
+// written to qkv[which][b][head][t][c] with which = n / d_model,
+// head = (n % d_model) / dk, c = n % dk, b = m / seq, t = m % seq.
+hipError_t launch_gemm_bf16_qkv_split(const void *X, const void *Wqkv, void *qkv, int batch, int seq, int d_model,
+                                      int heads, hipStream_t stream);
+
+}  // namespace tsd
