@@ -1,0 +1,258 @@
+"""Throughput of the attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--extra]
+
+One step = one attn_fwd launch over the causal workload B=4, H=16, N=4096,
+d=128 in bf16 (inputs already resident in HBM; two buffer sets alternate so
+the 256 MB Infinity Cache cannot hold a step's whole working set). Prints
+ONE JSON line with TFLOP/s (FLOPs counted as 4*B*H*N_q*N_k*d, halved for the
+causal mask), the kernel's roofline position, and the CPU oracle timed on a
+bounded sample of the same workload.
+
+Other modes (for profiling): --copy-calibration runs one plain 256 MiB
+device copy, whose FETCH_SIZE / WRITE_SIZE counters calibrate the HBM-byte
+counters of the attention kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s + % of MI355X bf16 MFMA peak, B4 H16 N4096 d128 causal"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = dict(workload="sdpa_bf16_b4_h16_n4096_d128_causal", B=4, H=16, N=4096, d=128, mask="causal",
+                dtype="bf16", scale="1/sqrt(128)")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_causal_b4h16n4096d128_hbm_traffic.json")
+KERNEL_SOURCES = ["transformer_scaled_dot_amd/csrc/attn_fwd_bf16.hip", "transformer_scaled_dot_amd/csrc/device_common.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def attn_flops(B, H, Nq, Nk, d, causal):
+    f = 4.0 * B * H * Nq * Nk * d
+    return f / 2 if causal else f
+
+
+def hbm_traffic_per_launch():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE, encoding="utf-8") as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_launches(fn, nsteps, warmup):
+    """Warm up, then time exactly nsteps launches between two device
+    synchronisations with HIP events on the launching (current) stream."""
+    import torch
+
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(nsteps):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / nsteps, wall
+
+
+def bench_attention(dev, cfg_id, nsteps, warmup, mask, sets=2, out_dtype=None):
+    import torch
+
+    import synth
+    import transformer_scaled_dot_amd as tsd
+
+    q, k, v, vl = synth.attn_inputs(cfg_id)
+    B, H, N, d = q.shape
+    bufs = []
+    for s in range(sets):
+        bufs.append((q.torch(dev), k.torch(dev), v.torch(dev),
+                     torch.empty((B, H, N, d), dtype=out_dtype or torch.bfloat16, device=dev)))
+    vl_t = torch.from_numpy(vl).to(dev) if vl is not None else None
+    del q, k, v
+
+    def step(i):
+        qq, kk, vv, oo = bufs[i % sets]
+        tsd.attn_fwd(qq, kk, vv, mask=mask, valid_lens=vl_t, out=oo, out_dtype=oo.dtype)
+
+    ms, wall = time_launches(step, nsteps, warmup)
+    if mask == "padding":
+        flops = attn_flops(B, H, N, N, d, False)
+    else:
+        flops = attn_flops(B, H, N, N, d, mask == "causal")
+    return dict(ms=ms, wall=wall, flops=flops, shape=(B, H, N, d), valid_lens=vl)
+
+
+def bench_mha(dev, nsteps, warmup, sets=4):
+    import torch
+
+    import synth
+    import transformer_scaled_dot_amd as tsd
+
+    x, wqkv, wo = synth.mha_inputs(4)
+    B, N, dm = x.shape
+    h = synth.CONFIGS[4]["h"]
+    need = tsd.mha_workspace_bytes(B, N, dm, h)
+    bufs = [(x.torch(dev), wqkv.torch(dev), wo.torch(dev), torch.empty((B, N, dm), dtype=torch.bfloat16, device=dev),
+             torch.empty(need, dtype=torch.uint8, device=dev)) for _ in range(sets)]
+
+    def step(i):
+        xx, ww, wwo, oo, ws = bufs[i % sets]
+        tsd.mha_fwd(xx, ww, wwo, h, out=oo, workspace=ws)
+
+    ms, wall = time_launches(step, nsteps, warmup)
+    dk = dm // h
+    flops = 8.0 * B * N * dm * dm + 4.0 * B * h * N * N * dk
+    return dict(ms=ms, wall=wall, flops=flops)
+
+
+def cpu_baseline(target_s=15.0):
+    """The CPU oracle on whole heads of the benchmark workload (same seeded
+    inputs), as many heads as fit in about target_s seconds."""
+    import oracle
+    import synth
+
+    q, k, v, _ = synth.attn_inputs(3)
+    B, H, N, d = q.shape
+    qf, kf, vf = q.f32, k.f32, v.f32
+
+    def run(heads):
+        sel = [(i // H, i % H) for i in heads]
+        Q = np.stack([qf[b, h] for b, h in sel])[None].astype(np.float64)
+        K = np.stack([kf[b, h] for b, h in sel])[None].astype(np.float64)
+        V = np.stack([vf[b, h] for b, h in sel])[None].astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.attention(Q, K, V, mask="causal")
+        return time.perf_counter() - t0
+
+    t1 = run([0])
+    nheads = int(max(1, min(B * H - 1, round(target_s / max(t1, 1e-3)) - 1)))
+    t2 = run(list(range(1, 1 + nheads)))
+    total_heads, total_t = 1 + nheads, t1 + t2
+    flops = total_heads * attn_flops(1, 1, N, N, d, True)
+    threads = oracle.max_threads()
+    return {"value": flops / total_t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of the %d (batch, head) slices of the workload, all %d causal rows each, float64; %.1f s"
+                      % (total_heads, B * H, N, total_t)}
+
+
+def copy_calibration(dev, nbytes=256 << 20):
+    import torch
+
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra", action="store_true", help="also time the padding, multi-head and 32K workloads")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    import transformer_scaled_dot_amd as tsd
+
+    tsd.load_library()
+    if args.copy_calibration:
+        copy_calibration(dev)
+        return
+
+    r = bench_attention(dev, 3, args.steps, args.warmup, "causal")
+    tflops = r["flops"] / (r["ms"] * 1e-3) / 1e12
+    B, H, N, d = r["shape"]
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) Q, K, V (SplitMix64 + Box-Muller, rounded to bf16)",
+        "config": dict(WORKLOAD, parallelism="none (1 GPU)"),
+        "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": hbm_traffic_per_launch(),
+            "kernel": "attn_fwd_bf16_kernel<128, causal, bf16 out>",
+            "algorithmic_flops_per_launch": r["flops"],
+            "avg_launch_ms": round(r["ms"], 5),
+        },
+        "wall_s_timed_region": round(r["wall"], 4),
+    }
+    if args.extra:
+        extra = {}
+        r2 = bench_attention(dev, 2, args.steps, args.warmup, "padding", sets=16)
+        B2, H2, N2, d2 = r2["shape"]
+        L = r2["valid_lens"].astype(np.float64)
+        alg_flops = 4.0 * H2 * d2 * N2 * L.sum()
+        hbm = 2.0 * B2 * H2 * N2 * d2 * 2 + 2.0 * H2 * d2 * 2 * L.sum()  # Q, O + valid K, V rows
+        extra["C2_padding_b8h8n512d64"] = {
+            "ms": round(r2["ms"], 5), "tflops_metric": round(r2["flops"] / r2["ms"] / 1e9, 2),
+            "tflops_valid_keys": round(alg_flops / r2["ms"] / 1e9, 2),
+            "hbm_gbs_algorithmic": round(hbm / r2["ms"] / 1e6, 1),
+            "hbm_frac": round(hbm / r2["ms"] / 1e6 / PEAK_HBM_GBS, 4)}
+        r4 = bench_mha(dev, args.steps, args.warmup)
+        extra["C4_mha_b4n2048dm512h8"] = {"ms": round(r4["ms"], 5),
+                                          "tflops": round(r4["flops"] / r4["ms"] / 1e9, 2)}
+        r5 = bench_attention(dev, 5, max(5, args.steps // 5), 2, "causal", sets=1)
+        extra["C5_causal_b1h32n32768d128"] = {"ms": round(r5["ms"], 4),
+                                              "tflops": round(r5["flops"] / r5["ms"] / 1e9, 2)}
+        out["extra"] = extra
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -65,8 +65,15 @@ def _load(path: str | None = None):
         lib.oracle_attn_rows.restype = ctypes.c_int
         lib.oracle_mha.argtypes = [P, P, P, I64, I64, I64, I64, P, ctypes.c_int]
         lib.oracle_mha.restype = ctypes.c_int
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = ctypes.c_int
         _libs[path] = lib
     return _libs[path]
+
+
+def max_threads(lib=None) -> int:
+    """Number of host threads an oracle call uses."""
+    return int(_load(lib).oracle_max_threads())
 
 
 def _f64(a) -> np.ndarray:

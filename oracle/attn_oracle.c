@@ -115,6 +115,9 @@ static int set_threads(int nthreads)
 #endif
 }
 
+/* Threads an oracle call uses (OpenMP's current maximum). */
+int oracle_max_threads(void) { return set_threads(0); }
+
 /*
  * Full attention. Q [B,H,Nq,d], K [B,H,Nk,d], V [B,H,Nk,dv] row-major
  * float64; O [B,H,Nq,dv]; A optional [B,H,Nq,Nk]. valid_lens [B] is read

@@ -36,12 +36,117 @@ namespace {
 
 constexpr int kBlockN = 64;  // keys per LDS tile
 
+// LDS tiles are dense [64 keys][D] bf16 with the 16-byte chunks of each row
+// XOR-swizzled: element (r, e) lives at r*D + 8*((e/8) ^ swz(r)) + e%8.
+// The swizzle makes both reads conflict-free at the 2-cycle minimum:
+//  - K reads (16 B per lane, 16 consecutive rows, same column chunk) land
+//    on 16 distinct bank groups;
+//  - V transposed reads (8 rows x 64 B per wave) spread over all banks.
 template <int D>
-struct AttnLds {
-    static constexpr int kStrideK = D + 8;   // K row pitch (elements): rows shift by 4 banks
-    static constexpr int kStrideV = D + 16;  // V row pitch: 4 rows of one tr-read hit disjoint banks
-    static constexpr int kTile = kBlockN * kStrideK + kBlockN * kStrideV;
-};
+__device__ __forceinline__ int swz(int r)
+{
+    if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);  // 16 chunks per 256-byte row
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);         // 8 chunks per 128-byte row
+}
+
+template <int D>
+__device__ __forceinline__ int swz_off(int r, int e)
+{
+    return r * D + ((((e >> 3) ^ swz<D>(r))) << 3) + (e & 7);
+}
+
+// One 64-key tile for one wave (32 query rows): S^T = K Q^T, mask, online
+// softmax update, O^T += V^T P^T.
+template <int D, int MASK>
+__device__ __forceinline__ void attend_tile(const uint16_t *sK, const uint16_t *sV, const bf16x8 (&qreg)[D / 16],
+                                            f32x16 (&acc)[D / 32], float &m_run, float &l_run, float c_log2,
+                                            int k0, int kv_len, int qrow, int lane, bool need_mask)
+{
+    constexpr int KS = D / 16, DB = D / 32;
+    const int l32 = lane & 31, hf = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
+
+    // ---- S^T = K Q^T (64 keys x 32 queries) ----
+    f32x16 s[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[jb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const bf16x8 a = *(const bf16x8 *)(sK + swz_off<D>(jb * 32 + l32, ks * 16 + hf * 8));
+            s[jb] = mfma32x32x16(a, qreg[ks], s[jb]);
+        }
+
+    // ---- mask: key j hidden from this lane's row when j >= kv_len or (causal) j > qrow ----
+    if (need_mask) {
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + jb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
+                const bool vis = key < kv_len && (MASK != kMaskCausal || key <= qrow);
+                if (!vis) s[jb][r] = -INFINITY;
+            }
+    }
+
+    // ---- online softmax (base 2; scale * log2(e) folded into c_log2 > 0, so a
+    //      masked score -inf gives exactly exp2(-inf) = 0) ----
+    float mx = s[0][0];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
+    mx = half_swap_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float mc = m_use * c_log2;
+    const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_use) * c_log2);
+    float lsum = 0.f;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(fmaf(s[jb][r], c_log2, -mc));
+            s[jb][r] = p;
+            lsum += p;
+        }
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
+    }
+
+    // ---- P in bf16 as B operands, 16 keys per MFMA ----
+    bf16x8 pb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int jb = c >> 1, r0 = (c & 1) * 8;
+        u32x4 w;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = pack_bf16x2(s[jb][r0 + 2 * u], s[jb][r0 + 2 * u + 1]);
+        pb[c] = __builtin_bit_cast(bf16x8, w);
+    }
+
+    // ---- O^T += V^T P^T ----
+    // MFMA k slot hf*8 + t of chunk c is key c*16 + (t/4)*8 + hf*4 + t%4, the
+    // order in which the S accumulator holds the keys; a transposed read of
+    // rows c*16 + hf*4 + (0..3) (+8) gives exactly those 8 keys per column.
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int row = c * 16 + hf * 4 + (i16 >> 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int col = db * 32 + (g16 & 1) * 16 + 4 * (i16 & 3);
+            const bf16x8 a = lds_tr_pair(sV + swz_off<D>(row, col), sV + swz_off<D>(row + 8, col));
+            acc[db] = mfma32x32x16(a, pb[c], acc[db]);
+        }
+    }
+}
 
 template <int D, int MASK, bool OUT_F32, int OLAYOUT, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
@@ -50,16 +155,17 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     int num_qtiles, int BH)
 {
     constexpr int BM = WAVES * 32;
-    constexpr int NT = WAVES * 64;
     constexpr int KS = D / 16;  // k-steps of the Q K^T contraction
     constexpr int DB = D / 32;  // 32-row blocks of O^T
-    constexpr int SK = AttnLds<D>::kStrideK, SV = AttnLds<D>::kStrideV, TILE = AttnLds<D>::kTile;
-    constexpr int CH = kBlockN * D / 8 / NT;  // 16-byte chunks per thread per tensor per tile
-    static_assert(kBlockN * D / 8 % NT == 0, "tile must split evenly over the workgroup");
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TILE];
+    constexpr int TILE = kBlockN * D;
+    constexpr int CPR = D / 8;                                  // 16-byte chunks per row
+    constexpr int CH = kBlockN * CPR / (WAVES * 64);            // chunk loads per lane per tensor per tile
+    static_assert(kBlockN * CPR % (WAVES * 64) == 0, "tile must split evenly over the workgroup");
+    // two buffers, each [K tile | V tile]
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, hf = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
+    const int l32 = lane & 31, hf = lane >> 5;
 
     // q-tile-major order: the q-tiles of one head are BH ids apart, which
     // lands them on the same XCD (and L2) when BH is a multiple of 8
@@ -102,138 +208,44 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
         for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    // global -> registers for one tile; keys at or past kv_end are never
-    // visible to any row of this workgroup and are not read (zero fill)
-    u32x4 kreg[CH], vreg[CH];
-    auto load_tile = [&](int t) {
+    // Global -> LDS without registers (global_load_lds_dwordx4): load j of
+    // this wave fills the 64 consecutive LDS chunks [(j*WAVES + wave)*64, +64)
+    // and lane i fetches the global chunk that the swizzle puts in slot i.
+    // Rows at or past kv_end are never visible to this workgroup: they are
+    // not read; the last valid row is fetched in their place (its weight is 0).
+    auto issue_tile = [&](int t, uint16_t *sK, uint16_t *sV) {
         const int k0 = t * kBlockN;
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + i * NT;
-            const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-            const int key = k0 + row;
-            if (key < kv_end) {
-                kreg[i] = *(const u32x4 *)(Kh + (size_t)key * D + col);
-                vreg[i] = *(const u32x4 *)(Vh + (size_t)key * D + col);
-            } else {
-                kreg[i] = u32x4{0u, 0u, 0u, 0u};
-                vreg[i] = u32x4{0u, 0u, 0u, 0u};
-            }
+        for (int j = 0; j < CH; ++j) {
+            const int slot = (j * WAVES + wave) * 64;
+            const int c = slot + lane;
+            const int r = c / CPR, x = c % CPR;
+            const int key = min(k0 + r, kv_end - 1);
+            const size_t g = (size_t)key * D + ((x ^ swz<D>(r)) << 3);
+            __builtin_amdgcn_global_load_lds(Kh + g, sK + slot * 8, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(Vh + g, sV + slot * 8, 16, 0, 0);
         }
     };
-    auto store_tile = [&](int buf) {
-        uint16_t *Ks = smem + buf * TILE;
-        uint16_t *Vs = Ks + kBlockN * SK;
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + i * NT;
-            const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-            *(u32x4 *)(Ks + row * SK + col) = kreg[i];
-            *(u32x4 *)(Vs + row * SV + col) = vreg[i];
-        }
-    };
+    // s_waitcnt vmcnt(0): the tile's LDS writes have landed
+    auto wait_tile = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
-    if (ntiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
+    if (ntiles > 0) issue_tile(0, smem, smem + TILE);
+    wait_tile();
     __syncthreads();
 
     const int qmin_w = q0 + wave * 32, qmax_w = qmin_w + 31;
     for (int t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles) load_tile(t + 1);
+        uint16_t *cur = smem + (t & 1) * 2 * TILE;
+        uint16_t *nxt = smem + ((t + 1) & 1) * 2 * TILE;
+        if (t + 1 < ntiles) issue_tile(t + 1, nxt, nxt + TILE);
         const int k0 = t * kBlockN;
-        const uint16_t *Ks = smem + (t & 1) * TILE;
-        const uint16_t *Vs = Ks + kBlockN * SK;
         const bool skip = (MASK == kMaskCausal) && (k0 > qmax_w);
         if (!skip) {
             const bool need_mask =
                 (k0 + kBlockN > kv_len) || (MASK == kMaskCausal && k0 + kBlockN - 1 > qmin_w);
-
-            // ---- S^T = K Q^T (64 keys x 32 queries per wave) ----
-            f32x16 s[2];
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[jb][r] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb) {
-                    const bf16x8 a = *(const bf16x8 *)(Ks + (jb * 32 + l32) * SK + ks * 16 + hf * 8);
-                    s[jb] = mfma32x32x16(a, qreg[ks], s[jb]);
-                }
-
-            // ---- mask: key j of this lane's row is hidden when j >= kv_len or (causal) j > qrow ----
-            if (need_mask) {
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + jb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-                        const bool vis = key < kv_len && (MASK != kMaskCausal || key <= qrow);
-                        if (!vis) s[jb][r] = -INFINITY;
-                    }
-            }
-
-            // ---- online softmax update (base 2, scale folded into c_log2) ----
-            float mx = -INFINITY;
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
-            mx = half_swap_max(mx);
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float mc = m_use * c_log2;
-            const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_use) * c_log2);
-            float lsum = 0.f;
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p = fast_exp2(fmaf(s[jb][r], c_log2, -mc));
-                    if (need_mask) p = (s[jb][r] == -INFINITY) ? 0.f : p;
-                    s[jb][r] = p;
-                    lsum += p;
-                }
-            l_run = l_run * alpha + lsum;
-            m_run = m_new;
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-                for (int i = 0; i < DB; ++i)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
-            }
-
-            // ---- P (bf16) as B operands, 16 keys per MFMA ----
-            bf16x8 pb[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int jb = c >> 1, r0 = (c & 1) * 8;
-                u32x4 w;
-                w[0] = pack_bf16x2(s[jb][r0 + 0], s[jb][r0 + 1]);
-                w[1] = pack_bf16x2(s[jb][r0 + 2], s[jb][r0 + 3]);
-                w[2] = pack_bf16x2(s[jb][r0 + 4], s[jb][r0 + 5]);
-                w[3] = pack_bf16x2(s[jb][r0 + 6], s[jb][r0 + 7]);
-                pb[c] = __builtin_bit_cast(bf16x8, w);
-            }
-
-            // ---- O^T += V^T P^T ----
-            // MFMA k slot hf*8 + t of chunk c is key c*16 + (t/4)*8 + hf*4 + t%4,
-            // the order in which the S accumulator holds the keys
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int key_lo = c * 16 + hf * 4 + (i16 >> 2);
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const int col = db * 32 + (g16 & 1) * 16 + 4 * (i16 & 3);
-                    const bf16x8 a = lds_tr_pair(Vs + key_lo * SV + col, Vs + (key_lo + 8) * SV + col);
-                    acc[db] = mfma32x32x16(a, pb[c], acc[db]);
-                }
-            }
+            attend_tile<D, MASK>(cur, cur + TILE, qreg, acc, m_run, l_run, c_log2, k0, kv_len, qrow, lane, need_mask);
         }
-        if (t + 1 < ntiles) store_tile((t + 1) & 1);
+        wait_tile();
         __syncthreads();
     }
 
@@ -274,7 +286,10 @@ hipError_t launch_variant(const void *Q, const void *K, const void *V, const int
     const long long grid = (long long)num_qtiles * BH;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const float c_log2 = scale * 1.4426950408889634f;  // exp(x) = exp2(x * log2(e))
+    // exp(x) = exp2(x * log2(e)). The kernel needs c_log2 > 0 so that masked
+    // scores (-inf) map to weight 0 without a select; below 1e-30 every
+    // visible exp2 argument rounds to 0 anyway, which is the scale = 0 result.
+    const float c_log2 = fmaxf(scale * 1.4426950408889634f, 1e-30f);
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, MASK, OUT_F32, OLAYOUT, WAVES>), dim3((unsigned)grid),
                        dim3(WAVES * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
                        valid_lens, c_log2, O, H, Nq, Nk, num_qtiles, BH);
