@@ -31,6 +31,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace tsd {
 namespace {
 
@@ -55,29 +57,67 @@ __device__ __forceinline__ int swz_off(int r, int e)
     return r * D + ((((e >> 3) ^ swz<D>(r))) << 3) + (e & 7);
 }
 
+// Per-lane LDS byte offsets used by every tile (buffer and key-chunk offsets
+// are added as instruction immediates).
+template <int D>
+struct TileAddrs {
+    uint32_t k[D / 16];      // K read (A operand of S^T) for k-step ks, key block 0
+    uint32_t v[D / 32][2];   // V transposed read for output block db, rows +0 / +8, key chunk 0
+};
+
+template <int D>
+__device__ __forceinline__ TileAddrs<D> tile_addrs(int lane)
+{
+    const int l32 = lane & 31, hf = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
+    TileAddrs<D> a;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) a.k[ks] = 2 * swz_off<D>(l32, ks * 16 + hf * 8);
+    const int row = hf * 4 + (i16 >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        const int col = db * 32 + (g16 & 1) * 16 + 4 * (i16 & 3);
+        a.v[db][0] = 2 * swz_off<D>(row, col);
+        a.v[db][1] = 2 * swz_off<D>(row + 8, col);
+    }
+    return a;
+}
+
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_read_b128(const uint8_t *base, uint32_t addr)
+{
+    return *(const bf16x8 *)(base + addr + OFF);
+}
+
 // One 64-key tile for one wave (32 query rows): S^T = K Q^T, mask, online
-// softmax update, O^T += V^T P^T.
-template <int D, int MASK>
-__device__ __forceinline__ void attend_tile(const uint16_t *sK, const uint16_t *sV, const bf16x8 (&qreg)[D / 16],
+// softmax update, O^T += V^T P^T. KOFF/VOFF: byte offsets of the K and V
+// tiles in LDS (compile-time, so they fold into instruction immediates).
+template <int D, int MASK, int KOFF, int VOFF>
+__device__ __forceinline__ void attend_tile(const uint8_t *lds, const TileAddrs<D> &ad, const bf16x8 (&qreg)[D / 16],
                                             f32x16 (&acc)[D / 32], float &m_run, float &l_run, float c_log2,
                                             int k0, int kv_len, int qrow, int lane, bool need_mask)
 {
     constexpr int KS = D / 16, DB = D / 32;
-    const int l32 = lane & 31, hf = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
+    const int hf = lane >> 5;
 
-    // ---- S^T = K Q^T (64 keys x 32 queries) ----
+    // ---- S^T = K Q^T (64 keys x 32 queries); K operands fetched one k-step ahead ----
     f32x16 s[2];
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[jb][r] = 0.f;
+    bf16x8 ka[2][2];
+    ka[0][0] = *(const bf16x8 *)(lds + ad.k[0] + KOFF);
+    ka[0][1] = *(const bf16x8 *)(lds + ad.k[0] + KOFF + 32 * D * 2);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-            const bf16x8 a = *(const bf16x8 *)(sK + swz_off<D>(jb * 32 + l32, ks * 16 + hf * 8));
-            s[jb] = mfma32x32x16(a, qreg[ks], s[jb]);
+    for (int ks = 0; ks < KS; ++ks) {
+        const int cur = ks & 1, nxt = cur ^ 1;
+        if (ks + 1 < KS) {
+            ka[nxt][0] = *(const bf16x8 *)(lds + ad.k[ks + 1] + KOFF);
+            ka[nxt][1] = *(const bf16x8 *)(lds + ad.k[ks + 1] + KOFF + 32 * D * 2);
         }
+        s[0] = mfma32x32x16(ka[cur][0], qreg[ks], s[0]);
+        s[1] = mfma32x32x16(ka[cur][1], qreg[ks], s[1]);
+    }
 
     // ---- mask: key j hidden from this lane's row when j >= kv_len or (causal) j > qrow ----
     if (need_mask) {
@@ -138,11 +178,11 @@ __device__ __forceinline__ void attend_tile(const uint16_t *sK, const uint16_t *
     // rows c*16 + hf*4 + (0..3) (+8) gives exactly those 8 keys per column.
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        const int row = c * 16 + hf * 4 + (i16 >> 2);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const int col = db * 32 + (g16 & 1) * 16 + 4 * (i16 & 3);
-            const bf16x8 a = lds_tr_pair(sV + swz_off<D>(row, col), sV + swz_off<D>(row + 8, col));
+            const uint8_t *p0 = lds + ad.v[db][0] + VOFF + c * 16 * D * 2;
+            const uint8_t *p1 = lds + ad.v[db][1] + VOFF + c * 16 * D * 2;
+            const bf16x8 a = lds_tr_pair((const uint16_t *)p0, (const uint16_t *)p1);
             acc[db] = mfma32x32x16(a, pb[c], acc[db]);
         }
     }
@@ -157,12 +197,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     constexpr int BM = WAVES * 32;
     constexpr int KS = D / 16;  // k-steps of the Q K^T contraction
     constexpr int DB = D / 32;  // 32-row blocks of O^T
-    constexpr int TILE = kBlockN * D;
+    constexpr int TILE_B = kBlockN * D * 2;                     // bytes of one K (or V) tile
     constexpr int CPR = D / 8;                                  // 16-byte chunks per row
     constexpr int CH = kBlockN * CPR / (WAVES * 64);            // chunk loads per lane per tensor per tile
     static_assert(kBlockN * CPR % (WAVES * 64) == 0, "tile must split evenly over the workgroup");
-    // two buffers, each [K tile | V tile]
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
+    static_assert(4 * TILE_B <= 65536, "buffer offsets must fit LDS instruction immediates");
+    // buffer 0 = [K | V] at bytes [0, 2*TILE_B), buffer 1 at [2*TILE_B, 4*TILE_B)
+    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_B];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
@@ -208,45 +249,64 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
         for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    // Global -> LDS without registers (global_load_lds_dwordx4): load j of
-    // this wave fills the 64 consecutive LDS chunks [(j*WAVES + wave)*64, +64)
-    // and lane i fetches the global chunk that the swizzle puts in slot i.
-    // Rows at or past kv_end are never visible to this workgroup: they are
-    // not read; the last valid row is fetched in their place (its weight is 0).
-    auto issue_tile = [&](int t, uint16_t *sK, uint16_t *sV) {
+    // Global -> LDS without registers: DMA j of this wave fills the 64
+    // consecutive LDS chunks [(j*WAVES + wave)*64, +64) of a tile; lane i
+    // fetches the global chunk that the swizzle puts in slot i. The per-lane
+    // byte offset within the tile's rows is fixed; the tile's first key moves
+    // the (uniform) base pointer. Rows at or past kv_end are never visible to
+    // this workgroup: they are not read; the last valid row is fetched in
+    // their place (its weight is exactly 0).
+    uint32_t voff[CH];
+    int drow[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        const int c = (j * WAVES + wave) * 64 + lane;
+        const int r = c / CPR, x = c % CPR;
+        drow[j] = r;
+        voff[j] = (uint32_t)(r * D + ((x ^ swz<D>(r)) << 3)) * 2;
+    }
+    const uint32_t lds0 = lds_addr(smem);
+    auto issue_tile = [&](int t, uint32_t buf_off) {
         const int k0 = t * kBlockN;
+        const uint16_t *kb = Kh + (size_t)k0 * D;
+        const uint16_t *vb = Vh + (size_t)k0 * D;
+        const bool tail = k0 + kBlockN > kv_end;
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
-            const int slot = (j * WAVES + wave) * 64;
-            const int c = slot + lane;
-            const int r = c / CPR, x = c % CPR;
-            const int key = min(k0 + r, kv_end - 1);
-            const size_t g = (size_t)key * D + ((x ^ swz<D>(r)) << 3);
-            __builtin_amdgcn_global_load_lds(Kh + g, sK + slot * 8, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(Vh + g, sV + slot * 8, 16, 0, 0);
+            uint32_t off = voff[j];
+            if (tail) {
+                const int r = min(drow[j], kv_end - 1 - k0);
+                off = off - (uint32_t)(drow[j] - r) * (D * 2);
+            }
+            const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + buf_off + (j * WAVES + wave) * 1024);
+            lds_dma16(dst, kb, off);
+            lds_dma16(dst + TILE_B, vb, off);
         }
     };
-    // s_waitcnt vmcnt(0): the tile's LDS writes have landed
-    auto wait_tile = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
-    if (ntiles > 0) issue_tile(0, smem, smem + TILE);
-    wait_tile();
+    const TileAddrs<D> ad = tile_addrs<D>(lane);
+    if (ntiles > 0) issue_tile(0, 0);
+    wait_vmcnt0();
     __syncthreads();
 
     const int qmin_w = q0 + wave * 32, qmax_w = qmin_w + 31;
-    for (int t = 0; t < ntiles; ++t) {
-        uint16_t *cur = smem + (t & 1) * 2 * TILE;
-        uint16_t *nxt = smem + ((t + 1) & 1) * 2 * TILE;
-        if (t + 1 < ntiles) issue_tile(t + 1, nxt, nxt + TILE);
+    auto step = [&](int t, auto buf) {
+        constexpr int B = decltype(buf)::value;
+        if (t + 1 < ntiles) issue_tile(t + 1, (B ^ 1) * 2 * TILE_B);
         const int k0 = t * kBlockN;
         const bool skip = (MASK == kMaskCausal) && (k0 > qmax_w);
         if (!skip) {
             const bool need_mask =
                 (k0 + kBlockN > kv_len) || (MASK == kMaskCausal && k0 + kBlockN - 1 > qmin_w);
-            attend_tile<D, MASK>(cur, cur + TILE, qreg, acc, m_run, l_run, c_log2, k0, kv_len, qrow, lane, need_mask);
+            attend_tile<D, MASK, B * 2 * TILE_B, B * 2 * TILE_B + TILE_B>(smem, ad, qreg, acc, m_run, l_run, c_log2,
+                                                                          k0, kv_len, qrow, lane, need_mask);
         }
-        wait_tile();
+        wait_vmcnt0();
         __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, std::integral_constant<int, 0>());
+        if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>());
     }
 
     // ---- epilogue: O = O_acc / l (0 for a row with no visible key) ----

@@ -68,4 +68,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Asynchronous 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4):
+// lane i reads base + voff (bytes) and writes LDS bytes
+// [lds + 16*i, lds + 16*i + 16). `lds` and `base` must be wave-uniform.
+// Completion is tracked by vmcnt only: wait with s_waitcnt vmcnt(0) before a
+// barrier that publishes the data. Written as inline asm so that the
+// compiler, which cannot tell which LDS buffer a DMA targets, does not
+// serialise unrelated LDS reads behind it. M0 is set here and is not used by
+// compiler-generated code in the kernels that call this; the s_nop covers
+// the M0-write -> LDS-DMA hazard.
+__device__ __forceinline__ void lds_dma16(uint32_t lds, const void *base, uint32_t voff)
+{
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds), "v"(voff), "s"(base)
+                 : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// LDS byte address of a __shared__ object (the M0 / ds address space).
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // s_waitcnt vmcnt(0)
+
 }  // namespace tsd
