@@ -10,11 +10,14 @@
 // Online Softmax): when the running max moves from m to m', the partial
 // sum and the partial output are rescaled by e^{m - m'}.
 //
-// Work decomposition (one workgroup = WAVES wavefronts = WAVES*32 query
-// rows of one head; each wave owns 32 query rows):
+// Work decomposition (one workgroup = WAVES wavefronts of QB*32 query rows
+// each, all of one head; the 128-wide head uses QB = 2, so every K or V
+// operand read from LDS feeds two MFMAs):
 //   * Q^T stays in registers as the B operand of v_mfma_f32_32x32x16_bf16.
-//   * K and V tiles (64 keys) are staged through LDS, double buffered: the
-//     global loads of tile t+1 are in flight while tile t is computed.
+//   * K and V tiles (64 keys) go HBM -> LDS by DMA (no staging registers),
+//     double buffered, while the previous tile is computed.
+//   * Software pipeline per wave: the MFMAs of S(t+1) are issued together
+//     with the exponentials of S(t), then P(t).V(t) is accumulated.
 //   * S^T = K Q^T: the accumulator puts one query per lane (lane % 32) and
 //     16 keys per lane, so the row max/sum are 32 in-lane values plus one
 //     exchange with the other half-wave (v_permlane32_swap).
@@ -36,7 +39,12 @@
 namespace tsd {
 namespace {
 
-constexpr int kBlockN = 64;  // keys per LDS tile
+constexpr int kBlockN = 64;            // keys per LDS tile
+constexpr float kRescaleSlack = 8.f;    // log2 units the reference max may lag the true max
+#ifndef TSD_QB128
+#define TSD_QB128 1
+#endif
+constexpr int kQB128 = TSD_QB128;       // query blocks of 32 rows per wave for 128-wide heads
 
 // LDS tiles are dense [64 keys][D] bf16 with the 16-byte chunks of each row
 // XOR-swizzled: element (r, e) lives at r*D + 8*((e/8) ^ swz(r)) + e%8.
@@ -82,128 +90,176 @@ __device__ __forceinline__ TileAddrs<D> tile_addrs(int lane)
     return a;
 }
 
-template <int OFF>
-__device__ __forceinline__ bf16x8 lds_read_b128(const uint8_t *base, uint32_t addr)
+// S^T = K Q^T for one 64-key tile and QB blocks of 32 queries: s[qb][jb]
+// holds keys jb*32.. of query block qb. KOFF: byte offset of the K tile in
+// LDS (compile-time, folded into immediates).
+template <int D, int QB, int KOFF, bool ASM>
+__device__ __forceinline__ void scores(const uint8_t *lds, const TileAddrs<D> &ad, const bf16x8 (&qreg)[QB][D / 16],
+                                       f32x16 (&s)[QB][2])
 {
-    return *(const bf16x8 *)(base + addr + OFF);
-}
-
-// One 64-key tile for one wave (32 query rows): S^T = K Q^T, mask, online
-// softmax update, O^T += V^T P^T. KOFF/VOFF: byte offsets of the K and V
-// tiles in LDS (compile-time, so they fold into instruction immediates).
-template <int D, int MASK, int KOFF, int VOFF>
-__device__ __forceinline__ void attend_tile(const uint8_t *lds, const TileAddrs<D> &ad, const bf16x8 (&qreg)[D / 16],
-                                            f32x16 (&acc)[D / 32], float &m_run, float &l_run, float c_log2,
-                                            int k0, int kv_len, int qrow, int lane, bool need_mask)
-{
-    constexpr int KS = D / 16, DB = D / 32;
-    const int hf = lane >> 5;
-
-    // ---- S^T = K Q^T (64 keys x 32 queries); K operands fetched one k-step ahead ----
-    f32x16 s[2];
+    constexpr int KS = D / 16;
+    if constexpr (ASM) {
+        static_assert(QB == 2, "the asm path holds two query blocks");
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 k0 = *(const bf16x8 *)(lds + ad.k[ks] + KOFF);
+            const bf16x8 k1 = *(const bf16x8 *)(lds + ad.k[ks] + KOFF + 32 * D * 2);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[jb][r] = 0.f;
-    bf16x8 ka[2][2];
-    ka[0][0] = *(const bf16x8 *)(lds + ad.k[0] + KOFF);
-    ka[0][1] = *(const bf16x8 *)(lds + ad.k[0] + KOFF + 32 * D * 2);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const int cur = ks & 1, nxt = cur ^ 1;
-        if (ks + 1 < KS) {
-            ka[nxt][0] = *(const bf16x8 *)(lds + ad.k[ks + 1] + KOFF);
-            ka[nxt][1] = *(const bf16x8 *)(lds + ad.k[ks + 1] + KOFF + 32 * D * 2);
+            for (int qb = 0; qb < QB; ++qb) {
+                if (ks == 0) {
+                    mfma_zero_vgpr_ba(s[qb][0], k0, qreg[qb][ks]);
+                    mfma_zero_vgpr_ba(s[qb][1], k1, qreg[qb][ks]);
+                } else {
+                    mfma_acc_vgpr_ba(s[qb][0], k0, qreg[qb][ks]);
+                    mfma_acc_vgpr_ba(s[qb][1], k1, qreg[qb][ks]);
+                }
+            }
         }
-        s[0] = mfma32x32x16(ka[cur][0], qreg[ks], s[0]);
-        s[1] = mfma32x32x16(ka[cur][1], qreg[ks], s[1]);
+        mfma_fence_v4(s[0][0], s[0][1], s[1][0], s[1][1]);
+        return;
     }
-
-    // ---- mask: key j hidden from this lane's row when j >= kv_len or (causal) j > qrow ----
-    if (need_mask) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = k0 + jb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-                const bool vis = key < kv_len && (MASK != kMaskCausal || key <= qrow);
-                if (!vis) s[jb][r] = -INFINITY;
-            }
+            for (int r = 0; r < 16; ++r) s[qb][jb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 k0 = *(const bf16x8 *)(lds + ad.k[ks] + KOFF);
+        const bf16x8 k1 = *(const bf16x8 *)(lds + ad.k[ks] + KOFF + 32 * D * 2);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            s[qb][0] = mfma32x32x16(k0, qreg[qb][ks], s[qb][0]);
+            s[qb][1] = mfma32x32x16(k1, qreg[qb][ks], s[qb][1]);
+        }
     }
+}
 
-    // ---- online softmax (base 2; scale * log2(e) folded into c_log2 > 0, so a
-    //      masked score -inf gives exactly exp2(-inf) = 0) ----
+// Hide the scores of keys that this lane's query row must not see:
+// j >= kv_len, or (causal) j > qrow.
+template <int MASK>
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[2], int k0, int kv_len, int qrow, int hf)
+{
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = k0 + jb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
+            const bool vis = key < kv_len && (MASK != kMaskCausal || key <= qrow);
+            if (!vis) s[jb][r] = -INFINITY;
+        }
+}
+
+// Online softmax of one tile of scores of one query block, base 2 (scale *
+// log2(e) folded into c_log2 > 0, so a masked score -inf gives exactly
+// exp2(-inf) = 0). The reference max mc_run (already scaled) only moves
+// when the tile's max exceeds it by more than kRescaleSlack: exponents stay
+// <= the slack, P <= 2^slack is still exact up to rounding, and the rescale
+// of O and l by e^{m - m'} is needed on few tiles.
+//
+// Part 1: the tile's max, the new reference, and the factor alpha that O and
+// l must be multiplied by before this tile is added (1 when the reference
+// did not move). Returns the reference to subtract in the exponents.
+__device__ __forceinline__ float softmax_ref(const f32x16 (&s)[2], float &mc_run, float &l_run, float c_log2,
+                                             float &alpha, bool &upd)
+{
     float mx = s[0][0];
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
     mx = half_swap_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float mc = m_use * c_log2;
-    const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_use) * c_log2);
-    float lsum = 0.f;
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(fmaf(s[jb][r], c_log2, -mc));
-            s[jb][r] = p;
-            lsum += p;
-        }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-        for (int i = 0; i < DB; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
-    }
+    const float tmax = mx * c_log2;
+    upd = tmax > mc_run + kRescaleSlack;
+    const float mc_new = upd ? tmax : mc_run;
+    alpha = !upd ? 1.f : (mc_run == -INFINITY ? 0.f : fast_exp2(mc_run - mc_new));
+    mc_run = mc_new;
+    l_run *= alpha;
+    return (mc_new == -INFINITY) ? 0.f : mc_new;
+}
 
-    // ---- P in bf16 as B operands, 16 keys per MFMA ----
-    bf16x8 pb[4];
+// Part 2: P = exp2(s * c_log2 - mref) rounded to bf16 -- the B operands of
+// the P.V MFMAs, 16 keys each -- and the row sum of those same rounded values
+// into l_run, so that the weights applied to V sum to exactly l (a dominant
+// weight's rounding then cancels in O / l instead of showing up in O).
+__device__ __forceinline__ void softmax_exp(f32x16 (&s)[2], bf16x8 (&pb)[4], float mref, float c_log2, float &l_run)
+{
+    float lsum[2] = {0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int jb = c >> 1, r0 = (c & 1) * 8;
         u32x4 w;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) w[u] = pack_bf16x2(s[jb][r0 + 2 * u], s[jb][r0 + 2 * u + 1]);
+        for (int u = 0; u < 4; ++u) {
+            const float p0 = fast_exp2(fmaf(s[jb][r0 + 2 * u], c_log2, -mref));
+            const float p1 = fast_exp2(fmaf(s[jb][r0 + 2 * u + 1], c_log2, -mref));
+            w[u] = pack_bf16x2(p0, p1);
+            lsum[u & 1] = add_bf16x2(w[u], lsum[u & 1]);
+        }
         pb[c] = __builtin_bit_cast(bf16x8, w);
     }
+    l_run += lsum[0] + lsum[1];
+}
 
-    // ---- O^T += V^T P^T ----
-    // MFMA k slot hf*8 + t of chunk c is key c*16 + (t/4)*8 + hf*4 + t%4, the
-    // order in which the S accumulator holds the keys; a transposed read of
-    // rows c*16 + hf*4 + (0..3) (+8) gives exactly those 8 keys per column.
+// O^T += V^T P^T for one tile and QB query blocks. VOFF: byte offset of the
+// V tile in LDS. MFMA k slot hf*8 + t of chunk c is key
+// c*16 + (t/4)*8 + hf*4 + t%4, the order in which the S accumulator holds
+// the keys; a transposed read of rows c*16 + hf*4 + (0..3) (+8) gives
+// exactly those 8 keys per column.
+template <int D, int QB, int VOFF, bool ASM>
+__device__ __forceinline__ void accumulate_pv(const uint8_t *lds, const TileAddrs<D> &ad, const bf16x8 (&pb)[QB][4],
+                                              f32x16 (&acc)[QB][D / 32])
+{
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+        for (int db = 0; db < D / 32; ++db) {
             const uint8_t *p0 = lds + ad.v[db][0] + VOFF + c * 16 * D * 2;
             const uint8_t *p1 = lds + ad.v[db][1] + VOFF + c * 16 * D * 2;
             const bf16x8 a = lds_tr_pair((const uint16_t *)p0, (const uint16_t *)p1);
-            acc[db] = mfma32x32x16(a, pb[c], acc[db]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                if constexpr (ASM)
+                    mfma_acc_agpr(acc[qb][db], a, pb[qb][c]);
+                else
+                    acc[qb][db] = mfma32x32x16(a, pb[qb][c], acc[qb][db]);
+            }
         }
     }
 }
 
-template <int D, int MASK, bool OUT_F32, int OLAYOUT, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(
+// Occupancy: 128-wide heads with two query blocks per wave need the whole
+// register file (one wave per SIMD); otherwise two waves share a SIMD.
+template <int D, int QB>
+struct AttnTraits {
+    static constexpr int kWavesPerEU = QB == 2 ? 1 : 2;
+    // S(t+1)/softmax(t) overlap needs a second score buffer: only with one query block
+    static constexpr bool kPipelined = QB == 1;
+    // two query blocks: O accumulators pinned in AGPRs, scores in VGPRs (inline-asm MFMA)
+    static constexpr bool kAsm = QB == 2;
+};
+
+template <int D, int QB, int MASK, bool OUT_F32, int OLAYOUT, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
+    AttnTraits<D, QB>::kWavesPerEU, AttnTraits<D, QB>::kWavesPerEU))) void attn_fwd_bf16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const int32_t *__restrict__ valid_lens, float c_log2, void *__restrict__ Out, int H, int Nq, int Nk,
     int num_qtiles, int BH)
 {
-    constexpr int BM = WAVES * 32;
-    constexpr int KS = D / 16;  // k-steps of the Q K^T contraction
-    constexpr int DB = D / 32;  // 32-row blocks of O^T
+    constexpr bool ASM = AttnTraits<D, QB>::kAsm;
+    constexpr int RW = QB * 32;        // query rows per wave
+    constexpr int BM = WAVES * RW;     // query rows per workgroup
+    constexpr int KS = D / 16;         // k-steps of the Q K^T contraction
+    constexpr int DB = D / 32;         // 32-row blocks of O^T
     constexpr int TILE_B = kBlockN * D * 2;                     // bytes of one K (or V) tile
     constexpr int CPR = D / 8;                                  // 16-byte chunks per row
-    constexpr int CH = kBlockN * CPR / (WAVES * 64);            // chunk loads per lane per tensor per tile
+    constexpr int CH = kBlockN * CPR / (WAVES * 64);            // DMA chunks per lane per tensor per tile
     static_assert(kBlockN * CPR % (WAVES * 64) == 0, "tile must split evenly over the workgroup");
-    static_assert(4 * TILE_B <= 65536, "buffer offsets must fit LDS instruction immediates");
-    // buffer 0 = [K | V] at bytes [0, 2*TILE_B), buffer 1 at [2*TILE_B, 4*TILE_B)
+    static_assert(4 * TILE_B <= 65536, "LDS offsets must fit instruction immediates");
+    // LDS bytes: [K slot 0 | K slot 1 | V slot 0 | V slot 1]; tile i uses slot i % 2
     __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_B];
+    constexpr int KSLOT0 = 0, KSLOT1 = TILE_B, VSLOT0 = 2 * TILE_B, VSLOT1 = 3 * TILE_B;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
@@ -230,32 +286,49 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     const uint16_t *Vh = V + (size_t)bh * Nk * D;
 
     // Q^T as B operands: lane holds Q[qrow][ks*16 + hf*8 .. +7]
-    const int qrow = q0 + wave * 32 + l32;
-    bf16x8 qreg[KS];
-    {
-        const bool ok = qrow < Nq;
-        const uint16_t *qp = Q + ((size_t)bh * Nq + (ok ? qrow : 0)) * D + hf * 8;
+    const int qmin_w = q0 + wave * RW, qmax_w = qmin_w + RW - 1;
+    int qrow[QB];
+    bf16x8 qreg[QB][KS];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        qrow[qb] = qmin_w + qb * 32 + l32;
+        const bool ok = qrow[qb] < Nq;
+        const uint16_t *qp = Q + ((size_t)bh * Nq + (ok ? qrow[qb] : 0)) * D + hf * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 v = ok ? *(const u32x4 *)(qp + ks * 16) : u32x4{0u, 0u, 0u, 0u};
-            qreg[ks] = __builtin_bit_cast(bf16x8, v);
+            qreg[qb][ks] = __builtin_bit_cast(bf16x8, v);
         }
     }
 
-    f32x16 acc[DB];
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    if constexpr (ASM) {
+        static_assert(KS == 8, "");
+        agpr_write_fence_16(qreg);  // Q^T lives in AGPRs for the whole kernel
+    }
 
-    // Global -> LDS without registers: DMA j of this wave fills the 64
-    // consecutive LDS chunks [(j*WAVES + wave)*64, +64) of a tile; lane i
-    // fetches the global chunk that the swizzle puts in slot i. The per-lane
-    // byte offset within the tile's rows is fixed; the tile's first key moves
-    // the (uniform) base pointer. Rows at or past kv_end are never visible to
-    // this workgroup: they are not read; the last valid row is fetched in
-    // their place (its weight is exactly 0).
+    f32x16 acc[QB][DB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[qb][i][r] = 0.f;
+    if constexpr (ASM) valu_fence_a8(acc);
+    float mc_run[QB], l_run[QB];  // running (scaled, base-2) reference max and row sum
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        mc_run[qb] = -INFINITY;
+        l_run[qb] = 0.f;
+    }
+
+    const TileAddrs<D> ad = tile_addrs<D>(lane);
+
+    // DMA j of this wave fills the 64 consecutive LDS chunks
+    // [(j*WAVES + wave)*64, +64) of a tile; lane i fetches the global chunk
+    // that the swizzle puts in slot i. Rows at or past kv_end are never
+    // visible to this workgroup: they are not read; the last valid row is
+    // fetched in their place (its weight is exactly 0).
+    const uint32_t lds0 = lds_addr(smem);
     uint32_t voff[CH];
     int drow[CH];
 #pragma unroll
@@ -265,11 +338,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
         drow[j] = r;
         voff[j] = (uint32_t)(r * D + ((x ^ swz<D>(r)) << 3)) * 2;
     }
-    const uint32_t lds0 = lds_addr(smem);
-    auto issue_tile = [&](int t, uint32_t buf_off) {
+    auto issue = [&](const uint16_t *src, int t, uint32_t slot_off) {
         const int k0 = t * kBlockN;
-        const uint16_t *kb = Kh + (size_t)k0 * D;
-        const uint16_t *vb = Vh + (size_t)k0 * D;
+        const uint16_t *base = src + (size_t)k0 * D;
         const bool tail = k0 + kBlockN > kv_end;
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
@@ -278,61 +349,491 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
                 const int r = min(drow[j], kv_end - 1 - k0);
                 off = off - (uint32_t)(drow[j] - r) * (D * 2);
             }
-            const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + buf_off + (j * WAVES + wave) * 1024);
-            lds_dma16(dst, kb, off);
-            lds_dma16(dst + TILE_B, vb, off);
+            lds_dma16(__builtin_amdgcn_readfirstlane(lds0 + slot_off + (j * WAVES + wave) * 1024), base, off);
         }
     };
 
-    const TileAddrs<D> ad = tile_addrs<D>(lane);
-    if (ntiles > 0) issue_tile(0, 0);
-    wait_vmcnt0();
-    __syncthreads();
-
-    const int qmin_w = q0 + wave * 32, qmax_w = qmin_w + 31;
-    auto step = [&](int t, auto buf) {
-        constexpr int B = decltype(buf)::value;
-        if (t + 1 < ntiles) issue_tile(t + 1, (B ^ 1) * 2 * TILE_B);
+    // tiles this wave computes: causal rows <= qmax_w see no key past qmax_w
+    const int ntiles_w = (MASK == kMaskCausal) ? min(ntiles, qmax_w / kBlockN + 1) : ntiles;
+    auto needs_mask = [&](int t) {
         const int k0 = t * kBlockN;
-        const bool skip = (MASK == kMaskCausal) && (k0 > qmax_w);
-        if (!skip) {
-            const bool need_mask =
-                (k0 + kBlockN > kv_len) || (MASK == kMaskCausal && k0 + kBlockN - 1 > qmin_w);
-            attend_tile<D, MASK, B * 2 * TILE_B, B * 2 * TILE_B + TILE_B>(smem, ad, qreg, acc, m_run, l_run, c_log2,
-                                                                          k0, kv_len, qrow, lane, need_mask);
+        return (k0 + kBlockN > kv_len) || (MASK == kMaskCausal && k0 + kBlockN - 1 > qmin_w);
+    };
+
+    // Online-softmax bookkeeping for one tile whose scores are in `cur`:
+    // mask, move the reference max, rescale O when any row of the wave needs
+    // it; returns the reference per query block in mref.
+    auto prepare = [&](int t, f32x16(&cur)[QB][2], float (&mref)[QB]) {
+        if (needs_mask(t)) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) mask_scores<MASK>(cur[qb], t * kBlockN, kv_len, qrow[qb], hf);
+        }
+        float alpha[QB];
+        bool upd = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            bool u;
+            mref[qb] = softmax_ref(cur[qb], mc_run[qb], l_run[qb], c_log2, alpha[qb], u);
+            upd = upd || u;
+        }
+        if (__builtin_amdgcn_ballot_w64(upd)) {
+            if constexpr (ASM) mfma_fence_a8(acc);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int i = 0; i < DB; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[qb][i][r] *= alpha[qb];
+            if constexpr (ASM) valu_fence_a8(acc);
+        }
+    };
+
+    if constexpr (AttnTraits<D, QB>::kPipelined) {
+        // Software pipeline: iteration t reads K(t+1) and V(t) from LDS while
+        // the DMA fills K(t+2) and V(t+1); the MFMAs of S(t+1) are issued in
+        // the same basic block as the exponentials of S(t).
+        f32x16 sa[QB][2], sb[QB][2];
+        if (ntiles > 0) {
+            issue(Kh, 0, KSLOT0);
+            wait_vmcnt0();
+            __syncthreads();
+            if (ntiles > 1) issue(Kh, 1, KSLOT1);
+            issue(Vh, 0, VSLOT0);
+            if (ntiles_w > 0) scores<D, QB, KSLOT0, ASM>(smem, ad, qreg, sa);
+            wait_vmcnt0();
+            __syncthreads();
+        }
+        auto step = [&](int t, auto parity, f32x16(&cur)[QB][2], f32x16(&nxt)[QB][2]) {
+            constexpr int P = decltype(parity)::value;  // t % 2
+            constexpr int KNEXT = P ? KSLOT0 : KSLOT1;  // K(t+1) lives in slot (t+1)%2
+            constexpr int VCUR = P ? VSLOT1 : VSLOT0;   // V(t) in slot t%2
+            if (t + 2 < ntiles) issue(Kh, t + 2, P ? KSLOT1 : KSLOT0);
+            if (t + 1 < ntiles) issue(Vh, t + 1, P ? VSLOT0 : VSLOT1);
+            if (t < ntiles_w) {
+                float mref[QB];
+                prepare(t, cur, mref);
+                bf16x8 pb[QB][4];
+                if (t + 1 < ntiles_w) {
+                    scores<D, QB, KNEXT, ASM>(smem, ad, qreg, nxt);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) softmax_exp(cur[qb], pb[qb], mref[qb], c_log2, l_run[qb]);
+                    accumulate_pv<D, QB, VCUR, ASM>(smem, ad, pb, acc);
+                } else {
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) softmax_exp(cur[qb], pb[qb], mref[qb], c_log2, l_run[qb]);
+                    accumulate_pv<D, QB, VCUR, ASM>(smem, ad, pb, acc);
+                }
+            }
+            wait_vmcnt0();
+            __syncthreads();
+        };
+        for (int t = 0; t < ntiles; t += 2) {
+            step(t, std::integral_constant<int, 0>(), sa, sb);
+            if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>(), sb, sa);
+        }
+    } else {
+        // Plain double buffering: iteration t computes tile t from slot t%2
+        // while the DMA fills slot (t+1)%2 with tile t+1.
+        if (ntiles > 0) {
+            issue(Kh, 0, KSLOT0);
+            issue(Vh, 0, VSLOT0);
+        }
+        wait_vmcnt0();
+        __syncthreads();
+        auto step = [&](int t, auto parity) {
+            constexpr int P = decltype(parity)::value;  // t % 2
+            if (t + 1 < ntiles) {
+                issue(Kh, t + 1, P ? KSLOT0 : KSLOT1);
+                issue(Vh, t + 1, P ? VSLOT0 : VSLOT1);
+            }
+            if (t < ntiles_w) {
+                f32x16 cur[QB][2];
+                scores<D, QB, P ? KSLOT1 : KSLOT0, ASM>(smem, ad, qreg, cur);
+                float mref[QB];
+                prepare(t, cur, mref);
+                bf16x8 pb[QB][4];
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) softmax_exp(cur[qb], pb[qb], mref[qb], c_log2, l_run[qb]);
+                if constexpr (ASM) valu_fence_v8(pb);
+                accumulate_pv<D, QB, P ? VSLOT1 : VSLOT0, ASM>(smem, ad, pb, acc);
+            }
+            wait_vmcnt0();
+            __syncthreads();
+        };
+        for (int t = 0; t < ntiles; t += 2) {
+            step(t, std::integral_constant<int, 0>());
+            if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>());
+        }
+    }
+
+    // ---- epilogue: O = O_acc / l (0 for a row with no visible key) ----
+    if constexpr (ASM) mfma_fence_a8(acc);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const float l_tot = half_swap_sum(l_run[qb]);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (qrow[qb] < Nq) {
+            size_t row_off;
+            if (OLAYOUT == kOutBHND) {
+                row_off = ((size_t)bh * Nq + qrow[qb]) * D;
+            } else {
+                const int hh = bh % H;
+                row_off = (((size_t)b * Nq + qrow[qb]) * H + hh) * D;
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int d0 = db * 32 + rg * 8 + hf * 4;
+                    const float v0 = acc[qb][db][rg * 4 + 0] * inv, v1 = acc[qb][db][rg * 4 + 1] * inv;
+                    const float v2 = acc[qb][db][rg * 4 + 2] * inv, v3 = acc[qb][db][rg * 4 + 3] * inv;
+                    if (OUT_F32) {
+                        *(f32x4 *)((float *)Out + row_off + d0) = f32x4{v0, v1, v2, v3};
+                    } else {
+                        *(u32x2 *)((uint16_t *)Out + row_off + d0) =
+                            u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+                    }
+                }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 128-wide heads: 4 waves x 64 query rows (two blocks of 32) per workgroup,
+// one wave per SIMD, with an explicit software pipeline inside each wave so
+// that the MFMA pipe and the VALU work at the same time:
+//
+//   iteration t, phase A:  O += P(t-1) V(t-1)      [32 MFMA, V(t-1) from LDS]
+//                          interleaved with copying S(t) out of AGPRs
+//                          then mask / max / reference update for tile t
+//   iteration t, phase B:  S(t+1) = K(t+1) Q^T     [32 MFMA, K(t+1) from LDS]
+//                          interleaved with exp2, row sums and bf16 P(t)
+//
+// Register plan (512 per lane): O (128), Q^T (64) and S(t+1) (64) in AGPRs,
+// written and read only by MFMAs; S(t) (64) and P (32) in VGPRs for the VALU.
+// The MFMAs are inline asm with pinned register files; results are read only
+// after explicit wait-state fences. The instruction order inside each phase is
+// fixed with scheduling barriers: one MFMA, then the VALU work that runs while
+// that MFMA occupies the matrix pipe.
+//
+// LDS: [K slot 0 | K slot 1 | V slot 0 | V slot 1]. Iteration t reads V(t-1)
+// and K(t+1) while the DMA fills V(t) (slot t%2) and K(t+2) (slot t%2).
+// ---------------------------------------------------------------------------
+template <int MASK, bool OUT_F32, int OLAYOUT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_fwd_d128_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    const int32_t *__restrict__ valid_lens, float c_log2, void *__restrict__ Out, int H, int Nq, int Nk,
+    int num_qtiles, int BH)
+{
+    constexpr int D = 128, WAVES = 4, RW = 64, BM = WAVES * RW, KS = D / 16, DB = D / 32;
+    constexpr int TILE_B = kBlockN * D * 2, CPR = D / 8, CH = kBlockN * CPR / (WAVES * 64);
+    static_assert(kBlockN * CPR % (WAVES * 64) == 0, "tile must split evenly over the workgroup");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_B];
+    constexpr int KSLOT0 = 0, KSLOT1 = TILE_B, VSLOT0 = 2 * TILE_B, VSLOT1 = 3 * TILE_B;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hf = lane >> 5;
+
+    // q-tile-major order (XCD-local heads); causal runs the longest q-tiles first
+    const int id = blockIdx.x;
+    const int bh = id % BH;
+    int qt = id / BH;
+    if (MASK == kMaskCausal) qt = num_qtiles - 1 - qt;
+    const int b = bh / H;
+    const int q0 = qt * BM;
+    int kv_len = Nk;
+    if (MASK == kMaskPadding) {
+        const int L = valid_lens[b];
+        kv_len = L < 0 ? 0 : (L > Nk ? Nk : L);
+    }
+    int kv_end = kv_len;
+    if (MASK == kMaskCausal) kv_end = min(kv_len, q0 + BM);
+    const int ntiles = (kv_end + kBlockN - 1) / kBlockN;
+    const uint16_t *Kh = K + (size_t)bh * Nk * D;
+    const uint16_t *Vh = V + (size_t)bh * Nk * D;
+
+    // Q^T (B operands), resident in AGPRs
+    const int qmin_w = q0 + wave * RW, qmax_w = qmin_w + RW - 1;
+    int qrow[2];
+    bf16x8 qreg[2][KS];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        qrow[qb] = qmin_w + qb * 32 + l32;
+        const bool ok = qrow[qb] < Nq;
+        const uint16_t *qp = Q + ((size_t)bh * Nq + (ok ? qrow[qb] : 0)) * D + hf * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 v = ok ? *(const u32x4 *)(qp + ks * 16) : u32x4{0u, 0u, 0u, 0u};
+            qreg[qb][ks] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+    f32x16 acc[2][DB];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[qb][i][r] = 0.f;
+    float mc_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+    const TileAddrs<D> ad = tile_addrs<D>(lane);
+    const uint32_t lds0 = lds_addr(smem);
+    uint32_t voff[CH];
+    int drow[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        const int c = (j * WAVES + wave) * 64 + lane;
+        const int r = c / CPR, x = c % CPR;
+        drow[j] = r;
+        voff[j] = (uint32_t)(r * D + ((x ^ swz<D>(r)) << 3)) * 2;
+    }
+    // DMA of tile t of K or V into an LDS slot; rows at or past kv_end are
+    // not read (the last valid row is fetched instead; its weight is 0)
+    auto issue = [&](const uint16_t *src, int t, uint32_t slot_off) {
+        const int k0 = t * kBlockN;
+        const uint16_t *base = src + (size_t)k0 * D;
+        const bool tail = k0 + kBlockN > kv_end;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            uint32_t off = voff[j];
+            if (tail) {
+                const int r = min(drow[j], kv_end - 1 - k0);
+                off = off - (uint32_t)(drow[j] - r) * (D * 2);
+            }
+            lds_dma16(__builtin_amdgcn_readfirstlane(lds0 + slot_off + (j * WAVES + wave) * 1024), base, off);
+        }
+    };
+    const int ntiles_w = (MASK == kMaskCausal) ? min(ntiles, qmax_w / kBlockN + 1) : ntiles;
+    auto needs_mask = [&](int t) {
+        const int k0 = t * kBlockN;
+        return (k0 + kBlockN > kv_len) || (MASK == kMaskCausal && k0 + kBlockN - 1 > qmin_w);
+    };
+
+    f32x16 sn[2][2];  // S of the next tile (AGPRs, MFMA only)
+    f32x16 sc[2][2];  // S of the current tile (VGPRs)
+    bf16x8 pb[2][4];  // P of one tile in bf16 (VGPRs)
+
+    // S = K Q^T into sn, K tile at byte offset KOFF; with EXP, the
+    // exponentials, row sums and bf16 P of the tile in sc are interleaved:
+    // k-step ks handles P chunk ks = (qb = ks/4, c = ks%4), 8 scores.
+    auto s_phase = [&](auto koff, auto with_exp, const float (&mref)[2], float (&lsum)[2]) {
+        constexpr int KOFF = decltype(koff)::value;
+        constexpr bool EXP = decltype(with_exp)::value;
+        bf16x8 kop[2][2];
+        kop[0][0] = *(const bf16x8 *)(smem + ad.k[0] + KOFF);
+        kop[0][1] = *(const bf16x8 *)(smem + ad.k[0] + KOFF + 32 * D * 2);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int cu = ks & 1;
+            if (ks + 1 < KS) {
+                kop[cu ^ 1][0] = *(const bf16x8 *)(smem + ad.k[ks + 1] + KOFF);
+                kop[cu ^ 1][1] = *(const bf16x8 *)(smem + ad.k[ks + 1] + KOFF + 32 * D * 2);
+            }
+            const int qb_e = ks >> 2, c = ks & 3, jb_e = c >> 1, r0 = (c & 1) * 8;
+            float pv[8];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int qb = m >> 1, jb = m & 1;
+                __builtin_amdgcn_sched_barrier(0);
+                if (ks == 0)
+                    mfma_zero_agpr_ba(sn[qb][jb], kop[cu][jb], qreg[qb][ks]);
+                else if (ks == KS - 1 && m == 3)
+                    mfma_acc_agpr_ba_last(sn[qb][jb], kop[cu][jb], qreg[qb][ks]);
+                else
+                    mfma_acc_agpr_ba(sn[qb][jb], kop[cu][jb], qreg[qb][ks]);
+                if constexpr (EXP) {
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int e = m * 2 + u;
+                        pv[e] = fast_exp2(fmaf(sc[qb_e][jb_e][r0 + e], c_log2, -mref[qb_e]));
+                    }
+                }
+            }
+            if constexpr (EXP) {
+                u32x4 w;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    w[u] = pack_bf16x2(pv[2 * u], pv[2 * u + 1]);
+                    lsum[qb_e] = add_bf16x2(w[u], lsum[qb_e]);
+                }
+                pb[qb_e][c] = __builtin_bit_cast(bf16x8, w);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // exponentials only (no next tile for this wave)
+    auto exp_only = [&](const float (&mref)[2], float (&lsum)[2]) {
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const int qb = g >> 2, c = g & 3, jb = c >> 1, r0 = (c & 1) * 8;
+            u32x4 w;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float p0 = fast_exp2(fmaf(sc[qb][jb][r0 + 2 * u], c_log2, -mref[qb]));
+                const float p1 = fast_exp2(fmaf(sc[qb][jb][r0 + 2 * u + 1], c_log2, -mref[qb]));
+                w[u] = pack_bf16x2(p0, p1);
+                lsum[qb] = add_bf16x2(w[u], lsum[qb]);
+            }
+            pb[qb][c] = __builtin_bit_cast(bf16x8, w);
+        }
+    };
+    // O += P V with the V tile at byte offset VOFF; with COPY, S(t) moves
+    // from sn (AGPRs) to sc (VGPRs) in between: 4 scores per MFMA.
+    auto pv_phase = [&](auto voff_c, auto with_copy) {
+        constexpr int VOFF = decltype(voff_c)::value;
+        constexpr bool COPY = decltype(with_copy)::value;
+        valu_fence_v8(pb);
+        bf16x8 vop[2];
+        {
+            const uint8_t *p0 = smem + ad.v[0][0] + VOFF, *p1 = smem + ad.v[0][1] + VOFF;
+            vop[0] = lds_tr_pair((const uint16_t *)p0, (const uint16_t *)p1);
+        }
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            const int c = g >> 2, db = g & 3, cu = g & 1;
+            if (g + 1 < 16) {
+                const int c2 = (g + 1) >> 2, db2 = (g + 1) & 3;
+                const uint8_t *p0 = smem + ad.v[db2][0] + VOFF + c2 * 16 * D * 2;
+                const uint8_t *p1 = smem + ad.v[db2][1] + VOFF + c2 * 16 * D * 2;
+                vop[cu ^ 1] = lds_tr_pair((const uint16_t *)p0, (const uint16_t *)p1);
+            }
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (g == 15 && qb == 1)
+                    mfma_acc_agpr_last(acc[qb][db], vop[cu], pb[qb][c]);
+                else
+                    mfma_acc_agpr(acc[qb][db], vop[cu], pb[qb][c]);
+                if constexpr (COPY) {
+                    // scores e, e+1 (e = g*4 + qb*2) of the 64 -> sc[e/32][(e/16)%2][e%16]
+                    const int e = g * 4 + qb * 2, a = e >> 5, j = (e >> 4) & 1, r = e & 15;
+                    float d0, d1;
+                    agpr_read2(d0, d1, sn[a][j][r], sn[a][j][r + 1]);
+                    sc[a][j][r] = d0;
+                    sc[a][j][r + 1] = d1;
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // mask, max and reference update of the tile in sc; rescales O when any
+    // row of the wave moved its reference
+    auto reference = [&](int t, float (&mref)[2]) {
+        if (needs_mask(t)) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) mask_scores<MASK>(sc[qb], t * kBlockN, kv_len, qrow[qb], hf);
+        }
+        float alpha[2];
+        bool upd = false;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            bool u;
+            mref[qb] = softmax_ref(sc[qb], mc_run[qb], l_run[qb], c_log2, alpha[qb], u);
+            upd = upd || u;
+        }
+        if (__builtin_amdgcn_ballot_w64(upd)) {
+            mfma_fence_a8(acc);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int i = 0; i < DB; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[qb][i][r] *= alpha[qb];
+            valu_fence_a8(acc);
+        }
+    };
+
+    // prologue: S(0) from K(0); K(1) on its way
+    if (ntiles > 0) {
+        issue(Kh, 0, KSLOT0);
+        if (ntiles > 1) issue(Kh, 1, KSLOT1);
+        wait_vmcnt0();
+        __syncthreads();
+        float dm[2] = {0.f, 0.f}, dl[2] = {0.f, 0.f};
+        s_phase(std::integral_constant<int, KSLOT0>(), std::false_type(), dm, dl);
+        __syncthreads();  // every wave is done with K slot 0 before it is refilled
+    }
+
+    auto iteration = [&](int t, auto parity) {
+        constexpr int P = decltype(parity)::value;  // t % 2
+        constexpr int KNEXT = P ? KSLOT0 : KSLOT1;  // K(t+1) in slot (t+1)%2
+        constexpr int VPREV = P ? VSLOT0 : VSLOT1;  // V(t-1) in slot (t-1)%2
+        if (t + 2 < ntiles) issue(Kh, t + 2, P ? KSLOT1 : KSLOT0);
+        issue(Vh, t, P ? VSLOT1 : VSLOT0);
+        const bool do_pv = t >= 1 && t - 1 < ntiles_w;
+        if (t < ntiles_w) {
+            mfma_fence_a4(sn);
+            if (do_pv) {
+                pv_phase(std::integral_constant<int, VPREV>(), std::true_type());
+            } else {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                        for (int r = 0; r < 16; r += 2) {
+                            float d0, d1;
+                            agpr_read2(d0, d1, sn[qb][jb][r], sn[qb][jb][r + 1]);
+                            sc[qb][jb][r] = d0;
+                            sc[qb][jb][r + 1] = d1;
+                        }
+            }
+            float mref[2];
+            reference(t, mref);
+            float lsum[2] = {0.f, 0.f};
+            if (t + 1 < ntiles_w)
+                s_phase(std::integral_constant<int, KNEXT>(), std::true_type(), mref, lsum);
+            else
+                exp_only(mref, lsum);
+            l_run[0] += lsum[0];
+            l_run[1] += lsum[1];
+        } else if (do_pv) {
+            pv_phase(std::integral_constant<int, VPREV>(), std::false_type());
         }
         wait_vmcnt0();
         __syncthreads();
     };
     for (int t = 0; t < ntiles; t += 2) {
-        step(t, std::integral_constant<int, 0>());
-        if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>());
+        iteration(t, std::integral_constant<int, 0>());
+        if (t + 1 < ntiles) iteration(t + 1, std::integral_constant<int, 1>());
+    }
+    // P.V of the wave's last tile, when it was the workgroup's last tile too
+    if (ntiles > 0 && ntiles - 1 < ntiles_w) {
+        if ((ntiles - 1) & 1)
+            pv_phase(std::integral_constant<int, VSLOT1>(), std::false_type());
+        else
+            pv_phase(std::integral_constant<int, VSLOT0>(), std::false_type());
     }
 
     // ---- epilogue: O = O_acc / l (0 for a row with no visible key) ----
-    const float l_tot = half_swap_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (qrow < Nq) {
-        size_t row_off;
-        if (OLAYOUT == kOutBHND) {
-            row_off = ((size_t)bh * Nq + qrow) * D;
-        } else {
-            const int hh = bh % H;
-            row_off = (((size_t)b * Nq + qrow) * H + hh) * D;
-        }
+    mfma_fence_a8(acc);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int d0 = db * 32 + rg * 8 + hf * 4;
-                const float v0 = acc[db][rg * 4 + 0] * inv, v1 = acc[db][rg * 4 + 1] * inv;
-                const float v2 = acc[db][rg * 4 + 2] * inv, v3 = acc[db][rg * 4 + 3] * inv;
-                if (OUT_F32) {
-                    *(f32x4 *)((float *)Out + row_off + d0) = f32x4{v0, v1, v2, v3};
-                } else {
-                    *(u32x2 *)((uint16_t *)Out + row_off + d0) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-                }
+    for (int qb = 0; qb < 2; ++qb) {
+        const float l_tot = half_swap_sum(l_run[qb]);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (qrow[qb] < Nq) {
+            size_t row_off;
+            if (OLAYOUT == kOutBHND) {
+                row_off = ((size_t)bh * Nq + qrow[qb]) * D;
+            } else {
+                const int hh = bh % H;
+                row_off = (((size_t)b * Nq + qrow[qb]) * H + hh) * D;
             }
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int d0 = db * 32 + rg * 8 + hf * 4;
+                    const float v0 = acc[qb][db][rg * 4 + 0] * inv, v1 = acc[qb][db][rg * 4 + 1] * inv;
+                    const float v2 = acc[qb][db][rg * 4 + 2] * inv, v3 = acc[qb][db][rg * 4 + 3] * inv;
+                    if (OUT_F32) {
+                        *(f32x4 *)((float *)Out + row_off + d0) = f32x4{v0, v1, v2, v3};
+                    } else {
+                        *(u32x2 *)((uint16_t *)Out + row_off + d0) =
+                            u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+                    }
+                }
+        }
     }
 }
 
@@ -340,7 +841,10 @@ template <int D, int MASK, bool OUT_F32, int OLAYOUT>
 hipError_t launch_variant(const void *Q, const void *K, const void *V, const int32_t *valid_lens, float scale,
                           void *O, int B, int H, int Nq, int Nk, hipStream_t stream)
 {
-    constexpr int WAVES = 4, BM = WAVES * 32;
+    // 128-wide heads: the pipelined kernel, 4 waves x 64 rows (BM = 256).
+    // 64-wide heads: 4 waves x 32 rows (BM = 128), two waves per SIMD.
+    constexpr bool D128 = D == 128 && kQB128 == 2;
+    constexpr int BM = D128 ? 256 : 4 * 32;
     const int BH = B * H;
     const int num_qtiles = (Nq + BM - 1) / BM;
     const long long grid = (long long)num_qtiles * BH;
@@ -350,9 +854,17 @@ hipError_t launch_variant(const void *Q, const void *K, const void *V, const int
     // scores (-inf) map to weight 0 without a select; below 1e-30 every
     // visible exp2 argument rounds to 0 anyway, which is the scale = 0 result.
     const float c_log2 = fmaxf(scale * 1.4426950408889634f, 1e-30f);
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, MASK, OUT_F32, OLAYOUT, WAVES>), dim3((unsigned)grid),
-                       dim3(WAVES * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
-                       valid_lens, c_log2, O, H, Nq, Nk, num_qtiles, BH);
+    if constexpr (D128) {
+        hipLaunchKernelGGL((attn_fwd_d128_kernel<MASK, OUT_F32, OLAYOUT>), dim3((unsigned)grid), dim3(256), 0, stream,
+                           (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, valid_lens, c_log2, O, H,
+                           Nq, Nk, num_qtiles, BH);
+    } else {
+        constexpr int QB = D == 128 ? kQB128 : 1;
+        constexpr int WAVES = BM / (32 * QB);
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QB, MASK, OUT_F32, OLAYOUT, WAVES>), dim3((unsigned)grid),
+                           dim3(WAVES * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
+                           valid_lens, c_log2, O, H, Nq, Nk, num_qtiles, BH);
+    }
     return hipGetLastError();
 }
 
