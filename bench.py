@@ -228,6 +228,9 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": hbm_traffic_per_launch(),
+            "traffic_unit": "bytes per launch between L2 and memory (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a "
+                            "256 MiB copy's counts)",
+            "algorithmic_bytes_per_launch": 4 * B * H * N * d * 2,
             "kernel": "attn_fwd_bf16_kernel<128, causal, bf16 out>",
             "algorithmic_flops_per_launch": r["flops"],
             "avg_launch_ms": round(r["ms"], 5),

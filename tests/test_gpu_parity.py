@@ -110,7 +110,8 @@ def test_f32_ragged(dev, d, mask):
 
 # ---------------------------------------------------------------- bf16 path
 
-SMALL = [(1, 1), (5, 5), (64, 64), (200, 200), (333, 333), (130, 77), (77, 300)]
+# up to three 256-row query tiles and ten 64-key tiles, with ragged tails on both
+SMALL = [(1, 1), (5, 5), (64, 64), (200, 200), (333, 333), (130, 77), (77, 300), (600, 600), (530, 620)]
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])

@@ -11,8 +11,8 @@
 // sum and the partial output are rescaled by e^{m - m'}.
 //
 // Work decomposition (one workgroup = WAVES wavefronts of QB*32 query rows
-// each, all of one head; the 128-wide head uses QB = 2, so every K or V
-// operand read from LDS feeds two MFMAs):
+// each, all of one head; by default QB = 1 and two waves share each SIMD,
+// 8 waves per workgroup for 128-wide heads, 4 for 64-wide ones):
 //   * Q^T stays in registers as the B operand of v_mfma_f32_32x32x16_bf16.
 //   * K and V tiles (64 keys) go HBM -> LDS by DMA (no staging registers),
 //     double buffered, while the previous tile is computed.
@@ -41,10 +41,20 @@ namespace {
 
 constexpr int kBlockN = 64;            // keys per LDS tile
 constexpr float kRescaleSlack = 8.f;    // log2 units the reference max may lag the true max
-#ifndef TSD_QB128
-#define TSD_QB128 1
+// Kernel design for 128-wide heads: 1 = generic kernel, 32 rows per wave,
+// software pipelined; 2 = generic kernel, 64 rows per wave (inline-asm MFMA,
+// O in AGPRs); 3 = the hand-pipelined 64-rows-per-wave kernel below.
+#ifndef TSD_D128_DESIGN
+#define TSD_D128_DESIGN 1
 #endif
-constexpr int kQB128 = TSD_QB128;       // query blocks of 32 rows per wave for 128-wide heads
+constexpr int kD128Design = TSD_D128_DESIGN;
+#ifndef TSD_WAVES128
+#define TSD_WAVES128 8
+#endif
+// Wavefronts per workgroup of the generic kernel. 128-wide heads: 8 waves
+// (two per SIMD) share one copy of each K/V tile in LDS, which halves the
+// LDS write traffic of the tile loads against two 4-wave workgroups per CU.
+constexpr int kWaves128 = TSD_WAVES128, kWaves64 = 4;
 
 // LDS tiles are dense [64 keys][D] bf16 with the 16-byte chunks of each row
 // XOR-swizzled: element (r, e) lives at r*D + 8*((e/8) ^ swz(r)) + e%8.
@@ -841,10 +851,10 @@ template <int D, int MASK, bool OUT_F32, int OLAYOUT>
 hipError_t launch_variant(const void *Q, const void *K, const void *V, const int32_t *valid_lens, float scale,
                           void *O, int B, int H, int Nq, int Nk, hipStream_t stream)
 {
-    // 128-wide heads: the pipelined kernel, 4 waves x 64 rows (BM = 256).
-    // 64-wide heads: 4 waves x 32 rows (BM = 128), two waves per SIMD.
-    constexpr bool D128 = D == 128 && kQB128 == 2;
-    constexpr int BM = D128 ? 256 : 4 * 32;
+    // 32 (QB = 1) or 64 (QB = 2) query rows per wave.
+    constexpr bool D128 = D == 128 && kD128Design == 3;
+    constexpr int QB = (D == 128 && kD128Design >= 2) ? 2 : 1;
+    constexpr int BM = (D128 ? 4 : (D == 128 ? kWaves128 : kWaves64)) * 32 * QB;
     const int BH = B * H;
     const int num_qtiles = (Nq + BM - 1) / BM;
     const long long grid = (long long)num_qtiles * BH;
@@ -859,7 +869,6 @@ hipError_t launch_variant(const void *Q, const void *K, const void *V, const int
                            (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, valid_lens, c_log2, O, H,
                            Nq, Nk, num_qtiles, BH);
     } else {
-        constexpr int QB = D == 128 ? kQB128 : 1;
         constexpr int WAVES = BM / (32 * QB);
         hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QB, MASK, OUT_F32, OLAYOUT, WAVES>), dim3((unsigned)grid),
                            dim3(WAVES * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
