@@ -35,15 +35,16 @@
 #include <math.h>
 
 #include <type_traits>
+#include <utility>
 
 namespace tsd {
 namespace {
 
 constexpr int kBlockN = 64;            // keys per LDS tile
 constexpr float kRescaleSlack = 8.f;    // log2 units the reference max may lag the true max
-// Kernel design for 128-wide heads: 1 = generic kernel, 32 rows per wave,
-// software pipelined; 2 = generic kernel, 64 rows per wave (inline-asm MFMA,
-// O in AGPRs); 3 = the hand-pipelined 64-rows-per-wave kernel below.
+// Kernel design for 128-wide heads: 1 = 32 rows per wave, software
+// pipelined; 2 = 64 rows per wave (inline-asm MFMA, O in AGPRs, one wave
+// per SIMD).
 #ifndef TSD_D128_DESIGN
 #define TSD_D128_DESIGN 1
 #endif
@@ -237,6 +238,38 @@ __device__ __forceinline__ void accumulate_pv(const uint8_t *lds, const TileAddr
             }
         }
     }
+}
+
+// O = O_acc / l for one block of 32 query rows (0 for a row with no
+// visible key), rounded to the output type and stored as [B,H,N,D] or as
+// the head concat [B,N,H,D].
+template <int D, bool OUT_F32, int OLAYOUT>
+__device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float l_run, int qrow, int bh, int H, int Nq,
+                                           int b, int hf, void *__restrict__ Out)
+{
+    const float l_tot = half_swap_sum(l_run);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qrow >= Nq) return;
+    size_t row_off;
+    if (OLAYOUT == kOutBHND) {
+        row_off = ((size_t)bh * Nq + qrow) * D;
+    } else {
+        const int hh = bh % H;
+        row_off = (((size_t)b * Nq + qrow) * H + hh) * D;
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const int d0 = db * 32 + rg * 8 + hf * 4;
+            const float v0 = acc[db][rg * 4 + 0] * inv, v1 = acc[db][rg * 4 + 1] * inv;
+            const float v2 = acc[db][rg * 4 + 2] * inv, v3 = acc[db][rg * 4 + 3] * inv;
+            if (OUT_F32) {
+                *(f32x4 *)((float *)Out + row_off + d0) = f32x4{v0, v1, v2, v3};
+            } else {
+                *(u32x2 *)((uint16_t *)Out + row_off + d0) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+            }
+        }
 }
 
 // Occupancy: 128-wide heads with two query blocks per wave need the whole
@@ -479,382 +512,18 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
     // ---- epilogue: O = O_acc / l (0 for a row with no visible key) ----
     if constexpr (ASM) mfma_fence_a8(acc);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float l_tot = half_swap_sum(l_run[qb]);
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        if (qrow[qb] < Nq) {
-            size_t row_off;
-            if (OLAYOUT == kOutBHND) {
-                row_off = ((size_t)bh * Nq + qrow[qb]) * D;
-            } else {
-                const int hh = bh % H;
-                row_off = (((size_t)b * Nq + qrow[qb]) * H + hh) * D;
-            }
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    const int d0 = db * 32 + rg * 8 + hf * 4;
-                    const float v0 = acc[qb][db][rg * 4 + 0] * inv, v1 = acc[qb][db][rg * 4 + 1] * inv;
-                    const float v2 = acc[qb][db][rg * 4 + 2] * inv, v3 = acc[qb][db][rg * 4 + 3] * inv;
-                    if (OUT_F32) {
-                        *(f32x4 *)((float *)Out + row_off + d0) = f32x4{v0, v1, v2, v3};
-                    } else {
-                        *(u32x2 *)((uint16_t *)Out + row_off + d0) =
-                            u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-                    }
-                }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// 128-wide heads: 4 waves x 64 query rows (two blocks of 32) per workgroup,
-// one wave per SIMD, with an explicit software pipeline inside each wave so
-// that the MFMA pipe and the VALU work at the same time:
-//
-//   iteration t, phase A:  O += P(t-1) V(t-1)      [32 MFMA, V(t-1) from LDS]
-//                          interleaved with copying S(t) out of AGPRs
-//                          then mask / max / reference update for tile t
-//   iteration t, phase B:  S(t+1) = K(t+1) Q^T     [32 MFMA, K(t+1) from LDS]
-//                          interleaved with exp2, row sums and bf16 P(t)
-//
-// Register plan (512 per lane): O (128), Q^T (64) and S(t+1) (64) in AGPRs,
-// written and read only by MFMAs; S(t) (64) and P (32) in VGPRs for the VALU.
-// The MFMAs are inline asm with pinned register files; results are read only
-// after explicit wait-state fences. The instruction order inside each phase is
-// fixed with scheduling barriers: one MFMA, then the VALU work that runs while
-// that MFMA occupies the matrix pipe.
-//
-// LDS: [K slot 0 | K slot 1 | V slot 0 | V slot 1]. Iteration t reads V(t-1)
-// and K(t+1) while the DMA fills V(t) (slot t%2) and K(t+2) (slot t%2).
-// ---------------------------------------------------------------------------
-template <int MASK, bool OUT_F32, int OLAYOUT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_fwd_d128_kernel(
-    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    const int32_t *__restrict__ valid_lens, float c_log2, void *__restrict__ Out, int H, int Nq, int Nk,
-    int num_qtiles, int BH)
-{
-    constexpr int D = 128, WAVES = 4, RW = 64, BM = WAVES * RW, KS = D / 16, DB = D / 32;
-    constexpr int TILE_B = kBlockN * D * 2, CPR = D / 8, CH = kBlockN * CPR / (WAVES * 64);
-    static_assert(kBlockN * CPR % (WAVES * 64) == 0, "tile must split evenly over the workgroup");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_B];
-    constexpr int KSLOT0 = 0, KSLOT1 = TILE_B, VSLOT0 = 2 * TILE_B, VSLOT1 = 3 * TILE_B;
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, hf = lane >> 5;
-
-    // q-tile-major order (XCD-local heads); causal runs the longest q-tiles first
-    const int id = blockIdx.x;
-    const int bh = id % BH;
-    int qt = id / BH;
-    if (MASK == kMaskCausal) qt = num_qtiles - 1 - qt;
-    const int b = bh / H;
-    const int q0 = qt * BM;
-    int kv_len = Nk;
-    if (MASK == kMaskPadding) {
-        const int L = valid_lens[b];
-        kv_len = L < 0 ? 0 : (L > Nk ? Nk : L);
-    }
-    int kv_end = kv_len;
-    if (MASK == kMaskCausal) kv_end = min(kv_len, q0 + BM);
-    const int ntiles = (kv_end + kBlockN - 1) / kBlockN;
-    const uint16_t *Kh = K + (size_t)bh * Nk * D;
-    const uint16_t *Vh = V + (size_t)bh * Nk * D;
-
-    // Q^T (B operands), resident in AGPRs
-    const int qmin_w = q0 + wave * RW, qmax_w = qmin_w + RW - 1;
-    int qrow[2];
-    bf16x8 qreg[2][KS];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        qrow[qb] = qmin_w + qb * 32 + l32;
-        const bool ok = qrow[qb] < Nq;
-        const uint16_t *qp = Q + ((size_t)bh * Nq + (ok ? qrow[qb] : 0)) * D + hf * 8;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4 v = ok ? *(const u32x4 *)(qp + ks * 16) : u32x4{0u, 0u, 0u, 0u};
-            qreg[qb][ks] = __builtin_bit_cast(bf16x8, v);
-        }
-    }
-    f32x16 acc[2][DB];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int i = 0; i < DB; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[qb][i][r] = 0.f;
-    float mc_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-
-    const TileAddrs<D> ad = tile_addrs<D>(lane);
-    const uint32_t lds0 = lds_addr(smem);
-    uint32_t voff[CH];
-    int drow[CH];
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-        const int c = (j * WAVES + wave) * 64 + lane;
-        const int r = c / CPR, x = c % CPR;
-        drow[j] = r;
-        voff[j] = (uint32_t)(r * D + ((x ^ swz<D>(r)) << 3)) * 2;
-    }
-    // DMA of tile t of K or V into an LDS slot; rows at or past kv_end are
-    // not read (the last valid row is fetched instead; its weight is 0)
-    auto issue = [&](const uint16_t *src, int t, uint32_t slot_off) {
-        const int k0 = t * kBlockN;
-        const uint16_t *base = src + (size_t)k0 * D;
-        const bool tail = k0 + kBlockN > kv_end;
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            uint32_t off = voff[j];
-            if (tail) {
-                const int r = min(drow[j], kv_end - 1 - k0);
-                off = off - (uint32_t)(drow[j] - r) * (D * 2);
-            }
-            lds_dma16(__builtin_amdgcn_readfirstlane(lds0 + slot_off + (j * WAVES + wave) * 1024), base, off);
-        }
-    };
-    const int ntiles_w = (MASK == kMaskCausal) ? min(ntiles, qmax_w / kBlockN + 1) : ntiles;
-    auto needs_mask = [&](int t) {
-        const int k0 = t * kBlockN;
-        return (k0 + kBlockN > kv_len) || (MASK == kMaskCausal && k0 + kBlockN - 1 > qmin_w);
-    };
-
-    f32x16 sn[2][2];  // S of the next tile (AGPRs, MFMA only)
-    f32x16 sc[2][2];  // S of the current tile (VGPRs)
-    bf16x8 pb[2][4];  // P of one tile in bf16 (VGPRs)
-
-    // S = K Q^T into sn, K tile at byte offset KOFF; with EXP, the
-    // exponentials, row sums and bf16 P of the tile in sc are interleaved:
-    // k-step ks handles P chunk ks = (qb = ks/4, c = ks%4), 8 scores.
-    auto s_phase = [&](auto koff, auto with_exp, const float (&mref)[2], float (&lsum)[2]) {
-        constexpr int KOFF = decltype(koff)::value;
-        constexpr bool EXP = decltype(with_exp)::value;
-        bf16x8 kop[2][2];
-        kop[0][0] = *(const bf16x8 *)(smem + ad.k[0] + KOFF);
-        kop[0][1] = *(const bf16x8 *)(smem + ad.k[0] + KOFF + 32 * D * 2);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int cu = ks & 1;
-            if (ks + 1 < KS) {
-                kop[cu ^ 1][0] = *(const bf16x8 *)(smem + ad.k[ks + 1] + KOFF);
-                kop[cu ^ 1][1] = *(const bf16x8 *)(smem + ad.k[ks + 1] + KOFF + 32 * D * 2);
-            }
-            const int qb_e = ks >> 2, c = ks & 3, jb_e = c >> 1, r0 = (c & 1) * 8;
-            float pv[8];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int qb = m >> 1, jb = m & 1;
-                __builtin_amdgcn_sched_barrier(0);
-                if (ks == 0)
-                    mfma_zero_agpr_ba(sn[qb][jb], kop[cu][jb], qreg[qb][ks]);
-                else if (ks == KS - 1 && m == 3)
-                    mfma_acc_agpr_ba_last(sn[qb][jb], kop[cu][jb], qreg[qb][ks]);
-                else
-                    mfma_acc_agpr_ba(sn[qb][jb], kop[cu][jb], qreg[qb][ks]);
-                if constexpr (EXP) {
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int e = m * 2 + u;
-                        pv[e] = fast_exp2(fmaf(sc[qb_e][jb_e][r0 + e], c_log2, -mref[qb_e]));
-                    }
-                }
-            }
-            if constexpr (EXP) {
-                u32x4 w;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    w[u] = pack_bf16x2(pv[2 * u], pv[2 * u + 1]);
-                    lsum[qb_e] = add_bf16x2(w[u], lsum[qb_e]);
-                }
-                pb[qb_e][c] = __builtin_bit_cast(bf16x8, w);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    // exponentials only (no next tile for this wave)
-    auto exp_only = [&](const float (&mref)[2], float (&lsum)[2]) {
-#pragma unroll
-        for (int g = 0; g < 8; ++g) {
-            const int qb = g >> 2, c = g & 3, jb = c >> 1, r0 = (c & 1) * 8;
-            u32x4 w;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float p0 = fast_exp2(fmaf(sc[qb][jb][r0 + 2 * u], c_log2, -mref[qb]));
-                const float p1 = fast_exp2(fmaf(sc[qb][jb][r0 + 2 * u + 1], c_log2, -mref[qb]));
-                w[u] = pack_bf16x2(p0, p1);
-                lsum[qb] = add_bf16x2(w[u], lsum[qb]);
-            }
-            pb[qb][c] = __builtin_bit_cast(bf16x8, w);
-        }
-    };
-    // O += P V with the V tile at byte offset VOFF; with COPY, S(t) moves
-    // from sn (AGPRs) to sc (VGPRs) in between: 4 scores per MFMA.
-    auto pv_phase = [&](auto voff_c, auto with_copy) {
-        constexpr int VOFF = decltype(voff_c)::value;
-        constexpr bool COPY = decltype(with_copy)::value;
-        valu_fence_v8(pb);
-        bf16x8 vop[2];
-        {
-            const uint8_t *p0 = smem + ad.v[0][0] + VOFF, *p1 = smem + ad.v[0][1] + VOFF;
-            vop[0] = lds_tr_pair((const uint16_t *)p0, (const uint16_t *)p1);
-        }
-#pragma unroll
-        for (int g = 0; g < 16; ++g) {
-            const int c = g >> 2, db = g & 3, cu = g & 1;
-            if (g + 1 < 16) {
-                const int c2 = (g + 1) >> 2, db2 = (g + 1) & 3;
-                const uint8_t *p0 = smem + ad.v[db2][0] + VOFF + c2 * 16 * D * 2;
-                const uint8_t *p1 = smem + ad.v[db2][1] + VOFF + c2 * 16 * D * 2;
-                vop[cu ^ 1] = lds_tr_pair((const uint16_t *)p0, (const uint16_t *)p1);
-            }
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                __builtin_amdgcn_sched_barrier(0);
-                if (g == 15 && qb == 1)
-                    mfma_acc_agpr_last(acc[qb][db], vop[cu], pb[qb][c]);
-                else
-                    mfma_acc_agpr(acc[qb][db], vop[cu], pb[qb][c]);
-                if constexpr (COPY) {
-                    // scores e, e+1 (e = g*4 + qb*2) of the 64 -> sc[e/32][(e/16)%2][e%16]
-                    const int e = g * 4 + qb * 2, a = e >> 5, j = (e >> 4) & 1, r = e & 15;
-                    float d0, d1;
-                    agpr_read2(d0, d1, sn[a][j][r], sn[a][j][r + 1]);
-                    sc[a][j][r] = d0;
-                    sc[a][j][r + 1] = d1;
-                }
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    // mask, max and reference update of the tile in sc; rescales O when any
-    // row of the wave moved its reference
-    auto reference = [&](int t, float (&mref)[2]) {
-        if (needs_mask(t)) {
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) mask_scores<MASK>(sc[qb], t * kBlockN, kv_len, qrow[qb], hf);
-        }
-        float alpha[2];
-        bool upd = false;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            bool u;
-            mref[qb] = softmax_ref(sc[qb], mc_run[qb], l_run[qb], c_log2, alpha[qb], u);
-            upd = upd || u;
-        }
-        if (__builtin_amdgcn_ballot_w64(upd)) {
-            mfma_fence_a8(acc);
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int i = 0; i < DB; ++i)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[qb][i][r] *= alpha[qb];
-            valu_fence_a8(acc);
-        }
-    };
-
-    // prologue: S(0) from K(0); K(1) on its way
-    if (ntiles > 0) {
-        issue(Kh, 0, KSLOT0);
-        if (ntiles > 1) issue(Kh, 1, KSLOT1);
-        wait_vmcnt0();
-        __syncthreads();
-        float dm[2] = {0.f, 0.f}, dl[2] = {0.f, 0.f};
-        s_phase(std::integral_constant<int, KSLOT0>(), std::false_type(), dm, dl);
-        __syncthreads();  // every wave is done with K slot 0 before it is refilled
-    }
-
-    auto iteration = [&](int t, auto parity) {
-        constexpr int P = decltype(parity)::value;  // t % 2
-        constexpr int KNEXT = P ? KSLOT0 : KSLOT1;  // K(t+1) in slot (t+1)%2
-        constexpr int VPREV = P ? VSLOT0 : VSLOT1;  // V(t-1) in slot (t-1)%2
-        if (t + 2 < ntiles) issue(Kh, t + 2, P ? KSLOT1 : KSLOT0);
-        issue(Vh, t, P ? VSLOT1 : VSLOT0);
-        const bool do_pv = t >= 1 && t - 1 < ntiles_w;
-        if (t < ntiles_w) {
-            mfma_fence_a4(sn);
-            if (do_pv) {
-                pv_phase(std::integral_constant<int, VPREV>(), std::true_type());
-            } else {
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                        for (int r = 0; r < 16; r += 2) {
-                            float d0, d1;
-                            agpr_read2(d0, d1, sn[qb][jb][r], sn[qb][jb][r + 1]);
-                            sc[qb][jb][r] = d0;
-                            sc[qb][jb][r + 1] = d1;
-                        }
-            }
-            float mref[2];
-            reference(t, mref);
-            float lsum[2] = {0.f, 0.f};
-            if (t + 1 < ntiles_w)
-                s_phase(std::integral_constant<int, KNEXT>(), std::true_type(), mref, lsum);
-            else
-                exp_only(mref, lsum);
-            l_run[0] += lsum[0];
-            l_run[1] += lsum[1];
-        } else if (do_pv) {
-            pv_phase(std::integral_constant<int, VPREV>(), std::false_type());
-        }
-        wait_vmcnt0();
-        __syncthreads();
-    };
-    for (int t = 0; t < ntiles; t += 2) {
-        iteration(t, std::integral_constant<int, 0>());
-        if (t + 1 < ntiles) iteration(t + 1, std::integral_constant<int, 1>());
-    }
-    // P.V of the wave's last tile, when it was the workgroup's last tile too
-    if (ntiles > 0 && ntiles - 1 < ntiles_w) {
-        if ((ntiles - 1) & 1)
-            pv_phase(std::integral_constant<int, VSLOT1>(), std::false_type());
-        else
-            pv_phase(std::integral_constant<int, VSLOT0>(), std::false_type());
-    }
-
-    // ---- epilogue: O = O_acc / l (0 for a row with no visible key) ----
-    mfma_fence_a8(acc);
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const float l_tot = half_swap_sum(l_run[qb]);
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        if (qrow[qb] < Nq) {
-            size_t row_off;
-            if (OLAYOUT == kOutBHND) {
-                row_off = ((size_t)bh * Nq + qrow[qb]) * D;
-            } else {
-                const int hh = bh % H;
-                row_off = (((size_t)b * Nq + qrow[qb]) * H + hh) * D;
-            }
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    const int d0 = db * 32 + rg * 8 + hf * 4;
-                    const float v0 = acc[qb][db][rg * 4 + 0] * inv, v1 = acc[qb][db][rg * 4 + 1] * inv;
-                    const float v2 = acc[qb][db][rg * 4 + 2] * inv, v3 = acc[qb][db][rg * 4 + 3] * inv;
-                    if (OUT_F32) {
-                        *(f32x4 *)((float *)Out + row_off + d0) = f32x4{v0, v1, v2, v3};
-                    } else {
-                        *(u32x2 *)((uint16_t *)Out + row_off + d0) =
-                            u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-                    }
-                }
-        }
-    }
+    for (int qb = 0; qb < QB; ++qb) store_rows<D, OUT_F32, OLAYOUT>(acc[qb], l_run[qb], qrow[qb], bh, H, Nq, b, hf, Out);
 }
 
 template <int D, int MASK, bool OUT_F32, int OLAYOUT>
 hipError_t launch_variant(const void *Q, const void *K, const void *V, const int32_t *valid_lens, float scale,
                           void *O, int B, int H, int Nq, int Nk, hipStream_t stream)
 {
-    // 32 (QB = 1) or 64 (QB = 2) query rows per wave.
-    constexpr bool D128 = D == 128 && kD128Design == 3;
-    constexpr int QB = (D == 128 && kD128Design >= 2) ? 2 : 1;
-    constexpr int BM = (D128 ? 4 : (D == 128 ? kWaves128 : kWaves64)) * 32 * QB;
+    // 32 (QB = 1) or 64 (QB = 2) query rows per wave; 64-row waves need the
+    // whole register file: one wave per SIMD, 4 per workgroup
+    constexpr int QB = (D == 128 && kD128Design == 2) ? 2 : 1;
+    constexpr int WAVES = QB == 2 ? 4 : (D == 128 ? kWaves128 : kWaves64);
+    constexpr int BM = WAVES * 32 * QB;
     const int BH = B * H;
     const int num_qtiles = (Nq + BM - 1) / BM;
     const long long grid = (long long)num_qtiles * BH;
@@ -864,16 +533,9 @@ hipError_t launch_variant(const void *Q, const void *K, const void *V, const int
     // scores (-inf) map to weight 0 without a select; below 1e-30 every
     // visible exp2 argument rounds to 0 anyway, which is the scale = 0 result.
     const float c_log2 = fmaxf(scale * 1.4426950408889634f, 1e-30f);
-    if constexpr (D128) {
-        hipLaunchKernelGGL((attn_fwd_d128_kernel<MASK, OUT_F32, OLAYOUT>), dim3((unsigned)grid), dim3(256), 0, stream,
-                           (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, valid_lens, c_log2, O, H,
-                           Nq, Nk, num_qtiles, BH);
-    } else {
-        constexpr int WAVES = BM / (32 * QB);
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QB, MASK, OUT_F32, OLAYOUT, WAVES>), dim3((unsigned)grid),
-                           dim3(WAVES * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
-                           valid_lens, c_log2, O, H, Nq, Nk, num_qtiles, BH);
-    }
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QB, MASK, OUT_F32, OLAYOUT, WAVES>), dim3((unsigned)grid),
+                       dim3(WAVES * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
+                       valid_lens, c_log2, O, H, Nq, Nk, num_qtiles, BH);
     return hipGetLastError();
 }
 

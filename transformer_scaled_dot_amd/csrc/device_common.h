@@ -60,40 +60,6 @@ __device__ __forceinline__ void mfma_zero_vgpr_ba(f32x16 &acc, const bf16x8 &a, 
     asm("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
 }
 
-// A operand from VGPRs, B operand from AGPRs, accumulator in AGPRs.
-__device__ __forceinline__ void mfma_acc_agpr_ba(f32x16 &acc, const bf16x8 &a, const bf16x8 &b)
-{
-    asm("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "a"(b));
-}
-
-__device__ __forceinline__ void mfma_zero_agpr_ba(f32x16 &acc, const bf16x8 &a, const bf16x8 &b)
-{
-    asm("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&a"(acc) : "v"(a), "a"(b));
-}
-
-// The same two MFMAs followed by >= 19 wait states: used as the last MFMA
-// of a phase, so that no later instruction -- including register copies the
-// compiler may insert anywhere after this statement -- can see unfinished
-// accumulators.
-__device__ __forceinline__ void mfma_acc_agpr_ba_last(f32x16 &acc, const bf16x8 &a, const bf16x8 &b)
-{
-    asm("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4"
-        : "+a"(acc)
-        : "v"(a), "a"(b));
-}
-
-__device__ __forceinline__ void mfma_acc_agpr_last(f32x16 &acc, const bf16x8 &a, const bf16x8 &b)
-{
-    asm("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4"
-        : "+a"(acc)
-        : "v"(a), "v"(b));
-}
-
-__device__ __forceinline__ void mfma_fence_a4(f32x16 (&x)[2][2])
-{
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+a"(x[0][0]), "+a"(x[0][1]), "+a"(x[1][0]), "+a"(x[1][1]));
-}
-
 // >= 19 wait states after a 16-pass MFMA wrote these accumulators, before
 // anything else reads or writes them.
 __device__ __forceinline__ void mfma_fence_v4(f32x16 &a, f32x16 &b, f32x16 &c, f32x16 &d)
@@ -130,13 +96,6 @@ __device__ __forceinline__ void valu_fence_v8(bf16x8 (&x)[2][4])
     asm volatile("s_nop 1"
                  : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]), "+v"(x[1][0]), "+v"(x[1][1]),
                    "+v"(x[1][2]), "+v"(x[1][3]));
-}
-
-// AGPR -> VGPR copy of two values at exactly this point of the instruction
-// stream (a plain assignment would let the compiler place the copy anywhere).
-__device__ __forceinline__ void agpr_read2(float &d0, float &d1, float s0, float s1)
-{
-    asm volatile("v_accvgpr_read_b32 %0, %2\n\tv_accvgpr_read_b32 %1, %3" : "=v"(d0), "=v"(d1) : "a"(s0), "a"(s1));
 }
 
 // Two transposed 4x4 reads make one 8-element MFMA operand.
