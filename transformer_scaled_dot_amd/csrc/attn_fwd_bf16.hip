@@ -44,9 +44,9 @@ constexpr int kBlockN = 64;            // keys per LDS tile
 constexpr float kRescaleSlack = 8.f;    // log2 units the reference max may lag the true max
 // Kernel design for 128-wide heads: 1 = 32 rows per wave, software
 // pipelined; 2 = 64 rows per wave (inline-asm MFMA, O in AGPRs, one wave
-// per SIMD).
+// per SIMD); 3 = 64 rows per wave with the hand-scheduled tile step.
 #ifndef TSD_D128_DESIGN
-#define TSD_D128_DESIGN 1
+#define TSD_D128_DESIGN 3
 #endif
 constexpr int kD128Design = TSD_D128_DESIGN;
 #ifndef TSD_WAVES128
@@ -515,13 +515,162 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
     for (int qb = 0; qb < QB; ++qb) store_rows<D, OUT_F32, OLAYOUT>(acc[qb], l_run[qb], qrow[qb], bh, H, Nq, b, hf, Out);
 }
 
+#include "attn_qb2_tile.inc"
+
+// Row max of one query block's 64 scores of a tile (both half-waves).
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[2])
+{
+    float mx = s[0][0];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
+    return half_swap_max(mx);
+}
+
+// ---------------------------------------------------------------------------
+// 128-wide heads, 64 query rows per wave (two blocks of 32), 4 waves per
+// workgroup, one wave per SIMD. Every K or V operand read from LDS feeds two
+// MFMAs, which halves the LDS bytes per MFMA against 32-row waves. The
+// steady-state tile step -- S(t+1) MFMAs, the exponentials of S(t), the
+// P(t).V(t) MFMAs and the row max of S(t+1) -- is one inline-asm block with a
+// fixed interleaved schedule (generated by gen_qb2_tile.py), since a single
+// wave per SIMD has no partner wave to hide its latencies. The tile's
+// bookkeeping (masking, reference max, rescale of O), the first and the last
+// tile of each wave run in C++ around it.
+//
+// Registers: O and Q^T in AGPRs, the two score buffers, P and the operand
+// staging in VGPRs, at the physical registers the asm block names.
+template <int MASK, bool OUT_F32, int OLAYOUT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_fwd_qb2_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    const int32_t *__restrict__ valid_lens, float c_log2, void *__restrict__ Out, int H, int Nq, int Nk,
+    int num_qtiles, int BH)
+{
+    constexpr int D = 128, QB = 2, WAVES = 4, RW = 64, BM = WAVES * RW;
+    constexpr int KS = D / 16, DB = D / 32;
+    constexpr int TILE_B = kBlockN * D * 2;
+    constexpr int CPR = D / 8;
+    constexpr int CH = kBlockN * CPR / (WAVES * 64);
+    static_assert(kBlockN * CPR % (WAVES * 64) == 0, "tile must split evenly over the workgroup");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_B];
+    constexpr int KSLOT0 = 0, KSLOT1 = TILE_B, VSLOT0 = 2 * TILE_B, VSLOT1 = 3 * TILE_B;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hf = lane >> 5;
+
+    const int id = blockIdx.x;
+    const int bh = id % BH;
+    int qt = id / BH;
+    if (MASK == kMaskCausal) qt = num_qtiles - 1 - qt;
+    const int b = bh / H;
+    const int q0 = qt * BM;
+
+    int kv_len = Nk;
+    if (MASK == kMaskPadding) {
+        const int L = valid_lens[b];
+        kv_len = L < 0 ? 0 : (L > Nk ? Nk : L);
+    }
+    int kv_end = kv_len;
+    if (MASK == kMaskCausal) kv_end = min(kv_len, q0 + BM);
+    const int ntiles = (kv_end + kBlockN - 1) / kBlockN;
+
+    const uint16_t *Kh = K + (size_t)bh * Nk * D;
+    const uint16_t *Vh = V + (size_t)bh * Nk * D;
+
+    const int qmin_w = q0 + wave * RW, qmax_w = qmin_w + RW - 1;
+    int qrow[QB];
+    u32x4 qv[QB][KS];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        qrow[qb] = qmin_w + qb * 32 + l32;
+        const bool ok = qrow[qb] < Nq;
+        const uint16_t *qp = Q + ((size_t)bh * Nq + (ok ? qrow[qb] : 0)) * D + hf * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qv[qb][ks] = ok ? *(const u32x4 *)(qp + ks * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+    // O = 0 and Q^T in the AGPRs the tile steps name
+    bf16x8 qreg[QB][KS];
+    f32x16 acc[QB][DB];
+    qb2_init(acc, qreg, qv);
+    float mc_run[QB] = {-INFINITY, -INFINITY}, l_run[QB] = {0.f, 0.f}, mx[QB] = {0.f, 0.f};
+
+    const TileAddrs<D> ad = tile_addrs<D>(lane);
+    const uint32_t lds0 = lds_addr(smem);
+    uint32_t voff[CH];
+    int drow[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        const int c = (j * WAVES + wave) * 64 + lane;
+        const int r = c / CPR, x = c % CPR;
+        drow[j] = r;
+        voff[j] = (uint32_t)(r * D + ((x ^ swz<D>(r)) << 3)) * 2;
+    }
+    auto issue = [&](const uint16_t *src, int t, uint32_t slot_off) {
+        const int k0 = t * kBlockN;
+        const uint16_t *base = src + (size_t)k0 * D;
+        const bool tail = k0 + kBlockN > kv_end;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            uint32_t off = voff[j];
+            if (tail) {
+                const int r = min(drow[j], kv_end - 1 - k0);
+                off = off - (uint32_t)(drow[j] - r) * (D * 2);
+            }
+            lds_dma16(__builtin_amdgcn_readfirstlane(lds0 + slot_off + (j * WAVES + wave) * 1024), base, off);
+        }
+    };
+
+    const int ntiles_w = (MASK == kMaskCausal) ? min(ntiles, qmax_w / kBlockN + 1) : ntiles;
+    // first tile of this wave that needs a mask: the tile crossing kv_len, or
+    // (causal) the first tile with a key past the wave's first row
+    int t_mask = kv_len / kBlockN;
+    if (MASK == kMaskCausal) t_mask = min(t_mask, (qmin_w + 1) / kBlockN);
+    // a visible key of row qrow satisfies key <= lim; the asm compares the key's
+    // offset within the tile (lane half included) against lim - tile start
+    int32_t lim[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) lim[qb] = (MASK == kMaskCausal ? min(qrow[qb], kv_len - 1) : kv_len - 1) - hf * 4;
+    const int t_tail = (kv_end % kBlockN) ? ntiles - 1 : 0x7fffffff;  // the one tile with rows past kv_end
+
+    // LDS byte addresses of the operand reads (the tile offsets are instruction immediates)
+    uint32_t kaddr[KS], vaddr[DB][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kaddr[ks] = lds0 + ad.k[ks];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        vaddr[db][0] = lds0 + ad.v[db][0];
+        vaddr[db][1] = lds0 + ad.v[db][1];
+    }
+    float mc0 = -INFINITY, mc1 = -INFINITY;
+    if (ntiles > 0) {
+        issue(Kh, 0, KSLOT0);
+        if (ntiles > 1) issue(Kh, 1, KSLOT1);
+        issue(Vh, 0, VSLOT0);
+        wait_vmcnt0();
+        __syncthreads();
+    }
+    const uint64_t kh = (uint64_t)Kh, vh = (uint64_t)Vh;
+    const uint32_t lbw = __builtin_amdgcn_readfirstlane(lds0 + wave * 1024);
+    // wave-uniform values go to the asm in SGPRs
+    auto u = [](int x) { return (int32_t)__builtin_amdgcn_readfirstlane(x); };
+    qb2_loop(acc, qreg, kaddr, vaddr, voff, drow, lim[0], lim[1], c_log2, l_run[0], l_run[1], mc0, mc1,
+             u(0), u(ntiles), u(ntiles_w), u(t_mask), u(t_tail), u(kv_end), u((uint32_t)kh), u((uint32_t)(kh >> 32)),
+             u((uint32_t)vh), u((uint32_t)(vh >> 32)), lbw);
+
+    mfma_fence_a8(acc);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) store_rows<D, OUT_F32, OLAYOUT>(acc[qb], l_run[qb], qrow[qb], bh, H, Nq, b, hf, Out);
+}
+
 template <int D, int MASK, bool OUT_F32, int OLAYOUT>
 hipError_t launch_variant(const void *Q, const void *K, const void *V, const int32_t *valid_lens, float scale,
                           void *O, int B, int H, int Nq, int Nk, hipStream_t stream)
 {
     // 32 (QB = 1) or 64 (QB = 2) query rows per wave; 64-row waves need the
     // whole register file: one wave per SIMD, 4 per workgroup
-    constexpr int QB = (D == 128 && kD128Design == 2) ? 2 : 1;
+    constexpr bool QB2ASM = D == 128 && kD128Design == 3;
+    constexpr int QB = (D == 128 && kD128Design >= 2) ? 2 : 1;
     constexpr int WAVES = QB == 2 ? 4 : (D == 128 ? kWaves128 : kWaves64);
     constexpr int BM = WAVES * 32 * QB;
     const int BH = B * H;
@@ -533,9 +682,14 @@ hipError_t launch_variant(const void *Q, const void *K, const void *V, const int
     // scores (-inf) map to weight 0 without a select; below 1e-30 every
     // visible exp2 argument rounds to 0 anyway, which is the scale = 0 result.
     const float c_log2 = fmaxf(scale * 1.4426950408889634f, 1e-30f);
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QB, MASK, OUT_F32, OLAYOUT, WAVES>), dim3((unsigned)grid),
-                       dim3(WAVES * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
-                       valid_lens, c_log2, O, H, Nq, Nk, num_qtiles, BH);
+    if constexpr (QB2ASM)
+        hipLaunchKernelGGL((attn_fwd_qb2_kernel<MASK, OUT_F32, OLAYOUT>), dim3((unsigned)grid), dim3(256), 0, stream,
+                           (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, valid_lens, c_log2, O, H,
+                           Nq, Nk, num_qtiles, BH);
+    else
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QB, MASK, OUT_F32, OLAYOUT, WAVES>), dim3((unsigned)grid),
+                           dim3(WAVES * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
+                           valid_lens, c_log2, O, H, Nq, Nk, num_qtiles, BH);
     return hipGetLastError();
 }
 

@@ -1,0 +1,432 @@
+"""Generate attn_qb2_tile.inc: the tile steps of the 64-rows-per-wave attention
+kernel for 128-wide heads, as inline-asm blocks with a fixed instruction
+schedule.
+
+A wave owns two 32-row query blocks (qb = 0, 1). One steady-state step for
+key tile t:
+  * S(t+1)^T = K(t+1) Q^T           32 MFMAs (8 k-steps x 2 key blocks x 2 qb)
+  * P(t) = exp2(S(t) * c - mref)    rounded to bf16; row sums added to l
+  * O^T += V(t)^T P(t)^T            32 MFMAs (4 key chunks x 4 d-blocks x 2 qb)
+  * the row max of S(t+1)           for the next step's reference update
+interleaved so that about five VALU instructions and one or two LDS reads sit
+between consecutive MFMAs (a wave alone on its SIMD has no partner wave to
+hide latencies). The first step of a wave computes only S(0) and its row max;
+the last one only P and P.V. Lane layouts are those of the C++ kernel
+(attn_fwd_bf16.hip): S^T has one query per lane, P goes from the score
+accumulator to the P.V MFMA in the permuted key order, V^T operands come from
+pairs of ds_read_b64_tr_b16.
+
+Every block names the same physical registers, bound through the asm
+constraints, so that single elements of the 16-register accumulators can be
+addressed and the compiler never has to move the operands between blocks:
+  a[0:127]    O[qb][db]         a[128:191]  Q^T[qb][ks]  (MFMA B operand)
+  v[0:63]     S buffer 0        v[64:127]   S buffer 1   (S[qb][jb], 16 each)
+  v[128:159]  P[qb][c]          v[160:175]  K operand staging (4 slots)
+  v[176:191]  V operand staging v[192:199]  exp temporaries
+  v[200:203]  max temporaries
+The per-lane scalars (LDS read addresses, mref, l and the row max) are plain
+register operands that the compiler places.
+For the schedule it emits, the generator checks that every MFMA operand read
+has completed (lgkmcnt) before its MFMA, that no staging slot is rewritten
+before its last reader has issued, that every P operand is written at least
+two instructions before its first MFMA, and that the row max reads the new S
+only after three further MFMAs (or 24 wait states) behind the last MFMA that
+wrote it. Blocks end with 24 wait states so that O is complete when C++ code
+next reads it.
+
+Run:  python gen_qb2_tile.py  (writes attn_qb2_tile.inc next to this file)
+"""
+from __future__ import annotations
+
+import os
+
+D, KS, DB, QB = 128, 8, 4, 2
+TILE_B = 64 * D * 2
+S_BUF = (0, 64)
+P0, KST, VST, TMP, MXT = 128, 160, 176, 192, 200
+CLOB_END = 204         # v[128:203] are the block's scratch registers
+O_A, Q_A = 0, 128
+NKS = NVS = 4          # staging slots
+LOOK = 5               # MFMAs between an operand's read and its first MFMA
+VALU_BUDGET = 5        # VALU cost units per MFMA slot (exp counts 2)
+ONES_BF16X2 = "0x3f803f80"
+
+
+def vr(base, n):
+    return "v[%d:%d]" % (base, base + n - 1)
+
+
+def ar(base, n):
+    return "a[%d:%d]" % (base, base + n - 1)
+
+
+def s_reg(buf, qb, jb, r):
+    return S_BUF[buf] + (qb * 2 + jb) * 16 + r
+
+
+def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mref1]"), mx=("%[mx0]", "%[mx1]")):
+    """Instruction list of one block.
+
+    x_buf: S buffer holding S(t) (exp + P.V part), y_buf: buffer receiving the
+    new scores; kslot / vslot: LDS tile slots (0 or 1) of the K and V tiles."""
+    koff = kslot * TILE_B
+    voff = 2 * TILE_B + vslot * TILE_B
+
+    mfma = []
+    if do_s:
+        for i in range(32):
+            ks, jb, qb = i // 4, (i // 2) % 2, i % 2
+            kop = ks * 2 + jb
+            dst = S_BUF[y_buf] + (qb * 2 + jb) * 16
+            src_c = "0" if ks == 0 else vr(dst, 16)
+            mfma.append(dict(op=("k", kop), kind="S", qb=qb, jb=jb,
+                             text="v_mfma_f32_32x32x16_bf16 %s, %s, %s, %s" % (
+                                 vr(dst, 16), vr(KST + 4 * (kop % NKS), 4), ar(Q_A + 4 * (qb * KS + ks), 4), src_c)))
+    if do_pv:
+        for j in range(32):
+            c, db, qb = j // 8, (j // 2) % 4, j % 2
+            vop = c * DB + db
+            acc = O_A + (qb * DB + db) * 16
+            mfma.append(dict(op=("v", vop), kind="PV", qb=qb, c=c,
+                             text="v_mfma_f32_32x32x16_bf16 %s, %s, %s, %s" % (
+                                 ar(acc, 16), vr(VST + 4 * (vop % NVS), 4), vr(P0 + 4 * (qb * 4 + c), 4),
+                                 ar(acc, 16))))
+    first_use, last_use = {}, {}
+    for m, f in enumerate(mfma):
+        first_use.setdefault(f["op"], m)
+        last_use[f["op"]] = m
+
+    reads = {}
+    for kop in range(2 * KS):
+        ks, jb = kop // 2, kop % 2
+        reads[("k", kop)] = ["ds_read_b128 %s, %s offset:%d" % (
+            vr(KST + 4 * (kop % NKS), 4), "%%[ka%d]" % ks, koff + jb * 32 * D * 2)]
+    for vop in range(4 * DB):
+        c, db = vop // DB, vop % DB
+        dst = VST + 4 * (vop % NVS)
+        reads[("v", vop)] = ["ds_read_b64_tr_b16 %s, %%[va%d_%d] offset:%d" % (vr(dst + 2 * h, 2), db, h,
+                                                                               voff + c * 16 * D * 2) for h in range(2)]
+    read_at = {}
+    for op, fu in first_use.items():
+        read_at.setdefault(max(fu - LOOK, 0), []).append(op)
+    for kind, nslots in (("k", NKS), ("v", NVS)):
+        for o in sorted(o for o in first_use if o[0] == kind):
+            nxt = (kind, o[1] + nslots)
+            if nxt in first_use:
+                assert max(first_use[nxt] - LOOK, 0) > last_use[o], ("staging slot reused too early", o, nxt)
+
+    items = []
+    if do_pv:
+        for c in range(4):
+            for qb in range(QB):
+                jb, r0 = c // 2, (c % 2) * 8
+                ins = [("v_fma_f32 v%d, v%d, %%[c], -%s" % (TMP + u, s_reg(x_buf, qb, jb, r0 + u), mref[qb]), 1)
+                       for u in range(8)]
+                ins += [("v_exp_f32 v%d, v%d" % (TMP + u, TMP + u), 2) for u in range(8)]
+                p = P0 + 4 * (qb * 4 + c)
+                cvt = ["v_cvt_pk_bf16_f32 v%d, v%d, v%d" % (p + w, TMP + 2 * w, TMP + 2 * w + 1) for w in range(4)]
+                dot = ["v_dot2c_f32_bf16 %%[l%d], %s, v%d" % (qb, ONES_BF16X2, p + w) for w in range(4)]
+                ins += [(t, 1) for t in (cvt[0], cvt[1], cvt[2], dot[0], cvt[3], dot[1], dot[2], dot[3])]
+                dl = min(m for m, f in enumerate(mfma) if f["kind"] == "PV" and f["qb"] == qb and f["c"] == c)
+                items.append(dict(ins=ins, deadline=dl - 1, ready=0, p=p, name="exp q%d c%d" % (qb, c)))
+    s_last = max((m for m, f in enumerate(mfma) if f["kind"] == "S"), default=None)
+    if do_max:
+        assert do_s
+        for qb in range(QB):
+            ins = []
+            for jb in range(2):
+                m = MXT + jb
+                vals = [s_reg(y_buf, qb, jb, r) for r in range(16)]
+                ins.append(("v_max3_f32 v%d, v%d, v%d, v%d" % (m, vals[0], vals[1], vals[2]), 1))
+                rest = vals[3:]
+                while rest:
+                    a, b = rest[0], rest[1] if len(rest) > 1 else rest[0]
+                    ins.append(("v_max3_f32 v%d, v%d, v%d, v%d" % (m, m, a, b), 1))
+                    rest = rest[2:]
+            ins.append(("v_max_f32 v%d, v%d, v%d" % (MXT, MXT, MXT + 1), 1))
+            ins.append(("v_mov_b32 v%d, v%d" % (MXT + 1, MXT), 1))
+            ins.append(("s_nop 1", 1))
+            ins.append(("v_permlane32_swap_b32 v%d, v%d" % (MXT, MXT + 1), 1))
+            ins.append(("v_max_f32 %s, v%d, v%d" % (mx[qb], MXT, MXT + 1), 1))
+            items.append(dict(ins=ins, deadline=10 ** 9, ready=s_last + 4, p=None, name="max q%d" % qb))
+
+    out = ["s_waitcnt lgkmcnt(0)"]
+    issued, pos, p_done = [], {}, {}
+    queue = [dict(it, k=0, order=n) for n, it in enumerate(items)]
+
+    def emit_reads(slot):
+        for op in read_at.get(slot, []):
+            for t in reads[op]:
+                out.append(t)
+                issued.append(op)
+            pos[op] = len(issued) - 1
+
+    def emit_valu(it):
+        t, cost = it["ins"][it["k"]]
+        out.append(t)
+        it["k"] += 1
+        if t.startswith("v_cvt_pk_bf16_f32"):
+            p_done[int(t.split()[1][1:].rstrip(",")) // 4 * 4] = len(out) - 1
+        return cost
+
+    emit_reads(0)
+    for m, f in enumerate(mfma):
+        if f["kind"] == "PV":
+            p = P0 + 4 * (f["qb"] * 4 + f["c"])
+            # nothing to overlap with yet (first P.V MFMAs of a block without S): finish that P operand here
+            for it in queue:
+                if it["p"] == p:
+                    while it["k"] < len(it["ins"]):
+                        emit_valu(it)
+            # at least two instructions between the last write of P and the MFMA that reads it
+            gap = sum(1 for t in out[p_done[p] + 1:] if not t.startswith("s_waitcnt"))
+            if gap < 2:
+                out.append("s_nop %d" % (1 - gap))
+        outstanding_after = len(issued) - 1 - pos[f["op"]]
+        assert 0 <= outstanding_after <= 15
+        out.append("s_waitcnt lgkmcnt(%d)" % outstanding_after)
+        out.append(f["text"])
+        emit_reads(m + 1)
+        budget = VALU_BUDGET
+        while budget > 0:
+            cand = [it for it in queue if it["k"] < len(it["ins"]) and it["ready"] <= m]
+            if not cand:
+                break
+            budget -= emit_valu(min(cand, key=lambda x: (x["deadline"], x["order"])))
+        if do_s:  # with the S part in front, every P operand is ready ahead of its MFMAs
+            for it in queue:
+                assert it["k"] == len(it["ins"]) or m < it["deadline"], ("deadline missed", it["name"], m)
+    # what is left (the row max when few MFMAs follow the S part) runs after the last MFMA issued
+    rest = [it for it in sorted(queue, key=lambda x: x["order"]) if it["k"] < len(it["ins"])]
+    if rest and s_last is not None and len(mfma) - 1 - s_last < 3:
+        out += ["s_nop 7", "s_nop 7", "s_nop 7"]
+    for it in rest:
+        while it["k"] < len(it["ins"]):
+            emit_valu(it)
+    out += ["s_nop 7", "s_nop 7", "s_nop 7"]
+    return out
+
+
+def o_binding():
+    outs = []
+    for qb in range(QB):
+        for db in range(DB):
+            b = O_A + (qb * DB + db) * 16
+            outs.append('"+{a[%d:%d]}"(o[%d][%d])' % (b, b + 15, qb, db))
+    return outs
+
+
+def q_binding():
+    return ['"{a[%d:%d]}"(q[%d][%d])' % (Q_A + 4 * (qb * KS + ks), Q_A + 4 * (qb * KS + ks) + 3, qb, ks)
+            for qb in range(QB) for ks in range(KS)]
+
+
+def ka_binding():
+    return ['[ka%d] "v"(ka[%d])' % (ks, ks) for ks in range(KS)]
+
+
+def va_binding():
+    return ['[va%d_%d] "v"(va[%d][%d])' % (db, h, db, h) for db in range(DB) for h in range(2)]
+
+
+# ---------------------------------------------------------------------------
+# The whole tile loop of a wave as one asm statement (so that no C++ control
+# flow sits between the blocks). Registers of the loop beyond the blocks':
+MREF_V = (204, 205)     # reference max of the current tile, per qb
+ALPHA_V = (206, 207)    # rescale factors
+NINF_V = 208            # -inf for the mask
+TMPL = 209              # v[209:212] scratch of the loop (DMA offsets, reference update)
+MX_V = (202, 203)       # row max of the current scores, per qb
+SREG = 88               # s[88:97] scratch SGPRs
+LOOP_CLOB_V = list(range(0, 213))   # S buffers, P, staging and the loop's own registers
+
+
+def dma(tile_reg, slot_off, base_lo, base_hi, tag):
+    """DMA of one K or V tile (index in SGPR tile_reg) into LDS at lbw + slot_off; rows past the
+    workgroup's last key are clamped to that key on the (single) tail tile."""
+    s_idx = "s%d" % tile_reg
+    o = ["s_cmp_ge_i32 %s, %%[nt]" % s_idx, "s_cbranch_scc1 L_no_%s_%%=" % tag,
+         "s_lshl_b32 s%d, %s, 14" % (SREG + 1, s_idx),
+         "s_add_u32 s%d, %s, s%d" % (SREG + 2, base_lo, SREG + 1),
+         "s_addc_u32 s%d, %s, 0" % (SREG + 3, base_hi),
+         "s_cmp_eq_u32 %s, %%[tt]" % s_idx, "s_cbranch_scc1 L_tail_%s_%%=" % tag]
+    for j in range(4):
+        o += ["s_add_u32 m0, %%[lbw], %d" % (slot_off + j * 4096), "s_nop 0",
+              "global_load_lds_dwordx4 %%[vo%d], s[%d:%d]" % (j, SREG + 2, SREG + 3)]
+    o += ["s_branch L_no_%s_%%=" % tag, "L_tail_%s_%%=:" % tag,
+          "s_lshl_b32 s%d, %s, 6" % (SREG + 1, s_idx),
+          "s_sub_i32 s%d, %%[kve], s%d" % (SREG + 1, SREG + 1),
+          "s_sub_i32 s%d, s%d, 1" % (SREG + 1, SREG + 1)]
+    for j in range(4):
+        t = TMPL + j
+        o += ["v_min_i32 v%d, s%d, %%[dr%d]" % (t, SREG + 1, j),
+              "v_sub_u32 v%d, %%[dr%d], v%d" % (t, j, t),
+              "v_lshlrev_b32 v%d, 8, v%d" % (t, t),
+              "v_sub_u32 v%d, %%[vo%d], v%d" % (t, j, t),
+              "s_add_u32 m0, %%[lbw], %d" % (slot_off + j * 4096), "s_nop 0",
+              "global_load_lds_dwordx4 v%d, s[%d:%d]" % (t, SREG + 2, SREG + 3)]
+    o += ["L_no_%s_%%=:" % tag]
+    return o
+
+
+def max_chain(buf, qb, dst):
+    o = []
+    for jb in range(2):
+        m = MXT + jb
+        vals = [s_reg(buf, qb, jb, r) for r in range(16)]
+        o.append("v_max3_f32 v%d, v%d, v%d, v%d" % (m, vals[0], vals[1], vals[2]))
+        rest = vals[3:]
+        while rest:
+            a, b = rest[0], rest[1] if len(rest) > 1 else rest[0]
+            o.append("v_max3_f32 v%d, v%d, v%d, v%d" % (m, m, a, b))
+            rest = rest[2:]
+    o += ["v_max_f32 v%d, v%d, v%d" % (MXT, MXT, MXT + 1), "v_mov_b32 v%d, v%d" % (MXT + 1, MXT), "s_nop 1",
+          "v_permlane32_swap_b32 v%d, v%d" % (MXT, MXT + 1), "v_max_f32 v%d, v%d, v%d" % (dst, MXT, MXT + 1)]
+    return o
+
+
+def iteration(parity):
+    P = parity
+    tag = "p%d" % P
+    o = []
+    # K(t+2) into K slot t % 2, V(t+1) into V slot (t+1) % 2
+    o += ["s_add_i32 s%d, %%[t], 2" % SREG]
+    o += dma(SREG, P * TILE_B, "%[khl]", "%[khh]", "k" + tag)
+    o += ["s_add_i32 s%d, %%[t], 1" % SREG]
+    o += dma(SREG, 2 * TILE_B + (1 - P) * TILE_B, "%[vhl]", "%[vhh]", "v" + tag)
+    o += ["s_cmp_ge_i32 %[t], %[ntw]", "s_cbranch_scc1 L_skip_%s_%%=" % tag]
+    # mask the current scores (buffer P) on tiles that need it, and take their row max again
+    o += ["s_cmp_lt_i32 %[t], %[tm]", "s_cbranch_scc1 L_nomask_%s_%%=" % tag,
+          "s_lshl_b32 s%d, %%[t], 6" % (SREG + 1), "v_mov_b32 v%d, 0xff800000" % NINF_V]
+    for qb in range(QB):
+        o.append("v_subrev_u32 v%d, s%d, %%[lim%d]" % (TMPL, SREG + 1, qb))
+        for jb in range(2):
+            for r in range(16):
+                off = jb * 32 + (r >> 2) * 8 + (r & 3)
+                sr = s_reg(P, qb, jb, r)
+                o += ["v_cmp_gt_i32 vcc, %d, v%d" % (off, TMPL), "v_cndmask_b32 v%d, v%d, v%d, vcc" % (sr, sr, NINF_V)]
+        o += max_chain(P, qb, MX_V[qb])
+    o += ["L_nomask_%s_%%=:" % tag]
+    # reference update: move the reference only when the tile max exceeds it by the slack
+    for qb in range(QB):
+        u = "s[%d:%d]" % (SREG + 4 + 2 * qb, SREG + 5 + 2 * qb)
+        o += ["v_mul_f32 v%d, v%d, %%[c]" % (TMPL, MX_V[qb]),
+              "v_add_f32 v%d, 0x41000000, %%[mc%d]" % (TMPL + 1, qb),
+              "v_cmp_gt_f32_e64 %s, v%d, v%d" % (u, TMPL, TMPL + 1),
+              "v_cndmask_b32_e64 v%d, %%[mc%d], v%d, %s" % (TMPL + 1, qb, TMPL, u),
+              "v_sub_f32 v%d, %%[mc%d], v%d" % (TMPL + 2, qb, TMPL + 1),
+              "v_exp_f32 v%d, v%d" % (TMPL + 2, TMPL + 2),
+              "v_mov_b32 %%[mc%d], v%d" % (qb, TMPL + 1),
+              "v_max_f32 v%d, 0xff7fffff, v%d" % (MREF_V[qb], TMPL + 1),
+              "v_cndmask_b32_e64 v%d, 1.0, v%d, %s" % (ALPHA_V[qb], TMPL + 2, u),
+              "v_mul_f32 %%[l%d], %%[l%d], v%d" % (qb, qb, ALPHA_V[qb])]
+    o += ["s_or_b64 vcc, s[%d:%d], s[%d:%d]" % (SREG + 4, SREG + 5, SREG + 6, SREG + 7),
+          "s_cbranch_vccz L_norescale_%s_%%=" % tag]
+    for qb in range(QB):
+        for r in range(64):
+            a = O_A + qb * 64 + r
+            t = P0 + (r % 16)
+            o += ["v_accvgpr_read_b32 v%d, a%d" % (t, a), "v_mul_f32 v%d, v%d, v%d" % (t, t, ALPHA_V[qb]),
+                  "v_accvgpr_write_b32 a%d, v%d" % (a, t)]
+    o += ["s_nop 1", "L_norescale_%s_%%=:" % tag]
+    # the step with the next tile's scores, or the wave's last tile
+    o += ["s_add_i32 s%d, %%[t], 1" % SREG, "s_cmp_lt_i32 s%d, %%[ntw]" % SREG,
+          "s_cbranch_scc0 L_last_%s_%%=" % tag]
+    mref = ("v%d" % MREF_V[0], "v%d" % MREF_V[1])
+    mx = ("v%d" % MX_V[0], "v%d" % MX_V[1])
+    o += gen(x_buf=P, y_buf=1 - P, kslot=1 - P, vslot=P, do_s=True, do_pv=True, do_max=True, mref=mref, mx=mx)
+    o += ["s_branch L_skip_%s_%%=" % tag, "L_last_%s_%%=:" % tag]
+    o += gen(x_buf=P, y_buf=1 - P, kslot=1 - P, vslot=P, do_s=False, do_pv=True, do_max=False, mref=mref, mx=mx)
+    o += ["L_skip_%s_%%=:" % tag, "s_waitcnt vmcnt(0)", "s_barrier"]
+    return o
+
+
+def loop_body():
+    # S(0) of the wave (K(0) is in K slot 0) and its row max, then the tile loop
+    o = ["s_cmp_le_i32 %[ntw], 0", "s_cbranch_scc1 L_top_%="]
+    o += gen(x_buf=1, y_buf=0, kslot=0, vslot=0, do_s=True, do_pv=False, do_max=True,
+             mx=("v%d" % MX_V[0], "v%d" % MX_V[1]))
+    o += ["L_top_%=:", "s_cmp_ge_i32 %[t], %[nt]", "s_cbranch_scc1 L_end_%="]
+    o += iteration(0)
+    o += ["s_add_i32 %[t], %[t], 1", "s_cmp_ge_i32 %[t], %[nt]", "s_cbranch_scc1 L_end_%="]
+    o += iteration(1)
+    o += ["s_add_i32 %[t], %[t], 1", "s_branch L_top_%=", "L_end_%=:"]
+    return o
+
+
+def render_loop():
+    body = loop_body()
+    outs = (o_binding() + ['[l0] "+v"(l0)', '[l1] "+v"(l1)', '[mc0] "+v"(mc0)', '[mc1] "+v"(mc1)', '[t] "+s"(t)'])
+    ins = (q_binding() + ka_binding() + va_binding() +
+           ['[vo%d] "v"(vo[%d])' % (j, j) for j in range(4)] + ['[dr%d] "v"(dr[%d])' % (j, j) for j in range(4)] +
+           ['[lim0] "v"(lim0)', '[lim1] "v"(lim1)', '[c] "s"(c_log2)', '[nt] "s"(ntiles)', '[ntw] "s"(ntiles_w)',
+            '[tm] "s"(t_mask)', '[tt] "s"(t_tail)', '[kve] "s"(kv_end)', '[khl] "s"(kh_lo)', '[khh] "s"(kh_hi)',
+            '[vhl] "s"(vh_lo)', '[vhh] "s"(vh_hi)', '[lbw] "s"(lbw)'])
+    clob = (['"v%d"' % r for r in LOOP_CLOB_V] + ['"s%d"' % r for r in range(SREG, SREG + 10)] +
+            ['"vcc"', '"m0"', '"scc"', '"memory"'])
+    return [
+        "// S(0) of the wave, then its tile loop: for t = 0 .. ntiles-1 (the same count in every wave of the",
+        "// workgroup, one barrier per tile): DMA of K(t+2) and V(t+1), then, while t < ntiles_w,",
+        "// mask (t >= t_mask), reference update, rescale of O when a row's reference moved,",
+        "// and the step with S(t+1) (t + 1 < ntiles_w) or the last step.",
+        "__device__ __forceinline__ void qb2_loop(f32x16 (&o)[2][4], const bf16x8 (&q)[2][8], const uint32_t (&ka)[8],",
+        "                                         const uint32_t (&va)[4][2], const uint32_t (&vo)[4],",
+        "                                         const int32_t (&dr)[4], int32_t lim0, int32_t lim1, float c_log2,",
+        "                                         float &l0, float &l1, float &mc0, float &mc1,",
+        "                                         int32_t t, int32_t ntiles, int32_t ntiles_w, int32_t t_mask,",
+        "                                         int32_t t_tail, int32_t kv_end, uint32_t kh_lo, uint32_t kh_hi,",
+        "                                         uint32_t vh_lo, uint32_t vh_hi, uint32_t lbw)",
+        "{",
+        "#pragma clang diagnostic push",
+        "#pragma clang diagnostic ignored \"-Winline-asm\"",
+        "    asm volatile(",
+        "\n".join('        "%s\\n"' % x for x in body),
+        "        : " + ",\n          ".join(outs),
+        "        : " + ",\n          ".join(ins),
+        "        : " + ", ".join(clob) + ");",
+        "#pragma clang diagnostic pop",
+        "}",
+        "",
+    ]
+
+
+def render():
+    lines = [
+        "// Generated by gen_qb2_tile.py; edit the generator, not this file.",
+        "// Tile steps of the 64-rows-per-wave kernel for 128-wide heads (see the",
+        "// generator for the schedule and the register plan).",
+        "",
+    ]
+    # O = 0 and Q^T into its AGPRs
+    zero = ["v_accvgpr_write_b32 a%d, 0" % r for r in range(O_A, O_A + 128)]
+    qmov = []
+    for qb in range(QB):
+        for ks in range(KS):
+            for w in range(4):
+                qmov.append("v_accvgpr_write_b32 a%d, %%[qv%d_%d]" % (Q_A + 4 * (qb * KS + ks) + w, qb * KS + ks, w))
+    lines += [
+        "__device__ __forceinline__ void qb2_init(f32x16 (&o)[2][4], bf16x8 (&q)[2][8], const u32x4 (&qv)[2][8])",
+        "{",
+        "    asm volatile(",
+        "\n".join('        "%s\\n"' % t for t in zero + qmov + ["s_nop 7"]),
+        "        : " + ",\n          ".join(
+            ['"={a[%d:%d]}"(o[%d][%d])' % (O_A + (qb * DB + db) * 16, O_A + (qb * DB + db) * 16 + 15, qb, db)
+             for qb in range(QB) for db in range(DB)] +
+            ['"={a[%d:%d]}"(q[%d][%d])' % (Q_A + 4 * (qb * KS + ks), Q_A + 4 * (qb * KS + ks) + 3, qb, ks)
+             for qb in range(QB) for ks in range(KS)]),
+        "        : " + ",\n          ".join(
+            ['[qv%d_%d] "v"(qv[%d][%d][%d])' % (qb * KS + ks, w, qb, ks, w)
+             for qb in range(QB) for ks in range(KS) for w in range(4)]) + ");",
+        "}",
+        "",
+    ]
+    lines += render_loop()
+    return "\n".join(lines)
+
+
+if __name__ == "__main__":
+    here = os.path.dirname(os.path.abspath(__file__))
+    text = render()
+    with open(os.path.join(here, "attn_qb2_tile.inc"), "w", encoding="utf-8") as f:
+        f.write(text)
+    print("wrote attn_qb2_tile.inc")
