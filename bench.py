@@ -35,7 +35,8 @@ PEAK_HBM_GBS = 8000.0
 WORKLOAD = dict(workload="sdpa_bf16_b4_h16_n4096_d128_causal", B=4, H=16, N=4096, d=128, mask="causal",
                 dtype="bf16", scale="1/sqrt(128)")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_causal_b4h16n4096d128_hbm_traffic.json")
-KERNEL_SOURCES = ["transformer_scaled_dot_amd/csrc/attn_fwd_bf16.hip", "transformer_scaled_dot_amd/csrc/device_common.h"]
+KERNEL_SOURCES = ["transformer_scaled_dot_amd/csrc/attn_fwd_bf16.hip", "transformer_scaled_dot_amd/csrc/attn_qb2_tile.inc",
+                  "transformer_scaled_dot_amd/csrc/device_common.h"]
 
 
 def kernel_source_hash() -> str:
@@ -231,7 +232,7 @@ def main():
             "traffic_unit": "bytes per launch between L2 and memory (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a "
                             "256 MiB copy's counts)",
             "algorithmic_bytes_per_launch": 4 * B * H * N * d * 2,
-            "kernel": "attn_fwd_bf16_kernel<128, causal, bf16 out>",
+            "kernel": "attn_fwd_qb2_kernel<causal, bf16 out>",
             "algorithmic_flops_per_launch": r["flops"],
             "avg_launch_ms": round(r["ms"], 5),
         },

@@ -16,23 +16,28 @@ the last one only P and P.V. Lane layouts are those of the C++ kernel
 accumulator to the P.V MFMA in the permuted key order, V^T operands come from
 pairs of ds_read_b64_tr_b16.
 
-Every block names the same physical registers, bound through the asm
-constraints, so that single elements of the 16-register accumulators can be
-addressed and the compiler never has to move the operands between blocks:
+The whole tile loop of a wave (S(0), then one step per key tile with the DMA,
+the mask, the reference update, the rescale and the barrier) is ONE asm
+statement, so the schedule inside it is exactly the one emitted here. O and
+Q^T are bound to fixed AGPRs through the constraints; everything else the loop
+works on lives in fixed registers that the statement declares clobbered:
   a[0:127]    O[qb][db]         a[128:191]  Q^T[qb][ks]  (MFMA B operand)
   v[0:63]     S buffer 0        v[64:127]   S buffer 1   (S[qb][jb], 16 each)
   v[128:159]  P[qb][c]          v[160:175]  K operand staging (4 slots)
   v[176:191]  V operand staging v[192:199]  exp temporaries
-  v[200:203]  max temporaries
-The per-lane scalars (LDS read addresses, mref, l and the row max) are plain
-register operands that the compiler places.
+  v[200:212]  row max, reference, rescale factors, DMA offsets
+  s[88:97]    tile indices and DMA addresses
+The per-lane and per-wave inputs (LDS addresses, DMA offsets, limits, l, the
+tile counts, base addresses) are compiler-placed operands; because the fixed
+ranges are clobbers, the compiler cannot place an operand inside them (a test
+compiles the kernel and checks every substituted register).
 For the schedule it emits, the generator checks that every MFMA operand read
 has completed (lgkmcnt) before its MFMA, that no staging slot is rewritten
 before its last reader has issued, that every P operand is written at least
 two instructions before its first MFMA, and that the row max reads the new S
 only after three further MFMAs (or 24 wait states) behind the last MFMA that
-wrote it. Blocks end with 24 wait states so that O is complete when C++ code
-next reads it.
+wrote it. The loop ends with 24 wait states so that O is complete when C++
+code next reads it.
 
 Run:  python gen_qb2_tile.py  (writes attn_qb2_tile.inc next to this file)
 """
