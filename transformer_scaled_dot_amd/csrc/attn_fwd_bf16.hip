@@ -631,7 +631,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int32_t lim[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) lim[qb] = (MASK == kMaskCausal ? min(qrow[qb], kv_len - 1) : kv_len - 1) - hf * 4;
-    const int t_tail = (kv_end % kBlockN) ? ntiles - 1 : 0x7fffffff;  // the one tile with rows past kv_end
 
     // LDS byte addresses of the operand reads (the tile offsets are instruction immediates)
     uint32_t kaddr[KS], vaddr[DB][2];
@@ -644,6 +643,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     float mc0 = -INFINITY, mc1 = -INFINITY;
     if (ntiles > 0) {
+        // the tile loop fetches no row at or past kv_end; V slot 1 is read (with weight 0) before any
+        // fetch has written such rows, so it starts as zeros rather than whatever LDS held
+#pragma unroll
+        for (int i = 0; i < TILE_B / (16 * 256); ++i)
+            *(u32x4 *)(smem + VSLOT1 + (i * 256 + tid) * 16) = u32x4{0u, 0u, 0u, 0u};
         issue(Kh, 0, KSLOT0);
         if (ntiles > 1) issue(Kh, 1, KSLOT1);
         issue(Vh, 0, VSLOT0);
@@ -654,8 +658,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint32_t lbw = __builtin_amdgcn_readfirstlane(lds0 + wave * 1024);
     // wave-uniform values go to the asm in SGPRs
     auto u = [](int x) { return (int32_t)__builtin_amdgcn_readfirstlane(x); };
-    qb2_loop(acc, qreg, kaddr, vaddr, voff, drow, lim[0], lim[1], c_log2, l_run[0], l_run[1], mc0, mc1,
-             u(0), u(ntiles), u(ntiles_w), u(t_mask), u(t_tail), u(kv_end), u((uint32_t)kh), u((uint32_t)(kh >> 32)),
+    qb2_loop(acc, qreg, kaddr, vaddr, voff, lim[0], lim[1], c_log2, l_run[0], l_run[1], mc0, mc1,
+             u(0), u(ntiles), u(ntiles_w), u(t_mask), u(kv_end), u((uint32_t)kh), u((uint32_t)(kh >> 32)),
              u((uint32_t)vh), u((uint32_t)(vh >> 32)), lbw);
 
     mfma_fence_a8(acc);

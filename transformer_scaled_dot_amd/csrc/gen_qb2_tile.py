@@ -54,6 +54,10 @@ O_A, Q_A = 0, 128
 NKS = NVS = 4          # staging slots
 LOOK = 5               # MFMAs between an operand's read and its first MFMA
 VALU_BUDGET = 5        # VALU cost units per MFMA slot (exp counts 2)
+DMA_COST = 2           # of those, taken by one DMA group (M0 write, load)
+WAIT_AHEAD = 3         # an LDS wait also covers the operands of up to this many following MFMAs ...
+WAIT_KEEP = 2          # ... leaving at least this many younger reads in flight
+O_WAIT = ["s_nop 7", "s_nop 7", "s_nop 7"]   # before reading O (or scores) written by the last MFMAs
 ONES_BF16X2 = "0x3f803f80"
 
 
@@ -69,11 +73,17 @@ def s_reg(buf, qb, jb, r):
     return S_BUF[buf] + (qb * 2 + jb) * 16 + r
 
 
-def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mref1]"), mx=("%[mx0]", "%[mx1]")):
+def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mref1]"), mx=("%[mx0]", "%[mx1]"),
+        dma_ins=(), ref_upd=False):
     """Instruction list of one block.
 
     x_buf: S buffer holding S(t) (exp + P.V part), y_buf: buffer receiving the
-    new scores; kslot / vslot: LDS tile slots (0 or 1) of the K and V tiles."""
+    new scores; kslot / vslot: LDS tile slots (0 or 1) of the K and V tiles.
+    dma_ins: groups of DMA instructions, one group issued behind each of the
+    first MFMAs (every other one); ref_upd: also move the reference of the new
+    scores (after their row max and after this block's row sums).
+    The block ends without waiting for its last MFMAs: code that reads O or
+    the new scores next must wait 24 wait states first (O_WAIT)."""
     koff = kslot * TILE_B
     voff = 2 * TILE_B + vslot * TILE_B
 
@@ -154,10 +164,26 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
             ins.append(("v_permlane32_swap_b32 v%d, v%d" % (MXT, MXT + 1), 1))
             ins.append(("v_max_f32 %s, v%d, v%d" % (mx[qb], MXT, MXT + 1), 1))
             items.append(dict(ins=ins, deadline=10 ** 9, ready=s_last + 4, p=None, name="max q%d" % qb))
+    if ref_upd:
+        assert do_max
+        for qb in range(QB):
+            items.append(dict(ins=[(x, 1) for x in ref_check(qb)], deadline=10 ** 9, ready=s_last + 4, p=None,
+                              name="ref q%d" % qb, after=["max q%d" % qb]))
 
     out = ["s_waitcnt lgkmcnt(0)"]
     issued, pos, p_done = [], {}, {}
+    waited = [-1]       # LDS reads up to this index are known complete (LDS returns in order)
     queue = [dict(it, k=0, order=n) for n, it in enumerate(items)]
+    by_name = {it["name"]: it for it in queue}
+
+    def done(name):
+        it = by_name[name]
+        return it["k"] == len(it["ins"])
+
+    dma_at = {2 * i: list(g) for i, g in enumerate(dma_ins)}
+    for g in dma_at.values():
+        assert len(g) == 2 and g[0].startswith("s_add_u32 m0") and "lds" in g[1]
+    assert len(mfma) > 2 * (len(dma_ins) - 1) or not dma_ins
 
     def emit_reads(slot):
         for op in read_at.get(slot, []):
@@ -187,14 +213,27 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
             gap = sum(1 for t in out[p_done[p] + 1:] if not t.startswith("s_waitcnt"))
             if gap < 2:
                 out.append("s_nop %d" % (1 - gap))
-        outstanding_after = len(issued) - 1 - pos[f["op"]]
-        assert 0 <= outstanding_after <= 15
-        out.append("s_waitcnt lgkmcnt(%d)" % outstanding_after)
-        out.append(f["text"])
-        emit_reads(m + 1)
+        if pos[f["op"]] > waited[0]:
+            # wait once for this operand and for those of the next MFMAs already read (they have had
+            # at least as long to arrive), rather than once per operand
+            upto = max([pos[f["op"]]] + [pos[g["op"]] for g in mfma[m + 1:m + 1 + WAIT_AHEAD]
+                                         if g["op"] in pos and pos[g["op"]] <= len(issued) - 1 - WAIT_KEEP])
+            outstanding_after = len(issued) - 1 - upto
+            assert 0 <= outstanding_after <= 15
+            out.append("s_waitcnt lgkmcnt(%d)" % outstanding_after)
+            waited[0] = upto
         budget = VALU_BUDGET
+        dma = dma_at.pop(m, None)
+        if dma:  # the MFMA is the wait state the LDS DMA needs after its M0 write
+            out.append(dma[0])
+            budget -= DMA_COST
+        out.append(f["text"])
+        if dma:
+            out.append(dma[1])
+        emit_reads(m + 1)
         while budget > 0:
-            cand = [it for it in queue if it["k"] < len(it["ins"]) and it["ready"] <= m]
+            cand = [it for it in queue if it["k"] < len(it["ins"]) and it["ready"] <= m
+                    and all(done(a) for a in it.get("after", ()))]
             if not cand:
                 break
             budget -= emit_valu(min(cand, key=lambda x: (x["deadline"], x["order"])))
@@ -202,13 +241,14 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
             for it in queue:
                 assert it["k"] == len(it["ins"]) or m < it["deadline"], ("deadline missed", it["name"], m)
     # what is left (the row max when few MFMAs follow the S part) runs after the last MFMA issued
+    assert not dma_at
     rest = [it for it in sorted(queue, key=lambda x: x["order"]) if it["k"] < len(it["ins"])]
     if rest and s_last is not None and len(mfma) - 1 - s_last < 3:
         out += ["s_nop 7", "s_nop 7", "s_nop 7"]
     for it in rest:
+        assert all(done(a) for a in it.get("after", ())), ("dependency order", it["name"])
         while it["k"] < len(it["ins"]):
             emit_valu(it)
-    out += ["s_nop 7", "s_nop 7", "s_nop 7"]
     return out
 
 
@@ -240,38 +280,64 @@ def va_binding():
 MREF_V = (204, 205)     # reference max of the current tile, per qb
 ALPHA_V = (206, 207)    # rescale factors
 NINF_V = 208            # -inf for the mask
-TMPL = 209              # v[209:212] scratch of the loop (DMA offsets, reference update)
+TMPL = 209              # v[209:214] scratch of the loop (mask limit, reference update: three per qb)
 MX_V = (202, 203)       # row max of the current scores, per qb
+KRES, VRES = 80, 84     # s[80:83] / s[84:87]: buffer descriptors of the K and V tiles being fetched
 SREG = 88               # s[88:97] scratch SGPRs
-LOOP_CLOB_V = list(range(0, 213))   # S buffers, P, staging and the loop's own registers
+UFLAG = (92, 94)        # s[92:93] / s[94:95]: rows whose reference moved, per qb
+THR_S = 96              # the slack (8) in an SGPR
+MCP_V = (215, 216)      # reference + slack, per qb
+LOOP_CLOB_V = list(range(0, 217))   # S buffers, P, staging and the loop's own registers
+LOOP_CLOB_S = list(range(KRES, SREG + 10))
+BUF_WORD3 = "0x20000"   # 32-bit data format, no stride: byte-addressed, range-checked raw buffer
 
 
-def dma(tile_reg, slot_off, base_lo, base_hi, tag):
-    """DMA of one K or V tile (index in SGPR tile_reg) into LDS at lbw + slot_off; rows past the
-    workgroup's last key are clamped to that key on the (single) tail tile."""
-    s_idx = "s%d" % tile_reg
-    o = ["s_cmp_ge_i32 %s, %%[nt]" % s_idx, "s_cbranch_scc1 L_no_%s_%%=" % tag,
-         "s_lshl_b32 s%d, %s, 14" % (SREG + 1, s_idx),
-         "s_add_u32 s%d, %s, s%d" % (SREG + 2, base_lo, SREG + 1),
-         "s_addc_u32 s%d, %s, 0" % (SREG + 3, base_hi),
-         "s_cmp_eq_u32 %s, %%[tt]" % s_idx, "s_cbranch_scc1 L_tail_%s_%%=" % tag]
-    for j in range(4):
-        o += ["s_add_u32 m0, %%[lbw], %d" % (slot_off + j * 4096), "s_nop 0",
-              "global_load_lds_dwordx4 %%[vo%d], s[%d:%d]" % (j, SREG + 2, SREG + 3)]
-    o += ["s_branch L_no_%s_%%=" % tag, "L_tail_%s_%%=:" % tag,
-          "s_lshl_b32 s%d, %s, 6" % (SREG + 1, s_idx),
-          "s_sub_i32 s%d, %%[kve], s%d" % (SREG + 1, SREG + 1),
-          "s_sub_i32 s%d, s%d, 1" % (SREG + 1, SREG + 1)]
-    for j in range(4):
-        t = TMPL + j
-        o += ["v_min_i32 v%d, s%d, %%[dr%d]" % (t, SREG + 1, j),
-              "v_sub_u32 v%d, %%[dr%d], v%d" % (t, j, t),
-              "v_lshlrev_b32 v%d, 8, v%d" % (t, t),
-              "v_sub_u32 v%d, %%[vo%d], v%d" % (t, j, t),
-              "s_add_u32 m0, %%[lbw], %d" % (slot_off + j * 4096), "s_nop 0",
-              "global_load_lds_dwordx4 v%d, s[%d:%d]" % (t, SREG + 2, SREG + 3)]
-    o += ["L_no_%s_%%=:" % tag]
-    return o
+def tile_res(res, tile_sreg, base_lo, base_hi):
+    """Buffer descriptor of one K or V tile of the head: base = head + tile * 16 KiB, size = the bytes of
+    the tile's rows below kv_end (0 past the end), so that rows past kv_end read as out of range and
+    never touch memory."""
+    return ["s_lshl_b32 s%d, %s, 14" % (SREG + 1, tile_sreg),
+            "s_add_u32 s%d, %s, s%d" % (res, base_lo, SREG + 1),
+            "s_addc_u32 s%d, %s, 0" % (res + 1, base_hi),
+            "s_lshl_b32 s%d, %%[kve], 8" % (res + 2),
+            "s_sub_i32 s%d, s%d, s%d" % (res + 2, res + 2, SREG + 1),
+            "s_max_i32 s%d, s%d, 0" % (res + 2, res + 2),
+            "s_mov_b32 s%d, %s" % (res + 3, BUF_WORD3)]
+
+
+def dma_groups(res, slot_off):
+    """The four loads of one tile (each 64 lanes x 16 B into 1 KiB of LDS at M0), one group each."""
+    return [["s_add_u32 m0, %%[lbw], %d" % (slot_off + j * 4096),
+             "buffer_load_dwordx4 %%[vo%d], s[%d:%d], 0 offen lds" % (j, res, res + 3)] for j in range(4)]
+
+
+def step_dma(parity):
+    """K(t+2) into K slot t % 2 and V(t+1) into V slot (t+1) % 2, as groups."""
+    return dma_groups(KRES, parity * TILE_B) + dma_groups(VRES, 2 * TILE_B + (1 - parity) * TILE_B)
+
+
+def ref_check(qb):
+    """Rows of qb whose new tile max exceeds the reference by more than the slack (flags only)."""
+    return ["v_mul_f32 v%d, v%d, %%[c]" % (TMPL + 3 * qb, MX_V[qb]),
+            "v_cmp_gt_f32_e64 s[%d:%d], v%d, v%d" % (UFLAG[qb], UFLAG[qb] + 1, TMPL + 3 * qb, MCP_V[qb])]
+
+
+def ref_update(qb, thr):
+    """Move the reference of qb's rows to the new tile max where it exceeds the old reference by more than
+    the slack (thr = 8, or +inf to keep it); alpha = exp2(old - new) (1 where it stays); l *= alpha."""
+    t0, t1, t2 = TMPL + 3 * qb, TMPL + 3 * qb + 1, TMPL + 3 * qb + 2
+    u = "s[%d:%d]" % (UFLAG[qb], UFLAG[qb] + 1)
+    return ["v_mul_f32 v%d, v%d, %%[c]" % (t0, MX_V[qb]),
+            "v_add_f32 v%d, %s, %%[mc%d]" % (t1, thr, qb),
+            "v_cmp_gt_f32_e64 %s, v%d, v%d" % (u, t0, t1),
+            "v_cndmask_b32_e64 v%d, %%[mc%d], v%d, %s" % (t1, qb, t0, u),
+            "v_sub_f32 v%d, %%[mc%d], v%d" % (t2, qb, t1),
+            "v_exp_f32 v%d, v%d" % (t2, t2),
+            "v_mov_b32 %%[mc%d], v%d" % (qb, t1),
+            "v_max_f32 v%d, 0xff7fffff, v%d" % (MREF_V[qb], t1),
+            "v_cndmask_b32_e64 v%d, 1.0, v%d, %s" % (ALPHA_V[qb], t2, u),
+            "v_mul_f32 %%[l%d], %%[l%d], v%d" % (qb, qb, ALPHA_V[qb]),
+            "v_add_f32 v%d, %s, %%[mc%d]" % (MCP_V[qb], thr, qb)]
 
 
 def max_chain(buf, qb, dst):
@@ -290,72 +356,105 @@ def max_chain(buf, qb, dst):
     return o
 
 
-def iteration(parity):
-    P = parity
-    tag = "p%d" % P
-    o = []
-    # K(t+2) into K slot t % 2, V(t+1) into V slot (t+1) % 2
-    o += ["s_add_i32 s%d, %%[t], 2" % SREG]
-    o += dma(SREG, P * TILE_B, "%[khl]", "%[khh]", "k" + tag)
-    o += ["s_add_i32 s%d, %%[t], 1" % SREG]
-    o += dma(SREG, 2 * TILE_B + (1 - P) * TILE_B, "%[vhl]", "%[vhh]", "v" + tag)
-    o += ["s_cmp_ge_i32 %[t], %[ntw]", "s_cbranch_scc1 L_skip_%s_%%=" % tag]
-    # mask the current scores (buffer P) on tiles that need it, and take their row max again
-    o += ["s_cmp_lt_i32 %[t], %[tm]", "s_cbranch_scc1 L_nomask_%s_%%=" % tag,
-          "s_lshl_b32 s%d, %%[t], 6" % (SREG + 1), "v_mov_b32 v%d, 0xff800000" % NINF_V]
+def res_advance(res):
+    """Move a tile descriptor on by one tile (16 KiB); the size stays clamped at 0."""
+    return ["s_add_u32 s%d, s%d, 0x4000" % (res, res), "s_addc_u32 s%d, s%d, 0" % (res + 1, res + 1),
+            "s_sub_i32 s%d, s%d, 0x4000" % (res + 2, res + 2), "s_max_i32 s%d, s%d, 0" % (res + 2, res + 2)]
+
+
+def mask_tile(tile_sreg, buf):
+    """Scores of tile T (index in tile_sreg) in buffer buf: -inf for keys past each row's last visible key,
+    then the row max again."""
+    o = ["s_lshl_b32 s%d, %s, 6" % (SREG + 1, tile_sreg), "v_mov_b32 v%d, 0xff800000" % NINF_V]
     for qb in range(QB):
         o.append("v_subrev_u32 v%d, s%d, %%[lim%d]" % (TMPL, SREG + 1, qb))
         for jb in range(2):
             for r in range(16):
                 off = jb * 32 + (r >> 2) * 8 + (r & 3)
-                sr = s_reg(P, qb, jb, r)
+                sr = s_reg(buf, qb, jb, r)
                 o += ["v_cmp_gt_i32 vcc, %d, v%d" % (off, TMPL), "v_cndmask_b32 v%d, v%d, v%d, vcc" % (sr, sr, NINF_V)]
-        o += max_chain(P, qb, MX_V[qb])
-    o += ["L_nomask_%s_%%=:" % tag]
-    # reference update: move the reference only when the tile max exceeds it by the slack
+        o += max_chain(buf, qb, MX_V[qb])
+    return o
+
+
+def full_ref():
+    o = ["s_mov_b32 s%d, 0x41000000" % THR_S]
     for qb in range(QB):
-        u = "s[%d:%d]" % (SREG + 4 + 2 * qb, SREG + 5 + 2 * qb)
-        o += ["v_mul_f32 v%d, v%d, %%[c]" % (TMPL, MX_V[qb]),
-              "v_add_f32 v%d, 0x41000000, %%[mc%d]" % (TMPL + 1, qb),
-              "v_cmp_gt_f32_e64 %s, v%d, v%d" % (u, TMPL, TMPL + 1),
-              "v_cndmask_b32_e64 v%d, %%[mc%d], v%d, %s" % (TMPL + 1, qb, TMPL, u),
-              "v_sub_f32 v%d, %%[mc%d], v%d" % (TMPL + 2, qb, TMPL + 1),
-              "v_exp_f32 v%d, v%d" % (TMPL + 2, TMPL + 2),
-              "v_mov_b32 %%[mc%d], v%d" % (qb, TMPL + 1),
-              "v_max_f32 v%d, 0xff7fffff, v%d" % (MREF_V[qb], TMPL + 1),
-              "v_cndmask_b32_e64 v%d, 1.0, v%d, %s" % (ALPHA_V[qb], TMPL + 2, u),
-              "v_mul_f32 %%[l%d], %%[l%d], v%d" % (qb, qb, ALPHA_V[qb])]
-    o += ["s_or_b64 vcc, s[%d:%d], s[%d:%d]" % (SREG + 4, SREG + 5, SREG + 6, SREG + 7),
-          "s_cbranch_vccz L_norescale_%s_%%=" % tag]
+        o += ref_update(qb, "s%d" % THR_S)
+    return o
+
+
+def rescale():
+    o = list(O_WAIT)
     for qb in range(QB):
         for r in range(64):
             a = O_A + qb * 64 + r
             t = P0 + (r % 16)
             o += ["v_accvgpr_read_b32 v%d, a%d" % (t, a), "v_mul_f32 v%d, v%d, v%d" % (t, t, ALPHA_V[qb]),
                   "v_accvgpr_write_b32 a%d, v%d" % (a, t)]
-    o += ["s_nop 1", "L_norescale_%s_%%=:" % tag]
-    # the step with the next tile's scores, or the wave's last tile
-    o += ["s_add_i32 s%d, %%[t], 1" % SREG, "s_cmp_lt_i32 s%d, %%[ntw]" % SREG,
-          "s_cbranch_scc0 L_last_%s_%%=" % tag]
-    mref = ("v%d" % MREF_V[0], "v%d" % MREF_V[1])
-    mx = ("v%d" % MX_V[0], "v%d" % MX_V[1])
-    o += gen(x_buf=P, y_buf=1 - P, kslot=1 - P, vslot=P, do_s=True, do_pv=True, do_max=True, mref=mref, mx=mx)
-    o += ["s_branch L_skip_%s_%%=" % tag, "L_last_%s_%%=:" % tag]
-    o += gen(x_buf=P, y_buf=1 - P, kslot=1 - P, vslot=P, do_s=False, do_pv=True, do_max=False, mref=mref, mx=mx)
-    o += ["L_skip_%s_%%=:" % tag, "s_waitcnt vmcnt(0)", "s_barrier"]
+    return o + ["s_nop 1"]
+
+
+def first_tile():
+    """S(0) of the wave, its mask where needed, its reference (O and l are still 0: no rescale)."""
+    o = ["s_cmp_le_i32 %[ntw], 0", "s_cbranch_scc1 L_first_done_%="]
+    o += gen(x_buf=1, y_buf=0, kslot=0, vslot=0, do_s=True, do_pv=False, do_max=True,
+             mx=("v%d" % MX_V[0], "v%d" % MX_V[1]))
+    o += ["s_mov_b32 s%d, 0" % SREG, "s_cmp_lt_i32 s%d, %%[tm]" % SREG, "s_cbranch_scc1 L_first_ref_%="]
+    o += mask_tile("s%d" % SREG, 0)
+    o += ["L_first_ref_%=:"] + full_ref() + ["L_first_done_%=:"]
     return o
 
 
+def iteration(parity):
+    """Step of tile t (S(t) in buffer `parity`, its reference applied). Returns the straight-line part and
+    the out-of-line parts (masked tiles, rescale, the wave's last step, waves without work), which end by
+    branching back."""
+    P = parity
+    tag = "p%d" % P
+    nxt = "s%d" % SREG
+    mref = ("v%d" % MREF_V[0], "v%d" % MREF_V[1])
+    mx = ("v%d" % MX_V[0], "v%d" % MX_V[1])
+    groups = step_dma(P)
+    o = res_advance(KRES) + res_advance(VRES) + ["s_add_i32 %s, %%[t], 1" % nxt]
+    o += ["s_cmp_ge_i32 %[t], %[ntw]", "s_cbranch_scc1 L_nocomp_%s_%%=" % tag,
+          "s_cmp_lt_i32 %s, %%[ntw]" % nxt, "s_cbranch_scc0 L_last_%s_%%=" % tag]
+    o += gen(x_buf=P, y_buf=1 - P, kslot=1 - P, vslot=P, do_s=True, do_pv=True, do_max=True, mref=mref, mx=mx,
+             dma_ins=groups, ref_upd=True)
+    # tile t+1 masked: mask, row max, reference and rescale out of line; otherwise the block's check
+    # says whether any row's reference must move (rare: then the update and the rescale, out of line)
+    uf = "s[%d:%d], s[%d:%d]" % (UFLAG[0], UFLAG[0] + 1, UFLAG[1], UFLAG[1] + 1)
+    o += ["s_cmp_ge_i32 %s, %%[tm]" % nxt, "s_cbranch_scc1 L_mask_%s_%%=" % tag,
+          "s_or_b64 vcc, %s" % uf, "s_cbranch_vccnz L_move_%s_%%=" % tag,
+          "L_after_%s_%%=:" % tag, "s_waitcnt vmcnt(0)", "s_barrier"]
+    ool = ["L_mask_%s_%%=:" % tag] + mask_tile(nxt, 1 - P) + full_ref()
+    ool += ["s_or_b64 vcc, %s" % uf, "s_cbranch_vccz L_after_%s_%%=" % tag] + rescale()
+    ool += ["s_branch L_after_%s_%%=" % tag]
+    ool += ["L_move_%s_%%=:" % tag] + full_ref() + rescale() + ["s_branch L_after_%s_%%=" % tag]
+    ool += ["L_last_%s_%%=:" % tag]
+    ool += gen(x_buf=P, y_buf=1 - P, kslot=1 - P, vslot=P, do_s=False, do_pv=True, do_max=False, mref=mref, mx=mx,
+               dma_ins=groups)
+    ool += ["s_branch L_after_%s_%%=" % tag, "L_nocomp_%s_%%=:" % tag]
+    for g in groups:
+        ool += g
+    ool += ["s_branch L_after_%s_%%=" % tag]
+    return o, ool
+
+
 def loop_body():
-    # S(0) of the wave (K(0) is in K slot 0) and its row max, then the tile loop
-    o = ["s_cmp_le_i32 %[ntw], 0", "s_cbranch_scc1 L_top_%="]
-    o += gen(x_buf=1, y_buf=0, kslot=0, vslot=0, do_s=True, do_pv=False, do_max=True,
-             mx=("v%d" % MX_V[0], "v%d" % MX_V[1]))
+    o = first_tile()
+    # descriptors one tile behind: each step first moves them to K(t+2) and V(t+1)
+    o += ["s_mov_b32 s%d, 1" % SREG] + tile_res(KRES, "s%d" % SREG, "%[khl]", "%[khh]")
+    o += ["s_mov_b32 s%d, 0" % SREG] + tile_res(VRES, "s%d" % SREG, "%[vhl]", "%[vhh]")
+    i0, ool0 = iteration(0)
+    i1, ool1 = iteration(1)
     o += ["L_top_%=:", "s_cmp_ge_i32 %[t], %[nt]", "s_cbranch_scc1 L_end_%="]
-    o += iteration(0)
+    o += i0
     o += ["s_add_i32 %[t], %[t], 1", "s_cmp_ge_i32 %[t], %[nt]", "s_cbranch_scc1 L_end_%="]
-    o += iteration(1)
-    o += ["s_add_i32 %[t], %[t], 1", "s_branch L_top_%=", "L_end_%=:"]
+    o += i1
+    o += ["s_add_i32 %[t], %[t], 1", "s_branch L_top_%="]
+    o += ool0 + ool1
+    o += ["L_end_%=:"] + list(O_WAIT)
     return o
 
 
@@ -363,23 +462,25 @@ def render_loop():
     body = loop_body()
     outs = (o_binding() + ['[l0] "+v"(l0)', '[l1] "+v"(l1)', '[mc0] "+v"(mc0)', '[mc1] "+v"(mc1)', '[t] "+s"(t)'])
     ins = (q_binding() + ka_binding() + va_binding() +
-           ['[vo%d] "v"(vo[%d])' % (j, j) for j in range(4)] + ['[dr%d] "v"(dr[%d])' % (j, j) for j in range(4)] +
+           ['[vo%d] "v"(vo[%d])' % (j, j) for j in range(4)] +
            ['[lim0] "v"(lim0)', '[lim1] "v"(lim1)', '[c] "s"(c_log2)', '[nt] "s"(ntiles)', '[ntw] "s"(ntiles_w)',
-            '[tm] "s"(t_mask)', '[tt] "s"(t_tail)', '[kve] "s"(kv_end)', '[khl] "s"(kh_lo)', '[khh] "s"(kh_hi)',
+            '[tm] "s"(t_mask)', '[kve] "s"(kv_end)', '[khl] "s"(kh_lo)', '[khh] "s"(kh_hi)',
             '[vhl] "s"(vh_lo)', '[vhh] "s"(vh_hi)', '[lbw] "s"(lbw)'])
-    clob = (['"v%d"' % r for r in LOOP_CLOB_V] + ['"s%d"' % r for r in range(SREG, SREG + 10)] +
+    clob = (['"v%d"' % r for r in LOOP_CLOB_V] + ['"s%d"' % r for r in LOOP_CLOB_S] +
             ['"vcc"', '"m0"', '"scc"', '"memory"'])
     return [
-        "// S(0) of the wave, then its tile loop: for t = 0 .. ntiles-1 (the same count in every wave of the",
-        "// workgroup, one barrier per tile): DMA of K(t+2) and V(t+1), then, while t < ntiles_w,",
-        "// mask (t >= t_mask), reference update, rescale of O when a row's reference moved,",
-        "// and the step with S(t+1) (t + 1 < ntiles_w) or the last step.",
+        "// S(0) of the wave and its reference, then its tile loop: for t = 0 .. ntiles-1 (the same count in",
+        "// every wave of the workgroup, one barrier per tile), while t < ntiles_w the step with S(t+1) and",
+        "// its reference (t + 1 < ntiles_w) or the last step, the DMA of K(t+2) and V(t+1) issued inside it;",
+        "// then the mask of S(t+1) where it needs one and the rescale of O where a reference moved (both",
+        "// out of line: the common path runs straight through).",
+        "// K and V are read through range-checked buffer descriptors: rows at or past kv_end are not read.",
         "__device__ __forceinline__ void qb2_loop(f32x16 (&o)[2][4], const bf16x8 (&q)[2][8], const uint32_t (&ka)[8],",
         "                                         const uint32_t (&va)[4][2], const uint32_t (&vo)[4],",
-        "                                         const int32_t (&dr)[4], int32_t lim0, int32_t lim1, float c_log2,",
+        "                                         int32_t lim0, int32_t lim1, float c_log2,",
         "                                         float &l0, float &l1, float &mc0, float &mc1,",
         "                                         int32_t t, int32_t ntiles, int32_t ntiles_w, int32_t t_mask,",
-        "                                         int32_t t_tail, int32_t kv_end, uint32_t kh_lo, uint32_t kh_hi,",
+        "                                         int32_t kv_end, uint32_t kh_lo, uint32_t kh_hi,",
         "                                         uint32_t vh_lo, uint32_t vh_hi, uint32_t lbw)",
         "{",
         "#pragma clang diagnostic push",
