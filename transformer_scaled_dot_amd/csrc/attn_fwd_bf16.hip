@@ -242,12 +242,13 @@ __device__ __forceinline__ void accumulate_pv(const uint8_t *lds, const TileAddr
 
 // O = O_acc / l for one block of 32 query rows (0 for a row with no
 // visible key), rounded to the output type and stored as [B,H,N,D] or as
-// the head concat [B,N,H,D].
-template <int D, bool OUT_F32, int OLAYOUT>
+// the head concat [B,N,H,D]. L_HALVES: each half-wave holds the row sum of
+// its own keys (else l_run is already the row's whole sum).
+template <int D, bool OUT_F32, int OLAYOUT, bool L_HALVES = true>
 __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float l_run, int qrow, int bh, int H, int Nq,
                                            int b, int hf, void *__restrict__ Out)
 {
-    const float l_tot = half_swap_sum(l_run);
+    const float l_tot = L_HALVES ? half_swap_sum(l_run) : l_run;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow >= Nq) return;
     size_t row_off;
@@ -663,8 +664,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
              u((uint32_t)vh), u((uint32_t)(vh >> 32)), lbw);
 
     mfma_fence_a8(acc);
+    // the row sums come from an MFMA over all 64 lanes: each lane holds its row's whole sum
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) store_rows<D, OUT_F32, OLAYOUT>(acc[qb], l_run[qb], qrow[qb], bh, H, Nq, b, hf, Out);
+    for (int qb = 0; qb < QB; ++qb)
+        store_rows<D, OUT_F32, OLAYOUT, false>(acc[qb], l_run[qb], qrow[qb], bh, H, Nq, b, hf, Out);
 }
 
 template <int D, int MASK, bool OUT_F32, int OLAYOUT>

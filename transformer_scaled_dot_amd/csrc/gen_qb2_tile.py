@@ -43,18 +43,22 @@ Run:  python gen_qb2_tile.py  (writes attn_qb2_tile.inc next to this file)
 """
 from __future__ import annotations
 
+import math
 import os
 
 D, KS, DB, QB = 128, 8, 4, 2
 TILE_B = 64 * D * 2
 S_BUF = (0, 64)
 P0, KST, VST, TMP, MXT = 128, 160, 176, 192, 200
+MXT_Q = ((200, 201), (217, 218))   # row-max temporaries of qb 0 and qb 1
 CLOB_END = 204         # v[128:203] are the block's scratch registers
 O_A, Q_A = 0, 128
+LSUM_A, ONES_A = 192, 224   # a[192:223]: row-sum accumulators (qb 0, 1); a[224:227]: all-ones operand
 NKS = NVS = 4          # staging slots
 LOOK = 5               # MFMAs between an operand's read and its first MFMA
-VALU_BUDGET = 5        # VALU cost units per MFMA slot (exp counts 2)
-DMA_COST = 2           # of those, taken by one DMA group (M0 write, load)
+SLOT_CYC = 30          # issue cycles between two MFMAs of a wave that keep the MFMA pipe busy
+ISSUE_CYC = 4          # issue cost of one instruction
+EXP_CYC = 8            # of a v_exp_f32
 WAIT_AHEAD = 3         # an LDS wait also covers the operands of up to this many following MFMAs ...
 WAIT_KEEP = 2          # ... leaving at least this many younger reads in flight
 O_WAIT = ["s_nop 7", "s_nop 7", "s_nop 7"]   # before reading O (or scores) written by the last MFMAs
@@ -102,12 +106,20 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
             c, db, qb = j // 8, (j // 2) % 4, j % 2
             vop = c * DB + db
             acc = O_A + (qb * DB + db) * 16
+            pop = vr(P0 + 4 * (qb * 4 + c), 4)
             mfma.append(dict(op=("v", vop), kind="PV", qb=qb, c=c,
                              text="v_mfma_f32_32x32x16_bf16 %s, %s, %s, %s" % (
-                                 ar(acc, 16), vr(VST + 4 * (vop % NVS), 4), vr(P0 + 4 * (qb * 4 + c), 4),
-                                 ar(acc, 16))))
+                                 ar(acc, 16), vr(VST + 4 * (vop % NVS), 4), pop, ar(acc, 16))))
+            if db == 0:
+                # row sums of the rounded weights: (all-ones) x P^T adds, in every row of a 32 x 32
+                # accumulator, the column sums of P, i.e. each query's sum over these 16 keys
+                ls = ar(LSUM_A + 16 * qb, 16)
+                mfma.append(dict(op=None, kind="SUM", qb=qb, c=c,
+                                 text="v_mfma_f32_32x32x16_bf16 %s, %s, %s, %s" % (ls, ar(ONES_A, 4), pop, ls)))
     first_use, last_use = {}, {}
     for m, f in enumerate(mfma):
+        if f["op"] is None:
+            continue
         first_use.setdefault(f["op"], m)
         last_use[f["op"]] = m
 
@@ -132,43 +144,55 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
 
     items = []
     if do_pv:
+        # half-chunks of 4 scores (one per lane and row block): 4 fma, 4 exp, 2 packs into P.
+        # Consecutive half-chunks use the two halves of v[192:199] in turn, and a half-chunk starts
+        # only once the one two before it (same registers) is complete, so two can interleave.
+        k = 0
         for c in range(4):
             for qb in range(QB):
-                jb, r0 = c // 2, (c % 2) * 8
-                ins = [("v_fma_f32 v%d, v%d, %%[c], -%s" % (TMP + u, s_reg(x_buf, qb, jb, r0 + u), mref[qb]), 1)
-                       for u in range(8)]
-                ins += [("v_exp_f32 v%d, v%d" % (TMP + u, TMP + u), 2) for u in range(8)]
-                p = P0 + 4 * (qb * 4 + c)
-                cvt = ["v_cvt_pk_bf16_f32 v%d, v%d, v%d" % (p + w, TMP + 2 * w, TMP + 2 * w + 1) for w in range(4)]
-                dot = ["v_dot2c_f32_bf16 %%[l%d], %s, v%d" % (qb, ONES_BF16X2, p + w) for w in range(4)]
-                ins += [(t, 1) for t in (cvt[0], cvt[1], cvt[2], dot[0], cvt[3], dot[1], dot[2], dot[3])]
-                dl = min(m for m, f in enumerate(mfma) if f["kind"] == "PV" and f["qb"] == qb and f["c"] == c)
-                items.append(dict(ins=ins, deadline=dl - 1, ready=0, p=p, name="exp q%d c%d" % (qb, c)))
+                jb = c // 2
+                dl = min(m for m, f in enumerate(mfma) if f["kind"] in ("PV", "SUM") and f["qb"] == qb and f["c"] == c)
+                for h in range(2):
+                    r0 = (c % 2) * 8 + 4 * h
+                    tb = TMP + 4 * (k % 2)
+                    fma = ["v_fma_f32 v%d, v%d, %%[c], -%s" % (tb + u, s_reg(x_buf, qb, jb, r0 + u), mref[qb])
+                           for u in range(4)]
+                    ex = ["v_exp_f32 v%d, v%d" % (tb + u, tb + u) for u in range(4)]
+                    p = P0 + 4 * (qb * 4 + c) + 2 * h
+                    cvt = ["v_cvt_pk_bf16_f32 v%d, v%d, v%d" % (p + w, tb + 2 * w, tb + 2 * w + 1) for w in range(2)]
+                    seq = [fma[0], fma[1], ex[0], fma[2], ex[1], fma[3], ex[2], ex[3], cvt[0], cvt[1]]
+                    items.append(dict(ins=seq, deadline=dl - 1, ready=0, p=P0 + 4 * (qb * 4 + c),
+                                      name="exp %d" % k, after=["exp %d" % (k - 2)] if k >= 2 else []))
+                    k += 1
     s_last = max((m for m, f in enumerate(mfma) if f["kind"] == "S"), default=None)
     if do_max:
         assert do_s
         for qb in range(QB):
-            ins = []
-            for jb in range(2):
-                m = MXT + jb
+            t0, t1 = MXT_Q[qb]
+            chains = []
+            for jb, m in ((0, t0), (1, t1)):
                 vals = [s_reg(y_buf, qb, jb, r) for r in range(16)]
-                ins.append(("v_max3_f32 v%d, v%d, v%d, v%d" % (m, vals[0], vals[1], vals[2]), 1))
+                ch = ["v_max3_f32 v%d, v%d, v%d, v%d" % (m, vals[0], vals[1], vals[2])]
                 rest = vals[3:]
                 while rest:
-                    a, b = rest[0], rest[1] if len(rest) > 1 else rest[0]
-                    ins.append(("v_max3_f32 v%d, v%d, v%d, v%d" % (m, m, a, b), 1))
+                    a_, b_ = rest[0], rest[1] if len(rest) > 1 else rest[0]
+                    ch.append("v_max3_f32 v%d, v%d, v%d, v%d" % (m, m, a_, b_))
                     rest = rest[2:]
-            ins.append(("v_max_f32 v%d, v%d, v%d" % (MXT, MXT, MXT + 1), 1))
-            ins.append(("v_mov_b32 v%d, v%d" % (MXT + 1, MXT), 1))
-            ins.append(("s_nop 1", 1))
-            ins.append(("v_permlane32_swap_b32 v%d, v%d" % (MXT, MXT + 1), 1))
-            ins.append(("v_max_f32 %s, v%d, v%d" % (mx[qb], MXT, MXT + 1), 1))
-            items.append(dict(ins=ins, deadline=10 ** 9, ready=s_last + 4, p=None, name="max q%d" % qb))
+                chains.append(ch)
+            ins = [x for pair in zip(*chains) for x in pair]   # the two chains alternate
+            ins += ["v_max_f32 v%d, v%d, v%d" % (t0, t0, t1), "v_mov_b32 v%d, v%d" % (t1, t0), "s_nop 1",
+                    "v_permlane32_swap_b32 v%d, v%d" % (t0, t1), "v_max_f32 %s, v%d, v%d" % (mx[qb], t0, t1)]
+            items.append(dict(ins=ins, deadline=len(mfma) + 8, ready=s_last + 4, p=None, name="max q%d" % qb))
     if ref_upd:
         assert do_max
         for qb in range(QB):
-            items.append(dict(ins=[(x, 1) for x in ref_check(qb)], deadline=10 ** 9, ready=s_last + 4, p=None,
+            items.append(dict(ins=ref_check(qb), deadline=len(mfma) + 8, ready=s_last + 4, p=None,
                               name="ref q%d" % qb, after=["max q%d" % qb]))
+
+    def cost(t):
+        if t.startswith("v_exp"):
+            return EXP_CYC
+        return ISSUE_CYC
 
     out = ["s_waitcnt lgkmcnt(0)"]
     issued, pos, p_done = [], {}, {}
@@ -180,10 +204,18 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
         it = by_name[name]
         return it["k"] == len(it["ins"])
 
+    def ready(it, m):
+        return it["k"] < len(it["ins"]) and it["ready"] <= m and all(done(a_) for a_ in it.get("after", ()))
+
     dma_at = {2 * i: list(g) for i, g in enumerate(dma_ins)}
     for g in dma_at.values():
         assert len(g) == 2 and g[0].startswith("s_add_u32 m0") and "lds" in g[1]
     assert len(mfma) > 2 * (len(dma_ins) - 1) or not dma_ins
+
+    # cycles of each slot (between two MFMA issues) left for the VALU work once the fixed
+    # instructions (operand reads, DMA, waits) are in
+    n_reads = [sum(len(reads[op]) for op in read_at.get(m + 1, [])) for m in range(len(mfma))]
+    avail = [SLOT_CYC - ISSUE_CYC * (n_reads[m] + 1 + (2 if m + 1 in dma_at else 0)) for m in range(len(mfma))]
 
     def emit_reads(slot):
         for op in read_at.get(slot, []):
@@ -192,51 +224,84 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
                 issued.append(op)
             pos[op] = len(issued) - 1
 
-    def emit_valu(it):
-        t, cost = it["ins"][it["k"]]
+    def emit(it):
+        t = it["ins"][it["k"]]
         out.append(t)
         it["k"] += 1
         if t.startswith("v_cvt_pk_bf16_f32"):
-            p_done[int(t.split()[1][1:].rstrip(",")) // 4 * 4] = len(out) - 1
-        return cost
+            p_done[int(t.split()[1][1:].rstrip(",")) // 4 * 4] = len(out) - 1  # the operand's last pack
+        return cost(t)
+
+    # the softmax half-chunks run at a steady pace that meets every P deadline: per slot, rate_c cycles
+    # of their instructions, rate_e of their exps (cumulative targets); the row max and the reference
+    # check use what the slots have left
+    rate_c = rate_e = 0.0
+    cum_c = cum_e = 0
+    for it in sorted((it for it in queue if it["name"].startswith("exp")), key=lambda x: x["deadline"]):
+        cum_c += sum(cost(t) for t in it["ins"])
+        cum_e += sum(1 for t in it["ins"] if t.startswith("v_exp"))
+        if it["deadline"] >= 0:
+            rate_c = max(rate_c, cum_c / (it["deadline"] + 1))
+            rate_e = max(rate_e, cum_e / (it["deadline"] + 1))
+    prog = {"c": 0, "e": 0}
 
     emit_reads(0)
     for m, f in enumerate(mfma):
-        if f["kind"] == "PV":
+        if f["kind"] in ("PV", "SUM"):
             p = P0 + 4 * (f["qb"] * 4 + f["c"])
             # nothing to overlap with yet (first P.V MFMAs of a block without S): finish that P operand here
+            def force(it):
+                for a_ in it.get("after", ()):
+                    force(by_name[a_])
+                while it["k"] < len(it["ins"]):
+                    emit(it)
             for it in queue:
                 if it["p"] == p:
-                    while it["k"] < len(it["ins"]):
-                        emit_valu(it)
+                    force(it)
             # at least two instructions between the last write of P and the MFMA that reads it
             gap = sum(1 for t in out[p_done[p] + 1:] if not t.startswith("s_waitcnt"))
             if gap < 2:
                 out.append("s_nop %d" % (1 - gap))
-        if pos[f["op"]] > waited[0]:
+        if f["op"] is not None and pos[f["op"]] > waited[0]:
             # wait once for this operand and for those of the next MFMAs already read (they have had
             # at least as long to arrive), rather than once per operand
             upto = max([pos[f["op"]]] + [pos[g["op"]] for g in mfma[m + 1:m + 1 + WAIT_AHEAD]
-                                         if g["op"] in pos and pos[g["op"]] <= len(issued) - 1 - WAIT_KEEP])
+                                         if g["op"] is not None and g["op"] in pos
+                                         and pos[g["op"]] <= len(issued) - 1 - WAIT_KEEP])
             outstanding_after = len(issued) - 1 - upto
             assert 0 <= outstanding_after <= 15
             out.append("s_waitcnt lgkmcnt(%d)" % outstanding_after)
             waited[0] = upto
-        budget = VALU_BUDGET
         dma = dma_at.pop(m, None)
         if dma:  # the MFMA is the wait state the LDS DMA needs after its M0 write
             out.append(dma[0])
-            budget -= DMA_COST
         out.append(f["text"])
         if dma:
             out.append(dma[1])
         emit_reads(m + 1)
-        while budget > 0:
-            cand = [it for it in queue if it["k"] < len(it["ins"]) and it["ready"] <= m
-                    and all(done(a) for a in it.get("after", ()))]
-            if not cand:
+        # fill the slot: the half-chunks up to their pace (earliest deadline first), then the rest
+        # within the slot's cycles
+        spent = 0
+        while True:
+            pick = None
+            for it in sorted((it for it in queue if ready(it, m)), key=lambda x: (x["deadline"], x["order"])):
+                t = it["ins"][it["k"]]
+                if it["name"].startswith("exp"):
+                    if prog["c"] >= rate_c * (m + 1) - 1e-9:
+                        continue
+                    if t.startswith("v_exp") and prog["e"] + 1 > math.ceil(rate_e * (m + 1) - 1e-9):
+                        continue
+                elif spent + cost(t) > avail[m]:
+                    continue
+                pick = it
                 break
-            budget -= emit_valu(min(cand, key=lambda x: (x["deadline"], x["order"])))
+            if pick is None:
+                break
+            t = pick["ins"][pick["k"]]
+            if pick["name"].startswith("exp"):
+                prog["c"] += cost(t)
+                prog["e"] += t.startswith("v_exp")
+            spent += emit(pick)
         if do_s:  # with the S part in front, every P operand is ready ahead of its MFMAs
             for it in queue:
                 assert it["k"] == len(it["ins"]) or m < it["deadline"], ("deadline missed", it["name"], m)
@@ -246,9 +311,9 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
     if rest and s_last is not None and len(mfma) - 1 - s_last < 3:
         out += ["s_nop 7", "s_nop 7", "s_nop 7"]
     for it in rest:
-        assert all(done(a) for a in it.get("after", ())), ("dependency order", it["name"])
+        assert all(done(a_) for a_ in it.get("after", ())), ("dependency order", it["name"])
         while it["k"] < len(it["ins"]):
-            emit_valu(it)
+            emit(it)
     return out
 
 
@@ -287,7 +352,7 @@ SREG = 88               # s[88:97] scratch SGPRs
 UFLAG = (92, 94)        # s[92:93] / s[94:95]: rows whose reference moved, per qb
 THR_S = 96              # the slack (8) in an SGPR
 MCP_V = (215, 216)      # reference + slack, per qb
-LOOP_CLOB_V = list(range(0, 217))   # S buffers, P, staging and the loop's own registers
+LOOP_CLOB_V = list(range(0, 219))   # S buffers, P, staging and the loop's own registers
 LOOP_CLOB_S = list(range(KRES, SREG + 10))
 BUF_WORD3 = "0x20000"   # 32-bit data format, no stride: byte-addressed, range-checked raw buffer
 
@@ -324,7 +389,7 @@ def ref_check(qb):
 
 def ref_update(qb, thr):
     """Move the reference of qb's rows to the new tile max where it exceeds the old reference by more than
-    the slack (thr = 8, or +inf to keep it); alpha = exp2(old - new) (1 where it stays); l *= alpha."""
+    the slack (thr = 8); alpha = exp2(old - new) (1 where it stays)."""
     t0, t1, t2 = TMPL + 3 * qb, TMPL + 3 * qb + 1, TMPL + 3 * qb + 2
     u = "s[%d:%d]" % (UFLAG[qb], UFLAG[qb] + 1)
     return ["v_mul_f32 v%d, v%d, %%[c]" % (t0, MX_V[qb]),
@@ -336,7 +401,6 @@ def ref_update(qb, thr):
             "v_mov_b32 %%[mc%d], v%d" % (qb, t1),
             "v_max_f32 v%d, 0xff7fffff, v%d" % (MREF_V[qb], t1),
             "v_cndmask_b32_e64 v%d, 1.0, v%d, %s" % (ALPHA_V[qb], t2, u),
-            "v_mul_f32 %%[l%d], %%[l%d], v%d" % (qb, qb, ALPHA_V[qb]),
             "v_add_f32 v%d, %s, %%[mc%d]" % (MCP_V[qb], thr, qb)]
 
 
@@ -385,7 +449,13 @@ def full_ref():
 
 
 def rescale():
+    """O *= alpha and l *= alpha per row (l: the first register of each row-sum accumulator, the one read
+    at the end)."""
     o = list(O_WAIT)
+    for qb in range(QB):
+        a = LSUM_A + 16 * qb
+        o += ["v_accvgpr_read_b32 v%d, a%d" % (P0, a), "v_mul_f32 v%d, v%d, v%d" % (P0, P0, ALPHA_V[qb]),
+              "v_accvgpr_write_b32 a%d, v%d" % (a, P0)]
     for qb in range(QB):
         for r in range(64):
             a = O_A + qb * 64 + r
@@ -442,7 +512,10 @@ def iteration(parity):
 
 
 def loop_body():
-    o = first_tile()
+    o = ["v_mov_b32 v0, %s" % ONES_BF16X2, "v_mov_b32 v1, 0"]
+    o += ["v_accvgpr_write_b32 a%d, v0" % (ONES_A + i) for i in range(4)]
+    o += ["v_accvgpr_write_b32 a%d, v1" % (LSUM_A + i) for i in range(32)]
+    o += ["s_nop 3"] + first_tile()
     # descriptors one tile behind: each step first moves them to K(t+2) and V(t+1)
     o += ["s_mov_b32 s%d, 1" % SREG] + tile_res(KRES, "s%d" % SREG, "%[khl]", "%[khh]")
     o += ["s_mov_b32 s%d, 0" % SREG] + tile_res(VRES, "s%d" % SREG, "%[vhl]", "%[vhh]")
@@ -455,6 +528,7 @@ def loop_body():
     o += ["s_add_i32 %[t], %[t], 1", "s_branch L_top_%="]
     o += ool0 + ool1
     o += ["L_end_%=:"] + list(O_WAIT)
+    o += ["v_accvgpr_read_b32 %%[l%d], a%d" % (qb, LSUM_A + 16 * qb) for qb in range(QB)]
     return o
 
 
@@ -466,7 +540,8 @@ def render_loop():
            ['[lim0] "v"(lim0)', '[lim1] "v"(lim1)', '[c] "s"(c_log2)', '[nt] "s"(ntiles)', '[ntw] "s"(ntiles_w)',
             '[tm] "s"(t_mask)', '[kve] "s"(kv_end)', '[khl] "s"(kh_lo)', '[khh] "s"(kh_hi)',
             '[vhl] "s"(vh_lo)', '[vhh] "s"(vh_hi)', '[lbw] "s"(lbw)'])
-    clob = (['"v%d"' % r for r in LOOP_CLOB_V] + ['"s%d"' % r for r in LOOP_CLOB_S] +
+    clob = (['"a%d"' % r for r in range(LSUM_A, ONES_A + 4)] + ['"v%d"' % r for r in LOOP_CLOB_V] +
+            ['"s%d"' % r for r in LOOP_CLOB_S] +
             ['"vcc"', '"m0"', '"scc"', '"memory"'])
     return [
         "// S(0) of the wave and its reference, then its tile loop: for t = 0 .. ntiles-1 (the same count in",
