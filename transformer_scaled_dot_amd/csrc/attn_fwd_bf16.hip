@@ -34,6 +34,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -271,6 +273,50 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float l_
                 *(u32x2 *)((uint16_t *)Out + row_off + d0) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
             }
         }
+}
+
+// O = O_acc / l for one block of 32 query rows, as bf16, staged through an 8 KiB LDS area of the wave so
+// that every store writes whole 256-byte rows (four rows per instruction) instead of 16 bytes per row.
+// l_tot: the row's whole sum; rows >= Nq are not stored. The area's 16-byte chunks are XOR-swizzled by
+// row so that both the 8-byte writes and the 16-byte reads spread over the banks.
+template <int OLAYOUT>
+__device__ __forceinline__ void store_rows_bf16_staged(const f32x16 (&acc)[4], float l_tot, int row0, int bh, int H,
+                                                       int Nq, int b, int lane, uint8_t *stage, void *__restrict__ Out)
+{
+    constexpr int D = 128;
+    // computed here rather than kept from the kernel's start: the lane-dependent addresses would otherwise
+    // be hoisted out of the workgroup's item loop and held across the tile loop, which has no registers
+    // to spare
+    asm volatile("" : "+v"(lane));
+    const int l32 = lane & 31, hf = lane >> 5;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const int c = db * 4 + rg;
+            const u32x2 v = {pack_bf16x2(acc[db][rg * 4 + 0] * inv, acc[db][rg * 4 + 1] * inv),
+                             pack_bf16x2(acc[db][rg * 4 + 2] * inv, acc[db][rg * 4 + 3] * inv)};
+            *(u32x2 *)(stage + l32 * 256 + ((c ^ (l32 & 15)) << 4) + hf * 8) = v;
+        }
+    // the wave's LDS operations complete in order: keep the compiler from moving the reads up
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = i * 4 + (lane >> 4), cc = lane & 15;
+        const u32x4 d = *(const u32x4 *)(stage + r * 256 + ((cc ^ (r & 15)) << 4));
+        const int row = row0 + r;
+        if (row < Nq) {
+            size_t row_off;
+            if (OLAYOUT == kOutBHND) {
+                row_off = ((size_t)bh * Nq + row) * D;
+            } else {
+                row_off = (((size_t)b * Nq + row) * H + bh % H) * D;
+            }
+            *(u32x4 *)((uint16_t *)Out + row_off + cc * 8) = d;
+        }
+    }
+    asm volatile("" ::: "memory");
 }
 
 // Occupancy: 128-wide heads with two query blocks per wave need the whole
@@ -532,107 +578,117 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2])
 // ---------------------------------------------------------------------------
 // 128-wide heads, 64 query rows per wave (two blocks of 32), 4 waves per
 // workgroup, one wave per SIMD. Every K or V operand read from LDS feeds two
-// MFMAs, which halves the LDS bytes per MFMA against 32-row waves. The
-// steady-state tile step -- S(t+1) MFMAs, the exponentials of S(t), the
-// P(t).V(t) MFMAs and the row max of S(t+1) -- is one inline-asm block with a
-// fixed interleaved schedule (generated by gen_qb2_tile.py), since a single
-// wave per SIMD has no partner wave to hide its latencies. The tile's
-// bookkeeping (masking, reference max, rescale of O), the first and the last
-// tile of each wave run in C++ around it.
+// MFMAs, which halves the LDS bytes per MFMA against 32-row waves. The whole
+// tile loop of a wave -- S(t+1) MFMAs, the exponentials of S(t), the
+// P(t).V(t) and row-sum MFMAs, the row max of S(t+1), the DMA of later K/V
+// tiles, masking, reference max and rescale of O -- is one inline-asm
+// statement with a fixed schedule (generated by gen_qb2_tile.py), since a
+// single wave per SIMD has no partner wave to hide its latencies.
 //
-// Registers: O and Q^T in AGPRs, the two score buffers, P and the operand
-// staging in VGPRs, at the physical registers the asm block names.
+// The grid is persistent: one workgroup per CU, each taking work items
+// (256 query rows of one (batch, head)) in a fixed order. For the causal mask
+// items are ranked heaviest first and dealt out boustrophedon-wise (even
+// rounds in workgroup order, odd rounds reversed by groups of 8 so that a
+// workgroup keeps its XCD), which gives every workgroup the same number of
+// tiles when the ranks split evenly; each workgroup starts its list at a
+// different item so that item boundaries are spread in time. The next item's
+// Q rows are fetched into LDS while the current item runs, and the tile
+// loop's fetches run on past the item's last tile into the next item's first
+// K/V tiles (tiles take slots of parity (t + off) % 2, off carried from item
+// to item). Outputs go out as whole rows through an LDS staging area.
+// LDS: K0 K1 V0 V1, the four waves' Q rows, 8 KiB of staging per wave
+// (160 KiB).
+//
+// Registers: O, Q^T, the row sums and an all-ones operand in AGPRs, the two
+// score buffers, P and the operand staging in VGPRs, at the physical
+// registers the asm names.
+struct Qb2Item {
+    int valid, bh, b, q0, kv_len, kv_end, ntiles;
+};
+
+// Item of workgroup w in round k: even rounds in workgroup order, odd rounds reversed (by groups of 8 when
+// G is a multiple of 8, so that the XCD stays the same).
+__device__ __forceinline__ int qb2_round_item(int w, int k, int G)
+{
+    const int i = (k & 1) ? ((G & 7) == 0 ? (G / 8 - 1 - w / 8) * 8 + (w & 7) : G - 1 - w) : w;
+    return k * G + i;
+}
+
+// The j-th item workgroup w processes (>= num_items: none). A workgroup takes its rounds' items starting
+// from round w mod (its item count), so that item boundaries -- where a workgroup waits for its next
+// item's first tiles -- do not fall at the same time on every CU.
+__device__ __forceinline__ int qb2_sched(int w, int j, int G, int num_items)
+{
+    const int rounds = num_items / G;
+    const int n_w = rounds + (qb2_round_item(w, rounds, G) < num_items ? 1 : 0);
+    if (j >= n_w) return num_items;
+    return qb2_round_item(w, (j + w) % n_w, G);
+}
+
+template <int MASK>
+__device__ __forceinline__ Qb2Item qb2_item(int p, int num_items, int num_qtiles, int BH, int H, int Nk,
+                                            const int32_t *__restrict__ valid_lens)
+{
+    constexpr int BM = 256;
+    Qb2Item it{};
+    it.valid = p < num_items;
+    if (!it.valid) return it;
+    it.bh = p % BH;
+    int qt = p / BH;
+    if (MASK == kMaskCausal) qt = num_qtiles - 1 - qt;
+    it.b = it.bh / H;
+    it.q0 = qt * BM;
+    it.kv_len = Nk;
+    if (MASK == kMaskPadding) {
+        const int L = valid_lens[it.b];
+        it.kv_len = L < 0 ? 0 : (L > Nk ? Nk : L);
+    }
+    it.kv_end = it.kv_len;
+    if (MASK == kMaskCausal) it.kv_end = min(it.kv_len, it.q0 + BM);
+    it.ntiles = (it.kv_end + kBlockN - 1) / kBlockN;
+    // wave-uniform by construction; say so, so that they stay in SGPRs
+    it.bh = __builtin_amdgcn_readfirstlane(it.bh);
+    it.b = __builtin_amdgcn_readfirstlane(it.b);
+    it.q0 = __builtin_amdgcn_readfirstlane(it.q0);
+    it.kv_len = __builtin_amdgcn_readfirstlane(it.kv_len);
+    it.kv_end = __builtin_amdgcn_readfirstlane(it.kv_end);
+    it.ntiles = __builtin_amdgcn_readfirstlane(it.ntiles);
+    return it;
+}
+
 template <int MASK, bool OUT_F32, int OLAYOUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_fwd_qb2_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const int32_t *__restrict__ valid_lens, float c_log2, void *__restrict__ Out, int H, int Nq, int Nk,
     int num_qtiles, int BH)
 {
-    constexpr int D = 128, QB = 2, WAVES = 4, RW = 64, BM = WAVES * RW;
+    constexpr int D = 128, QB = 2, WAVES = 4, RW = 64;
     constexpr int KS = D / 16, DB = D / 32;
     constexpr int TILE_B = kBlockN * D * 2;
     constexpr int CPR = D / 8;
     constexpr int CH = kBlockN * CPR / (WAVES * 64);
     static_assert(kBlockN * CPR % (WAVES * 64) == 0, "tile must split evenly over the workgroup");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_B];
-    constexpr int KSLOT0 = 0, KSLOT1 = TILE_B, VSLOT0 = 2 * TILE_B, VSLOT1 = 3 * TILE_B;
+    // K0 K1 V0 V1 (the tile loop's slots), then the Q rows of the four waves (the next item's while the
+    // current item's loop runs its last tiles)
+    __shared__ __attribute__((aligned(16))) uint8_t smem[10 * TILE_B];
+    constexpr int KSLOT0 = 0, KSLOT1 = TILE_B, VSLOT0 = 2 * TILE_B, VSLOT1 = 3 * TILE_B, QSLOT = 4 * TILE_B;
+    constexpr int STAGE = 8 * TILE_B;  // 8 KiB per wave for the output rows (bf16 output)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
-
-    const int id = blockIdx.x;
-    const int bh = id % BH;
-    int qt = id / BH;
-    if (MASK == kMaskCausal) qt = num_qtiles - 1 - qt;
-    const int b = bh / H;
-    const int q0 = qt * BM;
-
-    int kv_len = Nk;
-    if (MASK == kMaskPadding) {
-        const int L = valid_lens[b];
-        kv_len = L < 0 ? 0 : (L > Nk ? Nk : L);
-    }
-    int kv_end = kv_len;
-    if (MASK == kMaskCausal) kv_end = min(kv_len, q0 + BM);
-    const int ntiles = (kv_end + kBlockN - 1) / kBlockN;
-
-    const uint16_t *Kh = K + (size_t)bh * Nk * D;
-    const uint16_t *Vh = V + (size_t)bh * Nk * D;
-
-    const int qmin_w = q0 + wave * RW, qmax_w = qmin_w + RW - 1;
-    int qrow[QB];
-    u32x4 qv[QB][KS];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        qrow[qb] = qmin_w + qb * 32 + l32;
-        const bool ok = qrow[qb] < Nq;
-        const uint16_t *qp = Q + ((size_t)bh * Nq + (ok ? qrow[qb] : 0)) * D + hf * 8;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qv[qb][ks] = ok ? *(const u32x4 *)(qp + ks * 16) : u32x4{0u, 0u, 0u, 0u};
-    }
-    // O = 0 and Q^T in the AGPRs the tile steps name
-    bf16x8 qreg[QB][KS];
-    f32x16 acc[QB][DB];
-    qb2_init(acc, qreg, qv);
-    float mc_run[QB] = {-INFINITY, -INFINITY}, l_run[QB] = {0.f, 0.f}, mx[QB] = {0.f, 0.f};
+    const int G = gridDim.x, w = blockIdx.x;
+    const int num_items = num_qtiles * BH;
 
     const TileAddrs<D> ad = tile_addrs<D>(lane);
     const uint32_t lds0 = lds_addr(smem);
+    // lane's row of each 1 KiB DMA chunk and its byte offset (16-byte chunks XOR-swizzled)
+    auto dma_row = [&](int j) { return ((j * WAVES + wave) * 64 + lane) / CPR; };
     uint32_t voff[CH];
-    int drow[CH];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-        const int c = (j * WAVES + wave) * 64 + lane;
-        const int r = c / CPR, x = c % CPR;
-        drow[j] = r;
+        const int r = dma_row(j), x = ((j * WAVES + wave) * 64 + lane) % CPR;
         voff[j] = (uint32_t)(r * D + ((x ^ swz<D>(r)) << 3)) * 2;
     }
-    auto issue = [&](const uint16_t *src, int t, uint32_t slot_off) {
-        const int k0 = t * kBlockN;
-        const uint16_t *base = src + (size_t)k0 * D;
-        const bool tail = k0 + kBlockN > kv_end;
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            uint32_t off = voff[j];
-            if (tail) {
-                const int r = min(drow[j], kv_end - 1 - k0);
-                off = off - (uint32_t)(drow[j] - r) * (D * 2);
-            }
-            lds_dma16(__builtin_amdgcn_readfirstlane(lds0 + slot_off + (j * WAVES + wave) * 1024), base, off);
-        }
-    };
-
-    const int ntiles_w = (MASK == kMaskCausal) ? min(ntiles, qmax_w / kBlockN + 1) : ntiles;
-    // first tile of this wave that needs a mask: the tile crossing kv_len, or
-    // (causal) the first tile with a key past the wave's first row
-    int t_mask = kv_len / kBlockN;
-    if (MASK == kMaskCausal) t_mask = min(t_mask, (qmin_w + 1) / kBlockN);
-    // a visible key of row qrow satisfies key <= lim; the asm compares the key's
-    // offset within the tile (lane half included) against lim - tile start
-    int32_t lim[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) lim[qb] = (MASK == kMaskCausal ? min(qrow[qb], kv_len - 1) : kv_len - 1) - hf * 4;
-
     // LDS byte addresses of the operand reads (the tile offsets are instruction immediates)
     uint32_t kaddr[KS], vaddr[DB][2];
 #pragma unroll
@@ -642,32 +698,133 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         vaddr[db][0] = lds0 + ad.v[db][0];
         vaddr[db][1] = lds0 + ad.v[db][1];
     }
-    float mc0 = -INFINITY, mc1 = -INFINITY;
-    if (ntiles > 0) {
-        // the tile loop fetches no row at or past kv_end; V slot 1 is read (with weight 0) before any
-        // fetch has written such rows, so it starts as zeros rather than whatever LDS held
-#pragma unroll
-        for (int i = 0; i < TILE_B / (16 * 256); ++i)
-            *(u32x4 *)(smem + VSLOT1 + (i * 256 + tid) * 16) = u32x4{0u, 0u, 0u, 0u};
-        issue(Kh, 0, KSLOT0);
-        if (ntiles > 1) issue(Kh, 1, KSLOT1);
-        issue(Vh, 0, VSLOT0);
-        wait_vmcnt0();
-        __syncthreads();
-    }
-    const uint64_t kh = (uint64_t)Kh, vh = (uint64_t)Vh;
+
     const uint32_t lbw = __builtin_amdgcn_readfirstlane(lds0 + wave * 1024);
     // wave-uniform values go to the asm in SGPRs
     auto u = [](int x) { return (int32_t)__builtin_amdgcn_readfirstlane(x); };
-    qb2_loop(acc, qreg, kaddr, vaddr, voff, lim[0], lim[1], c_log2, l_run[0], l_run[1], mc0, mc1,
-             u(0), u(ntiles), u(ntiles_w), u(t_mask), u(kv_end), u((uint32_t)kh), u((uint32_t)(kh >> 32)),
-             u((uint32_t)vh), u((uint32_t)(vh >> 32)), lbw);
-
-    mfma_fence_a8(acc);
-    // the row sums come from an MFMA over all 64 lanes: each lane holds its row's whole sum
+    // 64 rows [r0, r0 + 64) of a [rows, D] matrix (r_end >= 1 rows) into an LDS tile slot (swizzled like
+    // every tile); rows at or past r_end repeat row r_end - 1, so nothing past the matrix is read. The
+    // offsets are taken from the first fetched row, r_base <= every fetched row, so none is negative
+    // (the whole tile may lie past r_end: the rows of a last partial Q tile).
+    auto issue = [&](const uint16_t *mat, int r0, int r_end, uint32_t slot_off) {
+        const int r_base = min(r0, r_end - 1);
+        const uint16_t *base = mat + (size_t)r_base * D;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-        store_rows<D, OUT_F32, OLAYOUT, false>(acc[qb], l_run[qb], qrow[qb], bh, H, Nq, b, hf, Out);
+        for (int j = 0; j < CH; ++j) {
+            // voff[j] = lane's tile row * 256 + its (swizzled) chunk's byte offset in the row
+            const int row = min(r0 + (int)(voff[j] >> 8), r_end - 1);
+            const uint32_t off = (voff[j] & 255u) + (uint32_t)(row - r_base) * (D * 2);
+            lds_dma16(lbw + slot_off + j * WAVES * 1024, base, off);
+        }
+    };
+    // first tiles of an item whose slots take parity off: K(0), K(1), V(0). The tile loop fetches no row at
+    // or past kv_end; the other V slot is read (with weight 0) before the item's own fetches have written
+    // such rows, so it holds zeros rather than what LDS held before. (Each wave fetches a quarter of every
+    // tile.)
+    auto first_tiles = [&](const Qb2Item &it, int off) {
+#pragma unroll
+        for (int i = 0; i < TILE_B / (16 * 256); ++i)
+            *(u32x4 *)(smem + VSLOT0 + (1 - off) * TILE_B + (i * 256 + tid) * 16) = u32x4{0u, 0u, 0u, 0u};
+        if (it.ntiles > 0) {
+            const uint16_t *Kh = K + (size_t)it.bh * Nk * D, *Vh = V + (size_t)it.bh * Nk * D;
+            issue(Kh, 0, it.kv_end, KSLOT0 + off * TILE_B);
+            if (it.ntiles > 1) issue(Kh, kBlockN, it.kv_end, KSLOT0 + (1 - off) * TILE_B);
+            issue(Vh, 0, it.kv_end, VSLOT0 + off * TILE_B);
+        }
+    };
+    // the item's Q rows (the four waves' 64-row blocks) into the Q slots
+    auto q_tiles = [&](const Qb2Item &it) {
+        const uint16_t *Qh = Q + (size_t)it.bh * Nq * D;
+#pragma unroll
+        for (int qw = 0; qw < WAVES; ++qw) issue(Qh, it.q0 + qw * RW, Nq, QSLOT + qw * TILE_B);
+    };
+
+    int k = 0, off = 0;
+    Qb2Item cur = qb2_item<MASK>(qb2_sched(w, 0, G, num_items), num_items, num_qtiles, BH, H, Nk, valid_lens);
+    if (!cur.valid) return;
+    q_tiles(cur);
+    first_tiles(cur, 0);
+    bool fetched = true;  // this item's first tiles were fetched outside a tile loop: wait for them
+    for (;;) {
+        if (fetched) wait_vmcnt0();
+        __syncthreads();
+        // O = 0 and Q^T (this wave's rows, from its Q slot) in the AGPRs the tile loop names
+        u32x4 qv[QB][KS];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qv[qb][ks] = *(const u32x4 *)(smem + QSLOT + wave * TILE_B + qb * 32 * D * 2 + ad.k[ks]);
+        bf16x8 qreg[QB][KS];
+        f32x16 acc[QB][DB];
+        qb2_init(acc, qreg, qv);
+        // every wave has its Q before any wave fetches the next item's Q rows into the Q slots; they
+        // arrive while this item's tiles run
+        __syncthreads();
+        const Qb2Item nxt =
+            qb2_item<MASK>(qb2_sched(w, ++k, G, num_items), num_items, num_qtiles, BH, H, Nk, valid_lens);
+        if (nxt.valid) q_tiles(nxt);
+
+        const int qmin_w = cur.q0 + wave * RW, qmax_w = qmin_w + RW - 1;
+        int32_t lim[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            // a visible key of row qrow satisfies key <= lim; the asm compares the key's
+            // offset within the tile (lane half included) against lim - tile start
+            const int qrow = qmin_w + qb * 32 + l32;
+            lim[qb] = (MASK == kMaskCausal ? min(qrow, cur.kv_len - 1) : cur.kv_len - 1) - hf * 4;
+        }
+        const int ntiles_w = (MASK == kMaskCausal) ? min(cur.ntiles, qmax_w / kBlockN + 1) : cur.ntiles;
+        // first tile of this wave that needs a mask: the tile crossing kv_len, or
+        // (causal) the first tile with a key past the wave's first row
+        int t_mask = cur.kv_len / kBlockN;
+        if (MASK == kMaskCausal) t_mask = min(t_mask, (qmin_w + 1) / kBlockN);
+        const uint64_t kh = (uint64_t)(K + (size_t)cur.bh * Nk * D), vh = (uint64_t)(V + (size_t)cur.bh * Nk * D);
+        const Qb2Item &nn = nxt.valid ? nxt : cur;  // a valid address even when there is no next item
+        const uint64_t nkh = (uint64_t)(K + (size_t)nn.bh * Nk * D), nvh = (uint64_t)(V + (size_t)nn.bh * Nk * D);
+        float l_run[QB] = {0.f, 0.f}, mc0 = -INFINITY, mc1 = -INFINITY;
+        qb2_loop(acc, qreg, kaddr, vaddr, voff, lim[0], lim[1], c_log2, l_run[0], l_run[1], mc0, mc1,
+                 u(0), u(cur.ntiles), u(ntiles_w), u(t_mask), u(cur.kv_end), u((uint32_t)kh),
+                 u((uint32_t)(kh >> 32)), u((uint32_t)vh), u((uint32_t)(vh >> 32)), lbw, u(off),
+                 u((uint32_t)nkh), u((uint32_t)(nkh >> 32)), u((uint32_t)nvh), u((uint32_t)(nvh >> 32)),
+                 u(nxt.valid ? nxt.kv_end : 0));
+
+        // The loop's last steps fetched the next item's K(0), K(1), V(0) into the slots of parity
+        // (off + ntiles) % 2 and ended with a barrier after they (and the next Q rows) had arrived. With
+        // fewer than two tiles it did not (K(0) of the next item would have been due before this item's
+        // first step): fetch them here.
+        const int off_next = (off + cur.ntiles) & 1;
+        fetched = cur.ntiles < 2;
+        if (nxt.valid && fetched) first_tiles(nxt, off_next);
+        mfma_fence_a8(acc);
+        // the row sums come from an MFMA over all 64 lanes: each lane holds its row's whole sum
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            if constexpr (OUT_F32)
+                store_rows<D, OUT_F32, OLAYOUT, false>(acc[qb], l_run[qb], cur.q0 + wave * RW + qb * 32 + l32, cur.bh,
+                                                       H, Nq, cur.b, hf, Out);
+            else
+                store_rows_bf16_staged<OLAYOUT>(acc[qb], l_run[qb], cur.q0 + wave * RW + qb * 32, cur.bh, H, Nq, cur.b,
+                                                lane, smem + STAGE + wave * 8192, Out);
+        }
+        if (!nxt.valid) break;
+        cur = nxt;
+        off = off_next;
+    }
+}
+
+// Compute units of the current device (cached per device): the persistent grid's size.
+int device_cu_count()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 template <int D, int MASK, bool OUT_F32, int OLAYOUT>
@@ -690,7 +847,8 @@ hipError_t launch_variant(const void *Q, const void *K, const void *V, const int
     // visible exp2 argument rounds to 0 anyway, which is the scale = 0 result.
     const float c_log2 = fmaxf(scale * 1.4426950408889634f, 1e-30f);
     if constexpr (QB2ASM)
-        hipLaunchKernelGGL((attn_fwd_qb2_kernel<MASK, OUT_F32, OLAYOUT>), dim3((unsigned)grid), dim3(256), 0, stream,
+        hipLaunchKernelGGL((attn_fwd_qb2_kernel<MASK, OUT_F32, OLAYOUT>),
+                           dim3((unsigned)std::min<long long>(grid, device_cu_count())), dim3(256), 0, stream,
                            (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, valid_lens, c_log2, O, H,
                            Nq, Nk, num_qtiles, BH);
     else

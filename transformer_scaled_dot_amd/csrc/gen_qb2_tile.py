@@ -351,6 +351,7 @@ KRES, VRES = 80, 84     # s[80:83] / s[84:87]: buffer descriptors of the K and V
 SREG = 88               # s[88:97] scratch SGPRs
 UFLAG = (92, 94)        # s[92:93] / s[94:95]: rows whose reference moved, per qb
 THR_S = 96              # the slack (8) in an SGPR
+NKVB_S = 97             # the next item's kv_end in bytes
 MCP_V = (215, 216)      # reference + slack, per qb
 LOOP_CLOB_V = list(range(0, 219))   # S buffers, P, staging and the loop's own registers
 LOOP_CLOB_S = list(range(KRES, SREG + 10))
@@ -465,15 +466,38 @@ def rescale():
     return o + ["s_nop 1"]
 
 
-def first_tile():
-    """S(0) of the wave, its mask where needed, its reference (O and l are still 0: no rescale)."""
+def first_tile(off):
+    """S(0) of the wave, its mask where needed, its reference (O and l are still 0: no rescale). Tiles of
+    the item take the slots and score buffers of parity (t + off) % 2: K(0) is in K slot off."""
+    tag = "f%d" % off
     o = ["s_cmp_le_i32 %[ntw], 0", "s_cbranch_scc1 L_first_done_%="]
-    o += gen(x_buf=1, y_buf=0, kslot=0, vslot=0, do_s=True, do_pv=False, do_max=True,
+    o += gen(x_buf=1 - off, y_buf=off, kslot=off, vslot=off, do_s=True, do_pv=False, do_max=True,
              mx=("v%d" % MX_V[0], "v%d" % MX_V[1]))
-    o += ["s_mov_b32 s%d, 0" % SREG, "s_cmp_lt_i32 s%d, %%[tm]" % SREG, "s_cbranch_scc1 L_first_ref_%="]
-    o += mask_tile("s%d" % SREG, 0)
-    o += ["L_first_ref_%=:"] + full_ref() + ["L_first_done_%=:"]
+    o += ["s_mov_b32 s%d, 0" % SREG, "s_cmp_lt_i32 s%d, %%[tm]" % SREG, "s_cbranch_scc1 L_%s_ref_%%=" % tag]
+    o += mask_tile("s%d" % SREG, off)
+    o += ["L_%s_ref_%%=:" % tag] + full_ref() + ["s_branch L_first_done_%="]
     return o
+
+
+def stream_res(res, x, base_lo, base_hi, nbase_lo, nbase_hi):
+    """Descriptor of tile x (a constant) of the stream this item's tiles continue into the next item's:
+    tile x of this item when x < nt, else tile x - nt of the next one."""
+    o = ["s_mov_b32 s%d, %d" % (SREG, x)] + tile_res(res, "s%d" % SREG, base_lo, base_hi)
+    o += ["s_cmp_ge_i32 s%d, %%[nt]" % SREG, "s_cbranch_scc0 L_sr%d_%d_%%=" % (res, x),
+          "s_sub_i32 s%d, s%d, %%[nt]" % (SREG, SREG)]
+    o += next_res(res, "s%d" % SREG, nbase_lo, nbase_hi) + ["L_sr%d_%d_%%=:" % (res, x)]
+    return o
+
+
+def next_res(res, tile_sreg, base_lo, base_hi):
+    """Descriptor of tile (tile_sreg) of the next item (size from its kv_end: 0 when there is none)."""
+    return ["s_lshl_b32 s%d, %s, 14" % (SREG + 1, tile_sreg),
+            "s_add_u32 s%d, %s, s%d" % (res, base_lo, SREG + 1),
+            "s_addc_u32 s%d, %s, 0" % (res + 1, base_hi),
+            "s_lshl_b32 s%d, %%[nkve], 8" % (res + 2),
+            "s_sub_i32 s%d, s%d, s%d" % (res + 2, res + 2, SREG + 1),
+            "s_max_i32 s%d, s%d, 0" % (res + 2, res + 2),
+            "s_mov_b32 s%d, %s" % (res + 3, BUF_WORD3)]
 
 
 def iteration(parity):
@@ -486,7 +510,15 @@ def iteration(parity):
     mref = ("v%d" % MREF_V[0], "v%d" % MREF_V[1])
     mx = ("v%d" % MX_V[0], "v%d" % MX_V[1])
     groups = step_dma(P)
-    o = res_advance(KRES) + res_advance(VRES) + ["s_add_i32 %s, %%[t], 1" % nxt]
+    # descriptors to K(t+2) and V(t+1) of the stream: past this item's last tile, the next item's first
+    # tiles (so that they are in their slots when this item ends)
+    o = res_advance(KRES) + res_advance(VRES)
+    o += ["s_add_i32 %s, %%[t], 2" % nxt, "s_cmp_eq_i32 %s, %%[nt]" % nxt,
+          "s_cselect_b32 s%d, %%[nkhl], s%d" % (KRES, KRES), "s_cselect_b32 s%d, %%[nkhh], s%d" % (KRES + 1, KRES + 1),
+          "s_cselect_b32 s%d, s%d, s%d" % (KRES + 2, NKVB_S, KRES + 2)]
+    o += ["s_add_i32 %s, %%[t], 1" % nxt, "s_cmp_eq_i32 %s, %%[nt]" % nxt,
+          "s_cselect_b32 s%d, %%[nvhl], s%d" % (VRES, VRES), "s_cselect_b32 s%d, %%[nvhh], s%d" % (VRES + 1, VRES + 1),
+          "s_cselect_b32 s%d, s%d, s%d" % (VRES + 2, NKVB_S, VRES + 2)]
     o += ["s_cmp_ge_i32 %[t], %[ntw]", "s_cbranch_scc1 L_nocomp_%s_%%=" % tag,
           "s_cmp_lt_i32 %s, %%[ntw]" % nxt, "s_cbranch_scc0 L_last_%s_%%=" % tag]
     o += gen(x_buf=P, y_buf=1 - P, kslot=1 - P, vslot=P, do_s=True, do_pv=True, do_max=True, mref=mref, mx=mx,
@@ -515,15 +547,19 @@ def loop_body():
     o = ["v_mov_b32 v0, %s" % ONES_BF16X2, "v_mov_b32 v1, 0"]
     o += ["v_accvgpr_write_b32 a%d, v0" % (ONES_A + i) for i in range(4)]
     o += ["v_accvgpr_write_b32 a%d, v1" % (LSUM_A + i) for i in range(32)]
-    o += ["s_nop 3"] + first_tile()
-    # descriptors one tile behind: each step first moves them to K(t+2) and V(t+1)
-    o += ["s_mov_b32 s%d, 1" % SREG] + tile_res(KRES, "s%d" % SREG, "%[khl]", "%[khh]")
-    o += ["s_mov_b32 s%d, 0" % SREG] + tile_res(VRES, "s%d" % SREG, "%[vhl]", "%[vhh]")
+    o += ["s_nop 3", "s_lshl_b32 s%d, %%[nkve], 8" % NKVB_S]
+    # S(0) with the item's parity
+    o += ["s_cmp_eq_u32 %[off], 0", "s_cbranch_scc0 L_first1_%="] + first_tile(0)
+    o += ["L_first1_%=:"] + first_tile(1) + ["L_first_done_%=:"]
+    # descriptors one tile behind: each step first moves them to K(t+2) and V(t+1) of the stream
+    o += stream_res(KRES, 1, "%[khl]", "%[khh]", "%[nkhl]", "%[nkhh]")
+    o += stream_res(VRES, 0, "%[vhl]", "%[vhh]", "%[nvhl]", "%[nvhh]")
     i0, ool0 = iteration(0)
     i1, ool1 = iteration(1)
+    o += ["s_cmp_eq_u32 %[off], 0", "s_cbranch_scc0 L_mid_%="]
     o += ["L_top_%=:", "s_cmp_ge_i32 %[t], %[nt]", "s_cbranch_scc1 L_end_%="]
     o += i0
-    o += ["s_add_i32 %[t], %[t], 1", "s_cmp_ge_i32 %[t], %[nt]", "s_cbranch_scc1 L_end_%="]
+    o += ["s_add_i32 %[t], %[t], 1", "L_mid_%=:", "s_cmp_ge_i32 %[t], %[nt]", "s_cbranch_scc1 L_end_%="]
     o += i1
     o += ["s_add_i32 %[t], %[t], 1", "s_branch L_top_%="]
     o += ool0 + ool1
@@ -539,7 +575,8 @@ def render_loop():
            ['[vo%d] "v"(vo[%d])' % (j, j) for j in range(4)] +
            ['[lim0] "v"(lim0)', '[lim1] "v"(lim1)', '[c] "s"(c_log2)', '[nt] "s"(ntiles)', '[ntw] "s"(ntiles_w)',
             '[tm] "s"(t_mask)', '[kve] "s"(kv_end)', '[khl] "s"(kh_lo)', '[khh] "s"(kh_hi)',
-            '[vhl] "s"(vh_lo)', '[vhh] "s"(vh_hi)', '[lbw] "s"(lbw)'])
+            '[vhl] "s"(vh_lo)', '[vhh] "s"(vh_hi)', '[lbw] "s"(lbw)', '[off] "s"(off)', '[nkhl] "s"(nkh_lo)',
+            '[nkhh] "s"(nkh_hi)', '[nvhl] "s"(nvh_lo)', '[nvhh] "s"(nvh_hi)', '[nkve] "s"(nkv_end)'])
     clob = (['"a%d"' % r for r in range(LSUM_A, ONES_A + 4)] + ['"v%d"' % r for r in LOOP_CLOB_V] +
             ['"s%d"' % r for r in LOOP_CLOB_S] +
             ['"vcc"', '"m0"', '"scc"', '"memory"'])
@@ -548,7 +585,9 @@ def render_loop():
         "// every wave of the workgroup, one barrier per tile), while t < ntiles_w the step with S(t+1) and",
         "// its reference (t + 1 < ntiles_w) or the last step, the DMA of K(t+2) and V(t+1) issued inside it;",
         "// then the mask of S(t+1) where it needs one and the rescale of O where a reference moved (both",
-        "// out of line: the common path runs straight through).",
+        "// out of line: the common path runs straight through). Tiles use the slots and score buffers of",
+        "// parity (t + off) % 2; the fetches continue past the item's last tile into the next item's first",
+        "// tiles (K(0), K(1), V(0) of the item given by nkh/nvh/nkv_end; nkv_end = 0: none).",
         "// K and V are read through range-checked buffer descriptors: rows at or past kv_end are not read.",
         "__device__ __forceinline__ void qb2_loop(f32x16 (&o)[2][4], const bf16x8 (&q)[2][8], const uint32_t (&ka)[8],",
         "                                         const uint32_t (&va)[4][2], const uint32_t (&vo)[4],",
@@ -556,7 +595,9 @@ def render_loop():
         "                                         float &l0, float &l1, float &mc0, float &mc1,",
         "                                         int32_t t, int32_t ntiles, int32_t ntiles_w, int32_t t_mask,",
         "                                         int32_t kv_end, uint32_t kh_lo, uint32_t kh_hi,",
-        "                                         uint32_t vh_lo, uint32_t vh_hi, uint32_t lbw)",
+        "                                         uint32_t vh_lo, uint32_t vh_hi, uint32_t lbw, int32_t off,",
+        "                                         uint32_t nkh_lo, uint32_t nkh_hi, uint32_t nvh_lo, uint32_t nvh_hi,",
+        "                                         int32_t nkv_end)",
         "{",
         "#pragma clang diagnostic push",
         "#pragma clang diagnostic ignored \"-Winline-asm\"",
