@@ -163,6 +163,39 @@ def test_causal_future_keys_never_reach_output(dev):
     assert np.array_equal(o1[:, :, 0], v.f64[:, :, 0])
 
 
+def test_d128_item_transitions_padding(dev):
+    """More (256-row query block, head) items than CUs, so that every workgroup of the 128-wide-head
+    kernel runs several items back to back, with key counts of 0, 1, under one tile, exactly one tile and
+    several tiles (the next item's first tiles are fetched by the previous item's tile loop, or separately
+    after items of fewer than two tiles). Keys at or past valid_len hold NaN: they are never fetched, so
+    they never reach an output."""
+    B, H, N = 8, 40, 260
+    q, k, v, _ = synth.attn_inputs(2, B=B, H=H, N=N, d=128)
+    vl = np.asarray([0, 1, 63, 64, 65, 128, 260, 17], dtype=np.int32)
+    kr, vr = k.raw.copy(), v.raw.copy()
+    for b in range(B):
+        kr[b, :, vl[b]:] = 0x7FC0
+        vr[b, :, vl[b]:] = 0x7FC0
+    got = gpu_attn(dev, q, synth.Tensor(kr, "bf16", k.shape), synth.Tensor(vr, "bf16", v.shape), mask="padding",
+                   vl=vl)
+    assert np.all(got[0] == 0.0)
+    heads = [1, 7, 20, 39]  # the oracle on a few heads of every batch (all heads are independent)
+    ref = oracle.attention(q.f64[:, heads], k.f64[:, heads], v.f64[:, heads], mask="padding", valid_lens=vl)
+    check("bf16 [8,40,260,128] padding, valid_lens %s, heads %s" % (vl.tolist(), heads), got[:, heads], ref, "bf16")
+
+
+@pytest.mark.parametrize("N", [40, 70, 300])
+def test_d128_item_transitions_causal(dev, N):
+    """Causal, 128-wide heads, B*H = 320 heads: at N = 40 every item has one key tile (all next-item tiles
+    fetched after the item), at 70 two, at 300 a mix of 4 and 5."""
+    B, H = 4, 80
+    q, k, v, _ = synth.attn_inputs(3, B=B, H=H, N=N, d=128)
+    got = gpu_attn(dev, q, k, v, mask="causal")
+    heads = [0, 33, 79]
+    ref = oracle.attention(q.f64[:, heads], k.f64[:, heads], v.f64[:, heads], mask="causal")
+    check("bf16 [4,80,%d,128] causal, heads %s" % (N, heads), got[:, heads], ref, "bf16")
+
+
 def test_empty_and_degenerate(dev):
     import transformer_scaled_dot_amd as tsd
 

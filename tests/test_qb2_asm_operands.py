@@ -7,7 +7,9 @@ operands inside the fixed scratch ranges, the loop would overwrite its own
 addresses and fault. These tests compile the kernel file to gfx950 assembly,
 line the emitted loop up against the generator's template and check every
 substituted operand register; they also check that the committed include is
-what the generator emits.
+what the generator emits, the LDS slots each step reads and fetches into, and
+(on a model of the slots) that every read finds the tile it expects across
+the items a workgroup runs back to back.
 """
 from __future__ import annotations
 
@@ -17,6 +19,7 @@ import re
 import shutil
 import subprocess
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -113,3 +116,95 @@ def test_loop_operands_outside_fixed_registers(device_asm):
                     pytest.fail("operand %s in unexpected register %s" % (name, reg))
                 checked += 1
     assert checked > 1000
+
+
+# --------------------------------------------------------------------------------------------------
+# LDS slot protocol of the generated loop: which slot each step reads and which one its fetches write,
+# and (as a model) which tile sits in each slot when it is read, across the items a workgroup runs.
+
+TB = 64 * 128 * 2
+
+
+def _slots(ins):
+    kr, vr, kw, vw = set(), set(), set(), set()
+    for t in ins:
+        m = re.match(r"ds_read_b128 v\[\d+:\d+\], %\[ka\d\] offset:(\d+)", t)
+        if m:
+            kr.add(int(m.group(1)) // TB)
+        m = re.match(r"ds_read_b64_tr_b16 v\[\d+:\d+\], %\[va\d_\d\] offset:(\d+)", t)
+        if m:
+            vr.add(int(m.group(1)) // TB - 2)
+        m = re.match(r"s_add_u32 m0, %\[lbw\], (\d+)", t)
+        if m:
+            sl = int(m.group(1)) // TB
+            (kw if sl < 2 else vw).add(sl % 2)
+    return kr, vr, kw, vw
+
+
+def test_step_slots():
+    g = _gen()
+    for P in (0, 1):
+        o, ool = g.iteration(P)
+        full = o[o.index("s_cbranch_scc0 L_last_p%d_%%=" % P):]
+        last = ool[ool.index("L_last_p%d_%%=:" % P):ool.index("L_nocomp_p%d_%%=:" % P)]
+        noc = ool[ool.index("L_nocomp_p%d_%%=:" % P):]
+        for part in (full, last, noc):
+            kr, vr, kw, vw = _slots(part)
+            assert kw == {P} and vw == {1 - P}   # K(t+2) -> K slot P, V(t+1) -> V slot 1-P
+            assert not (kr & kw) and not (vr & vw)
+        kr, vr, _, _ = _slots(full)
+        assert kr == {1 - P} and vr == {P}       # S(t+1) reads K(t+1), P.V reads V(t)
+        kr, vr, _, _ = _slots(last)
+        assert kr == set() and vr == {P}
+    for off in (0, 1):
+        kr, vr, kw, vw = _slots(g.first_tile(off))
+        assert kr == {off} and not vr and not kw and not vw
+    # step 0 fetches K(2) into the slot S(0) reads K(0) from: a barrier must separate them
+    body = g.loop_body()
+    assert "s_barrier" in body[body.index("L_first_done_%=:"):body.index("L_top_%=:")]
+    o, _ = g.iteration(0)
+    assert o[-2:] == ["s_waitcnt vmcnt(0)", "s_barrier"] or "s_barrier" in o[-3:]
+
+
+def _run_items(items):
+    """Tiles in the K/V slots as a workgroup runs items with the given tile counts: step t of an item
+    fetches tiles t+2 (K) and t+1 (V) of the stream that continues into the next item; items of fewer
+    than two tiles leave the next item's first tiles to a separate fetch."""
+    K, V = [None, None], [None, None]
+
+    def fetch_first(i, off):
+        if items[i] > 0:
+            K[off] = (i, 0)
+            if items[i] > 1:
+                K[1 - off] = (i, 1)
+            V[off] = (i, 0)
+
+    off = 0
+    fetch_first(0, off)
+    for i, nt in enumerate(items):
+        nxt = i + 1 if i + 1 < len(items) else None
+
+        def stream(x):
+            if x < nt:
+                return (i, x)
+            return (nxt, x - nt) if nxt is not None else None
+
+        if nt > 0:
+            assert K[off] == (i, 0) and V[off] == (i, 0)
+        for t in range(nt):
+            P = (t + off) % 2
+            if t + 1 < nt:
+                assert K[1 - P] == (i, t + 1)
+            assert V[P] == (i, t)
+            K[P] = stream(t + 2)
+            V[1 - P] = stream(t + 1)
+        off_next = (off + nt) % 2
+        if nxt is not None and nt < 2:
+            fetch_first(nxt, off_next)
+        off = off_next
+
+
+def test_item_stream_model():
+    rng = np.random.default_rng(7)
+    for _ in range(5000):
+        _run_items([int(x) for x in rng.choice([0, 1, 2, 3, 4, 5, 8], size=int(rng.integers(1, 7)))])

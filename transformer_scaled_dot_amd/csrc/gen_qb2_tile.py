@@ -551,6 +551,8 @@ def loop_body():
     # S(0) with the item's parity
     o += ["s_cmp_eq_u32 %[off], 0", "s_cbranch_scc0 L_first1_%="] + first_tile(0)
     o += ["L_first1_%=:"] + first_tile(1) + ["L_first_done_%=:"]
+    # step 0 fetches K(2) into the slot K(0) came from: no wave may still be reading K(0)
+    o += ["s_barrier"]
     # descriptors one tile behind: each step first moves them to K(t+2) and V(t+1) of the stream
     o += stream_res(KRES, 1, "%[khl]", "%[khh]", "%[nkhl]", "%[nkhh]")
     o += stream_res(VRES, 0, "%[vhl]", "%[vhh]", "%[nvhl]", "%[nvhh]")
