@@ -277,8 +277,10 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float l_
 
 // O = O_acc / l for one block of 32 query rows, as bf16, staged through an 8 KiB LDS area of the wave so
 // that every store writes whole 256-byte rows (four rows per instruction) instead of 16 bytes per row.
-// l_tot: the row's whole sum; rows >= Nq are not stored. The area's 16-byte chunks are XOR-swizzled by
-// row so that both the 8-byte writes and the 16-byte reads spread over the banks.
+// l_tot: the row's whole sum. The stores go through a buffer descriptor that covers exactly the block's
+// rows below Nq, so rows past Nq are dropped by the range check (no per-row branch). The area's 16-byte
+// chunks are XOR-swizzled by row so that both the 8-byte writes and the 16-byte reads spread over the
+// banks.
 template <int OLAYOUT>
 __device__ __forceinline__ void store_rows_bf16_staged(const f32x16 (&acc)[4], float l_tot, int row0, int bh, int H,
                                                        int Nq, int b, int lane, uint8_t *stage, void *__restrict__ Out)
@@ -289,7 +291,7 @@ __device__ __forceinline__ void store_rows_bf16_staged(const f32x16 (&acc)[4], f
     // to spare
     asm volatile("" : "+v"(lane));
     const int l32 = lane & 31, hf = lane >> 5;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -301,20 +303,17 @@ __device__ __forceinline__ void store_rows_bf16_staged(const f32x16 (&acc)[4], f
         }
     // the wave's LDS operations complete in order: keep the compiler from moving the reads up
     asm volatile("" ::: "memory");
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    const int stride = (OLAYOUT == kOutBHND ? D : H * D) * 2;  // bytes from one output row to the next
+    const size_t first = OLAYOUT == kOutBHND ? ((size_t)bh * Nq + row0) * D : (((size_t)b * Nq + row0) * H + bh % H) * D;
+    const int nrows = min(32, Nq - row0);
+    const int nbytes = nrows > 0 ? (nrows - 1) * stride + D * 2 : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((uint16_t *)Out + first, (short)0, nbytes, 0x20000);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int r = i * 4 + (lane >> 4), cc = lane & 15;
         const u32x4 d = *(const u32x4 *)(stage + r * 256 + ((cc ^ (r & 15)) << 4));
-        const int row = row0 + r;
-        if (row < Nq) {
-            size_t row_off;
-            if (OLAYOUT == kOutBHND) {
-                row_off = ((size_t)bh * Nq + row) * D;
-            } else {
-                row_off = (((size_t)b * Nq + row) * H + bh % H) * D;
-            }
-            *(u32x4 *)((uint16_t *)Out + row_off + cc * 8) = d;
-        }
+        __builtin_amdgcn_raw_buffer_store_b128(d, rs, r * stride + cc * 16, 0, 0);
     }
     asm volatile("" ::: "memory");
 }
