@@ -65,23 +65,29 @@ def hbm_traffic_per_launch():
     return t.get("bytes_per_launch")
 
 
-def time_launches(fn, nsteps, warmup):
+def time_launches(fn, nsteps, warmup, per_launch=False):
     """Warm up, then time exactly nsteps launches between two device
-    synchronisations with HIP events on the launching (current) stream."""
+    synchronisations with HIP events on the launching (current) stream.
+    Returns (mean ms per launch, wall seconds, per-launch ms or None): with
+    per_launch, an event between consecutive launches gives each launch's
+    time as well (the mean is still first event to last)."""
     import torch
 
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps + 1 if per_launch else 2)]
     t0 = time.perf_counter()
-    start.record()
+    ev[0].record()
     for i in range(nsteps):
         fn(i)
-    end.record()
+        if per_launch:
+            ev[i + 1].record()
+    ev[-1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return start.elapsed_time(end) / nsteps, wall
+    each = [ev[i].elapsed_time(ev[i + 1]) for i in range(nsteps)] if per_launch else None
+    return ev[0].elapsed_time(ev[-1]) / nsteps, wall, each
 
 
 def bench_attention(dev, cfg_id, nsteps, warmup, mask, sets=2, out_dtype=None):
@@ -103,12 +109,15 @@ def bench_attention(dev, cfg_id, nsteps, warmup, mask, sets=2, out_dtype=None):
         qq, kk, vv, oo = bufs[i % sets]
         tsd.attn_fwd(qq, kk, vv, mask=mask, valid_lens=vl_t, out=oo, out_dtype=oo.dtype)
 
-    ms, wall = time_launches(step, nsteps, warmup)
+    ms, wall, _ = time_launches(step, nsteps, warmup)
+    # a second pass with an event between launches for the per-launch spread (the events could add a
+    # little between launches, so the mean above comes from a pass without them)
+    _, _, each = time_launches(step, nsteps, 0, per_launch=True)
     if mask == "padding":
         flops = attn_flops(B, H, N, N, d, False)
     else:
         flops = attn_flops(B, H, N, N, d, mask == "causal")
-    return dict(ms=ms, wall=wall, flops=flops, shape=(B, H, N, d), valid_lens=vl)
+    return dict(ms=ms, wall=wall, flops=flops, shape=(B, H, N, d), valid_lens=vl, each=each)
 
 
 def bench_mha(dev, nsteps, warmup, sets=4):
@@ -128,7 +137,7 @@ def bench_mha(dev, nsteps, warmup, sets=4):
         xx, ww, wwo, oo, ws = bufs[i % sets]
         tsd.mha_fwd(xx, ww, wwo, h, out=oo, workspace=ws)
 
-    ms, wall = time_launches(step, nsteps, warmup)
+    ms, wall, _ = time_launches(step, nsteps, warmup)
     dk = dm // h
     flops = 8.0 * B * N * dm * dm + 4.0 * B * h * N * N * dk
     return dict(ms=ms, wall=wall, flops=flops)
@@ -235,8 +244,13 @@ def main():
             "kernel": "attn_fwd_qb2_kernel<causal, bf16 out>",
             "algorithmic_flops_per_launch": r["flops"],
             "avg_launch_ms": round(r["ms"], 5),
+            "launch_ms_median": round(float(np.median(r["each"])), 5),
+            "launch_ms_min": round(float(np.min(r["each"])), 5),
         },
         "wall_s_timed_region": round(r["wall"], 4),
+        # the shader clock right after the timed launches, with every CU's matrix pipe busy; the peak above
+        # assumes 2.4 GHz
+        "sclk_mhz_after": round(tsd.clock_probe_mhz(dev), 0),
     }
     if args.extra:
         extra = {}

@@ -123,6 +123,20 @@ TSD_API attn_status_t mha_fwd(const void *X, const void *W_qkv, const void *W_o,
                       int32_t seq, int32_t d_model, int32_t dtype, void *workspace, size_t workspace_bytes,
                       void *stream);
 
+/*
+ * attn_clock_probe -- measurement support, not part of the attention path:
+ * the shader clock the GPU sustains while busy. One workgroup per compute
+ * unit runs back-to-back matrix instructions for spin_us microseconds of
+ * wall time and records, per workgroup, the shader-clock ticks
+ * (s_memtime) and the 100 MHz wall-clock ticks (s_memrealtime) that
+ * elapsed; mean MHz = 100 * sum(ticks) / sum(wall ticks).
+ *
+ *   out      device uint64 [2 * blocks]: (ticks, wall ticks) per workgroup
+ *   blocks   1 .. 65536 workgroups (use the compute-unit count)
+ *   spin_us  1 .. 100000
+ */
+TSD_API attn_status_t attn_clock_probe(uint64_t *out, int32_t blocks, int32_t spin_us, void *stream);
+
 /* Static description of a status code. */
 TSD_API const char *attn_status_string(int32_t status);
 

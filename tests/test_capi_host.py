@@ -122,3 +122,9 @@ def test_binding_refuses_cpu_tensors(lib):
     x = torch.zeros(1, 4, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         tsd.mha_fwd(x, torch.zeros(128, 384, dtype=torch.bfloat16), torch.zeros(128, 128, dtype=torch.bfloat16), 2)
+
+
+@pytest.mark.parametrize("args", [(0, 256, 1000), (8, 0, 1000), (8, 65537, 1000), (8, 256, 0), (8, 256, 100001)])
+def test_clock_probe_rejects(lib, args):
+    ptr, blocks, spin = args
+    assert lib.attn_clock_probe(ctypes.c_void_p(ptr), blocks, spin, None) == EINVAL

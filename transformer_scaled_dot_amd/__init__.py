@@ -25,7 +25,8 @@ ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 MASK_KINDS = {"none": 0, "causal": 1, "padding": 2}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
-EXPORTS = ("attn_fwd", "mha_workspace_bytes", "mha_fwd", "attn_status_string", "attn_last_error")
+EXPORTS = ("attn_fwd", "mha_workspace_bytes", "mha_fwd", "attn_clock_probe", "attn_status_string",
+           "attn_last_error")
 
 _lib = None
 
@@ -54,6 +55,8 @@ def load_library():
     lib.mha_workspace_bytes.restype = ctypes.c_size_t
     lib.mha_fwd.argtypes = [P, P, P, I32, P, I32, I32, I32, I32, P, ctypes.c_size_t, P]
     lib.mha_fwd.restype = ctypes.c_int
+    lib.attn_clock_probe.argtypes = [P, I32, I32, P]
+    lib.attn_clock_probe.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [I32]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
@@ -179,3 +182,19 @@ def mha_fwd(x, w_qkv, w_o, h: int, out=None, workspace=None):
                      ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream_ptr(x.device))
     _raise_for(lib, st, "mha_fwd")
     return out
+
+
+def clock_probe_mhz(device=None, spin_us: int = 2000) -> float:
+    """Mean shader clock (MHz) over one workgroup per compute unit kept busy with matrix instructions for
+    ``spin_us`` of wall time (measurement support; synchronises the device)."""
+    import torch
+
+    lib = load_library()
+    device = torch.device("cuda", 0) if device is None else torch.device(device)
+    blocks = torch.cuda.get_device_properties(device).multi_processor_count
+    out = torch.zeros(2 * blocks, dtype=torch.int64, device=device)
+    st = lib.attn_clock_probe(ctypes.c_void_p(out.data_ptr()), blocks, int(spin_us), _stream_ptr(device))
+    _raise_for(lib, st, "attn_clock_probe")
+    v = out.view(blocks, 2).sum(dim=0).cpu().tolist()
+    return 100.0 * v[0] / max(v[1], 1)
+
