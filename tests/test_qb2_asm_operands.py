@@ -208,3 +208,39 @@ def test_item_stream_model():
     rng = np.random.default_rng(7)
     for _ in range(5000):
         _run_items([int(x) for x in rng.choice([0, 1, 2, 3, 4, 5, 8], size=int(rng.integers(1, 7)))])
+
+
+def test_diagonal_step_slots_and_mask():
+    """The step that masks the wave's causal diagonal tile inside its block uses the same slots as the
+    plain step, and its mask hides exactly the keys past each row: with the tile starting at the wave's
+    first row, lane (l32, hf) of query block qb holds row qb*32 + l32 and, in score register r of key
+    block jb, key jb*32 + (r//4)*8 + hf*4 + r%4."""
+    g = _gen()
+    for P in (0, 1):
+        _, ool = g.iteration(P)
+        diag = ool[ool.index("L_diag_p%d_%%=:" % P):ool.index("L_last_p%d_%%=:" % P)]
+        kr, vr, kw, vw = _slots(diag)
+        assert kr == {1 - P} and vr == {P} and kw == {P} and vw == {1 - P}
+    for buf in (0, 1):
+        for qb in range(2):
+            ins = g.diag_mask(buf, qb)
+            movs = {int(re.match(r"v_mov_b32 v(\d+), v%d" % g.NINF_V, t).group(1)) for t in ins
+                    if t.startswith("v_mov_b32")}
+            cmps = {}
+            for a, b in zip(ins, ins[1:]):
+                m = re.match(r"v_cmp_gt_i32_e64 s\[\d+:\d+\], (\d+), v\d+", a)
+                if m:
+                    cmps[int(re.match(r"v_cndmask_b32_e64 v(\d+),", b).group(1))] = int(m.group(1))
+            for jb in range(2):
+                for r in range(16):
+                    reg = g.s_reg(buf, qb, jb, r)
+                    for l32 in range(32):
+                        for hf in range(2):
+                            key, row = jb * 32 + (r // 4) * 8 + hf * 4 + r % 4, qb * 32 + l32
+                            if reg in movs:
+                                masked = True
+                            elif reg in cmps:
+                                masked = cmps[reg] > row - hf * 4   # off > lim - tile start
+                            else:
+                                masked = False
+                            assert masked == (key > row), (buf, qb, jb, r, l32, hf)

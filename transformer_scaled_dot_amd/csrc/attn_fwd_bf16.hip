@@ -774,10 +774,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             lim[qb] = (MASK == kMaskCausal ? min(qrow, cur.kv_len - 1) : cur.kv_len - 1) - hf * 4;
         }
         const int ntiles_w = (MASK == kMaskCausal) ? min(cur.ntiles, qmax_w / kBlockN + 1) : cur.ntiles;
-        // first tile of this wave that needs a mask: the tile crossing kv_len, or
-        // (causal) the first tile with a key past the wave's first row
-        int t_mask = cur.kv_len / kBlockN;
-        if (MASK == kMaskCausal) t_mask = min(t_mask, (qmin_w + 1) / kBlockN);
+        // The one tile of this wave that needs a mask: the tile crossing kv_len (masked after its scores,
+        // out of line), or, causal, the wave's diagonal tile, which starts at the wave's first row (a
+        // multiple of 64) and is masked inside its step. Causal rows past kv_len are past Nq: not stored.
+        const int t_mask = (MASK == kMaskCausal) ? 0x7fffffff : cur.kv_len / kBlockN;
+        const int t_diag = (MASK == kMaskCausal) ? qmin_w / kBlockN : 0x7fffffff;
         const uint64_t kh = (uint64_t)(K + (size_t)cur.bh * Nk * D), vh = (uint64_t)(V + (size_t)cur.bh * Nk * D);
         const Qb2Item &nn = nxt.valid ? nxt : cur;  // a valid address even when there is no next item
         const uint64_t nkh = (uint64_t)(K + (size_t)nn.bh * Nk * D), nvh = (uint64_t)(V + (size_t)nn.bh * Nk * D);
@@ -786,7 +787,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                  u(0), u(cur.ntiles), u(ntiles_w), u(t_mask), u(cur.kv_end), u((uint32_t)kh),
                  u((uint32_t)(kh >> 32)), u((uint32_t)vh), u((uint32_t)(vh >> 32)), lbw, u(off),
                  u((uint32_t)nkh), u((uint32_t)(nkh >> 32)), u((uint32_t)nvh), u((uint32_t)(nvh >> 32)),
-                 u(nxt.valid ? nxt.kv_end : 0));
+                 u(nxt.valid ? nxt.kv_end : 0), u(t_diag));
 
         // The loop's last steps fetched the next item's K(0), K(1), V(0) into the slots of parity
         // (off + ntiles) % 2 and ended with a barrier after they (and the next Q rows) had arrived. With

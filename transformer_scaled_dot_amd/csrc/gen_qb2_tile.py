@@ -56,7 +56,7 @@ O_A, Q_A = 0, 128
 LSUM_A, ONES_A = 192, 224   # a[192:223]: row-sum accumulators (qb 0, 1); a[224:227]: all-ones operand
 NKS = NVS = 4          # staging slots
 LOOK = 5               # MFMAs between an operand's read and its first MFMA
-SLOT_CYC = 30          # issue cycles between two MFMAs of a wave that keep the MFMA pipe busy
+SLOT_CYC = 26          # issue cycles between two MFMAs of a wave that keep the MFMA pipe busy (measured best)
 ISSUE_CYC = 4          # issue cost of one instruction
 EXP_CYC = 8            # of a v_exp_f32
 WAIT_AHEAD = 3         # an LDS wait also covers the operands of up to this many following MFMAs ...
@@ -78,14 +78,16 @@ def s_reg(buf, qb, jb, r):
 
 
 def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mref1]"), mx=("%[mx0]", "%[mx1]"),
-        dma_ins=(), ref_upd=False):
+        dma_ins=(), ref_upd=False, diag=False):
     """Instruction list of one block.
 
     x_buf: S buffer holding S(t) (exp + P.V part), y_buf: buffer receiving the
     new scores; kslot / vslot: LDS tile slots (0 or 1) of the K and V tiles.
     dma_ins: groups of DMA instructions, one group issued behind each of the
     first MFMAs (every other one); ref_upd: also move the reference of the new
-    scores (after their row max and after this block's row sums).
+    scores (after their row max and after this block's row sums); diag: the new scores are those of the
+    wave's causal diagonal tile (its first key is the wave's first row; tile start * 64 in s89): mask
+    them (keys past each row's own) before their row max.
     The block ends without waiting for its last MFMAs: code that reads O or
     the new scores next must wait 24 wait states first (O_WAIT)."""
     koff = kslot * TILE_B
@@ -182,7 +184,11 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
             ins = [x for pair in zip(*chains) for x in pair]   # the two chains alternate
             ins += ["v_max_f32 v%d, v%d, v%d" % (t0, t0, t1), "v_mov_b32 v%d, v%d" % (t1, t0), "s_nop 1",
                     "v_permlane32_swap_b32 v%d, v%d" % (t0, t1), "v_max_f32 %s, v%d, v%d" % (mx[qb], t0, t1)]
-            items.append(dict(ins=ins, deadline=len(mfma) + 8, ready=s_last + 4, p=None, name="max q%d" % qb))
+            if diag:
+                items.append(dict(ins=diag_mask(y_buf, qb), deadline=len(mfma) + 8, ready=s_last + 4, p=None,
+                                  name="diag q%d" % qb))
+            items.append(dict(ins=ins, deadline=len(mfma) + 8, ready=s_last + 4, p=None, name="max q%d" % qb,
+                              after=["diag q%d" % qb] if diag else []))
     if ref_upd:
         assert do_max
         for qb in range(QB):
@@ -310,10 +316,11 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
     rest = [it for it in sorted(queue, key=lambda x: x["order"]) if it["k"] < len(it["ins"])]
     if rest and s_last is not None and len(mfma) - 1 - s_last < 3:
         out += ["s_nop 7", "s_nop 7", "s_nop 7"]
-    for it in rest:
-        assert all(done(a_) for a_ in it.get("after", ())), ("dependency order", it["name"])
+    while rest:
+        it = next(x for x in rest if all(done(a_) for a_ in x.get("after", ())))
         while it["k"] < len(it["ins"]):
             emit(it)
+        rest.remove(it)
     return out
 
 
@@ -352,9 +359,10 @@ SREG = 88               # s[88:97] scratch SGPRs
 UFLAG = (92, 94)        # s[92:93] / s[94:95]: rows whose reference moved, per qb
 THR_S = 96              # the slack (8) in an SGPR
 NKVB_S = 97             # the next item's kv_end in bytes
+DIAG_S = ((98, 99), (90, 91))   # lane masks of the in-block diagonal mask, per qb
 MCP_V = (215, 216)      # reference + slack, per qb
 LOOP_CLOB_V = list(range(0, 219))   # S buffers, P, staging and the loop's own registers
-LOOP_CLOB_S = list(range(KRES, SREG + 10))
+LOOP_CLOB_S = list(range(KRES, SREG + 12))
 BUF_WORD3 = "0x20000"   # 32-bit data format, no stride: byte-addressed, range-checked raw buffer
 
 
@@ -403,6 +411,23 @@ def ref_update(qb, thr):
             "v_max_f32 v%d, 0xff7fffff, v%d" % (MREF_V[qb], t1),
             "v_cndmask_b32_e64 v%d, 1.0, v%d, %s" % (ALPHA_V[qb], t2, u),
             "v_add_f32 v%d, %s, %%[mc%d]" % (MCP_V[qb], thr, qb)]
+
+
+def diag_mask(buf, qb):
+    """-inf for the keys past each row's own on the wave's causal diagonal tile (tile and wave start at the
+    same key/row, a multiple of 64): block (qb 0, keys 32..63) is all masked, (qb 1, keys 0..31) all
+    visible, the two 32 x 32 diagonal blocks are compared against the row's limit (lim - tile start,
+    the lane half folded into lim)."""
+    t, m = TMPL + 3 * qb, "s[%d:%d]" % DIAG_S[qb]
+    o = ["v_subrev_u32 v%d, s%d, %%[lim%d]" % (t, SREG + 1, qb)]
+    jb = qb  # the diagonal block of this row block
+    for r in range(16):
+        off = jb * 32 + (r >> 2) * 8 + (r & 3)
+        sr = s_reg(buf, qb, jb, r)
+        o += ["v_cmp_gt_i32_e64 %s, %d, v%d" % (m, off, t), "v_cndmask_b32_e64 v%d, v%d, v%d, %s" % (sr, sr, NINF_V, m)]
+    if qb == 0:
+        o += ["v_mov_b32 v%d, v%d" % (s_reg(buf, 0, 1, r), NINF_V) for r in range(16)]
+    return o
 
 
 def max_chain(buf, qb, dst):
@@ -473,7 +498,8 @@ def first_tile(off):
     o = ["s_cmp_le_i32 %[ntw], 0", "s_cbranch_scc1 L_first_done_%="]
     o += gen(x_buf=1 - off, y_buf=off, kslot=off, vslot=off, do_s=True, do_pv=False, do_max=True,
              mx=("v%d" % MX_V[0], "v%d" % MX_V[1]))
-    o += ["s_mov_b32 s%d, 0" % SREG, "s_cmp_lt_i32 s%d, %%[tm]" % SREG, "s_cbranch_scc1 L_%s_ref_%%=" % tag]
+    o += ["s_mov_b32 s%d, 0" % SREG, "s_cmp_eq_u32 %[dg], 0", "s_cbranch_scc1 L_%s_mask_%%=" % tag,
+          "s_cmp_lt_i32 s%d, %%[tm]" % SREG, "s_cbranch_scc1 L_%s_ref_%%=" % tag, "L_%s_mask_%%=:" % tag]
     o += mask_tile("s%d" % SREG, off)
     o += ["L_%s_ref_%%=:" % tag] + full_ref() + ["s_branch L_first_done_%="]
     return o
@@ -520,7 +546,8 @@ def iteration(parity):
           "s_cselect_b32 s%d, %%[nvhl], s%d" % (VRES, VRES), "s_cselect_b32 s%d, %%[nvhh], s%d" % (VRES + 1, VRES + 1),
           "s_cselect_b32 s%d, s%d, s%d" % (VRES + 2, NKVB_S, VRES + 2)]
     o += ["s_cmp_ge_i32 %[t], %[ntw]", "s_cbranch_scc1 L_nocomp_%s_%%=" % tag,
-          "s_cmp_lt_i32 %s, %%[ntw]" % nxt, "s_cbranch_scc0 L_last_%s_%%=" % tag]
+          "s_cmp_lt_i32 %s, %%[ntw]" % nxt, "s_cbranch_scc0 L_last_%s_%%=" % tag,
+          "s_cmp_eq_u32 %s, %%[dg]" % nxt, "s_cbranch_scc1 L_diag_%s_%%=" % tag]
     o += gen(x_buf=P, y_buf=1 - P, kslot=1 - P, vslot=P, do_s=True, do_pv=True, do_max=True, mref=mref, mx=mx,
              dma_ins=groups, ref_upd=True)
     # tile t+1 masked: mask, row max, reference and rescale out of line; otherwise the block's check
@@ -533,6 +560,11 @@ def iteration(parity):
     ool += ["s_or_b64 vcc, %s" % uf, "s_cbranch_vccz L_after_%s_%%=" % tag] + rescale()
     ool += ["s_branch L_after_%s_%%=" % tag]
     ool += ["L_move_%s_%%=:" % tag] + full_ref() + rescale() + ["s_branch L_after_%s_%%=" % tag]
+    # the step whose new scores are the wave's causal diagonal tile: masked inside the block
+    ool += ["L_diag_%s_%%=:" % tag, "s_lshl_b32 s%d, %s, 6" % (SREG + 1, nxt)]
+    ool += gen(x_buf=P, y_buf=1 - P, kslot=1 - P, vslot=P, do_s=True, do_pv=True, do_max=True, mref=mref, mx=mx,
+               dma_ins=groups, ref_upd=True, diag=True)
+    ool += ["s_or_b64 vcc, %s" % uf, "s_cbranch_vccnz L_move_%s_%%=" % tag, "s_branch L_after_%s_%%=" % tag]
     ool += ["L_last_%s_%%=:" % tag]
     ool += gen(x_buf=P, y_buf=1 - P, kslot=1 - P, vslot=P, do_s=False, do_pv=True, do_max=False, mref=mref, mx=mx,
                dma_ins=groups)
@@ -547,7 +579,7 @@ def loop_body():
     o = ["v_mov_b32 v0, %s" % ONES_BF16X2, "v_mov_b32 v1, 0"]
     o += ["v_accvgpr_write_b32 a%d, v0" % (ONES_A + i) for i in range(4)]
     o += ["v_accvgpr_write_b32 a%d, v1" % (LSUM_A + i) for i in range(32)]
-    o += ["s_nop 3", "s_lshl_b32 s%d, %%[nkve], 8" % NKVB_S]
+    o += ["s_nop 3", "s_lshl_b32 s%d, %%[nkve], 8" % NKVB_S, "v_mov_b32 v%d, 0xff800000" % NINF_V]
     # S(0) with the item's parity
     o += ["s_cmp_eq_u32 %[off], 0", "s_cbranch_scc0 L_first1_%="] + first_tile(0)
     o += ["L_first1_%=:"] + first_tile(1) + ["L_first_done_%=:"]
@@ -578,7 +610,8 @@ def render_loop():
            ['[lim0] "v"(lim0)', '[lim1] "v"(lim1)', '[c] "s"(c_log2)', '[nt] "s"(ntiles)', '[ntw] "s"(ntiles_w)',
             '[tm] "s"(t_mask)', '[kve] "s"(kv_end)', '[khl] "s"(kh_lo)', '[khh] "s"(kh_hi)',
             '[vhl] "s"(vh_lo)', '[vhh] "s"(vh_hi)', '[lbw] "s"(lbw)', '[off] "s"(off)', '[nkhl] "s"(nkh_lo)',
-            '[nkhh] "s"(nkh_hi)', '[nvhl] "s"(nvh_lo)', '[nvhh] "s"(nvh_hi)', '[nkve] "s"(nkv_end)'])
+            '[nkhh] "s"(nkh_hi)', '[nvhl] "s"(nvh_lo)', '[nvhh] "s"(nvh_hi)', '[nkve] "s"(nkv_end)',
+            '[dg] "s"(t_diag)'])
     clob = (['"a%d"' % r for r in range(LSUM_A, ONES_A + 4)] + ['"v%d"' % r for r in LOOP_CLOB_V] +
             ['"s%d"' % r for r in LOOP_CLOB_S] +
             ['"vcc"', '"m0"', '"scc"', '"memory"'])
@@ -589,7 +622,8 @@ def render_loop():
         "// then the mask of S(t+1) where it needs one and the rescale of O where a reference moved (both",
         "// out of line: the common path runs straight through). Tiles use the slots and score buffers of",
         "// parity (t + off) % 2; the fetches continue past the item's last tile into the next item's first",
-        "// tiles (K(0), K(1), V(0) of the item given by nkh/nvh/nkv_end; nkv_end = 0: none).",
+        "// tiles (K(0), K(1), V(0) of the item given by nkh/nvh/nkv_end; nkv_end = 0: none). t_diag: the",
+        "// wave's causal diagonal tile, masked inside its step (else out of range; t_mask then covers it).",
         "// K and V are read through range-checked buffer descriptors: rows at or past kv_end are not read.",
         "__device__ __forceinline__ void qb2_loop(f32x16 (&o)[2][4], const bf16x8 (&q)[2][8], const uint32_t (&ka)[8],",
         "                                         const uint32_t (&va)[4][2], const uint32_t (&vo)[4],",
@@ -599,7 +633,7 @@ def render_loop():
         "                                         int32_t kv_end, uint32_t kh_lo, uint32_t kh_hi,",
         "                                         uint32_t vh_lo, uint32_t vh_hi, uint32_t lbw, int32_t off,",
         "                                         uint32_t nkh_lo, uint32_t nkh_hi, uint32_t nvh_lo, uint32_t nvh_hi,",
-        "                                         int32_t nkv_end)",
+        "                                         int32_t nkv_end, int32_t t_diag)",
         "{",
         "#pragma clang diagnostic push",
         "#pragma clang diagnostic ignored \"-Winline-asm\"",
