@@ -87,7 +87,7 @@ def test_loop_operands_outside_fixed_registers(device_asm):
     tmpl = [ln for ln in g.loop_body()]
     pats = [_template_regex(ln) for ln in tmpl]
     fixed_v = set(g.LOOP_CLOB_V)
-    fixed_s = set(range(g.SREG, g.SREG + 10))
+    fixed_s = set(g.LOOP_CLOB_S)
     blocks = re.findall(r";;#ASMSTART\n(.*?);;#ASMEND", device_asm, flags=re.S)
     loops = []
     for b in blocks:
@@ -145,15 +145,17 @@ def test_step_slots():
     g = _gen()
     for P in (0, 1):
         o, ool = g.iteration(P)
-        full = o[o.index("s_cbranch_scc0 L_last_p%d_%%=" % P):]
+        common = o[o.index("s_cbranch_scc0 L_slow_p%d_%%=" % P):]
+        general = ool[ool.index("L_slow_p%d_%%=:" % P):ool.index("L_mask_p%d_%%=:" % P)]
         last = ool[ool.index("L_last_p%d_%%=:" % P):ool.index("L_nocomp_p%d_%%=:" % P)]
         noc = ool[ool.index("L_nocomp_p%d_%%=:" % P):]
-        for part in (full, last, noc):
+        for part in (common, general, last, noc):
             kr, vr, kw, vw = _slots(part)
             assert kw == {P} and vw == {1 - P}   # K(t+2) -> K slot P, V(t+1) -> V slot 1-P
             assert not (kr & kw) and not (vr & vw)
-        kr, vr, _, _ = _slots(full)
-        assert kr == {1 - P} and vr == {P}       # S(t+1) reads K(t+1), P.V reads V(t)
+        for part in (common, general):
+            kr, vr, _, _ = _slots(part)
+            assert kr == {1 - P} and vr == {P}   # S(t+1) reads K(t+1), P.V reads V(t)
         kr, vr, _, _ = _slots(last)
         assert kr == set() and vr == {P}
     for off in (0, 1):
@@ -244,3 +246,175 @@ def test_diagonal_step_slots_and_mask():
                             else:
                                 masked = False
                             assert masked == (key > row), (buf, qb, jb, r, l32, hf)
+
+
+# --------------------------------------------------------------------------------------------------
+# Scalar control of the generated loop, executed on a model: the scalar instructions run as written
+# (vector, LDS and matrix instructions are skipped), each buffer load records the descriptor and LDS
+# address it is issued with, and each step records the path it took.
+
+M32 = (1 << 32) - 1
+
+
+def _s32(x):
+    x &= M32
+    return x - (1 << 32) if x >> 31 else x
+
+
+class _ScalarModel:
+    def __init__(self, body, ops, rng):
+        self.body, self.ops, self.rng = body, dict(ops), rng
+        self.labels = {ln[:-1]: i for i, ln in enumerate(body) if ln.endswith(":")}
+        self.s, self.scc, self.vcc, self.m0 = {}, None, None, None
+        self.steps, self.loads, self.paths = [], [], []
+
+    def val(self, x):
+        x = x.strip()
+        if x.startswith("%["):
+            return self.ops[x[2:-1]] & M32
+        if re.fullmatch(r"s\d+", x):
+            return self.s[int(x[1:])]
+        return int(x, 0) & M32
+
+    def put(self, d, v):
+        d = d.strip()
+        if d == "m0":
+            self.m0 = v & M32
+        elif d.startswith("%["):
+            self.ops[d[2:-1]] = _s32(v)
+        else:
+            self.s[int(d[1:])] = v & M32
+
+    def run(self, limit=200000):
+        pc, n = 0, 0
+        while pc < len(self.body):
+            n += 1
+            assert n < limit, "loop did not end"
+            ln = self.body[pc]
+            pc += 1
+            if ln.endswith(":"):
+                lab = ln[:-1]
+                if lab == "L_end_%=":
+                    return
+                m = re.match(r"L_(slow|mask|move|diag|last|nocomp)_p\d_%=$", lab)
+                if m and self.paths:
+                    self.paths[-1].add(m.group(1))
+                continue
+            op, _, args = ln.partition(" ")
+            a = [x.strip() for x in args.split(",")] if args else []
+            if not op.startswith(("s_", "buffer_load")):
+                continue
+            if op in ("s_waitcnt", "s_nop"):
+                continue
+            if op == "s_barrier":
+                self.steps.append(self.loads)
+                self.loads = []
+                self.paths.append(set())
+                continue
+            if op == "buffer_load_dwordx4":
+                r = int(re.match(r"s\[(\d+):\d+\]", a[1]).group(1))
+                base = self.s[r] | (self.s[r + 1] << 32)
+                self.loads.append((r, base, _s32(self.s[r + 2]), self.s[r + 3], self.m0))
+                continue
+            if op == "s_mov_b32":
+                self.put(a[0], self.val(a[1]))
+            elif op == "s_add_u32":
+                v = self.val(a[1]) + self.val(a[2])
+                self.put(a[0], v)
+                self.scc = v >> 32
+            elif op == "s_addc_u32":
+                assert self.scc is not None, ln
+                v = self.val(a[1]) + self.val(a[2]) + self.scc
+                self.put(a[0], v)
+                self.scc = v >> 32
+            elif op in ("s_add_i32", "s_sub_i32", "s_max_i32", "s_min_i32"):
+                x, y = _s32(self.val(a[1])), _s32(self.val(a[2]))
+                v = {"s_add_i32": x + y, "s_sub_i32": x - y, "s_max_i32": max(x, y), "s_min_i32": min(x, y)}[op]
+                assert -(1 << 31) <= v < (1 << 31), "signed overflow: %s" % ln
+                self.put(a[0], v)
+                self.scc = None
+            elif op == "s_lshl_b32":
+                self.put(a[0], self.val(a[1]) << self.val(a[2]))
+                self.scc = None
+            elif op.startswith("s_cmp_"):
+                cmp, ty = op[6:8], op[9:]
+                x, y = self.val(a[0]), self.val(a[1])
+                if ty == "i32":
+                    x, y = _s32(x), _s32(y)
+                self.scc = int({"eq": x == y, "lg": x != y, "ge": x >= y, "gt": x > y, "lt": x < y,
+                                "le": x <= y}[cmp])
+            elif op == "s_cselect_b32":
+                assert self.scc is not None, ln
+                self.put(a[0], self.val(a[1]) if self.scc else self.val(a[2]))
+            elif op == "s_or_b64":
+                assert a[0] == "vcc"
+                self.vcc = int(self.rng.random() < 0.3)   # a row's reference moves
+            elif op in ("s_cbranch_scc0", "s_cbranch_scc1"):
+                assert self.scc is not None, ln
+                if self.scc == int(op[-1]):
+                    pc = self.labels[a[0]]
+            elif op in ("s_cbranch_vccnz", "s_cbranch_vccz"):
+                assert self.vcc is not None, ln
+                if bool(self.vcc) == (op == "s_cbranch_vccnz"):
+                    pc = self.labels[a[0]]
+            elif op == "s_branch":
+                pc = self.labels[a[0]]
+            else:
+                pytest.fail("scalar instruction without a model: %s" % ln)
+        pytest.fail("fell off the end of the loop")
+
+
+def test_loop_scalar_control_model():
+    """For items of every tile count, wave extent, masked tile and diagonal tile: step t issues the four
+    loads of K(t+2) into K slot (t+off)%2 and of V(t+1) into the other V slot, each with the descriptor of
+    that tile of the stream (this item's tiles, then the next item's; its size the bytes below that
+    item's kv_end, never negative), and takes the path its tile calls for."""
+    g = _gen()
+    body = g.loop_body()
+    rng = np.random.default_rng(11)
+    TILE, BIG = 0x4000, 0x7FFFFFFF
+    for case in range(3000):
+        kve = int(rng.integers(0, 64 * 7))
+        nt = (kve + 63) // 64
+        ntw = int(rng.integers(0, nt + 1))
+        tm = int(rng.choice([BIG, int(rng.integers(0, nt + 2))]))
+        dg = int(rng.choice([BIG, int(rng.integers(0, nt + 2))]))
+        off = int(rng.integers(0, 2))
+        nkve = int(rng.choice([0, int(rng.integers(1, 64 * 5))]))
+        # bases with low words near a 4 GiB boundary, so that the carries into the high word happen
+        bases = {k: int(rng.integers(1, 1 << 16)) << 32 | (M32 + 1 - TILE * int(rng.integers(1, 6)))
+                 for k in ("kh", "vh", "nkh", "nvh")}
+        ops = {"t": 0, "nt": nt, "ntw": ntw, "tm": tm, "dg": dg, "off": off, "kve": kve, "nkve": nkve, "lbw": 0}
+        for k, b in bases.items():
+            ops[k + "l"], ops[k + "h"] = b & M32, b >> 32
+        m = _ScalarModel(body, ops, rng)
+        m.run()
+        assert m.ops["t"] == nt
+        assert not m.steps[0]                      # the barrier after S(0): nothing fetched before it
+        steps, paths = m.steps[1:], m.paths[:-1]
+        assert len(steps) == nt, (case, ops)
+
+        def desc(h, x):
+            if x < nt:
+                return bases[h] + x * TILE, max(0, kve * 256 - x * TILE)
+            return bases["n" + h] + (x - nt) * TILE, max(0, nkve * 256 - (x - nt) * TILE)
+
+        for t in range(nt):
+            P = (t + off) % 2
+            want = [(g.KRES,) + desc("kh", t + 2) + (0x20000, P * TB + j * 4096) for j in range(4)]
+            want += [(g.VRES,) + desc("vh", t + 1) + (0x20000, 2 * TB + (1 - P) * TB + j * 4096) for j in range(4)]
+            assert sorted(steps[t]) == sorted(want), (case, ops, t)
+            p = paths[t] - {"move"}
+            if t >= ntw:
+                exp = {"slow", "nocomp"}
+            elif t + 1 >= ntw:
+                exp = {"slow", "last"}
+            elif t + 1 == dg:
+                exp = {"slow", "diag"}
+            elif t + 1 >= tm:
+                exp = {"slow", "mask"}
+            elif t + 2 >= nt:
+                exp = {"slow"}
+            else:
+                exp = set() if t + 1 < min(ntw, dg, tm) else {"slow"}
+            assert p == exp, (case, ops, t, paths[t])

@@ -360,9 +360,10 @@ UFLAG = (92, 94)        # s[92:93] / s[94:95]: rows whose reference moved, per q
 THR_S = 96              # the slack (8) in an SGPR
 NKVB_S = 97             # the next item's kv_end in bytes
 DIAG_S = ((98, 99), (90, 91))   # lane masks of the in-block diagonal mask, per qb
+TF_S = 100              # the first step that is not a common step
 MCP_V = (215, 216)      # reference + slack, per qb
 LOOP_CLOB_V = list(range(0, 219))   # S buffers, P, staging and the loop's own registers
-LOOP_CLOB_S = list(range(KRES, SREG + 12))
+LOOP_CLOB_S = list(range(KRES, SREG + 13))
 BUF_WORD3 = "0x20000"   # 32-bit data format, no stride: byte-addressed, range-checked raw buffer
 
 
@@ -526,44 +527,58 @@ def next_res(res, tile_sreg, base_lo, base_hi):
             "s_mov_b32 s%d, %s" % (res + 3, BUF_WORD3)]
 
 
+def res_advance_fast(res):
+    """res_advance while the tile stays below the item's last (the size cannot reach 0)."""
+    return ["s_add_u32 s%d, s%d, 0x4000" % (res, res), "s_addc_u32 s%d, s%d, 0" % (res + 1, res + 1),
+            "s_sub_i32 s%d, s%d, 0x4000" % (res + 2, res + 2)]
+
+
 def iteration(parity):
     """Step of tile t (S(t) in buffer `parity`, its reference applied). Returns the straight-line part and
-    the out-of-line parts (masked tiles, rescale, the wave's last step, waves without work), which end by
-    branching back."""
+    the out-of-line parts, which end by branching back. The straight-line part is the common step (t below
+    the bound kept in s[TF_S]: the step computes S(t+1), needs no mask, and its fetches stay inside the item); every other
+    step -- past the item's last tiles, the wave's last step, the diagonal or masked tile, waves without
+    work -- takes the general path out of line, as do the rare reference moves."""
     P = parity
     tag = "p%d" % P
     nxt = "s%d" % SREG
     mref = ("v%d" % MREF_V[0], "v%d" % MREF_V[1])
     mx = ("v%d" % MX_V[0], "v%d" % MX_V[1])
     groups = step_dma(P)
-    # descriptors to K(t+2) and V(t+1) of the stream: past this item's last tile, the next item's first
-    # tiles (so that they are in their slots when this item ends)
-    o = res_advance(KRES) + res_advance(VRES)
-    o += ["s_add_i32 %s, %%[t], 2" % nxt, "s_cmp_eq_i32 %s, %%[nt]" % nxt,
-          "s_cselect_b32 s%d, %%[nkhl], s%d" % (KRES, KRES), "s_cselect_b32 s%d, %%[nkhh], s%d" % (KRES + 1, KRES + 1),
-          "s_cselect_b32 s%d, s%d, s%d" % (KRES + 2, NKVB_S, KRES + 2)]
-    o += ["s_add_i32 %s, %%[t], 1" % nxt, "s_cmp_eq_i32 %s, %%[nt]" % nxt,
-          "s_cselect_b32 s%d, %%[nvhl], s%d" % (VRES, VRES), "s_cselect_b32 s%d, %%[nvhh], s%d" % (VRES + 1, VRES + 1),
-          "s_cselect_b32 s%d, s%d, s%d" % (VRES + 2, NKVB_S, VRES + 2)]
-    o += ["s_cmp_ge_i32 %[t], %[ntw]", "s_cbranch_scc1 L_nocomp_%s_%%=" % tag,
-          "s_cmp_lt_i32 %s, %%[ntw]" % nxt, "s_cbranch_scc0 L_last_%s_%%=" % tag,
-          "s_cmp_eq_u32 %s, %%[dg]" % nxt, "s_cbranch_scc1 L_diag_%s_%%=" % tag]
-    o += gen(x_buf=P, y_buf=1 - P, kslot=1 - P, vslot=P, do_s=True, do_pv=True, do_max=True, mref=mref, mx=mx,
-             dma_ins=groups, ref_upd=True)
-    # tile t+1 masked: mask, row max, reference and rescale out of line; otherwise the block's check
-    # says whether any row's reference must move (rare: then the update and the rescale, out of line)
     uf = "s[%d:%d], s[%d:%d]" % (UFLAG[0], UFLAG[0] + 1, UFLAG[1], UFLAG[1] + 1)
-    o += ["s_cmp_ge_i32 %s, %%[tm]" % nxt, "s_cbranch_scc1 L_mask_%s_%%=" % tag,
-          "s_or_b64 vcc, %s" % uf, "s_cbranch_vccnz L_move_%s_%%=" % tag,
+    full = lambda **kw: gen(x_buf=P, y_buf=1 - P, kslot=1 - P, vslot=P, do_s=True, do_pv=True, do_max=True,
+                            mref=mref, mx=mx, dma_ins=groups, ref_upd=True, **kw)
+    # common step
+    o = ["s_cmp_lt_i32 %%[t], s%d" % TF_S, "s_cbranch_scc0 L_slow_%s_%%=" % tag]
+    o += res_advance_fast(KRES) + res_advance_fast(VRES)
+    o += full()
+    o += ["s_or_b64 vcc, %s" % uf, "s_cbranch_vccnz L_move_%s_%%=" % tag,
           "L_after_%s_%%=:" % tag, "s_waitcnt vmcnt(0)", "s_barrier"]
-    ool = ["L_mask_%s_%%=:" % tag] + mask_tile(nxt, 1 - P) + full_ref()
+    # general step: descriptors to K(t+2) and V(t+1) of the stream (past this item's last tile, the next
+    # item's first tiles, so that they are in their slots when this item ends)
+    ool = ["L_slow_%s_%%=:" % tag, "s_cmp_ge_i32 %[t], %[nt]", "s_cbranch_scc1 L_end_%="]
+    ool += res_advance(KRES) + res_advance(VRES)
+    ool += ["s_add_i32 %s, %%[t], 2" % nxt, "s_cmp_eq_i32 %s, %%[nt]" % nxt,
+            "s_cselect_b32 s%d, %%[nkhl], s%d" % (KRES, KRES), "s_cselect_b32 s%d, %%[nkhh], s%d" % (KRES + 1, KRES + 1),
+            "s_cselect_b32 s%d, s%d, s%d" % (KRES + 2, NKVB_S, KRES + 2)]
+    ool += ["s_add_i32 %s, %%[t], 1" % nxt, "s_cmp_eq_i32 %s, %%[nt]" % nxt,
+            "s_cselect_b32 s%d, %%[nvhl], s%d" % (VRES, VRES), "s_cselect_b32 s%d, %%[nvhh], s%d" % (VRES + 1, VRES + 1),
+            "s_cselect_b32 s%d, s%d, s%d" % (VRES + 2, NKVB_S, VRES + 2)]
+    ool += ["s_cmp_ge_i32 %[t], %[ntw]", "s_cbranch_scc1 L_nocomp_%s_%%=" % tag,
+            "s_cmp_lt_i32 %s, %%[ntw]" % nxt, "s_cbranch_scc0 L_last_%s_%%=" % tag,
+            "s_cmp_eq_u32 %s, %%[dg]" % nxt, "s_cbranch_scc1 L_diag_%s_%%=" % tag]
+    ool += full()
+    # tile t+1 masked: mask, row max, reference and rescale out of line; otherwise the block's check
+    # says whether any row's reference must move (rare: then the update and the rescale)
+    ool += ["s_cmp_ge_i32 %s, %%[tm]" % nxt, "s_cbranch_scc1 L_mask_%s_%%=" % tag,
+            "s_or_b64 vcc, %s" % uf, "s_cbranch_vccnz L_move_%s_%%=" % tag, "s_branch L_after_%s_%%=" % tag]
+    ool += ["L_mask_%s_%%=:" % tag] + mask_tile(nxt, 1 - P) + full_ref()
     ool += ["s_or_b64 vcc, %s" % uf, "s_cbranch_vccz L_after_%s_%%=" % tag] + rescale()
     ool += ["s_branch L_after_%s_%%=" % tag]
     ool += ["L_move_%s_%%=:" % tag] + full_ref() + rescale() + ["s_branch L_after_%s_%%=" % tag]
     # the step whose new scores are the wave's causal diagonal tile: masked inside the block
     ool += ["L_diag_%s_%%=:" % tag, "s_lshl_b32 s%d, %s, 6" % (SREG + 1, nxt)]
-    ool += gen(x_buf=P, y_buf=1 - P, kslot=1 - P, vslot=P, do_s=True, do_pv=True, do_max=True, mref=mref, mx=mx,
-               dma_ins=groups, ref_upd=True, diag=True)
+    ool += full(diag=True)
     ool += ["s_or_b64 vcc, %s" % uf, "s_cbranch_vccnz L_move_%s_%%=" % tag, "s_branch L_after_%s_%%=" % tag]
     ool += ["L_last_%s_%%=:" % tag]
     ool += gen(x_buf=P, y_buf=1 - P, kslot=1 - P, vslot=P, do_s=False, do_pv=True, do_max=False, mref=mref, mx=mx,
@@ -588,13 +603,16 @@ def loop_body():
     # descriptors one tile behind: each step first moves them to K(t+2) and V(t+1) of the stream
     o += stream_res(KRES, 1, "%[khl]", "%[khh]", "%[nkhl]", "%[nkhh]")
     o += stream_res(VRES, 0, "%[vhl]", "%[vhh]", "%[nvhl]", "%[nvhh]")
+    # steps t < tf are common steps: tf = min(nt - 2, ntw - 1, t_diag - 1, t_mask - 1)
+    o += ["s_add_i32 s%d, %%[nt], -2" % TF_S]
+    for x in ("%[ntw]", "%[dg]", "%[tm]"):
+        o += ["s_add_i32 s%d, %s, -1" % (SREG + 1, x), "s_min_i32 s%d, s%d, s%d" % (TF_S, TF_S, SREG + 1)]
     i0, ool0 = iteration(0)
     i1, ool1 = iteration(1)
     o += ["s_cmp_eq_u32 %[off], 0", "s_cbranch_scc0 L_mid_%="]
-    o += ["L_top_%=:", "s_cmp_ge_i32 %[t], %[nt]", "s_cbranch_scc1 L_end_%="]
-    o += i0
-    o += ["s_add_i32 %[t], %[t], 1", "L_mid_%=:", "s_cmp_ge_i32 %[t], %[nt]", "s_cbranch_scc1 L_end_%="]
-    o += i1
+    # (tf <= nt - 2: a common step never ends the loop; the general one checks t against nt first)
+    o += ["L_top_%=:"] + i0
+    o += ["s_add_i32 %[t], %[t], 1", "L_mid_%=:"] + i1
     o += ["s_add_i32 %[t], %[t], 1", "s_branch L_top_%="]
     o += ool0 + ool1
     o += ["L_end_%=:"] + list(O_WAIT)
