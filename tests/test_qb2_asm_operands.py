@@ -418,3 +418,57 @@ def test_loop_scalar_control_model():
             else:
                 exp = set() if t + 1 < min(ntw, dg, tm) else {"slow"}
             assert p == exp, (case, ops, t, paths[t])
+
+
+def _ones_pattern_model(lane):
+    """Executes the generated instructions that build the row-sum A operand, for one lane."""
+    g = _gen()
+    v, vcc = {}, None
+    for t in g.ones_pattern():
+        op, _, args = t.partition(" ")
+        a = [x.strip() for x in args.split(",")]
+        val = lambda x: v[int(x[1:])] if x.startswith("v") else int(x, 0) & 0xFFFFFFFF
+        if op == "v_mbcnt_lo_u32_b32":
+            v[int(a[0][1:])] = min(lane, 32) + val(a[2])
+        elif op == "v_mbcnt_hi_u32_b32":
+            v[int(a[0][1:])] = max(lane - 32, 0) + val(a[2])
+        elif op == "v_lshrrev_b32":
+            v[int(a[0][1:])] = val(a[2]) >> val(a[1])
+        elif op == "v_xor_b32":
+            v[int(a[0][1:])] = val(a[1]) ^ val(a[2])
+        elif op == "v_and_b32":
+            v[int(a[0][1:])] = val(a[1]) & val(a[2])
+        elif op == "v_cmp_eq_u32":
+            vcc = val(a[1]) == val(a[2])
+        elif op == "v_mov_b32":
+            v[int(a[0][1:])] = val(a[1])
+        elif op == "v_cndmask_b32":
+            v[int(a[0][1:])] = val(a[2]) if vcc else val(a[1])
+        else:
+            pytest.fail("no model for %s" % t)
+    return v[0]
+
+
+def test_row_sum_product_gives_each_lane_its_query_sum():
+    """The row sums come from a 16 x 16 x 32 product whose B operand is the P^T register of the 32 x 32 x 16
+    P.V product (lane l: query l % 32, keys 8 (l / 32) .. + 7 of 16) and whose A operand is the generated
+    0/1 pattern. With the 16 x 16 layouts (A: lane l gives row l % 16, B: column l % 16, both at k-group
+    l / 16; D: lane l holds column l % 16, rows 4 (l / 16) .. + 3), every D value a lane holds must be the
+    sum of its own query's 16 weights, whatever order the k-group's eight elements take."""
+    rng = np.random.default_rng(3)
+    P = rng.random((32, 16))                      # P[query][key]
+    Bl = np.array([P[l % 32, 8 * (l // 32):8 * (l // 32) + 8] for l in range(64)])   # lane -> 8 values
+    ones = {0x3F803F80: 1.0, 0: 0.0}
+    Al = np.array([[ones[_ones_pattern_model(l)]] * 8 for l in range(64)])
+    for perm in (np.arange(8), rng.permutation(8)):
+        A = np.zeros((16, 32))
+        B = np.zeros((32, 16))
+        for l in range(64):
+            for j in range(8):
+                k = 8 * (l // 16) + perm[j]
+                A[l % 16, k] = Al[l, j]
+                B[k, l % 16] = Bl[l, j]
+        Dm = A @ B
+        for l in range(64):
+            for i in range(4):
+                np.testing.assert_allclose(Dm[4 * (l // 16) + i, l % 16], P[l % 32].sum(), rtol=1e-12)

@@ -281,9 +281,10 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float l_
 // rows below Nq, so rows past Nq are dropped by the range check (no per-row branch). The area's 16-byte
 // chunks are XOR-swizzled by row so that both the 8-byte writes and the 16-byte reads spread over the
 // banks.
+// pk[db] holds the block's 16 values of the lane, already divided by the row sum, as bf16 pairs.
 template <int OLAYOUT>
-__device__ __forceinline__ void store_rows_bf16_staged(const f32x16 (&acc)[4], float l_tot, int row0, int bh, int H,
-                                                       int Nq, int b, int lane, uint8_t *stage, void *__restrict__ Out)
+__device__ __forceinline__ void store_rows_bf16_staged(const u32x8 (&pk)[4], int row0, int bh, int H, int Nq, int b,
+                                                       int lane, uint8_t *stage, void *__restrict__ Out)
 {
     constexpr int D = 128;
     // computed here rather than kept from the kernel's start: the lane-dependent addresses would otherwise
@@ -291,14 +292,12 @@ __device__ __forceinline__ void store_rows_bf16_staged(const f32x16 (&acc)[4], f
     // to spare
     asm volatile("" : "+v"(lane));
     const int l32 = lane & 31, hf = lane >> 5;
-    const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
             const int c = db * 4 + rg;
-            const u32x2 v = {pack_bf16x2(acc[db][rg * 4 + 0] * inv, acc[db][rg * 4 + 1] * inv),
-                             pack_bf16x2(acc[db][rg * 4 + 2] * inv, acc[db][rg * 4 + 3] * inv)};
+            const u32x2 v = {pk[db][rg * 2], pk[db][rg * 2 + 1]};
             *(u32x2 *)(stage + l32 * 256 + ((c ^ (l32 & 15)) << 4) + hf * 8) = v;
         }
     // the wave's LDS operations complete in order: keep the compiler from moving the reads up
@@ -745,8 +744,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     first_tiles(cur, 0);
     bool fetched = true;  // this item's first tiles were fetched outside a tile loop: wait for them
     for (;;) {
-        if (fetched) wait_vmcnt0();
-        __syncthreads();
+        // Every fetch into the Q and K/V slots is cooperative. When the tile loop streamed this item's first
+        // tiles, its last step waited for all of them (and for the Q rows issued before it) and ended with a
+        // barrier; otherwise wait here, then barrier, so that every wave sees the whole tiles.
+        if (fetched) {
+            wait_vmcnt0();
+            __syncthreads();
+        }
         // O = 0 and Q^T (this wave's rows, from its Q slot) in the AGPRs the tile loop names
         u32x4 qv[QB][KS];
 #pragma unroll
@@ -793,19 +797,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // (off + ntiles) % 2 and ended with a barrier after they (and the next Q rows) had arrived. With
         // fewer than two tiles it did not (K(0) of the next item would have been due before this item's
         // first step): fetch them here.
+        // the row sums come from an MFMA over all 64 lanes: each lane holds its row's whole sum. bf16 output:
+        // O / l packed straight from the O registers, before anything else needs registers
+        u32x8 pk[QB][DB];
+        if constexpr (!OUT_F32) {
+            float inv[QB];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) inv[qb] = l_run[qb] > 0.f ? __builtin_amdgcn_rcpf(l_run[qb]) : 0.f;
+            qb2_out_bf16(acc, inv[0], inv[1], pk);
+        }
         const int off_next = (off + cur.ntiles) & 1;
         fetched = cur.ntiles < 2;
         if (nxt.valid && fetched) first_tiles(nxt, off_next);
-        mfma_fence_a8(acc);
-        // the row sums come from an MFMA over all 64 lanes: each lane holds its row's whole sum
+        if constexpr (OUT_F32) mfma_fence_a8(acc);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            if constexpr (OUT_F32)
+            if constexpr (OUT_F32) {
                 store_rows<D, OUT_F32, OLAYOUT, false>(acc[qb], l_run[qb], cur.q0 + wave * RW + qb * 32 + l32, cur.bh,
                                                        H, Nq, cur.b, hf, Out);
-            else
-                store_rows_bf16_staged<OLAYOUT>(acc[qb], l_run[qb], cur.q0 + wave * RW + qb * 32, cur.bh, H, Nq, cur.b,
-                                                lane, smem + STAGE + wave * 8192, Out);
+            } else {
+                store_rows_bf16_staged<OLAYOUT>(pk[qb], cur.q0 + wave * RW + qb * 32, cur.bh, H, Nq, cur.b, lane,
+                                                smem + STAGE + wave * 8192, Out);
+            }
         }
         if (!nxt.valid) break;
         cur = nxt;

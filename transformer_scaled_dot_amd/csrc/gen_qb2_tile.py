@@ -53,7 +53,7 @@ P0, KST, VST, TMP, MXT = 128, 160, 176, 192, 200
 MXT_Q = ((200, 201), (217, 218))   # row-max temporaries of qb 0 and qb 1
 CLOB_END = 204         # v[128:203] are the block's scratch registers
 O_A, Q_A = 0, 128
-LSUM_A, ONES_A = 192, 224   # a[192:223]: row-sum accumulators (qb 0, 1); a[224:227]: all-ones operand
+LSUM_A, ONES_A = 192, 224   # a[192:199]: row-sum accumulators (qb 0, 1); a[224:227]: their 0/1 operand
 NKS = NVS = 4          # staging slots
 LOOK = 5               # MFMAs between an operand's read and its first MFMA
 SLOT_CYC = 26          # issue cycles between two MFMAs of a wave that keep the MFMA pipe busy (measured best)
@@ -113,11 +113,15 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
                              text="v_mfma_f32_32x32x16_bf16 %s, %s, %s, %s" % (
                                  ar(acc, 16), vr(VST + 4 * (vop % NVS), 4), pop, ar(acc, 16))))
             if db == 0:
-                # row sums of the rounded weights: (all-ones) x P^T adds, in every row of a 32 x 32
-                # accumulator, the column sums of P, i.e. each query's sum over these 16 keys
-                ls = ar(LSUM_A + 16 * qb, 16)
+                # row sums of the rounded weights, from the same P^T operand read as the 32 x 16 B operand
+                # of a 16 x 16 x 32 product (half the matrix-pipe time of a 32 x 32 x 16 one): lane l
+                # holds query l % 32 and 8 of its 16 keys, i.e. column l % 16 and k-group l / 16 of B.
+                # The 0/1 A operand (ones_pattern) adds the k-groups of parity p = (row / 4) % 2 into
+                # each row, so output row m, column n is the sum of query n + 16 p over the 16 keys,
+                # and the four rows lane l holds (4 (l / 16) .. + 3) all carry its own query's sum.
+                ls = ar(LSUM_A + 4 * qb, 4)
                 mfma.append(dict(op=None, kind="SUM", qb=qb, c=c,
-                                 text="v_mfma_f32_32x32x16_bf16 %s, %s, %s, %s" % (ls, ar(ONES_A, 4), pop, ls)))
+                                 text="v_mfma_f32_16x16x32_bf16 %s, %s, %s, %s" % (ls, ar(ONES_A, 4), pop, ls)))
     first_use, last_use = {}, {}
     for m, f in enumerate(mfma):
         if f["op"] is None:
@@ -221,7 +225,8 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
     # cycles of each slot (between two MFMA issues) left for the VALU work once the fixed
     # instructions (operand reads, DMA, waits) are in
     n_reads = [sum(len(reads[op]) for op in read_at.get(m + 1, [])) for m in range(len(mfma))]
-    avail = [SLOT_CYC - ISSUE_CYC * (n_reads[m] + 1 + (2 if m + 1 in dma_at else 0)) for m in range(len(mfma))]
+    avail = [(SLOT_CYC if mfma[m]["kind"] != "SUM" else SLOT_CYC // 2) -
+             ISSUE_CYC * (n_reads[m] + 1 + (2 if m + 1 in dma_at else 0)) for m in range(len(mfma))]
 
     def emit_reads(slot):
         for op in read_at.get(slot, []):
@@ -480,7 +485,7 @@ def rescale():
     at the end)."""
     o = list(O_WAIT)
     for qb in range(QB):
-        a = LSUM_A + 16 * qb
+        a = LSUM_A + 4 * qb
         o += ["v_accvgpr_read_b32 v%d, a%d" % (P0, a), "v_mul_f32 v%d, v%d, v%d" % (P0, P0, ALPHA_V[qb]),
               "v_accvgpr_write_b32 a%d, v%d" % (a, P0)]
     for qb in range(QB):
@@ -590,10 +595,18 @@ def iteration(parity):
     return o, ool
 
 
+def ones_pattern():
+    """v0 = the A operand of the row-sum products for this lane: eight bf16 ones where the lane's k-group
+    parity ((l / 16) % 2) equals its row's parity (((l % 16) / 4) % 2), zeros elsewhere."""
+    return ["v_mbcnt_lo_u32_b32 v0, -1, 0", "v_mbcnt_hi_u32_b32 v0, -1, v0", "v_lshrrev_b32 v1, 4, v0",
+            "v_lshrrev_b32 v0, 2, v0", "v_xor_b32 v0, v0, v1", "v_and_b32 v0, 1, v0", "v_cmp_eq_u32 vcc, 0, v0",
+            "v_mov_b32 v1, %s" % ONES_BF16X2, "v_cndmask_b32 v0, 0, v1, vcc"]
+
+
 def loop_body():
-    o = ["v_mov_b32 v0, %s" % ONES_BF16X2, "v_mov_b32 v1, 0"]
+    o = ones_pattern()
     o += ["v_accvgpr_write_b32 a%d, v0" % (ONES_A + i) for i in range(4)]
-    o += ["v_accvgpr_write_b32 a%d, v1" % (LSUM_A + i) for i in range(32)]
+    o += ["v_accvgpr_write_b32 a%d, 0" % (LSUM_A + i) for i in range(4 * QB)]
     o += ["s_nop 3", "s_lshl_b32 s%d, %%[nkve], 8" % NKVB_S, "v_mov_b32 v%d, 0xff800000" % NINF_V]
     # S(0) with the item's parity
     o += ["s_cmp_eq_u32 %[off], 0", "s_cbranch_scc0 L_first1_%="] + first_tile(0)
@@ -616,7 +629,7 @@ def loop_body():
     o += ["s_add_i32 %[t], %[t], 1", "s_branch L_top_%="]
     o += ool0 + ool1
     o += ["L_end_%=:"] + list(O_WAIT)
-    o += ["v_accvgpr_read_b32 %%[l%d], a%d" % (qb, LSUM_A + 16 * qb) for qb in range(QB)]
+    o += ["v_accvgpr_read_b32 %%[l%d], a%d" % (qb, LSUM_A + 4 * qb) for qb in range(QB)]
     return o
 
 
@@ -673,8 +686,10 @@ def render():
         "// generator for the schedule and the register plan).",
         "",
     ]
-    # O = 0 and Q^T into its AGPRs
-    zero = ["v_accvgpr_write_b32 a%d, 0" % r for r in range(O_A, O_A + 128)]
+    # O = 0 (each 32 x 32 block by one MFMA of zero operands, 16 AGPRs per instruction) and Q^T into its AGPRs
+    zero = ["v_mov_b32 v%d, 0" % r for r in range(ZERO_V, ZERO_V + 4)] + ["s_nop 4"]
+    zero += ["v_mfma_f32_32x32x16_bf16 a[%d:%d], v[%d:%d], v[%d:%d], 0" % (b, b + 15, ZERO_V, ZERO_V + 3, ZERO_V,
+                                                                           ZERO_V + 3) for b in range(O_A, O_A + 128, 16)]
     qmov = []
     for qb in range(QB):
         for ks in range(KS):
@@ -684,7 +699,7 @@ def render():
         "__device__ __forceinline__ void qb2_init(f32x16 (&o)[2][4], bf16x8 (&q)[2][8], const u32x4 (&qv)[2][8])",
         "{",
         "    asm volatile(",
-        "\n".join('        "%s\\n"' % t for t in zero + qmov + ["s_nop 7"]),
+        "\n".join('        "%s\\n"' % t for t in zero + qmov + list(O_WAIT)),
         "        : " + ",\n          ".join(
             ['"={a[%d:%d]}"(o[%d][%d])' % (O_A + (qb * DB + db) * 16, O_A + (qb * DB + db) * 16 + 15, qb, db)
              for qb in range(QB) for db in range(DB)] +
@@ -692,12 +707,49 @@ def render():
              for qb in range(QB) for ks in range(KS)]),
         "        : " + ",\n          ".join(
             ['[qv%d_%d] "v"(qv[%d][%d][%d])' % (qb * KS + ks, w, qb, ks, w)
-             for qb in range(QB) for ks in range(KS) for w in range(4)]) + ");",
+             for qb in range(QB) for ks in range(KS) for w in range(4)]),
+        "        : " + ", ".join('"v%d"' % r for r in range(ZERO_V, ZERO_V + 4)) + ");",
         "}",
         "",
     ]
     lines += render_loop()
+    lines += [""] + render_out_bf16()
     return "\n".join(lines)
+
+
+ZERO_V = 0         # v[0:3] = 0: operands of the MFMAs that clear O
+OUT_TMP_V = 0      # v[0:31]: two sets of 16 products
+OUT_PK_V = 32      # v[32:95]: the packed rows, 8 registers per 32 x 32 block of O
+OUT_INV_V = 96     # v96, v97: 1/l of each query block
+
+
+def render_out_bf16():
+    """O / l as bf16 pairs straight from the O AGPRs: per 32 x 32 block of O (qb, db), the 16 values a lane
+    holds are read, scaled by the reciprocal of their row's sum and packed two by two (element 2j in the
+    low half of pair j)."""
+    ins = ["v_mov_b32 v%d, %%[inv0]" % OUT_INV_V, "v_mov_b32 v%d, %%[inv1]" % (OUT_INV_V + 1)]
+    for k in range(QB * DB):
+        qb, b, t, pk = k // DB, O_A + 16 * k, OUT_TMP_V + 16 * (k % 2), OUT_PK_V + 8 * k
+        ins += ["v_accvgpr_read_b32 v%d, a%d" % (t + r, b + r) for r in range(16)]
+        ins += ["v_mul_f32 v%d, v%d, v%d" % (t + r, t + r, OUT_INV_V + qb) for r in range(16)]
+        ins += ["v_cvt_pk_bf16_f32 v%d, v%d, v%d" % (pk + j, t + 2 * j, t + 2 * j + 1) for j in range(8)]
+    outs = ['"={v[%d:%d]}"(pk[%d][%d])' % (OUT_PK_V + 8 * k, OUT_PK_V + 8 * k + 7, k // DB, k % DB)
+            for k in range(QB * DB)]
+    inps = ['"{a[%d:%d]}"(o[%d][%d])' % (O_A + 16 * k, O_A + 16 * k + 15, k // DB, k % DB) for k in range(QB * DB)]
+    inps += ['[inv0] "v"(inv0)', '[inv1] "v"(inv1)']
+    clob = ['"v%d"' % r for r in list(range(OUT_TMP_V, OUT_TMP_V + 32)) + [OUT_INV_V, OUT_INV_V + 1]]
+    return [
+        "__device__ __forceinline__ void qb2_out_bf16(const f32x16 (&o)[2][4], float inv0, float inv1,",
+        "                                             u32x8 (&pk)[2][4])",
+        "{",
+        "    asm volatile(",
+        "\n".join('        "%s\\n"' % t for t in ins),
+        "        : " + ",\n          ".join(outs),
+        "        : " + ",\n          ".join(inps),
+        "        : " + ", ".join(clob) + ");",
+        "}",
+        "",
+    ]
 
 
 if __name__ == "__main__":
