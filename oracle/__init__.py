@@ -8,11 +8,18 @@ shares no code with the HIP library (it is plain C, float64, in
 Every function takes float64 numpy arrays holding the exact input values
 (bfloat16 or float32 inputs widened to float64) and returns float64.
 
+Masks: none, causal (key j hidden when j > i), padding (keys j >= valid_len[b])
+and causal_padding (hidden by either rule). K/V may have fewer heads than Q:
+query head h reads K/V head h // (H // H_kv) ("Self-Attention 机制", section
+MHA -> MQA -> GQA -> MLA). The per-row log-sum-exp of the visible scaled
+scores can be returned alongside the output.
+
 Pins (tests/test_oracle_pins.py) tie it to what the pages fix: the
 3-token hand-worked example of "04. Self-Attention: Transformer 的核心计算"
 (section 六) and of "Transformer 详解" (section 手算一遍), row sums of 1,
 exact zeros at masked positions, permutation equivariance, closed forms, and
-torch's float64 CPU attention routine on tiny shapes.
+torch's float64 CPU routines (attention, with grouped K/V heads, and
+logsumexp) on tiny shapes.
 """
 from __future__ import annotations
 
@@ -26,7 +33,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attn_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-MASK = {"none": 0, "causal": 1, "padding": 2}
+MASK = {"none": 0, "causal": 1, "padding": 2, "causal_padding": 3}
+_USES_VALID_LENS = ("padding", "causal_padding")
 
 _libs = {}
 
@@ -57,11 +65,11 @@ def _load(path: str | None = None):
         lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
-        lib.oracle_attn.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_int, P, ctypes.c_double, P, P,
-                                    ctypes.c_int]
+        lib.oracle_attn.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, I64, ctypes.c_int, P, ctypes.c_double, P,
+                                    P, P, ctypes.c_int]
         lib.oracle_attn.restype = ctypes.c_int
-        lib.oracle_attn_rows.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_int, P, ctypes.c_double,
-                                         P, I64, P, ctypes.c_int]
+        lib.oracle_attn_rows.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, I64, ctypes.c_int, P,
+                                         ctypes.c_double, P, I64, P, P, ctypes.c_int]
         lib.oracle_attn_rows.restype = ctypes.c_int
         lib.oracle_mha.argtypes = [P, P, P, I64, I64, I64, I64, P, ctypes.c_int]
         lib.oracle_mha.restype = ctypes.c_int
@@ -85,65 +93,80 @@ def _ptr(a) -> ctypes.c_void_p:
 
 
 def _check_attn(q, k, v, mask, valid_lens):
+    """q [B,H,Nq,d]; k, v [B,H_kv,Nk,d(v)] with H_kv dividing H (query head h reads K/V head
+    h // (H // H_kv))."""
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
+    if mask not in MASK:
+        raise ValueError("unknown mask %r" % (mask,))
     B, H, Nq, d = q.shape
-    if k.shape[:2] != (B, H) or v.shape[:3] != k.shape[:3] or k.shape[3] != d:
+    Hkv = k.shape[1]
+    if k.shape[0] != B or Hkv < 1 or H % Hkv or v.shape[:3] != k.shape[:3] or k.shape[3] != d:
         raise ValueError("shape mismatch")
     vl = None
-    if mask == "padding":
+    if mask in _USES_VALID_LENS:
         if valid_lens is None:
             raise ValueError("padding mask needs valid_lens")
         vl = np.ascontiguousarray(valid_lens, dtype=np.int32)
         if vl.shape != (B,):
             raise ValueError("valid_lens must be [B]")
-    return B, H, Nq, k.shape[2], d, v.shape[3], vl
+    return B, H, k.shape[1], Nq, k.shape[2], d, v.shape[3], vl
 
 
-def attention(q, k, v, mask="none", valid_lens=None, scale=None, return_weights=False, threads=0, lib=None):
+def attention(q, k, v, mask="none", valid_lens=None, scale=None, return_weights=False, threads=0, lib=None,
+              return_lse=False):
     """O = softmax(q k^T * scale + M) v per (batch, head); optionally the
-    weights A [B,H,Nq,Nk]. ``scale`` defaults to 1/sqrt(d)."""
+    weights A [B,H,Nq,Nk] and the per-row log-sum-exp of the visible scaled
+    scores [B,H,Nq] (returned in that order after O). ``scale`` defaults to
+    1/sqrt(d). k and v may have fewer heads than q (grouped K/V heads)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
-    B, H, Nq, Nk, d, dv, vl = _check_attn(q, k, v, mask, valid_lens)
+    B, H, Hkv, Nq, Nk, d, dv, vl = _check_attn(q, k, v, mask, valid_lens)
     scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
     O = np.zeros((B, H, Nq, dv), dtype=np.float64)
     A = np.zeros((B, H, Nq, Nk), dtype=np.float64) if return_weights else None
-    rc = _load(lib).oracle_attn(_ptr(q), _ptr(k), _ptr(v), B, H, Nq, Nk, d, dv, MASK[mask], _ptr(vl), scale, _ptr(O),
-                             _ptr(A), int(threads))
+    L = np.zeros((B, H, Nq), dtype=np.float64) if return_lse else None
+    rc = _load(lib).oracle_attn(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, Nq, Nk, d, dv, MASK[mask], _ptr(vl), scale,
+                             _ptr(O), _ptr(A), _ptr(L), int(threads))
     if rc < 0:
         raise ValueError("oracle_attn rejected its arguments")
-    return (O, A) if return_weights else O
+    out = [O] + ([A] if return_weights else []) + ([L] if return_lse else [])
+    return tuple(out) if len(out) > 1 else O
 
 
-def attention_rows(q, k, v, rows, mask="none", valid_lens=None, scale=None, threads=0, lib=None):
-    """Output rows for flat indices r = (b*H + h)*Nq + i; returns [len(rows), dv]."""
+def attention_rows(q, k, v, rows, mask="none", valid_lens=None, scale=None, threads=0, lib=None, return_lse=False):
+    """Output rows for flat indices r = (b*H + h)*Nq + i; returns [len(rows), dv]
+    (and the rows' log-sum-exp [len(rows)] with ``return_lse``)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
-    B, H, Nq, Nk, d, dv, vl = _check_attn(q, k, v, mask, valid_lens)
+    B, H, Hkv, Nq, Nk, d, dv, vl = _check_attn(q, k, v, mask, valid_lens)
     scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     O = np.zeros((rows.size, dv), dtype=np.float64)
-    rc = _load(lib).oracle_attn_rows(_ptr(q), _ptr(k), _ptr(v), B, H, Nq, Nk, d, dv, MASK[mask], _ptr(vl), scale,
-                                  _ptr(rows), rows.size, _ptr(O), int(threads))
+    L = np.zeros(rows.size, dtype=np.float64) if return_lse else None
+    rc = _load(lib).oracle_attn_rows(_ptr(q), _ptr(k), _ptr(v), B, H, Hkv, Nq, Nk, d, dv, MASK[mask], _ptr(vl),
+                                  scale, _ptr(rows), rows.size, _ptr(O), _ptr(L), int(threads))
     if rc < 0:
         raise ValueError("oracle_attn_rows rejected its arguments")
-    return O
+    return (O, L) if return_lse else O
 
 
-def attention_rows_per_head(q, k, v, rows, mask="none", valid_lens=None, scale=None, threads=0):
+def attention_rows_per_head(q, k, v, rows, mask="none", valid_lens=None, scale=None, threads=0, return_lse=False):
     """Like :func:`attention_rows`, but ``q, k, v`` may be any arrays that
     index as [b, h] -> [N, d] (e.g. float32 views of huge inputs): only the
     heads that the rows touch are widened to float64, one head at a time."""
     rows = np.asarray(rows, dtype=np.int64)
     H, Nq = q.shape[1], q.shape[2]
+    grp = H // k.shape[1]
     out = np.zeros((rows.size, v.shape[3]), dtype=np.float64)
+    lse = np.zeros(rows.size, dtype=np.float64)
     bh_of = rows // Nq
     for bh in np.unique(bh_of):
         b, h = divmod(int(bh), H)
         sel = np.nonzero(bh_of == bh)[0]
-        vl = None if mask != "padding" else np.asarray([valid_lens[b]], dtype=np.int32)
-        out[sel] = attention_rows(_f64(q[b, h])[None, None], _f64(k[b, h])[None, None], _f64(v[b, h])[None, None],
-                                  rows[sel] % Nq, mask=mask, valid_lens=vl, scale=scale, threads=threads)
-    return out
+        vl = None if mask not in _USES_VALID_LENS else np.asarray([valid_lens[b]], dtype=np.int32)
+        out[sel], lse[sel] = attention_rows(_f64(q[b, h])[None, None], _f64(k[b, h // grp])[None, None],
+                                            _f64(v[b, h // grp])[None, None], rows[sel] % Nq, mask=mask,
+                                            valid_lens=vl, scale=scale, threads=threads, return_lse=True)
+    return (out, lse) if return_lse else out
 
 
 def mha(x, w_qkv, w_o, h, threads=0, lib=None):

@@ -29,6 +29,16 @@
  *    query row; padded query rows are computed normally.
  *  - causal hides keys j > i (diagonal visible); it is defined here for any
  *    N_q, N_k with that same index rule.
+ *  - causal and padding together (the decoder's masked self-attention over a
+ *    padded batch) hide a key when either rule hides it: visible iff j <= i
+ *    and j < valid_len.
+ *  - grouped K/V heads (page 5, section MHA -> MQA -> GQA -> MLA: every h/g
+ *    query heads share one K/V head): query head h reads K/V head
+ *    h / (H / H_kv), i.e. consecutive query heads form a group. H_kv = H is
+ *    the plain multi-head case, H_kv = 1 the single shared K/V head.
+ *  - the optional per-row log-sum-exp is ln sum_j exp(s_j) over the visible
+ *    scaled scores s_j (-inf for a row without a visible key): the log of
+ *    the softmax denominator, so that weight_j = exp(s_j - lse).
  *  - a row with no visible key has no softmax; its output is 0 (convention,
  *    not fixed by the pages: parity unpinned for that case).
  *
@@ -42,14 +52,20 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_MASK_NONE = 0, ORACLE_MASK_CAUSAL = 1, ORACLE_MASK_PADDING = 2 };
+enum { ORACLE_MASK_NONE = 0, ORACLE_MASK_CAUSAL = 1, ORACLE_MASK_PADDING = 2, ORACLE_MASK_CAUSAL_PADDING = 3 };
 
 /* Is key j visible to query i?  (page 1 section 七; page 2 section 掩码) */
 static int visible(int mask_kind, int64_t i, int64_t j, int64_t valid_len)
 {
     if (mask_kind == ORACLE_MASK_CAUSAL) return j <= i;
     if (mask_kind == ORACLE_MASK_PADDING) return j < valid_len;
+    if (mask_kind == ORACLE_MASK_CAUSAL_PADDING) return j <= i && j < valid_len;
     return 1;
+}
+
+static int uses_valid_lens(int mask_kind)
+{
+    return mask_kind == ORACLE_MASK_PADDING || mask_kind == ORACLE_MASK_CAUSAL_PADDING;
 }
 
 /*
@@ -60,10 +76,11 @@ static int visible(int mask_kind, int64_t i, int64_t j, int64_t valid_len)
  *   s    : [Nk]       caller's scratch for the row of scaled scores
  *   o    : [dv]       output row
  *   a    : [Nk]       optional attention-weight row (may be NULL)
+ *   lse  : [1]        optional log-sum-exp of the row's visible scaled scores (may be NULL)
  */
 static void attention_row(const double *q, const double *Kbh, const double *Vbh, int64_t Nk, int64_t d,
                           int64_t dv, int mask_kind, int64_t i, int64_t valid_len, double scale, double *s,
-                          double *o, double *a)
+                          double *o, double *a, double *lse)
 {
     /* stage 1 + 2: s_j = (q . k_j) * scale for every visible key */
     int any = 0;
@@ -76,8 +93,9 @@ static void attention_row(const double *q, const double *Kbh, const double *Vbh,
     }
 
     for (int64_t c = 0; c < dv; ++c) o[c] = 0.0;
-    if (!any) { /* no visible key: output 0, weights 0 */
+    if (!any) { /* no visible key: output 0, weights 0, log of an empty sum */
         if (a) for (int64_t j = 0; j < Nk; ++j) a[j] = 0.0;
+        if (lse) *lse = -INFINITY;
         return;
     }
 
@@ -94,6 +112,8 @@ static void attention_row(const double *q, const double *Kbh, const double *Vbh,
             s[j] = 0.0; /* e^{-inf} = 0 exactly */
         }
     }
+    /* ln sum_j exp(s_j) = m + ln sum_j exp(s_j - m) */
+    if (lse) *lse = m + log(z);
     for (int64_t j = 0; j < Nk; ++j) s[j] = s[j] / z;
 
     /* stage 4: weighted sum of the value rows */
@@ -118,18 +138,34 @@ static int set_threads(int nthreads)
 /* Threads an oracle call uses (OpenMP's current maximum). */
 int oracle_max_threads(void) { return set_threads(0); }
 
-/*
- * Full attention. Q [B,H,Nq,d], K [B,H,Nk,d], V [B,H,Nk,dv] row-major
- * float64; O [B,H,Nq,dv]; A optional [B,H,Nq,Nk]. valid_lens [B] is read
- * only for the padding mask. Returns the number of threads used, or -1 on
- * bad arguments.
- */
-int oracle_attn(const double *Q, const double *K, const double *V, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
-                int64_t d, int64_t dv, int mask_kind, const int32_t *valid_lens, double scale, double *O, double *A,
-                int nthreads)
+/* Offset of the K (or V) head that query head bh = b*H + h reads: head
+ * h / (H / Hkv) of batch b, heads of n elements each. */
+static int64_t kv_head_offset(int64_t bh, int64_t H, int64_t Hkv, int64_t n)
 {
-    if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || d <= 0 || dv <= 0) return -1;
-    if (mask_kind == ORACLE_MASK_PADDING && !valid_lens) return -1;
+    int64_t b = bh / H, h = bh % H;
+    return (b * Hkv + h / (H / Hkv)) * n;
+}
+
+static int bad_args(int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, int64_t dv,
+                    int mask_kind, const int32_t *valid_lens)
+{
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || d <= 0 || dv <= 0) return 1;
+    if (Hkv <= 0 || (H > 0 && H % Hkv != 0)) return 1;
+    if (mask_kind < 0 || mask_kind > ORACLE_MASK_CAUSAL_PADDING) return 1;
+    return uses_valid_lens(mask_kind) && !valid_lens;
+}
+
+/*
+ * Full attention. Q [B,H,Nq,d], K [B,Hkv,Nk,d], V [B,Hkv,Nk,dv] row-major
+ * float64; O [B,H,Nq,dv]; A optional [B,H,Nq,Nk]; LSE optional [B,H,Nq].
+ * valid_lens [B] is read only for the masks that use it. Returns the number
+ * of threads used, or -1 on bad arguments.
+ */
+int oracle_attn(const double *Q, const double *K, const double *V, int64_t B, int64_t H, int64_t Hkv, int64_t Nq,
+                int64_t Nk, int64_t d, int64_t dv, int mask_kind, const int32_t *valid_lens, double scale, double *O,
+                double *A, double *LSE, int nthreads)
+{
+    if (bad_args(B, H, Hkv, Nq, Nk, d, dv, mask_kind, valid_lens)) return -1;
     int used = set_threads(nthreads);
     int64_t rows = B * H * Nq;
 #pragma omp parallel
@@ -140,9 +176,10 @@ int oracle_attn(const double *Q, const double *K, const double *V, int64_t B, in
             int64_t i = r % Nq;
             int64_t bh = r / Nq;
             int64_t b = bh / H;
-            int64_t L = (mask_kind == ORACLE_MASK_PADDING) ? valid_lens[b] : Nk;
-            attention_row(Q + r * d, K + bh * Nk * d, V + bh * Nk * dv, Nk, d, dv, mask_kind, i, L, scale, s,
-                          O + r * dv, A ? A + r * Nk : NULL);
+            int64_t L = uses_valid_lens(mask_kind) ? valid_lens[b] : Nk;
+            attention_row(Q + r * d, K + kv_head_offset(bh, H, Hkv, Nk * d), V + kv_head_offset(bh, H, Hkv, Nk * dv),
+                          Nk, d, dv, mask_kind, i, L, scale, s, O + r * dv, A ? A + r * Nk : NULL,
+                          LSE ? LSE + r : NULL);
         }
         free(s);
     }
@@ -151,15 +188,15 @@ int oracle_attn(const double *Q, const double *K, const double *V, int64_t B, in
 
 /*
  * A subset of rows of the same attention: rows[] holds flat indices
- * r = (b*H + h)*Nq + i; O_rows is [nrows, dv]. Rows are independent, so
- * each one is exact, not an approximation of the full computation.
+ * r = (b*H + h)*Nq + i; O_rows is [nrows, dv], LSE_rows optional [nrows].
+ * Rows are independent, so each one is exact, not an approximation of the
+ * full computation.
  */
-int oracle_attn_rows(const double *Q, const double *K, const double *V, int64_t B, int64_t H, int64_t Nq,
-                     int64_t Nk, int64_t d, int64_t dv, int mask_kind, const int32_t *valid_lens, double scale,
-                     const int64_t *rows, int64_t nrows, double *O_rows, int nthreads)
+int oracle_attn_rows(const double *Q, const double *K, const double *V, int64_t B, int64_t H, int64_t Hkv,
+                     int64_t Nq, int64_t Nk, int64_t d, int64_t dv, int mask_kind, const int32_t *valid_lens,
+                     double scale, const int64_t *rows, int64_t nrows, double *O_rows, double *LSE_rows, int nthreads)
 {
-    if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || d <= 0 || dv <= 0) return -1;
-    if (mask_kind == ORACLE_MASK_PADDING && !valid_lens) return -1;
+    if (bad_args(B, H, Hkv, Nq, Nk, d, dv, mask_kind, valid_lens)) return -1;
     int used = set_threads(nthreads);
     int bad = 0;
 #pragma omp parallel
@@ -172,9 +209,10 @@ int oracle_attn_rows(const double *Q, const double *K, const double *V, int64_t 
             int64_t i = r % Nq;
             int64_t bh = r / Nq;
             int64_t b = bh / H;
-            int64_t L = (mask_kind == ORACLE_MASK_PADDING) ? valid_lens[b] : Nk;
-            attention_row(Q + r * d, K + bh * Nk * d, V + bh * Nk * dv, Nk, d, dv, mask_kind, i, L, scale, s,
-                          O_rows + t * dv, NULL);
+            int64_t L = uses_valid_lens(mask_kind) ? valid_lens[b] : Nk;
+            attention_row(Q + r * d, K + kv_head_offset(bh, H, Hkv, Nk * d), V + kv_head_offset(bh, H, Hkv, Nk * dv),
+                          Nk, d, dv, mask_kind, i, L, scale, s, O_rows + t * dv, NULL,
+                          LSE_rows ? LSE_rows + t : NULL);
         }
         free(s);
     }
@@ -239,7 +277,8 @@ int oracle_mha(const double *X, const double *Wqkv, const double *Wo, int64_t B,
 
     /* per-head attention, no mask, scale 1/sqrt(d_k) */
     double *Oh = P; /* P is no longer needed; reuse its first B*h*N*dk doubles */
-    oracle_attn(Qh, Kh, Vh, B, h, N, N, dk, dk, ORACLE_MASK_NONE, NULL, 1.0 / sqrt((double)dk), Oh, NULL, nthreads);
+    oracle_attn(Qh, Kh, Vh, B, h, h, N, N, dk, dk, ORACLE_MASK_NONE, NULL, 1.0 / sqrt((double)dk), Oh, NULL, NULL,
+                nthreads);
 
     /* concat: [B,h,N,dk] -> [B,N,h*dk] */
     for (int64_t b = 0; b < B; ++b)

@@ -118,7 +118,12 @@ def _visible(mask, Nq, Nk, L=None):
         return j <= i
     if mask == "padding":
         return np.broadcast_to(j < L, (Nq, Nk))
+    if mask == "causal_padding":
+        return (j <= i) & (j < L)
     return np.ones((Nq, Nk), dtype=bool)
+
+
+_ALL_MASKS = ("none", "causal", "padding", "causal_padding")
 
 
 def pin_rows_sum_to_one(lib):
@@ -126,7 +131,7 @@ def pin_rows_sum_to_one(lib):
     A.sum(-1); p4 section 手算一遍)."""
     for t, (B, H, Nq, Nk, d) in enumerate(_SHAPES):
         q, k, v = _inputs(100 + 10 * t, B, H, Nq, Nk, d)
-        for mask in ("none", "causal", "padding"):
+        for mask in _ALL_MASKS:
             vl = np.arange(B, dtype=np.int32) % Nk + 1
             _, A = oracle.attention(q, k, v, mask=mask, valid_lens=vl, return_weights=True, lib=lib)
             np.testing.assert_allclose(A.sum(-1), 1.0, atol=1e-13)
@@ -138,7 +143,7 @@ def pin_masked_weights_exactly_zero(lib):
     for t, (B, H, Nq, Nk, d) in enumerate(_SHAPES):
         q, k, v = _inputs(200 + 10 * t, B, H, Nq, Nk, d)
         vl = (np.arange(B, dtype=np.int32) * 3) % Nk + 1
-        for mask in ("causal", "padding"):
+        for mask in ("causal", "padding", "causal_padding"):
             _, A = oracle.attention(q, k, v, mask=mask, valid_lens=vl, return_weights=True, lib=lib)
             for b in range(B):
                 vis = _visible(mask, Nq, Nk, vl[b])
@@ -218,6 +223,11 @@ def pin_zero_scale_gives_mean_of_visible_values(lib):
     for b in range(B):
         np.testing.assert_allclose(Op[b], np.broadcast_to(v[b, :, : vl[b]].mean(axis=1, keepdims=True),
                                                           Op[b].shape), atol=1e-14)
+    # both: row i averages V[0 .. min(i, L-1)] (the prefix means stop growing at the padding boundary)
+    Ocp = oracle.attention(q, k, v, mask="causal_padding", valid_lens=vl, scale=0.0, lib=lib)
+    for b in range(B):
+        for i in range(N):
+            np.testing.assert_allclose(Ocp[b, :, i], pref[b, :, min(i, vl[b] - 1)], atol=1e-14)
 
 
 def pin_single_key_returns_its_value(lib):
@@ -261,8 +271,8 @@ def pin_matches_torch_float64_attention(lib):
     for t, (B, H, Nq, Nk, d) in enumerate(_SHAPES + [(2, 2, 33, 17, 16)]):
         q, k, v = _inputs(1100 + 10 * t, B, H, Nq, Nk, d, std=1.5)
         vl = (np.arange(B, dtype=np.int32) * 5) % Nk + 1
-        for mask in ("none", "causal", "padding"):
-            if mask == "causal" and Nq > Nk:
+        for mask in _ALL_MASKS:
+            if mask.startswith("causal") and Nq > Nk:
                 continue
             keep = np.stack([_visible(mask, Nq, Nk, vl[b]) for b in range(B)])[:, None]
             ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
@@ -314,10 +324,108 @@ def pin_row_subset_equals_full(lib):
     q, k, v = _inputs(1400, B, H, Nq, Nk, d)
     vl = np.asarray([5, 11], dtype=np.int32)
     rows = np.asarray([0, 1, 10, 17, 33, 44, 65], dtype=np.int64)
-    for mask in ("none", "causal", "padding"):
-        O = oracle.attention(q, k, v, mask=mask, valid_lens=vl, lib=lib).reshape(-1, d)
-        Or = oracle.attention_rows(q, k, v, rows, mask=mask, valid_lens=vl, lib=lib)
-        assert np.array_equal(Or, O[rows])
+    for mask in _ALL_MASKS:
+        O, L = oracle.attention(q, k, v, mask=mask, valid_lens=vl, lib=lib, return_lse=True)
+        Or, Lr = oracle.attention_rows(q, k, v, rows, mask=mask, valid_lens=vl, lib=lib, return_lse=True)
+        assert np.array_equal(Or, O.reshape(-1, d)[rows]) and np.array_equal(Lr, L.reshape(-1)[rows])
+    # grouped K/V heads: the same on three query heads sharing one K/V head
+    kg, vg = k[:, :1], v[:, :1]
+    O = oracle.attention(q, kg, vg, mask="causal", lib=lib).reshape(-1, d)
+    Or = oracle.attention_rows(q, kg, vg, rows, mask="causal", lib=lib)
+    assert np.array_equal(Or, O[rows])
+
+
+# --- log-sum-exp of the scores ----------------------------------------------
+
+def pin_lse_hand_example_page1(lib):
+    """p1 section 六 prints e^{s_3j} and their sum for row 3: the log-sum-exp is the log of that sum;
+    rows 1 and 2 share their sum of raw exponentials."""
+    g, X = _hand()
+    p = g["page1"]
+    _, L = oracle.attention(X[None, None], X[None, None], X[None, None], return_lse=True, lib=lib)
+    L = L[0, 0]
+    np.testing.assert_allclose(np.exp(L[2]), p["row3_exp_sum"], atol=3 * p["tol"])
+    np.testing.assert_allclose(np.exp(L[2]), np.sum(p["row3_exp"]), atol=3 * p["tol"])
+    assert L[0] == L[1]
+
+
+def pin_lse_zero_scale_counts_visible_keys(lib):
+    """scale = 0: every visible score is 0, so the log-sum-exp is ln(number of visible keys) and -inf for a
+    row with none."""
+    B, H, N, d = 2, 2, 6, 3
+    q, k, v = _inputs(1500, B, H, N, N, d)
+    vl = np.asarray([0, 4], dtype=np.int32)
+    for mask in _ALL_MASKS:
+        _, L = oracle.attention(q, k, v, mask=mask, valid_lens=vl, scale=0.0, return_lse=True, lib=lib)
+        for b in range(B):
+            n = _visible(mask, N, N, vl[b]).sum(axis=1)
+            with np.errstate(divide="ignore"):
+                want = np.log(n.astype(np.float64))
+            np.testing.assert_array_equal(np.isneginf(L[b]), np.broadcast_to(n == 0, L[b].shape))
+            np.testing.assert_allclose(L[b][:, n > 0], np.broadcast_to(want[n > 0], (H, int((n > 0).sum()))),
+                                       atol=1e-14)
+
+
+def pin_lse_matches_torch_logsumexp(lib):
+    """torch.logsumexp over the masked scaled scores (float64 CPU), and the weights are exp(s - lse)."""
+    import torch
+
+    for t, (B, H, Nq, Nk, d) in enumerate(_SHAPES):
+        q, k, v = _inputs(1600 + 10 * t, B, H, Nq, Nk, d, std=2.0)
+        vl = (np.arange(B, dtype=np.int32) * 3) % Nk + 1
+        scale = 0.7
+        s = torch.from_numpy(np.einsum("bhid,bhjd->bhij", q, k) * scale)
+        for mask in _ALL_MASKS:
+            if mask.startswith("causal") and Nq > Nk:
+                continue
+            keep = torch.from_numpy(np.stack([_visible(mask, Nq, Nk, vl[b]) for b in range(B)])[:, None])
+            ref = torch.logsumexp(s.masked_fill(~keep, float("-inf")), dim=-1).numpy()
+            _, A, L = oracle.attention(q, k, v, mask=mask, valid_lens=vl, scale=scale, return_weights=True,
+                                       return_lse=True, lib=lib)
+            np.testing.assert_allclose(L, ref, atol=1e-12, rtol=0)
+            w = np.where(keep.numpy(), np.exp(s.numpy() - L[..., None]), 0.0)
+            np.testing.assert_allclose(A, w, atol=1e-12, rtol=0)
+
+
+# --- grouped K/V heads --------------------------------------------------------
+
+def pin_grouped_kv_heads_match_torch(lib):
+    """p5 section MHA -> MQA -> GQA -> MLA: every H / H_kv query heads share one K/V head. torch's float64
+    attention with enable_gqa (consecutive query heads per K/V head) computes the same."""
+    import torch
+    import torch.nn.functional as F
+
+    for t, (B, H, Hkv, Nq, Nk, d) in enumerate([(2, 4, 2, 5, 7, 4), (1, 6, 3, 9, 9, 8), (2, 3, 1, 4, 6, 5)]):
+        q = _randn(1700 + 10 * t, (B, H, Nq, d))
+        k = _randn(1701 + 10 * t, (B, Hkv, Nk, d))
+        v = _randn(1702 + 10 * t, (B, Hkv, Nk, d))
+        vl = (np.arange(B, dtype=np.int32) * 2) % Nk + 1
+        for mask in _ALL_MASKS:
+            if mask.startswith("causal") and Nq > Nk:
+                continue
+            keep = torch.from_numpy(np.stack([_visible(mask, Nq, Nk, vl[b]) for b in range(B)])[:, None])
+            ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                                                 attn_mask=keep, enable_gqa=True).numpy()
+            O = oracle.attention(q, k, v, mask=mask, valid_lens=vl, lib=lib)
+            np.testing.assert_allclose(O, ref, atol=1e-12, rtol=0)
+
+
+def pin_group_sizes_degenerate(lib):
+    """H_kv = H is the plain multi-head case; H_kv = 1 (one K/V head for all query heads) gives, for each
+    query head, what a single-head call on that head's queries gives."""
+    B, H, N, d = 2, 4, 6, 5
+    q, k, v = _inputs(1800, B, H, N, N, d)
+    O = oracle.attention(q, k, v, mask="causal", lib=lib)
+    assert np.array_equal(O, oracle.attention(q, k, v, mask="causal", lib=lib))
+    Om = oracle.attention(q, k[:, :1], v[:, :1], mask="causal", lib=lib)
+    for h in range(H):
+        Oh = oracle.attention(q[:, h:h + 1], k[:, :1], v[:, :1], mask="causal", lib=lib)
+        assert np.array_equal(Om[:, h:h + 1], Oh)
+    # and each group of two query heads reads its own K/V head
+    Og = oracle.attention(q, k[:, :2], v[:, :2], mask="causal", lib=lib)
+    for h in range(H):
+        Oh = oracle.attention(q[:, h:h + 1], k[:, h // 2:h // 2 + 1], v[:, h // 2:h // 2 + 1], mask="causal", lib=lib)
+        assert np.array_equal(Og[:, h:h + 1], Oh)
 
 
 PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

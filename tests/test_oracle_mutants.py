@@ -27,6 +27,12 @@ MUTANTS = {
     "mha_heads_interleaved_on_concat": ("C[(b * N + t) * d_model + hh * dk + c]",
                                         "C[(b * N + t) * d_model + c * h + hh]"),
     "mha_scale_by_d_model": ("1.0 / sqrt((double)dk)", "1.0 / sqrt((double)d_model)"),
+    "causal_padding_either_rule": ("return j <= i && j < valid_len;", "return j <= i || j < valid_len;"),
+    "causal_padding_ignores_lengths": ("return mask_kind == ORACLE_MASK_PADDING || mask_kind == ORACLE_MASK_CAUSAL_PADDING;",
+                                       "return mask_kind == ORACLE_MASK_PADDING;"),
+    "kv_heads_interleaved": ("return (b * Hkv + h / (H / Hkv)) * n;", "return (b * Hkv + h % Hkv) * n;"),
+    "lse_without_max": ("if (lse) *lse = m + log(z);", "if (lse) *lse = log(z);"),
+    "lse_base_two": ("if (lse) *lse = m + log(z);", "if (lse) *lse = m + log2(z);"),
 }
 
 
