@@ -12,6 +12,14 @@
  *             "attention-mechanism" page, section 掩码 (padded positions are
  *             set to -inf as well).
  *
+ *   attn_fwd_ex  attn_fwd with grouped K/V heads and the per-row
+ *             log-sum-exp. "Self-Attention 机制", section
+ *             MHA -> MQA -> GQA -> MLA: every heads/kv_heads query heads
+ *             share one K/V head (kv_heads = heads: plain multi-head,
+ *             kv_heads = 1: one shared K/V head). The log-sum-exp is the log
+ *             of the softmax denominator of each row, from which any weight
+ *             of the pages' attention matrix A is exp(s_ij - lse_i).
+ *
  *   mha_fwd   Y = Concat(head_1..head_h) W_O, head_i = Attention of the
  *             i-th d_k-wide column block of X W_Q, X W_K, X W_V, with the
  *             three projections fused into one GEMM against
@@ -60,7 +68,9 @@ typedef enum {
 typedef enum {
     ATTN_MASK_NONE = 0,
     ATTN_MASK_CAUSAL = 1,  /* key j hidden from query i when j > i (diagonal visible) */
-    ATTN_MASK_PADDING = 2  /* key j hidden from every query of batch b when j >= valid_lens[b] */
+    ATTN_MASK_PADDING = 2, /* key j hidden from every query of batch b when j >= valid_lens[b] */
+    ATTN_MASK_CAUSAL_PADDING = 3 /* hidden when either rule hides it: visible iff j <= i and j < valid_lens[b]
+                                    (the decoder's masked self-attention over a padded batch) */
 } attn_mask_kind_t;
 
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
@@ -71,8 +81,9 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
  *   Q          [batch, heads, seq_q, head_dim]   in_dtype
  *   K, V       [batch, heads, seq_k, head_dim]   in_dtype   (d_v = d_k = head_dim)
  *   mask_kind  attn_mask_kind_t
- *   valid_lens device int32 [batch]; read only for ATTN_MASK_PADDING (may be
- *              NULL otherwise). Values are clamped to [0, seq_k] on the device.
+ *   valid_lens device int32 [batch]; read only for ATTN_MASK_PADDING and
+ *              ATTN_MASK_CAUSAL_PADDING (may be NULL otherwise). Values are
+ *              clamped to [0, seq_k] on the device.
  *   scale      multiplies Q K^T; finite and >= 0 (the pages use 1/sqrt(d_k)).
  *   O          [batch, heads, seq_q, head_dim]   out_dtype
  *
@@ -84,12 +95,36 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
  *   in_dtype BF16: head_dim 64 or 128; out_dtype BF16 or F32; products in
  *                  bf16 with float32 accumulation, softmax in float32.
  *   in_dtype F32:  head_dim 16, 32, 64 or 128; out_dtype F32; all float32.
- *   ATTN_MASK_CAUSAL requires seq_q == seq_k.
+ *   ATTN_MASK_CAUSAL and ATTN_MASK_CAUSAL_PADDING require seq_q == seq_k.
  *   batch*heads, seq_q, seq_k < 2^31; seq_q, seq_k may be 0 (nothing to do).
  */
 TSD_API attn_status_t attn_fwd(const void *Q, const void *K, const void *V, int32_t mask_kind, const int32_t *valid_lens,
                        float scale, void *O, int32_t batch, int32_t heads, int32_t seq_q, int32_t seq_k,
                        int32_t head_dim, int32_t in_dtype, int32_t out_dtype, void *stream);
+
+/*
+ * attn_fwd_ex -- attn_fwd with grouped K/V heads and an optional per-row
+ * log-sum-exp output. attn_fwd(...) is attn_fwd_ex(..., lse = NULL, ...,
+ * kv_heads = heads, ...).
+ *
+ *   K, V       [batch, kv_heads, seq_k, head_dim]; query head h of batch b
+ *              reads K/V head h / (heads / kv_heads) of batch b, i.e.
+ *              consecutive query heads form a group.
+ *   kv_heads   >= 1 and divides heads (else ATTN_EINVAL).
+ *   lse        NULL, or device float32 [batch, heads, seq_q], 4-byte
+ *              aligned, not overlapping any other tensor: receives
+ *              ln sum_j exp(scale * q_i . k_j) over the visible keys j of
+ *              each query row (natural log; -inf for a row without a
+ *              visible key). With bf16 inputs the sum is that of the
+ *              bf16-rounded weights the kernel applies to V.
+ *
+ * Every other argument, the errors and the supported set are those of
+ * attn_fwd.
+ */
+TSD_API attn_status_t attn_fwd_ex(const void *Q, const void *K, const void *V, int32_t mask_kind,
+                          const int32_t *valid_lens, float scale, void *O, float *lse, int32_t batch,
+                          int32_t heads, int32_t kv_heads, int32_t seq_q, int32_t seq_k, int32_t head_dim,
+                          int32_t in_dtype, int32_t out_dtype, void *stream);
 
 /*
  * mha_workspace_bytes -- device workspace mha_fwd needs for these sizes:

@@ -79,6 +79,35 @@ def test_attn_fwd_rejects(lib, kw, status):
     assert lib.attn_last_error() != b""
 
 
+def call_attn_ex(lib, Q=FAKE, K=FAKE + (1 << 28), V=FAKE + (2 << 28), mask=0, vl=0, scale=0.125, O=FAKE + (3 << 28),
+                 lse=0, B=1, H=4, Hkv=2, Nq=8, Nk=8, d=64, ind=BF16, outd=BF16):
+    P = ctypes.c_void_p
+    return lib.attn_fwd_ex(P(Q), P(K), P(V), mask, P(vl), ctypes.c_float(scale), P(O), P(lse), B, H, Hkv, Nq, Nk, d,
+                           ind, outd, P(0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hkv=0), EINVAL),
+    (dict(Hkv=3), EINVAL),                        # does not divide H = 4
+    (dict(Hkv=-2), EINVAL),
+    (dict(mask=3, vl=0), EINVAL),                 # causal and padding need valid_lens
+    (dict(mask=4), EINVAL),
+    (dict(lse=FAKE + (4 << 28) + 2), EINVAL),     # lse misaligned
+    (dict(lse=FAKE + (3 << 28)), EINVAL),         # lse overlaps O
+    (dict(lse=FAKE), EINVAL),                     # lse overlaps Q
+    (dict(mask=3, vl=FAKE + (5 << 28), Nq=8, Nk=9), EUNSUP),
+    (dict(d=32), EUNSUP),
+])
+def test_attn_fwd_ex_rejects(lib, kw, status):
+    assert call_attn_ex(lib, **kw) == status
+    assert lib.attn_last_error() != b""
+
+
+def test_attn_fwd_ex_empty_is_ok_without_gpu(lib):
+    assert call_attn_ex(lib, Nq=0, lse=FAKE + (4 << 28)) == 0
+    assert call_attn_ex(lib, B=0, mask=3, vl=FAKE + (5 << 28)) == 0
+
+
 def test_attn_fwd_empty_is_ok_without_gpu(lib):
     # no output element: nothing is launched
     assert call_attn(lib, Nq=0) == 0

@@ -6,8 +6,9 @@ supplies device memory and the current HIP stream, every arithmetic step runs
 in the library's HIP kernels. There is no CPU fallback: if the library is not
 built, or a tensor is not on the GPU, the call raises.
 
-    attn_fwd(q, k, v, mask="none"|"causal"|"padding", valid_lens=None,
-             scale=None, out_dtype=None) -> o
+    attn_fwd(q, k, v, mask="none"|"causal"|"padding"|"causal_padding",
+             valid_lens=None, scale=None, out_dtype=None, return_lse=False)
+             -> o  (or (o, lse))
     mha_fwd(x, w_qkv, w_o, h) -> y
 """
 from __future__ import annotations
@@ -22,10 +23,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtsd_attn.so")
 
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
-MASK_KINDS = {"none": 0, "causal": 1, "padding": 2}
+MASK_KINDS = {"none": 0, "causal": 1, "padding": 2, "causal_padding": 3}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
-EXPORTS = ("attn_fwd", "mha_workspace_bytes", "mha_fwd", "attn_clock_probe", "attn_status_string",
+EXPORTS = ("attn_fwd", "attn_fwd_ex", "mha_workspace_bytes", "mha_fwd", "attn_clock_probe", "attn_status_string",
            "attn_last_error")
 
 _lib = None
@@ -51,6 +52,8 @@ def load_library():
     P, I32 = ctypes.c_void_p, ctypes.c_int32
     lib.attn_fwd.argtypes = [P, P, P, I32, P, ctypes.c_float, P, I32, I32, I32, I32, I32, I32, I32, P]
     lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd_ex.argtypes = [P, P, P, I32, P, ctypes.c_float, P, P, I32, I32, I32, I32, I32, I32, I32, I32, P]
+    lib.attn_fwd_ex.restype = ctypes.c_int
     lib.mha_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.mha_workspace_bytes.restype = ctypes.c_size_t
     lib.mha_fwd.argtypes = [P, P, P, I32, P, I32, I32, I32, I32, P, ctypes.c_size_t, P]
@@ -100,31 +103,39 @@ def _stream_ptr(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def attn_fwd(q, k, v, mask: str = "none", valid_lens=None, scale: float | None = None, out_dtype=None, out=None):
-    """O = softmax(q k^T * scale + M) v for q [B,H,Nq,d], k, v [B,H,Nk,d].
+def attn_fwd(q, k, v, mask: str = "none", valid_lens=None, scale: float | None = None, out_dtype=None, out=None,
+             return_lse: bool = False, lse=None):
+    """O = softmax(q k^T * scale + M) v for q [B,H,Nq,d], k, v [B,H_kv,Nk,d].
 
-    ``mask``: "none", "causal" (key j > query i hidden) or "padding" (key j
-    >= valid_lens[b] hidden; ``valid_lens`` an int32 GPU tensor [B]).
+    ``mask``: "none", "causal" (key j > query i hidden), "padding" (key j
+    >= valid_lens[b] hidden; ``valid_lens`` an int32 GPU tensor [B]) or
+    "causal_padding" (hidden by either rule). k and v may have H_kv heads,
+    H_kv dividing H: query head h reads K/V head h // (H // H_kv).
     ``scale`` defaults to 1/sqrt(d). ``out_dtype`` defaults to q's dtype;
-    bf16 inputs may request a float32 output. Enqueued on the current stream.
+    bf16 inputs may request a float32 output. With ``return_lse`` (or an
+    ``lse`` tensor given) the call also returns the float32 [B,H,Nq]
+    log-sum-exp of each row's visible scaled scores. Enqueued on the
+    current stream.
     """
     import torch
 
     lib = load_library()
     if mask not in MASK_KINDS:
         raise ValueError("mask must be one of %s" % sorted(MASK_KINDS))
-    _check_gpu(q, k, v, valid_lens)
+    _check_gpu(q, k, v, valid_lens, lse)
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, H, N, d]")
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
-    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
-        raise ValueError("k and v must be [B, H, Nk, d] matching q")
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != (B, Hkv, Nk, d):
+        raise ValueError("k and v must be [B, H_kv, Nk, d] matching q")
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("the K/V head count must divide the query head count")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share a dtype")
-    if mask == "padding":
+    if mask in ("padding", "causal_padding"):
         if valid_lens is None or valid_lens.dtype != torch.int32 or tuple(valid_lens.shape) != (B,):
-            raise ValueError("padding mask needs valid_lens: int32 GPU tensor of shape [B]")
+            raise ValueError("%s mask needs valid_lens: int32 GPU tensor of shape [B]" % mask)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if out is None:
@@ -133,13 +144,19 @@ def attn_fwd(q, k, v, mask: str = "none", valid_lens=None, scale: float | None =
         _check_gpu(out)
         if tuple(out.shape) != (B, H, Nq, d) or out.dtype != out_dtype:
             raise ValueError("out has the wrong shape or dtype")
-    st = lib.attn_fwd(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
-                      MASK_KINDS[mask],
-                      ctypes.c_void_p(valid_lens.data_ptr() if (mask == "padding") else 0),
-                      ctypes.c_float(scale), ctypes.c_void_p(out.data_ptr()), B, H, Nq, Nk, d, _dtype_code(q),
-                      _dtype_code(out), _stream_ptr(q.device))
+    if lse is not None:
+        if tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be a float32 [B, H, Nq] tensor")
+    elif return_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    uses_lens = mask in ("padding", "causal_padding")
+    st = lib.attn_fwd_ex(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                         ctypes.c_void_p(v.data_ptr()), MASK_KINDS[mask],
+                         ctypes.c_void_p(valid_lens.data_ptr() if uses_lens else 0), ctypes.c_float(scale),
+                         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
+                         B, H, Hkv, Nq, Nk, d, _dtype_code(q), _dtype_code(out), _stream_ptr(q.device))
     _raise_for(lib, st, "attn_fwd")
-    return out
+    return (out, lse) if lse is not None else out
 
 
 def mha_workspace_bytes(batch: int, seq: int, d_model: int, h: int, dtype=None) -> int:

@@ -159,7 +159,7 @@ __device__ __forceinline__ void mask_scores(f32x16 (&s)[2], int k0, int kv_len, 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int key = k0 + jb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-            const bool vis = key < kv_len && (MASK != kMaskCausal || key <= qrow);
+            const bool vis = key < kv_len && (!mask_causal(MASK) || key <= qrow);
             if (!vis) s[jb][r] = -INFINITY;
         }
 }
@@ -275,6 +275,16 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float l_
         }
 }
 
+// Log-sum-exp of one query row, written by the lanes of the first half-wave: the weights were
+// P = exp2(s * scale * log2(e) - mc) and l = sum P, so ln sum_j exp(s_j * scale) = ln(2) * (mc + log2(l))
+// (-inf for a row without a visible key, l = 0).
+__device__ __forceinline__ void store_lse(float *__restrict__ lse, float l, float mc, int qrow, int bh, int Nq,
+                                          int hf)
+{
+    if (hf == 0 && qrow < Nq)
+        lse[(size_t)bh * Nq + qrow] = l > 0.f ? (mc + log2f(l)) * 0.69314718055994531f : -INFINITY;
+}
+
 // O = O_acc / l for one block of 32 query rows, as bf16, staged through an 8 KiB LDS area of the wave so
 // that every store writes whole 256-byte rows (four rows per instruction) instead of 16 bytes per row.
 // l_tot: the row's whole sum. The stores go through a buffer descriptor that covers exactly the block's
@@ -333,7 +343,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
     AttnTraits<D, QB>::kWavesPerEU, AttnTraits<D, QB>::kWavesPerEU))) void attn_fwd_bf16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const int32_t *__restrict__ valid_lens, float c_log2, void *__restrict__ Out, int H, int Nq, int Nk,
-    int num_qtiles, int BH)
+    int num_qtiles, int BH, AttnHeads hd)
 {
     constexpr bool ASM = AttnTraits<D, QB>::kAsm;
     constexpr int RW = QB * 32;        // query rows per wave
@@ -357,21 +367,22 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
     const int id = blockIdx.x;
     const int bh = id % BH;
     int qt = id / BH;
-    if (MASK == kMaskCausal) qt = num_qtiles - 1 - qt;
+    if (mask_causal(MASK)) qt = num_qtiles - 1 - qt;
     const int b = bh / H;
     const int q0 = qt * BM;
 
     int kv_len = Nk;
-    if (MASK == kMaskPadding) {
+    if (mask_padding(MASK)) {
         const int L = valid_lens[b];
         kv_len = L < 0 ? 0 : (L > Nk ? Nk : L);
     }
     int kv_end = kv_len;
-    if (MASK == kMaskCausal) kv_end = min(kv_len, q0 + BM);
+    if (mask_causal(MASK)) kv_end = min(kv_len, q0 + BM);
     const int ntiles = (kv_end + kBlockN - 1) / kBlockN;
 
-    const uint16_t *Kh = K + (size_t)bh * Nk * D;
-    const uint16_t *Vh = V + (size_t)bh * Nk * D;
+    const size_t kvh = (size_t)b * hd.kv_heads + (bh - b * H) / hd.group;
+    const uint16_t *Kh = K + kvh * Nk * D;
+    const uint16_t *Vh = V + kvh * Nk * D;
 
     // Q^T as B operands: lane holds Q[qrow][ks*16 + hf*8 .. +7]
     const int qmin_w = q0 + wave * RW, qmax_w = qmin_w + RW - 1;
@@ -442,10 +453,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
     };
 
     // tiles this wave computes: causal rows <= qmax_w see no key past qmax_w
-    const int ntiles_w = (MASK == kMaskCausal) ? min(ntiles, qmax_w / kBlockN + 1) : ntiles;
+    const int ntiles_w = mask_causal(MASK) ? min(ntiles, qmax_w / kBlockN + 1) : ntiles;
     auto needs_mask = [&](int t) {
         const int k0 = t * kBlockN;
-        return (k0 + kBlockN > kv_len) || (MASK == kMaskCausal && k0 + kBlockN - 1 > qmin_w);
+        return (k0 + kBlockN > kv_len) || (mask_causal(MASK) && k0 + kBlockN - 1 > qmin_w);
     };
 
     // Online-softmax bookkeeping for one tile whose scores are in `cur`:
@@ -558,6 +569,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
     if constexpr (ASM) mfma_fence_a8(acc);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) store_rows<D, OUT_F32, OLAYOUT>(acc[qb], l_run[qb], qrow[qb], bh, H, Nq, b, hf, Out);
+    if (hd.lse) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) store_lse(hd.lse, half_swap_sum(l_run[qb]), mc_run[qb], qrow[qb], bh, Nq, hf);
+    }
 }
 
 #include "attn_qb2_tile.inc"
@@ -601,7 +616,7 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2])
 // score buffers, P and the operand staging in VGPRs, at the physical
 // registers the asm names.
 struct Qb2Item {
-    int valid, bh, b, q0, kv_len, kv_end, ntiles;
+    int valid, bh, b, kvh, q0, kv_len, kv_end, ntiles;
 };
 
 // Item of workgroup w in round k: even rounds in workgroup order, odd rounds reversed (by groups of 8 when
@@ -625,7 +640,7 @@ __device__ __forceinline__ int qb2_sched(int w, int j, int G, int num_items)
 
 template <int MASK>
 __device__ __forceinline__ Qb2Item qb2_item(int p, int num_items, int num_qtiles, int BH, int H, int Nk,
-                                            const int32_t *__restrict__ valid_lens)
+                                            const int32_t *__restrict__ valid_lens, const AttnHeads &hd)
 {
     constexpr int BM = 256;
     Qb2Item it{};
@@ -633,20 +648,22 @@ __device__ __forceinline__ Qb2Item qb2_item(int p, int num_items, int num_qtiles
     if (!it.valid) return it;
     it.bh = p % BH;
     int qt = p / BH;
-    if (MASK == kMaskCausal) qt = num_qtiles - 1 - qt;
+    if (mask_causal(MASK)) qt = num_qtiles - 1 - qt;
     it.b = it.bh / H;
+    it.kvh = it.b * hd.kv_heads + (it.bh - it.b * H) / hd.group;
     it.q0 = qt * BM;
     it.kv_len = Nk;
-    if (MASK == kMaskPadding) {
+    if (mask_padding(MASK)) {
         const int L = valid_lens[it.b];
         it.kv_len = L < 0 ? 0 : (L > Nk ? Nk : L);
     }
     it.kv_end = it.kv_len;
-    if (MASK == kMaskCausal) it.kv_end = min(it.kv_len, it.q0 + BM);
+    if (mask_causal(MASK)) it.kv_end = min(it.kv_len, it.q0 + BM);
     it.ntiles = (it.kv_end + kBlockN - 1) / kBlockN;
     // wave-uniform by construction; say so, so that they stay in SGPRs
     it.bh = __builtin_amdgcn_readfirstlane(it.bh);
     it.b = __builtin_amdgcn_readfirstlane(it.b);
+    it.kvh = __builtin_amdgcn_readfirstlane(it.kvh);
     it.q0 = __builtin_amdgcn_readfirstlane(it.q0);
     it.kv_len = __builtin_amdgcn_readfirstlane(it.kv_len);
     it.kv_end = __builtin_amdgcn_readfirstlane(it.kv_end);
@@ -658,7 +675,7 @@ template <int MASK, bool OUT_F32, int OLAYOUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_fwd_qb2_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const int32_t *__restrict__ valid_lens, float c_log2, void *__restrict__ Out, int H, int Nq, int Nk,
-    int num_qtiles, int BH)
+    int num_qtiles, int BH, AttnHeads hd)
 {
     constexpr int D = 128, QB = 2, WAVES = 4, RW = 64;
     constexpr int KS = D / 16, DB = D / 32;
@@ -724,7 +741,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int i = 0; i < TILE_B / (16 * 256); ++i)
             *(u32x4 *)(smem + VSLOT0 + (1 - off) * TILE_B + (i * 256 + tid) * 16) = u32x4{0u, 0u, 0u, 0u};
         if (it.ntiles > 0) {
-            const uint16_t *Kh = K + (size_t)it.bh * Nk * D, *Vh = V + (size_t)it.bh * Nk * D;
+            const uint16_t *Kh = K + (size_t)it.kvh * Nk * D, *Vh = V + (size_t)it.kvh * Nk * D;
             issue(Kh, 0, it.kv_end, KSLOT0 + off * TILE_B);
             if (it.ntiles > 1) issue(Kh, kBlockN, it.kv_end, KSLOT0 + (1 - off) * TILE_B);
             issue(Vh, 0, it.kv_end, VSLOT0 + off * TILE_B);
@@ -738,7 +755,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
 
     int k = 0, off = 0;
-    Qb2Item cur = qb2_item<MASK>(qb2_sched(w, 0, G, num_items), num_items, num_qtiles, BH, H, Nk, valid_lens);
+    Qb2Item cur = qb2_item<MASK>(qb2_sched(w, 0, G, num_items), num_items, num_qtiles, BH, H, Nk, valid_lens, hd);
     if (!cur.valid) return;
     q_tiles(cur);
     first_tiles(cur, 0);
@@ -765,7 +782,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // arrive while this item's tiles run
         __syncthreads();
         const Qb2Item nxt =
-            qb2_item<MASK>(qb2_sched(w, ++k, G, num_items), num_items, num_qtiles, BH, H, Nk, valid_lens);
+            qb2_item<MASK>(qb2_sched(w, ++k, G, num_items), num_items, num_qtiles, BH, H, Nk, valid_lens, hd);
         if (nxt.valid) q_tiles(nxt);
 
         const int qmin_w = cur.q0 + wave * RW, qmax_w = qmin_w + RW - 1;
@@ -775,17 +792,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             // a visible key of row qrow satisfies key <= lim; the asm compares the key's
             // offset within the tile (lane half included) against lim - tile start
             const int qrow = qmin_w + qb * 32 + l32;
-            lim[qb] = (MASK == kMaskCausal ? min(qrow, cur.kv_len - 1) : cur.kv_len - 1) - hf * 4;
+            lim[qb] = (mask_causal(MASK) ? min(qrow, cur.kv_len - 1) : cur.kv_len - 1) - hf * 4;
         }
-        const int ntiles_w = (MASK == kMaskCausal) ? min(cur.ntiles, qmax_w / kBlockN + 1) : cur.ntiles;
-        // The one tile of this wave that needs a mask: the tile crossing kv_len (masked after its scores,
-        // out of line), or, causal, the wave's diagonal tile, which starts at the wave's first row (a
-        // multiple of 64) and is masked inside its step. Causal rows past kv_len are past Nq: not stored.
-        const int t_mask = (MASK == kMaskCausal) ? 0x7fffffff : cur.kv_len / kBlockN;
-        const int t_diag = (MASK == kMaskCausal) ? qmin_w / kBlockN : 0x7fffffff;
-        const uint64_t kh = (uint64_t)(K + (size_t)cur.bh * Nk * D), vh = (uint64_t)(V + (size_t)cur.bh * Nk * D);
+        const int ntiles_w = mask_causal(MASK) ? min(cur.ntiles, qmax_w / kBlockN + 1) : cur.ntiles;
+        // The tiles of this wave that need a mask: from the tile crossing kv_len on (masked after their
+        // scores, out of line, against key <= lim), or, causal, the wave's diagonal tile, which starts at
+        // the wave's first row (a multiple of 64) and is masked inside its step. Causal rows past Nk are
+        // past Nq: not stored. With the padding mask as well, the diagonal tile keeps its in-step mask
+        // only when no key before its end (or before Nk) is past kv_len; otherwise every tile from the
+        // one crossing kv_len on takes the general mask, which applies both rules.
+        int t_mask = cur.kv_len / kBlockN, t_diag = 0x7fffffff;
+        if (mask_causal(MASK) &&
+            (!mask_padding(MASK) || cur.kv_len >= min(Nk, (qmin_w / kBlockN + 1) * kBlockN))) {
+            t_mask = 0x7fffffff;
+            t_diag = qmin_w / kBlockN;
+        }
+        const uint64_t kh = (uint64_t)(K + (size_t)cur.kvh * Nk * D), vh = (uint64_t)(V + (size_t)cur.kvh * Nk * D);
         const Qb2Item &nn = nxt.valid ? nxt : cur;  // a valid address even when there is no next item
-        const uint64_t nkh = (uint64_t)(K + (size_t)nn.bh * Nk * D), nvh = (uint64_t)(V + (size_t)nn.bh * Nk * D);
+        const uint64_t nkh = (uint64_t)(K + (size_t)nn.kvh * Nk * D), nvh = (uint64_t)(V + (size_t)nn.kvh * Nk * D);
         float l_run[QB] = {0.f, 0.f}, mc0 = -INFINITY, mc1 = -INFINITY;
         qb2_loop(acc, qreg, kaddr, vaddr, voff, lim[0], lim[1], c_log2, l_run[0], l_run[1], mc0, mc1,
                  u(0), u(cur.ntiles), u(ntiles_w), u(t_mask), u(cur.kv_end), u((uint32_t)kh),
@@ -820,6 +844,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                                 smem + STAGE + wave * 8192, Out);
             }
         }
+        if (hd.lse) {
+            store_lse(hd.lse, l_run[0], mc0, cur.q0 + wave * RW + l32, cur.bh, Nq, hf);
+            store_lse(hd.lse, l_run[1], mc1, cur.q0 + wave * RW + 32 + l32, cur.bh, Nq, hf);
+        }
         if (!nxt.valid) break;
         cur = nxt;
         off = off_next;
@@ -842,7 +870,7 @@ int device_cu_count()
 
 template <int D, int MASK, bool OUT_F32, int OLAYOUT>
 hipError_t launch_variant(const void *Q, const void *K, const void *V, const int32_t *valid_lens, float scale,
-                          void *O, int B, int H, int Nq, int Nk, hipStream_t stream)
+                          void *O, int B, int H, int Nq, int Nk, AttnHeads hd, hipStream_t stream)
 {
     // 32 (QB = 1) or 64 (QB = 2) query rows per wave; 64-row waves need the
     // whole register file: one wave per SIMD, 4 per workgroup
@@ -863,34 +891,39 @@ hipError_t launch_variant(const void *Q, const void *K, const void *V, const int
         hipLaunchKernelGGL((attn_fwd_qb2_kernel<MASK, OUT_F32, OLAYOUT>),
                            dim3((unsigned)std::min<long long>(grid, device_cu_count())), dim3(256), 0, stream,
                            (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, valid_lens, c_log2, O, H,
-                           Nq, Nk, num_qtiles, BH);
+                           Nq, Nk, num_qtiles, BH, hd);
     else
         hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QB, MASK, OUT_F32, OLAYOUT, WAVES>), dim3((unsigned)grid),
                            dim3(WAVES * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
-                           valid_lens, c_log2, O, H, Nq, Nk, num_qtiles, BH);
+                           valid_lens, c_log2, O, H, Nq, Nk, num_qtiles, BH, hd);
     return hipGetLastError();
 }
 
 template <int D, int MASK>
 hipError_t dispatch_out(const void *Q, const void *K, const void *V, const int32_t *vl, float scale, void *O,
-                        int out_f32, int out_layout, int B, int H, int Nq, int Nk, hipStream_t s)
+                        int out_f32, int out_layout, int B, int H, int Nq, int Nk, AttnHeads hd, hipStream_t s)
 {
     if (out_layout == kOutBNHD) {
-        if (out_f32) return launch_variant<D, MASK, true, kOutBNHD>(Q, K, V, vl, scale, O, B, H, Nq, Nk, s);
-        return launch_variant<D, MASK, false, kOutBNHD>(Q, K, V, vl, scale, O, B, H, Nq, Nk, s);
+        if (out_f32) return launch_variant<D, MASK, true, kOutBNHD>(Q, K, V, vl, scale, O, B, H, Nq, Nk, hd, s);
+        return launch_variant<D, MASK, false, kOutBNHD>(Q, K, V, vl, scale, O, B, H, Nq, Nk, hd, s);
     }
-    if (out_f32) return launch_variant<D, MASK, true, kOutBHND>(Q, K, V, vl, scale, O, B, H, Nq, Nk, s);
-    return launch_variant<D, MASK, false, kOutBHND>(Q, K, V, vl, scale, O, B, H, Nq, Nk, s);
+    if (out_f32) return launch_variant<D, MASK, true, kOutBHND>(Q, K, V, vl, scale, O, B, H, Nq, Nk, hd, s);
+    return launch_variant<D, MASK, false, kOutBHND>(Q, K, V, vl, scale, O, B, H, Nq, Nk, hd, s);
 }
 
 template <int D>
 hipError_t dispatch_mask(const void *Q, const void *K, const void *V, int mask, const int32_t *vl, float scale,
-                         void *O, int out_f32, int out_layout, int B, int H, int Nq, int Nk, hipStream_t s)
+                         void *O, int out_f32, int out_layout, int B, int H, int Nq, int Nk, AttnHeads hd,
+                         hipStream_t s)
 {
     switch (mask) {
-    case kMaskCausal: return dispatch_out<D, kMaskCausal>(Q, K, V, vl, scale, O, out_f32, out_layout, B, H, Nq, Nk, s);
-    case kMaskPadding: return dispatch_out<D, kMaskPadding>(Q, K, V, vl, scale, O, out_f32, out_layout, B, H, Nq, Nk, s);
-    default: return dispatch_out<D, kMaskNone>(Q, K, V, vl, scale, O, out_f32, out_layout, B, H, Nq, Nk, s);
+    case kMaskCausal:
+        return dispatch_out<D, kMaskCausal>(Q, K, V, vl, scale, O, out_f32, out_layout, B, H, Nq, Nk, hd, s);
+    case kMaskPadding:
+        return dispatch_out<D, kMaskPadding>(Q, K, V, vl, scale, O, out_f32, out_layout, B, H, Nq, Nk, hd, s);
+    case kMaskCausalPadding:
+        return dispatch_out<D, kMaskCausalPadding>(Q, K, V, vl, scale, O, out_f32, out_layout, B, H, Nq, Nk, hd, s);
+    default: return dispatch_out<D, kMaskNone>(Q, K, V, vl, scale, O, out_f32, out_layout, B, H, Nq, Nk, hd, s);
     }
 }
 
@@ -898,12 +931,12 @@ hipError_t dispatch_mask(const void *Q, const void *K, const void *V, int mask, 
 
 hipError_t launch_attn_bf16(const void *Q, const void *K, const void *V, int mask, const int32_t *valid_lens,
                             float scale, void *O, int out_f32, int out_layout, int B, int H, int Nq, int Nk, int D,
-                            hipStream_t stream)
+                            AttnHeads hd, hipStream_t stream)
 {
     if (D == 128)
-        return dispatch_mask<128>(Q, K, V, mask, valid_lens, scale, O, out_f32, out_layout, B, H, Nq, Nk, stream);
+        return dispatch_mask<128>(Q, K, V, mask, valid_lens, scale, O, out_f32, out_layout, B, H, Nq, Nk, hd, stream);
     if (D == 64)
-        return dispatch_mask<64>(Q, K, V, mask, valid_lens, scale, O, out_f32, out_layout, B, H, Nq, Nk, stream);
+        return dispatch_mask<64>(Q, K, V, mask, valid_lens, scale, O, out_f32, out_layout, B, H, Nq, Nk, hd, stream);
     return hipErrorInvalidValue;
 }
 

@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const float *__restri
                                                            const float *__restrict__ V,
                                                            const int32_t *__restrict__ valid_lens, float scale,
                                                            float *__restrict__ O, int H, int Nq, int Nk,
-                                                           int num_qtiles)
+                                                           int num_qtiles, AttnHeads hd)
 {
     constexpr int CPL = D / 16;  // columns per lane
     __shared__ float Ks[kKeyTile][D + 1];
@@ -40,15 +40,16 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const float *__restri
     const int qrow = q0 + row;
 
     int kv_len = Nk;
-    if (MASK == kMaskPadding) {
+    if (mask_padding(MASK)) {
         const int L = valid_lens[b];
         kv_len = L < 0 ? 0 : (L > Nk ? Nk : L);
     }
     int kv_end = kv_len;
-    if (MASK == kMaskCausal) kv_end = min(kv_len, q0 + kRows);
+    if (mask_causal(MASK)) kv_end = min(kv_len, q0 + kRows);
 
-    const float *Kh = K + (size_t)bh * Nk * D;
-    const float *Vh = V + (size_t)bh * Nk * D;
+    const size_t kvh = (size_t)b * hd.kv_heads + (bh - b * H) / hd.group;
+    const float *Kh = K + kvh * Nk * D;
+    const float *Vh = V + kvh * Nk * D;
     float q[CPL], o[CPL];
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const float *__restri
             part += __shfl_xor(part, 2, 16);
             part += __shfl_xor(part, 1, 16);
             const int key = k0 + j;
-            const bool vis = key < kv_len && (MASK != kMaskCausal || key <= qrow);
+            const bool vis = key < kv_len && (!mask_causal(MASK) || key <= qrow);
             if (vis) {
                 const float s = part * scale;
                 const float m_new = fmaxf(m, s);
@@ -95,43 +96,47 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const float *__restri
         const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
         for (int e = 0; e < CPL; ++e) O[((size_t)bh * Nq + qrow) * D + sub + 16 * e] = o[e] * inv;
+        // log of the softmax denominator: m is the row max of the scaled scores, l = sum exp(s - m)
+        if (hd.lse && sub == 0) hd.lse[(size_t)bh * Nq + qrow] = l > 0.f ? m + logf(l) : -INFINITY;
     }
 }
 
 template <int D, int MASK>
 hipError_t launch(const float *Q, const float *K, const float *V, const int32_t *vl, float scale, float *O, int B,
-                  int H, int Nq, int Nk, hipStream_t s)
+                  int H, int Nq, int Nk, AttnHeads hd, hipStream_t s)
 {
     const int num_qtiles = (Nq + kRows - 1) / kRows;
     const long long grid = (long long)num_qtiles * B * H;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((attn_fwd_f32_kernel<D, MASK>), dim3((unsigned)grid), dim3(256), 0, s, Q, K, V, vl, scale, O,
-                       H, Nq, Nk, num_qtiles);
+                       H, Nq, Nk, num_qtiles, hd);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t dispatch(const float *Q, const float *K, const float *V, int mask, const int32_t *vl, float scale,
-                    float *O, int B, int H, int Nq, int Nk, hipStream_t s)
+                    float *O, int B, int H, int Nq, int Nk, AttnHeads hd, hipStream_t s)
 {
     switch (mask) {
-    case kMaskCausal: return launch<D, kMaskCausal>(Q, K, V, vl, scale, O, B, H, Nq, Nk, s);
-    case kMaskPadding: return launch<D, kMaskPadding>(Q, K, V, vl, scale, O, B, H, Nq, Nk, s);
-    default: return launch<D, kMaskNone>(Q, K, V, vl, scale, O, B, H, Nq, Nk, s);
+    case kMaskCausal: return launch<D, kMaskCausal>(Q, K, V, vl, scale, O, B, H, Nq, Nk, hd, s);
+    case kMaskPadding: return launch<D, kMaskPadding>(Q, K, V, vl, scale, O, B, H, Nq, Nk, hd, s);
+    case kMaskCausalPadding: return launch<D, kMaskCausalPadding>(Q, K, V, vl, scale, O, B, H, Nq, Nk, hd, s);
+    default: return launch<D, kMaskNone>(Q, K, V, vl, scale, O, B, H, Nq, Nk, hd, s);
     }
 }
 
 }  // namespace
 
 hipError_t launch_attn_f32(const float *Q, const float *K, const float *V, int mask, const int32_t *valid_lens,
-                           float scale, float *O, int B, int H, int Nq, int Nk, int D, hipStream_t stream)
+                           float scale, float *O, int B, int H, int Nq, int Nk, int D, AttnHeads hd,
+                           hipStream_t stream)
 {
     switch (D) {
-    case 16: return dispatch<16>(Q, K, V, mask, valid_lens, scale, O, B, H, Nq, Nk, stream);
-    case 32: return dispatch<32>(Q, K, V, mask, valid_lens, scale, O, B, H, Nq, Nk, stream);
-    case 64: return dispatch<64>(Q, K, V, mask, valid_lens, scale, O, B, H, Nq, Nk, stream);
-    case 128: return dispatch<128>(Q, K, V, mask, valid_lens, scale, O, B, H, Nq, Nk, stream);
+    case 16: return dispatch<16>(Q, K, V, mask, valid_lens, scale, O, B, H, Nq, Nk, hd, stream);
+    case 32: return dispatch<32>(Q, K, V, mask, valid_lens, scale, O, B, H, Nq, Nk, hd, stream);
+    case 64: return dispatch<64>(Q, K, V, mask, valid_lens, scale, O, B, H, Nq, Nk, hd, stream);
+    case 128: return dispatch<128>(Q, K, V, mask, valid_lens, scale, O, B, H, Nq, Nk, hd, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -44,15 +44,20 @@ constexpr long long kI32Max = 0x7fffffffLL;
 
 extern "C" {
 
-attn_status_t attn_fwd(const void *Q, const void *K, const void *V, int32_t mask_kind, const int32_t *valid_lens,
-                       float scale, void *O, int32_t batch, int32_t heads, int32_t seq_q, int32_t seq_k,
-                       int32_t head_dim, int32_t in_dtype, int32_t out_dtype, void *stream)
+attn_status_t attn_fwd_ex(const void *Q, const void *K, const void *V, int32_t mask_kind, const int32_t *valid_lens,
+                          float scale, void *O, float *lse, int32_t batch, int32_t heads, int32_t kv_heads,
+                          int32_t seq_q, int32_t seq_k, int32_t head_dim, int32_t in_dtype, int32_t out_dtype,
+                          void *stream)
 {
     g_last_error[0] = '\0';
     if (batch < 0 || heads < 0 || seq_q < 0 || seq_k < 0 || head_dim <= 0)
         return fail(ATTN_EINVAL, "attn_fwd: negative size or head_dim <= 0 (batch=%d heads=%d seq_q=%d seq_k=%d "
                                  "head_dim=%d)", batch, heads, seq_q, seq_k, head_dim);
-    if (mask_kind != ATTN_MASK_NONE && mask_kind != ATTN_MASK_CAUSAL && mask_kind != ATTN_MASK_PADDING)
+    if (kv_heads <= 0 || (heads > 0 && heads % kv_heads != 0))
+        return fail(ATTN_EINVAL, "attn_fwd: kv_heads must be positive and divide heads (heads=%d kv_heads=%d)", heads,
+                    kv_heads);
+    if (mask_kind != ATTN_MASK_NONE && mask_kind != ATTN_MASK_CAUSAL && mask_kind != ATTN_MASK_PADDING &&
+        mask_kind != ATTN_MASK_CAUSAL_PADDING)
         return fail(ATTN_EINVAL, "attn_fwd: unknown mask_kind %d", mask_kind);
     if ((in_dtype != ATTN_F32 && in_dtype != ATTN_BF16) || (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16))
         return fail(ATTN_EINVAL, "attn_fwd: unknown dtype (in %d, out %d)", in_dtype, out_dtype);
@@ -64,34 +69,49 @@ attn_status_t attn_fwd(const void *Q, const void *K, const void *V, int32_t mask
         return fail(ATTN_EUNSUPPORTED, "attn_fwd: f32 supports head_dim 16, 32, 64 or 128, got %d", head_dim);
     if (in_dtype == ATTN_F32 && out_dtype != ATTN_F32)
         return fail(ATTN_EUNSUPPORTED, "attn_fwd: f32 inputs need an f32 output");
-    if (mask_kind == ATTN_MASK_CAUSAL && seq_q != seq_k)
+    const bool causal = mask_kind == ATTN_MASK_CAUSAL || mask_kind == ATTN_MASK_CAUSAL_PADDING;
+    const bool padding = mask_kind == ATTN_MASK_PADDING || mask_kind == ATTN_MASK_CAUSAL_PADDING;
+    if (causal && seq_q != seq_k)
         return fail(ATTN_EUNSUPPORTED, "attn_fwd: causal mask needs seq_q == seq_k (%d != %d)", seq_q, seq_k);
     const long long bh = (long long)batch * heads;
     if (bh > kI32Max) return fail(ATTN_EINVAL, "attn_fwd: batch*heads too large");
 
     const size_t ib = dtype_bytes(in_dtype), ob = dtype_bytes(out_dtype);
-    const size_t nq = (size_t)bh * seq_q * head_dim, nk = (size_t)bh * seq_k * head_dim;
+    const size_t nq = (size_t)bh * seq_q * head_dim, nk = (size_t)batch * kv_heads * seq_k * head_dim;
+    const size_t nl = (size_t)bh * seq_q * sizeof(float);
     if (nq == 0) return ATTN_OK;  // no output element
     if (!Q || !O) return fail(ATTN_EINVAL, "attn_fwd: null Q or O");
     if (nk && (!K || !V)) return fail(ATTN_EINVAL, "attn_fwd: null K or V");
-    if (mask_kind == ATTN_MASK_PADDING && !valid_lens)
-        return fail(ATTN_EINVAL, "attn_fwd: padding mask needs valid_lens");
+    if (padding && !valid_lens) return fail(ATTN_EINVAL, "attn_fwd: padding mask needs valid_lens");
     if (!aligned(Q, 16) || !aligned(O, 16) || (nk && (!aligned(K, 16) || !aligned(V, 16))))
         return fail(ATTN_EINVAL, "attn_fwd: Q, K, V and O must be 16-byte aligned");
-    if (valid_lens && mask_kind == ATTN_MASK_PADDING && !aligned(valid_lens, 4))
+    if (valid_lens && padding && !aligned(valid_lens, 4))
         return fail(ATTN_EINVAL, "attn_fwd: valid_lens must be 4-byte aligned");
+    if (lse && !aligned(lse, 4)) return fail(ATTN_EINVAL, "attn_fwd: lse must be 4-byte aligned");
     if (overlaps(O, nq * ob, Q, nq * ib) || overlaps(O, nq * ob, K, nk * ib) || overlaps(O, nq * ob, V, nk * ib))
         return fail(ATTN_EINVAL, "attn_fwd: O overlaps an input");
+    if (lse && (overlaps(lse, nl, Q, nq * ib) || overlaps(lse, nl, K, nk * ib) || overlaps(lse, nl, V, nk * ib) ||
+                overlaps(lse, nl, O, nq * ob)))
+        return fail(ATTN_EINVAL, "attn_fwd: lse overlaps an input or O");
 
+    const tsd::AttnHeads hd{kv_heads, heads > 0 ? heads / kv_heads : 1, lse};
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (in_dtype == ATTN_BF16)
         e = tsd::launch_attn_bf16(Q, K, V, mask_kind, valid_lens, scale, O, out_dtype == ATTN_F32, tsd::kOutBHND,
-                                  batch, heads, seq_q, seq_k, head_dim, s);
+                                  batch, heads, seq_q, seq_k, head_dim, hd, s);
     else
         e = tsd::launch_attn_f32((const float *)Q, (const float *)K, (const float *)V, mask_kind, valid_lens, scale,
-                                 (float *)O, batch, heads, seq_q, seq_k, head_dim, s);
+                                 (float *)O, batch, heads, seq_q, seq_k, head_dim, hd, s);
     return from_hip(e, "attn_fwd launch");
+}
+
+attn_status_t attn_fwd(const void *Q, const void *K, const void *V, int32_t mask_kind, const int32_t *valid_lens,
+                       float scale, void *O, int32_t batch, int32_t heads, int32_t seq_q, int32_t seq_k,
+                       int32_t head_dim, int32_t in_dtype, int32_t out_dtype, void *stream)
+{
+    return attn_fwd_ex(Q, K, V, mask_kind, valid_lens, scale, O, nullptr, batch, heads, heads > 0 ? heads : 1, seq_q,
+                       seq_k, head_dim, in_dtype, out_dtype, stream);
 }
 
 static attn_status_t mha_check(int32_t batch, int32_t seq, int32_t d_model, int32_t h, int32_t dtype)
@@ -148,7 +168,7 @@ attn_status_t mha_fwd(const void *X, const void *W_qkv, const void *W_o, int32_t
     hipError_t e = tsd::launch_gemm_bf16_qkv_split(X, W_qkv, qkv, batch, seq, d_model, h, s);
     if (e != hipSuccess) return from_hip(e, "mha_fwd projection GEMM");
     e = tsd::launch_attn_bf16(qkv, qkv + tok, qkv + 2 * tok, tsd::kMaskNone, nullptr, 1.0f / sqrtf((float)dk), ctx,
-                              0, tsd::kOutBNHD, batch, h, seq, seq, dk, s);
+                              0, tsd::kOutBNHD, batch, h, seq, seq, dk, tsd::AttnHeads{h, 1, nullptr}, s);
     if (e != hipSuccess) return from_hip(e, "mha_fwd attention");
     e = tsd::launch_gemm_bf16(ctx, W_o, O, batch * seq, d_model, d_model, s);
     return from_hip(e, "mha_fwd output GEMM");

@@ -8,17 +8,32 @@
 
 namespace tsd {
 
-enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskPadding = 2 };
+// Bit 0: causal (key j hidden from query i when j > i); bit 1: padding (keys j >= valid_lens[b] hidden).
+enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskPadding = 2, kMaskCausalPadding = 3 };
+constexpr bool mask_causal(int m) { return (m & kMaskCausal) != 0; }
+constexpr bool mask_padding(int m) { return (m & kMaskPadding) != 0; }
+
+// Grouped K/V heads and the optional per-row log-sum-exp of one attention call: query head h of batch b
+// reads K/V head b * kv_heads + h / group (group = H / kv_heads); lse, when not null, receives
+// ln sum_j exp(s_ij) over the visible scaled scores of each query row, [B,H,Nq] float32 (-inf for a row
+// without a visible key).
+struct AttnHeads {
+    int kv_heads;
+    int group;
+    float *lse;
+};
+
 enum OutLayout { kOutBHND = 0, kOutBNHD = 1 };  // [B,H,N,D] or concatenated heads [B,N,H*D]
 
 // bf16 attention, head_dim 64 or 128, output bf16 (out_f32 = 0) or f32.
 hipError_t launch_attn_bf16(const void *Q, const void *K, const void *V, int mask, const int32_t *valid_lens,
                             float scale, void *O, int out_f32, int out_layout, int B, int H, int Nq, int Nk, int D,
-                            hipStream_t stream);
+                            AttnHeads heads, hipStream_t stream);
 
 // f32 attention, head_dim 16, 32, 64 or 128, output f32, layout [B,H,N,D].
 hipError_t launch_attn_f32(const float *Q, const float *K, const float *V, int mask, const int32_t *valid_lens,
-                           float scale, float *O, int B, int H, int Nq, int Nk, int D, hipStream_t stream);
+                           float scale, float *O, int B, int H, int Nq, int Nk, int D, AttnHeads heads,
+                           hipStream_t stream);
 
 // C = A[M,K] * B[K,N] in bf16 with f32 accumulation, bf16 output.
 // Plain epilogue: C row-major [M,N].
