@@ -143,6 +143,31 @@ def bench_mha(dev, nsteps, warmup, sets=4):
     return dict(ms=ms, wall=wall, flops=flops)
 
 
+def bench_grouped_lse(dev, nsteps, warmup, sets=2):
+    """The causal 4K workload with 4 K/V heads for its 16 query heads, the causal-and-padding mask (every
+    valid length = N, so the work is the causal work) and the per-row log-sum-exp written out."""
+    import torch
+
+    import synth
+    import transformer_scaled_dot_amd as tsd
+
+    B, H, Hkv, N, d = 4, 16, 4, 4096, 128
+    bufs = []
+    for s in range(sets):
+        q = synth.normal_tensor(9100 + 3 * s, (B, H, N, d)).torch(dev)
+        k = synth.normal_tensor(9101 + 3 * s, (B, Hkv, N, d)).torch(dev)
+        v = synth.normal_tensor(9102 + 3 * s, (B, Hkv, N, d)).torch(dev)
+        bufs.append((q, k, v, torch.empty_like(q), torch.empty((B, H, N), dtype=torch.float32, device=dev)))
+    vl = torch.full((B,), N, dtype=torch.int32, device=dev)
+
+    def step(i):
+        q, k, v, o, lse = bufs[i % sets]
+        tsd.attn_fwd(q, k, v, mask="causal_padding", valid_lens=vl, out=o, lse=lse)
+
+    ms, _, _ = time_launches(step, nsteps, warmup)
+    return dict(ms=ms, flops=attn_flops(B, H, N, N, d, True))
+
+
 def cpu_baseline(target_s=15.0):
     """The CPU oracle on whole heads of the benchmark workload (same seeded
     inputs), as many heads as fit in about target_s seconds."""
@@ -192,7 +217,8 @@ def main():
     # ms under this load, and the figure of interest is the sustained rate
     ap.add_argument("--warmup", type=int, default=1500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--extra", action="store_true", help="also time the padding, multi-head and 32K workloads")
+    ap.add_argument("--extra", action="store_true",
+                    help="also time the padding, multi-head and 32K workloads and the grouped-heads/log-sum-exp variant")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -270,6 +296,9 @@ def main():
         r5 = bench_attention(dev, 5, max(5, args.steps // 20), 5, "causal", sets=1)
         extra["C5_causal_b1h32n32768d128"] = {"ms": round(r5["ms"], 4),
                                               "tflops": round(r5["flops"] / r5["ms"] / 1e9, 2)}
+        rg = bench_grouped_lse(dev, args.steps, max(200, args.warmup // 4))
+        extra["C3_gqa_h16_kv4_causal_padding_lse"] = {"ms": round(rg["ms"], 5),
+                                                     "tflops": round(rg["flops"] / rg["ms"] / 1e9, 2)}
         out["extra"] = extra
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()

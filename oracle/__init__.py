@@ -12,7 +12,8 @@ Masks: none, causal (key j hidden when j > i), padding (keys j >= valid_len[b])
 and causal_padding (hidden by either rule). K/V may have fewer heads than Q:
 query head h reads K/V head h // (H // H_kv) ("Self-Attention 机制", section
 MHA -> MQA -> GQA -> MLA). The per-row log-sum-exp of the visible scaled
-scores can be returned alongside the output.
+scores can be returned alongside the output, and attention_backward gives
+the gradients with respect to Q, K and V by the chain rule.
 
 Pins (tests/test_oracle_pins.py) tie it to what the pages fix: the
 3-token hand-worked example of "04. Self-Attention: Transformer 的核心计算"
@@ -71,6 +72,9 @@ def _load(path: str | None = None):
         lib.oracle_attn_rows.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, I64, ctypes.c_int, P,
                                          ctypes.c_double, P, I64, P, P, ctypes.c_int]
         lib.oracle_attn_rows.restype = ctypes.c_int
+        lib.oracle_attn_bwd.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, I64, ctypes.c_int, P,
+                                        ctypes.c_double, P, P, P, ctypes.c_int]
+        lib.oracle_attn_bwd.restype = ctypes.c_int
         lib.oracle_mha.argtypes = [P, P, P, I64, I64, I64, I64, P, ctypes.c_int]
         lib.oracle_mha.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
@@ -131,6 +135,24 @@ def attention(q, k, v, mask="none", valid_lens=None, scale=None, return_weights=
         raise ValueError("oracle_attn rejected its arguments")
     out = [O] + ([A] if return_weights else []) + ([L] if return_lse else [])
     return tuple(out) if len(out) > 1 else O
+
+
+def attention_backward(q, k, v, do, mask="none", valid_lens=None, scale=None, threads=0, lib=None):
+    """Gradients (dq, dk, dv) of sum(O * do) for O = attention(q, k, v, ...):
+    the chain rule through the forward stages (softmax Jacobian included);
+    dk, dv have k's and v's shapes (grouped K/V heads sum their query
+    heads' contributions)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H, Hkv, Nq, Nk, d, dv, vl = _check_attn(q, k, v, mask, valid_lens)
+    if do.shape != (B, H, Nq, dv):
+        raise ValueError("do must have the output's shape")
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    dq, dk, dvv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    rc = _load(lib).oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), B, H, Hkv, Nq, Nk, d, dv, MASK[mask],
+                                 _ptr(vl), scale, _ptr(dq), _ptr(dk), _ptr(dvv), int(threads))
+    if rc < 0:
+        raise ValueError("oracle_attn_bwd rejected its arguments")
+    return dq, dk, dvv
 
 
 def attention_rows(q, k, v, rows, mask="none", valid_lens=None, scale=None, threads=0, lib=None, return_lse=False):

@@ -220,6 +220,79 @@ int oracle_attn_rows(const double *Q, const double *K, const double *V, int64_t 
 }
 
 /*
+ * Gradients of the attention above with respect to Q, K and V, given the
+ * gradient dO of the output (same shapes as Q, K, V, O; float64). The pages
+ * give no backward algorithm (they motivate gradients through the scaling:
+ * "04. Self-Attention", section 四 stage 2); this is the chain rule applied
+ * to the four forward stages in reverse, per (batch, query head, row i):
+ *   a_j  = the row's softmax weights (stage 3; 0 at masked j)
+ *   dV_j += a_j dO_i                       (stage 4: o_i = sum_j a_j v_j)
+ *   da_j  = dO_i . v_j
+ *   ds_j  = a_j (da_j - sum_k a_k da_k)    (stage 3: the softmax Jacobian)
+ *   dQ_i  = scale sum_j ds_j k_j           (stages 1-2: s_j = scale q_i . k_j)
+ *   dK_j += scale ds_j q_i
+ * With grouped K/V heads the contributions of every query head of a group
+ * add up in its K/V head. A row without a visible key contributes nothing.
+ * Parallel over (batch, K/V head): the rows that add into one K/V head run
+ * in one thread, in a fixed order.
+ */
+int oracle_attn_bwd(const double *Q, const double *K, const double *V, const double *dO, int64_t B, int64_t H,
+                    int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, int64_t dv, int mask_kind,
+                    const int32_t *valid_lens, double scale, double *dQ, double *dK, double *dV, int nthreads)
+{
+    if (bad_args(B, H, Hkv, Nq, Nk, d, dv, mask_kind, valid_lens)) return -1;
+    int used = set_threads(nthreads);
+    const int64_t group = H > 0 ? H / Hkv : 1;
+    for (int64_t x = 0; x < B * Hkv * Nk * d; ++x) dK[x] = 0.0;
+    for (int64_t x = 0; x < B * Hkv * Nk * dv; ++x) dV[x] = 0.0;
+#pragma omp parallel
+    {
+        double *a = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        double *o = (double *)malloc(sizeof(double) * (size_t)(dv > 0 ? dv : 1));
+        double *da = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bk = 0; bk < B * Hkv; ++bk) {
+            const int64_t b = bk / Hkv, hk = bk % Hkv;
+            const double *Kbh = K + bk * Nk * d, *Vbh = V + bk * Nk * dv;
+            double *dKbh = dK + bk * Nk * d, *dVbh = dV + bk * Nk * dv;
+            const int64_t L = uses_valid_lens(mask_kind) ? valid_lens[b] : Nk;
+            for (int64_t h = hk * group; h < (hk + 1) * group; ++h) {
+                const int64_t bh = b * H + h;
+                for (int64_t i = 0; i < Nq; ++i) {
+                    const int64_t r = bh * Nq + i;
+                    const double *q = Q + r * d, *g = dO + r * dv;
+                    double *dq = dQ + r * d;
+                    for (int64_t c = 0; c < d; ++c) dq[c] = 0.0;
+                    attention_row(q, Kbh, Vbh, Nk, d, dv, mask_kind, i, L, scale, s, o, a, NULL);
+                    double dot = 0.0; /* sum_k a_k da_k */
+                    for (int64_t j = 0; j < Nk; ++j) {
+                        da[j] = 0.0;
+                        if (a[j] == 0.0) continue;
+                        for (int64_t c = 0; c < dv; ++c) da[j] += g[c] * Vbh[j * dv + c];
+                        dot += a[j] * da[j];
+                    }
+                    for (int64_t j = 0; j < Nk; ++j) {
+                        if (a[j] == 0.0) continue;
+                        for (int64_t c = 0; c < dv; ++c) dVbh[j * dv + c] += a[j] * g[c];
+                        const double ds = a[j] * (da[j] - dot);
+                        for (int64_t c = 0; c < d; ++c) {
+                            dq[c] += scale * ds * Kbh[j * d + c];
+                            dKbh[j * d + c] += scale * ds * q[c];
+                        }
+                    }
+                }
+            }
+        }
+        free(a);
+        free(s);
+        free(o);
+        free(da);
+    }
+    return used;
+}
+
+/*
  * C[M,N] = A[M,Kd] B[Kd,N], row-major. Each output element is summed over
  * the inner index in ascending order; the loop nest walks B by rows only so
  * that the plain triple loop stays cache friendly.

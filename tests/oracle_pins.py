@@ -428,4 +428,89 @@ def pin_group_sizes_degenerate(lib):
         assert np.array_equal(Og[:, h:h + 1], Oh)
 
 
+# --- gradients ------------------------------------------------------------------
+
+def _fwd_loss(q, k, v, g, mask, vl, scale, lib):
+    return float(np.sum(oracle.attention(q, k, v, mask=mask, valid_lens=vl, scale=scale, lib=lib) * g))
+
+
+def pin_backward_matches_torch_autograd(lib):
+    """torch autograd through float64 attention on the CPU (with enable_gqa and a boolean keep mask)."""
+    import torch
+    import torch.nn.functional as F
+
+    for t, (B, H, Hkv, Nq, Nk, d) in enumerate([(2, 2, 2, 6, 6, 4), (1, 4, 2, 7, 9, 5), (2, 3, 1, 5, 5, 3)]):
+        q = _randn(1900 + 10 * t, (B, H, Nq, d))
+        k = _randn(1901 + 10 * t, (B, Hkv, Nk, d))
+        v = _randn(1902 + 10 * t, (B, Hkv, Nk, d))
+        g = _randn(1903 + 10 * t, (B, H, Nq, d))
+        vl = (np.arange(B, dtype=np.int32) * 3) % Nk + 2
+        for mask in _ALL_MASKS:
+            if mask.startswith("causal") and Nq > Nk:
+                continue
+            keep = torch.from_numpy(np.stack([_visible(mask, Nq, Nk, vl[b]) for b in range(B)])[:, None])
+            Q, K, V = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+            O = F.scaled_dot_product_attention(Q, K, V, attn_mask=keep, enable_gqa=True, scale=0.8)
+            (O * torch.from_numpy(g)).sum().backward()
+            dq, dk, dv = oracle.attention_backward(q, k, v, g, mask=mask, valid_lens=vl, scale=0.8, lib=lib)
+            np.testing.assert_allclose(dq, Q.grad.numpy(), atol=1e-12, rtol=0)
+            np.testing.assert_allclose(dk, K.grad.numpy(), atol=1e-12, rtol=0)
+            np.testing.assert_allclose(dv, V.grad.numpy(), atol=1e-12, rtol=0)
+
+
+def pin_backward_finite_differences(lib):
+    """Central differences of sum(O * g) on a tiny shape, for a few entries of each of Q, K and V."""
+    B, H, Hkv, N, d = 1, 2, 1, 5, 3
+    q, k, v = _randn(2000, (B, H, N, d)), _randn(2001, (B, Hkv, N, d)), _randn(2002, (B, Hkv, N, d))
+    g = _randn(2003, (B, H, N, d))
+    vl = np.asarray([4], dtype=np.int32)
+    eps = 1e-5
+    for mask in ("causal", "causal_padding"):
+        grads = oracle.attention_backward(q, k, v, g, mask=mask, valid_lens=vl, scale=0.7, lib=lib)
+        for which, (x, gx) in enumerate(zip((q, k, v), grads)):
+            for e in range(0, x.size, 3):
+                xp, xm = x.copy(), x.copy()
+                xp.flat[e] += eps
+                xm.flat[e] -= eps
+                args_p = [q, k, v]
+                args_m = [q, k, v]
+                args_p[which], args_m[which] = xp, xm
+                fd = (_fwd_loss(*args_p, g, mask, vl, 0.7, lib) - _fwd_loss(*args_m, g, mask, vl, 0.7, lib)) / (2 * eps)
+                assert abs(fd - gx.flat[e]) <= 1e-8, (mask, which, e, fd, gx.flat[e])
+
+
+def pin_backward_translation_invariances(lib):
+    """Adding one vector to every key shifts each row's scores by a constant (softmax unchanged): the key
+    gradients of a head sum to 0. Adding one vector to every value row shifts every output row that sees a
+    key by it: the value gradients of a head sum to the output gradients of those rows."""
+    B, H, N, d = 2, 3, 8, 4
+    q, k, v = _inputs(2100, B, H, N, N, d)
+    g = _randn(2104, (B, H, N, d))
+    vl = np.asarray([0, 5], dtype=np.int32)
+    for mask in _ALL_MASKS:
+        _, dk, dv = oracle.attention_backward(q, k, v, g, mask=mask, valid_lens=vl, lib=lib)
+        np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-13)
+        for b in range(B):
+            sees = _visible(mask, N, N, vl[b]).any(axis=1)
+            np.testing.assert_allclose(dv[b].sum(axis=1), g[b][:, sees].sum(axis=1), atol=1e-13)
+
+
+def pin_backward_zero_scale_and_masked_keys(lib):
+    """scale = 0: scores do not depend on Q or K, so dQ = dK = 0 exactly, and each row spreads its output
+    gradient uniformly over its visible keys. Keys no row can see (j >= valid_len) get zero gradients."""
+    B, H, N, d = 2, 2, 6, 3
+    q, k, v = _inputs(2200, B, H, N, N, d)
+    g = _randn(2203, (B, H, N, d))
+    vl = np.asarray([2, 6], dtype=np.int32)
+    for mask in _ALL_MASKS:
+        dq, dk, dv = oracle.attention_backward(q, k, v, g, mask=mask, valid_lens=vl, scale=0.0, lib=lib)
+        assert np.all(dq == 0.0) and np.all(dk == 0.0)
+        for b in range(B):
+            vis = _visible(mask, N, N, vl[b]).astype(np.float64)
+            w = vis / np.maximum(vis.sum(axis=1, keepdims=True), 1)
+            np.testing.assert_allclose(dv[b], np.einsum("ij,hic->hjc", w, g[b]), atol=1e-14)
+    _, dk, dv = oracle.attention_backward(q, k, v, g, mask="padding", valid_lens=vl, lib=lib)
+    assert np.all(dk[0, :, 2:] == 0.0) and np.all(dv[0, :, 2:] == 0.0)
+
+
 PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

@@ -33,6 +33,12 @@ MUTANTS = {
     "kv_heads_interleaved": ("return (b * Hkv + h / (H / Hkv)) * n;", "return (b * Hkv + h % Hkv) * n;"),
     "lse_without_max": ("if (lse) *lse = m + log(z);", "if (lse) *lse = log(z);"),
     "lse_base_two": ("if (lse) *lse = m + log(z);", "if (lse) *lse = m + log2(z);"),
+    "bwd_softmax_jacobian_without_row_term": ("const double ds = a[j] * (da[j] - dot);",
+                                              "const double ds = a[j] * da[j];"),
+    "bwd_dk_without_scale": ("dKbh[j * d + c] += scale * ds * q[c];", "dKbh[j * d + c] += ds * q[c];"),
+    "bwd_dv_weighted_by_da": ("dVbh[j * dv + c] += a[j] * g[c];", "dVbh[j * dv + c] += da[j] * g[c];"),
+    "bwd_group_first_head_only": ("for (int64_t h = hk * group; h < (hk + 1) * group; ++h) {",
+                                  "for (int64_t h = hk * group; h < hk * group + 1; ++h) {"),
 }
 
 
