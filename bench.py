@@ -36,7 +36,7 @@ WORKLOAD = dict(workload="sdpa_bf16_b4_h16_n4096_d128_causal", B=4, H=16, N=4096
                 dtype="bf16", scale="1/sqrt(128)")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_causal_b4h16n4096d128_hbm_traffic.json")
 KERNEL_SOURCES = ["transformer_scaled_dot_amd/csrc/attn_fwd_bf16.hip", "transformer_scaled_dot_amd/csrc/attn_qb2_tile.inc",
-                  "transformer_scaled_dot_amd/csrc/device_common.h"]
+                  "transformer_scaled_dot_amd/csrc/device_common.h", "transformer_scaled_dot_amd/csrc/attn_tiles.h"]
 
 
 def kernel_source_hash() -> str:
@@ -168,6 +168,31 @@ def bench_grouped_lse(dev, nsteps, warmup, sets=2):
     return dict(ms=ms, flops=attn_flops(B, H, N, N, d, True))
 
 
+def bench_backward(dev, nsteps, warmup, sets=2):
+    """The backward pass at the causal 4K shape (B4 H16 N4096 d128): dQ, dK, dV from the forward's O and
+    log-sum-exp and a synthetic output gradient. FLOPs: the five N x N x d products of the chain rule
+    (S recomputed, dP, dV, dK, dQ), halved for causal, i.e. 2.5 times the forward's."""
+    import torch
+
+    import synth
+    import transformer_scaled_dot_amd as tsd
+
+    B, H, N, d = 4, 16, 4096, 128
+    bufs = []
+    for s in range(sets):
+        q, k, v, g = (synth.normal_tensor(9200 + 4 * s + i, (B, H, N, d)).torch(dev) for i in range(4))
+        o, lse = tsd.attn_fwd(q, k, v, mask="causal", return_lse=True)
+        ws = torch.empty(tsd.load_library().attn_bwd_workspace_bytes(B, H, N), dtype=torch.uint8, device=dev)
+        bufs.append((q, k, v, g, o, lse, ws))
+
+    def step(i):
+        q, k, v, g, o, lse, ws = bufs[i % sets]
+        tsd.attn_bwd(q, k, v, o, g, lse, mask="causal", workspace=ws)
+
+    ms, _, _ = time_launches(step, nsteps, warmup)
+    return dict(ms=ms, flops=2.5 * attn_flops(B, H, N, N, d, True))
+
+
 def cpu_baseline(target_s=15.0):
     """The CPU oracle on whole heads of the benchmark workload (same seeded
     inputs), as many heads as fit in about target_s seconds."""
@@ -218,7 +243,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", action="store_true",
-                    help="also time the padding, multi-head and 32K workloads and the grouped-heads/log-sum-exp variant")
+                    help="also time the padding, multi-head and 32K workloads, the grouped-heads/log-sum-exp "
+                         "variant and the backward pass")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -299,6 +325,9 @@ def main():
         rg = bench_grouped_lse(dev, args.steps, max(200, args.warmup // 4))
         extra["C3_gqa_h16_kv4_causal_padding_lse"] = {"ms": round(rg["ms"], 5),
                                                      "tflops": round(rg["flops"] / rg["ms"] / 1e9, 2)}
+        rb = bench_backward(dev, max(20, args.steps // 5), 20)
+        extra["C3_backward_causal_b4h16n4096d128"] = {"ms": round(rb["ms"], 4),
+                                                      "tflops": round(rb["flops"] / rb["ms"] / 1e9, 2)}
         out["extra"] = extra
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()

@@ -127,6 +127,39 @@ TSD_API attn_status_t attn_fwd_ex(const void *Q, const void *K, const void *V, i
                           int32_t in_dtype, int32_t out_dtype, void *stream);
 
 /*
+ * attn_bwd -- gradients of attn_fwd_ex's O with respect to Q, K and V.
+ * The pages give no backward algorithm; this is the chain rule through
+ * the forward stages ("04. Self-Attention", section 四), the weights
+ * recomputed from the forward's log-sum-exp:
+ *   P_ij = exp(scale q_i.k_j - lse_i) (0 where masked), dV_j = sum_i P_ij dO_i,
+ *   dS_ij = P_ij (dO_i.v_j - dO_i.O_i), dQ_i = scale sum_j dS_ij k_j,
+ *   dK_j = scale sum_i dS_ij q_i (grouped K/V heads: summed over the group).
+ *
+ *   Q, O, dO   [batch, heads, seq_q, head_dim]     bf16
+ *   K, V       [batch, kv_heads, seq_k, head_dim]  bf16
+ *   lse        [batch, heads, seq_q] float32, as written by attn_fwd_ex for
+ *              the same inputs, mask and scale
+ *   mask_kind, valid_lens, scale, kv_heads: as for attn_fwd_ex
+ *   dQ         [batch, heads, seq_q, head_dim]     bf16, written
+ *   dK, dV     [batch, kv_heads, seq_k, head_dim]  bf16, written
+ *   workspace  device scratch of attn_bwd_workspace_bytes(batch, heads,
+ *              seq_q) bytes, 256-byte aligned (holds dO_i . O_i per row)
+ *
+ * Outputs and workspace must not overlap inputs or each other. Supported
+ * set: bf16, head_dim 64 or 128 (else ATTN_EUNSUPPORTED); the causal masks
+ * need seq_q == seq_k. P and dS are rounded to bf16 for the matrix
+ * products, accumulation is float32.
+ */
+TSD_API attn_status_t attn_bwd(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                       const float *lse, int32_t mask_kind, const int32_t *valid_lens, float scale, void *dQ,
+                       void *dK, void *dV, int32_t batch, int32_t heads, int32_t kv_heads, int32_t seq_q,
+                       int32_t seq_k, int32_t head_dim, int32_t dtype, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* attn_bwd_workspace_bytes -- workspace attn_bwd needs (0 for bad sizes). */
+TSD_API size_t attn_bwd_workspace_bytes(int32_t batch, int32_t heads, int32_t seq_q);
+
+/*
  * mha_workspace_bytes -- device workspace mha_fwd needs for these sizes:
  * Q, K, V split into heads ([3, batch, h, seq, d_model/h]) plus the
  * concatenated head outputs ([batch, seq, d_model]), in bf16. Returns 0

@@ -17,7 +17,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["attn_fwd", "mha_fwd", "mha_workspace_bytes", "library_path", "load_library", "AttnError"]
+__all__ = ["attn_fwd", "attn_bwd", "mha_fwd", "mha_workspace_bytes", "library_path", "load_library", "AttnError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtsd_attn.so")
@@ -26,8 +26,8 @@ ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 MASK_KINDS = {"none": 0, "causal": 1, "padding": 2, "causal_padding": 3}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
-EXPORTS = ("attn_fwd", "attn_fwd_ex", "mha_workspace_bytes", "mha_fwd", "attn_clock_probe", "attn_status_string",
-           "attn_last_error")
+EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_bwd_workspace_bytes", "mha_workspace_bytes", "mha_fwd",
+           "attn_clock_probe", "attn_status_string", "attn_last_error")
 
 _lib = None
 
@@ -54,6 +54,11 @@ def load_library():
     lib.attn_fwd.restype = ctypes.c_int
     lib.attn_fwd_ex.argtypes = [P, P, P, I32, P, ctypes.c_float, P, P, I32, I32, I32, I32, I32, I32, I32, I32, P]
     lib.attn_fwd_ex.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [P, P, P, P, P, P, I32, P, ctypes.c_float, P, P, P, I32, I32, I32, I32, I32, I32, I32,
+                             P, ctypes.c_size_t, P]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd_workspace_bytes.argtypes = [I32, I32, I32]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.mha_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.mha_workspace_bytes.restype = ctypes.c_size_t
     lib.mha_fwd.argtypes = [P, P, P, I32, P, I32, I32, I32, I32, P, ctypes.c_size_t, P]
@@ -157,6 +162,47 @@ def attn_fwd(q, k, v, mask: str = "none", valid_lens=None, scale: float | None =
                          B, H, Hkv, Nq, Nk, d, _dtype_code(q), _dtype_code(out), _stream_ptr(q.device))
     _raise_for(lib, st, "attn_fwd")
     return (out, lse) if lse is not None else out
+
+
+def attn_bwd(q, k, v, o, do, lse, mask: str = "none", valid_lens=None, scale: float | None = None, workspace=None):
+    """Gradients (dq, dk, dv) of attn_fwd's output with respect to q, k and v, given the output gradient
+    ``do``, the forward's output ``o`` and its log-sum-exp ``lse`` (from attn_fwd(..., return_lse=True)
+    with the same inputs, mask and scale). bf16, head_dim 64 or 128; k and v may have H_kv heads.
+    Enqueued on the current stream."""
+    import torch
+
+    lib = load_library()
+    if mask not in MASK_KINDS:
+        raise ValueError("mask must be one of %s" % sorted(MASK_KINDS))
+    _check_gpu(q, k, v, o, do, lse, valid_lens, workspace)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != (B, Hkv, Nk, d):
+        raise ValueError("k and v must be [B, H_kv, Nk, d] matching q")
+    if tuple(o.shape) != tuple(q.shape) or tuple(do.shape) != tuple(q.shape):
+        raise ValueError("o and do must have q's shape")
+    if tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 [B, H, Nq] tensor")
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("the K/V head count must divide the query head count")
+    uses_lens = mask in ("padding", "causal_padding")
+    if uses_lens and (valid_lens is None or valid_lens.dtype != torch.int32 or tuple(valid_lens.shape) != (B,)):
+        raise ValueError("%s mask needs valid_lens: int32 GPU tensor of shape [B]" % mask)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = int(lib.attn_bwd_workspace_bytes(B, H, Nq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    P = ctypes.c_void_p
+    st = lib.attn_bwd(P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()), P(o.data_ptr()), P(do.data_ptr()),
+                      P(lse.data_ptr()), MASK_KINDS[mask], P(valid_lens.data_ptr() if uses_lens else 0),
+                      ctypes.c_float(scale), P(dq.data_ptr()), P(dk.data_ptr()), P(dv.data_ptr()), B, H, Hkv, Nq,
+                      Nk, d, _dtype_code(q), P(workspace.data_ptr()),
+                      ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream_ptr(q.device))
+    _raise_for(lib, st, "attn_bwd")
+    return dq, dk, dv
 
 
 def mha_workspace_bytes(batch: int, seq: int, d_model: int, h: int, dtype=None) -> int:

@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtsd_attn.so")
-SOURCES = ["attn_fwd_bf16.hip", "attn_fwd_f32.hip", "gemm_bf16.hip", "clock_probe.hip", "capi.hip"]
+SOURCES = ["attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "attn_fwd_f32.hip", "gemm_bf16.hip", "clock_probe.hip", "capi.hip"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,390 @@
+// Scaled dot-product attention backward, bf16 inputs, gfx950 MFMA.
+//
+// The gradients of O = softmax(Q K^T * scale + M) V with respect to Q, K and V, given dO, the forward's
+// output O and its per-row log-sum-exp lse. The pages motivate gradients ("04. Self-Attention", section
+// 四 stage 2) but give no backward algorithm; this is the chain rule through the forward stages, with the
+// weights recomputed from lse instead of stored:
+//   P_ij  = exp(scale * q_i . k_j - lse_i)   (0 where the mask hides j from i)
+//   dV_j  = sum_i P_ij dO_i
+//   dP_ij = dO_i . v_j
+//   dS_ij = P_ij (dP_ij - D_i),  D_i = dO_i . O_i  (= sum_j P_ij dP_ij: the softmax Jacobian's row term)
+//   dQ_i  = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i
+// Three kernels:
+//   attn_bwd_delta: D_i for every query row (float32, in the caller's workspace);
+//   attn_bwd_dkdv:  one workgroup per 128 keys of one (batch, K/V head), 32 keys per wave; it walks the
+//                   query tiles (of every query head of the K/V head's group) and keeps dK and dV in
+//                   registers: S = Q K^T and dP = dO V^T with one key per lane, then dV^T += dO^T P and
+//                   dK^T += Q^T dS with P and dS taken straight from those accumulators;
+//   attn_bwd_dq:    one workgroup per 128 query rows of one (batch, head), 32 rows per wave; it walks the
+//                   key tiles like the forward: S^T = K Q^T and dP^T = V dO^T with one query per lane, then
+//                   dQ^T += K^T dS^T.
+// Both main kernels use the forward's tile layout and contractions (attn_tiles.h); Q/dO (dK/dV kernel) or
+// K/V (dQ kernel) tiles of 64 rows go to LDS by DMA, double buffered. P and dS are rounded to bf16 for the
+// MFMAs, products accumulate in float32.
+#include "attn_tiles.h"
+#include "device_common.h"
+#include "kernels.h"
+
+#include <math.h>
+
+#include <type_traits>
+
+namespace tsd {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// D_i = dO_i . O_i for `rows` rows of D bf16 values; D/8 consecutive lanes per row, 16 bytes each.
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const uint16_t *__restrict__ O,
+                                                             const uint16_t *__restrict__ dO,
+                                                             float *__restrict__ delta, long long rows)
+{
+    constexpr int LPR = D / 8;
+    const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long row = t / LPR;
+    const int part = (int)(t % LPR);
+    float acc = 0.f;
+    if (row < rows) {
+        const u32x4 o = *(const u32x4 *)(O + row * D + part * 8);
+        const u32x4 g = *(const u32x4 *)(dO + row * D + part * 8);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc += bf16_lo(o[w]) * bf16_lo(g[w]) + bf16_hi(o[w]) * bf16_hi(g[w]);
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
+    if (row < rows && part == 0) delta[row] = acc;
+}
+
+// Rows of the wave's 32-row block (this lane's row, 8 bf16 of each 16-wide k-step) as B operands; rows at
+// or past n read as zero.
+template <int D>
+__device__ __forceinline__ void load_rows_b(const uint16_t *__restrict__ base, int row, int n, int hf,
+                                            bf16x8 (&reg)[1][D / 16])
+{
+    const bool ok = row < n;
+    const uint16_t *p = base + (size_t)(ok ? row : 0) * D + hf * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const u32x4 v = ok ? *(const u32x4 *)(p + ks * 16) : u32x4{0u, 0u, 0u, 0u};
+        reg[0][ks] = __builtin_bit_cast(bf16x8, v);
+    }
+}
+
+// P or dS of one 64 x 32 accumulator pair packed as the four 16-row B operands of accumulate_pv.
+__device__ __forceinline__ void pack_operands(const f32x16 (&x)[2], bf16x8 (&pb)[1][4])
+{
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int jb = c >> 1, r0 = (c & 1) * 8;
+        u32x4 w;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = pack_bf16x2(x[jb][r0 + 2 * u], x[jb][r0 + 2 * u + 1]);
+        pb[0][c] = __builtin_bit_cast(bf16x8, w);
+    }
+}
+
+// DMA of one 64-row tile (rows r0 .. r0 + 63 of a [n, D] bf16 matrix) into LDS at slot_off, rows at or past
+// n replaced by row n - 1 (their results are masked). voff/drow: this lane's chunk offsets within a tile.
+template <int D, int CH>
+__device__ __forceinline__ void issue_tile(uint32_t lds0, const uint16_t *src, int r0, int n, uint32_t slot_off,
+                                           const uint32_t (&voff)[CH], const int (&drow)[CH], int wave)
+{
+    constexpr int WAVES = 4;
+    const uint16_t *base = src + (size_t)r0 * D;
+    const bool tail = r0 + kBlockN > n;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        uint32_t off = voff[j];
+        if (tail) {
+            const int r = min(drow[j], n - 1 - r0);
+            off = off - (uint32_t)(drow[j] - r) * (D * 2);
+        }
+        lds_dma16(__builtin_amdgcn_readfirstlane(lds0 + slot_off + (j * WAVES + wave) * 1024), base, off);
+    }
+}
+
+template <int D>
+struct TileDma {
+    static constexpr int CPR = D / 8;
+    static constexpr int CH = kBlockN * CPR / (4 * 64);
+    uint32_t voff[CH];
+    int drow[CH];
+    __device__ TileDma(int wave, int lane)
+    {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int c = (j * 4 + wave) * 64 + lane;
+            const int r = c / CPR, x = c % CPR;
+            drow[j] = r;
+            voff[j] = (uint32_t)(r * D + ((x ^ swz<D>(r)) << 3)) * 2;
+        }
+    }
+};
+
+// dK and dV for 128 keys of one (batch, K/V head).
+template <int D, int MASK>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    const uint16_t *__restrict__ dO, const float *__restrict__ lse, const float *__restrict__ delta,
+    const int32_t *__restrict__ valid_lens, float c_log2, float scale, uint16_t *__restrict__ dK,
+    uint16_t *__restrict__ dV, int H, int Hkv, int group, int Nq, int Nk, int num_kblocks)
+{
+    constexpr int DB = D / 32, TILE_B = kBlockN * D * 2;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_B];  // Q slots 0, 1; dO slots 0, 1
+    constexpr int QS0 = 0, QS1 = TILE_B, GS0 = 2 * TILE_B, GS1 = 3 * TILE_B;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int kbk = blockIdx.x % num_kblocks, bk = blockIdx.x / num_kblocks;
+    const int b = bk / Hkv, hk = bk % Hkv;
+    const int kwg0 = kbk * 128, key = kwg0 + wave * 32 + l32;
+
+    int kv_len = Nk;
+    if (mask_padding(MASK)) {
+        const int L = valid_lens[b];
+        kv_len = L < 0 ? 0 : (L > Nk ? Nk : L);
+    }
+    bf16x8 kreg[1][D / 16], vreg[1][D / 16];
+    load_rows_b<D>(K + (size_t)bk * Nk * D, key, Nk, hf, kreg);
+    load_rows_b<D>(V + (size_t)bk * Nk * D, key, Nk, hf, vreg);
+
+    f32x16 dk[1][DB], dv[1][DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dk[0][i][r] = dv[0][i][r] = 0.f;
+
+    const TileAddrs<D> ad = tile_addrs<D>(lane);
+    const TileDma<D> dma(wave, lane);
+    const uint32_t lds0 = lds_addr(smem);
+    // query tiles that can see one of these keys: causal rows below the first key see none of them
+    const int nqt = (Nq + kBlockN - 1) / kBlockN;
+    const int t0 = mask_causal(MASK) ? min(kwg0 / kBlockN, nqt) : 0;
+    const int per_head = kwg0 < kv_len ? nqt - t0 : 0;
+    const int n = group * per_head;
+    const int h0 = hk * group;
+
+    auto head_ptrs = [&](int u, const uint16_t *&qh, const uint16_t *&gh, int &bh, int &t) {
+        const int h = h0 + u / per_head;
+        t = t0 + u % per_head;
+        bh = b * H + h;
+        qh = Q + (size_t)bh * Nq * D;
+        gh = dO + (size_t)bh * Nq * D;
+    };
+    auto issue = [&](int u, uint32_t qs, uint32_t gs) {
+        const uint16_t *qh, *gh;
+        int bh, t;
+        head_ptrs(u, qh, gh, bh, t);
+        issue_tile<D, TileDma<D>::CH>(lds0, qh, t * kBlockN, Nq, qs, dma.voff, dma.drow, wave);
+        issue_tile<D, TileDma<D>::CH>(lds0, gh, t * kBlockN, Nq, gs, dma.voff, dma.drow, wave);
+    };
+    if (n > 0) issue(0, QS0, GS0);
+    wait_vmcnt0();
+    __syncthreads();
+    auto step = [&](int u, auto parity) {
+        constexpr int P = decltype(parity)::value;
+        constexpr int QS = P ? QS1 : QS0, GS = P ? GS1 : GS0;
+        if (u + 1 < n) issue(u + 1, P ? QS0 : QS1, P ? GS0 : GS1);
+        const uint16_t *qh, *gh;
+        int bh, t;
+        head_ptrs(u, qh, gh, bh, t);
+        // S = Q K^T and dP = dO V^T: one key per lane, rows = queries jb*32 + (r/4)*8 + hf*4 + r%4
+        f32x16 s[1][2], dp[1][2];
+        scores<D, 1, QS, false>(smem, ad, kreg, s);
+        scores<D, 1, GS, false>(smem, ad, vreg, dp);
+        const float *lh = lse + (size_t)bh * Nq, *dh = delta + (size_t)bh * Nq;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int q4 = t * kBlockN + jb * 32 + g * 8 + hf * 4;
+                float l4[4], d4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int qc = min(q4 + e, Nq - 1);
+                    l4[e] = lh[qc];
+                    d4[e] = dh[qc];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int q = q4 + e, r = g * 4 + e;
+                    const bool vis = q < Nq && key < kv_len && (!mask_causal(MASK) || key <= q);
+                    const float p = vis ? fast_exp2(fmaf(s[0][jb][r], c_log2, -l4[e] * kLog2e)) : 0.f;
+                    s[0][jb][r] = p;
+                    dp[0][jb][r] = p * (dp[0][jb][r] - d4[e]);
+                }
+            }
+        bf16x8 pb[1][4], sb[1][4];
+        pack_operands(s[0], pb);
+        pack_operands(dp[0], sb);
+        accumulate_pv<D, 1, GS, false>(smem, ad, pb, dv);  // dV^T += dO^T P
+        accumulate_pv<D, 1, QS, false>(smem, ad, sb, dk);  // dK^T += Q^T dS
+        wait_vmcnt0();
+        __syncthreads();
+    };
+    for (int u = 0; u < n; u += 2) {
+        step(u, std::integral_constant<int, 0>());
+        if (u + 1 < n) step(u + 1, std::integral_constant<int, 1>());
+    }
+    // dV = acc, dK = scale * acc, rows = keys of this (batch, K/V head)
+    store_rows<D, false, kOutBHND, false>(dv[0], 1.f, key, bk, Hkv, Nk, b, hf, dV);
+    store_rows<D, false, kOutBHND, false>(dk[0], 1.f / scale, key, bk, Hkv, Nk, b, hf, dK);
+}
+
+// dQ for 128 query rows of one (batch, head).
+template <int D, int MASK>
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    const uint16_t *__restrict__ dO, const float *__restrict__ lse, const float *__restrict__ delta,
+    const int32_t *__restrict__ valid_lens, float c_log2, float scale, uint16_t *__restrict__ dQ, int H,
+    int Hkv, int group, int Nq, int Nk, int num_qtiles, int BH)
+{
+    constexpr int DB = D / 32, TILE_B = kBlockN * D * 2;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_B];  // K slots 0, 1; V slots 0, 1
+    constexpr int KS0 = 0, KS1 = TILE_B, VS0 = 2 * TILE_B, VS1 = 3 * TILE_B;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int bh = blockIdx.x % BH;
+    int qt = blockIdx.x / BH;
+    if (mask_causal(MASK)) qt = num_qtiles - 1 - qt;  // longest first
+    const int b = bh / H, h = bh % H;
+    const size_t kvbh = (size_t)b * Hkv + h / group;
+    const int q0 = qt * 128, qrow = q0 + wave * 32 + l32;
+
+    int kv_len = Nk;
+    if (mask_padding(MASK)) {
+        const int L = valid_lens[b];
+        kv_len = L < 0 ? 0 : (L > Nk ? Nk : L);
+    }
+    int kv_end = kv_len;
+    if (mask_causal(MASK)) kv_end = min(kv_len, q0 + 128);
+    const int ntiles = (kv_end + kBlockN - 1) / kBlockN;
+
+    bf16x8 qreg[1][D / 16], greg[1][D / 16];
+    load_rows_b<D>(Q + (size_t)bh * Nq * D, qrow, Nq, hf, qreg);
+    load_rows_b<D>(dO + (size_t)bh * Nq * D, qrow, Nq, hf, greg);
+    const bool qok = qrow < Nq;
+    const float l_row = qok ? lse[(size_t)bh * Nq + qrow] : 0.f;
+    // a row without a visible key (lse = -inf) has no weights and dQ = 0: subtract 0 instead, so that its
+    // masked scores give exp2(-inf) = 0 rather than -inf - (-inf)
+    const float lse2 = isinf(l_row) ? 0.f : l_row * kLog2e;
+    const float d_row = qok ? delta[(size_t)bh * Nq + qrow] : 0.f;
+
+    f32x16 dq[1][DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dq[0][i][r] = 0.f;
+
+    const TileAddrs<D> ad = tile_addrs<D>(lane);
+    const TileDma<D> dma(wave, lane);
+    const uint32_t lds0 = lds_addr(smem);
+    const uint16_t *Kh = K + kvbh * Nk * D, *Vh = V + kvbh * Nk * D;
+    if (ntiles > 0) {
+        issue_tile<D, TileDma<D>::CH>(lds0, Kh, 0, kv_end, KS0, dma.voff, dma.drow, wave);
+        issue_tile<D, TileDma<D>::CH>(lds0, Vh, 0, kv_end, VS0, dma.voff, dma.drow, wave);
+    }
+    wait_vmcnt0();
+    __syncthreads();
+    auto step = [&](int t, auto parity) {
+        constexpr int P = decltype(parity)::value;
+        constexpr int KS = P ? KS1 : KS0, VS = P ? VS1 : VS0;
+        if (t + 1 < ntiles) {
+            issue_tile<D, TileDma<D>::CH>(lds0, Kh, (t + 1) * kBlockN, kv_end, P ? KS0 : KS1, dma.voff, dma.drow,
+                                          wave);
+            issue_tile<D, TileDma<D>::CH>(lds0, Vh, (t + 1) * kBlockN, kv_end, P ? VS0 : VS1, dma.voff, dma.drow,
+                                          wave);
+        }
+        // S^T = K Q^T and dP^T = V dO^T: one query per lane, rows = keys
+        f32x16 s[1][2], dp[1][2];
+        scores<D, 1, KS, false>(smem, ad, qreg, s);
+        scores<D, 1, VS, false>(smem, ad, greg, dp);
+        mask_scores<MASK>(s[0], t * kBlockN, kv_len, qrow, hf);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(fmaf(s[0][jb][r], c_log2, -lse2));
+                dp[0][jb][r] = p * (dp[0][jb][r] - d_row);
+            }
+        bf16x8 sb[1][4];
+        pack_operands(dp[0], sb);
+        accumulate_pv<D, 1, KS, false>(smem, ad, sb, dq);  // dQ^T += K^T dS^T
+        wait_vmcnt0();
+        __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, std::integral_constant<int, 0>());
+        if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>());
+    }
+    store_rows<D, false, kOutBHND, false>(dq[0], 1.f / scale, qrow, bh, H, Nq, b, hf, dQ);
+}
+
+template <int D, int MASK>
+hipError_t launch_bwd(const void *Q, const void *K, const void *V, const void *O, const void *dO, const float *lse,
+                      const int32_t *vl, float scale, void *dQ, void *dK, void *dV, int B, int H, int Hkv, int Nq,
+                      int Nk, float *delta, hipStream_t s)
+{
+    const long long rows = (long long)B * H * Nq;
+    const int group = H / Hkv;
+    const float c_log2 = scale * kLog2e;
+    if (rows > 0) {
+        const long long threads = rows * (D / 8);
+        hipLaunchKernelGGL((attn_bwd_delta_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                           (const uint16_t *)O, (const uint16_t *)dO, delta, rows);
+    }
+    const int num_kblocks = (Nk + 127) / 128;
+    const long long g1 = (long long)num_kblocks * B * Hkv;
+    if (g1 > 0)
+        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, MASK>), dim3((unsigned)g1), dim3(256), 0, s, (const uint16_t *)Q,
+                           (const uint16_t *)K, (const uint16_t *)V, (const uint16_t *)dO, lse, delta, vl, c_log2,
+                           scale, (uint16_t *)dK, (uint16_t *)dV, H, Hkv, group, Nq, Nk, num_kblocks);
+    const int num_qtiles = (Nq + 127) / 128;
+    const long long g2 = (long long)num_qtiles * B * H;
+    if (g2 > 0)
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<D, MASK>), dim3((unsigned)g2), dim3(256), 0, s, (const uint16_t *)Q,
+                           (const uint16_t *)K, (const uint16_t *)V, (const uint16_t *)dO, lse, delta, vl, c_log2,
+                           scale, (uint16_t *)dQ, H, Hkv, group, Nq, Nk, num_qtiles, B * H);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch_bwd(const void *Q, const void *K, const void *V, const void *O, const void *dO, const float *lse,
+                        int mask, const int32_t *vl, float scale, void *dQ, void *dK, void *dV, int B, int H, int Hkv,
+                        int Nq, int Nk, float *delta, hipStream_t s)
+{
+    switch (mask) {
+    case kMaskCausal:
+        return launch_bwd<D, kMaskCausal>(Q, K, V, O, dO, lse, vl, scale, dQ, dK, dV, B, H, Hkv, Nq, Nk, delta, s);
+    case kMaskPadding:
+        return launch_bwd<D, kMaskPadding>(Q, K, V, O, dO, lse, vl, scale, dQ, dK, dV, B, H, Hkv, Nq, Nk, delta, s);
+    case kMaskCausalPadding:
+        return launch_bwd<D, kMaskCausalPadding>(Q, K, V, O, dO, lse, vl, scale, dQ, dK, dV, B, H, Hkv, Nq, Nk, delta,
+                                                 s);
+    default:
+        return launch_bwd<D, kMaskNone>(Q, K, V, O, dO, lse, vl, scale, dQ, dK, dV, B, H, Hkv, Nq, Nk, delta, s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                                const float *lse, int mask, const int32_t *valid_lens, float scale, void *dQ, void *dK,
+                                void *dV, int B, int H, int Hkv, int Nq, int Nk, int D, float *delta,
+                                hipStream_t stream)
+{
+    if (D == 128)
+        return dispatch_bwd<128>(Q, K, V, O, dO, lse, mask, valid_lens, scale, dQ, dK, dV, B, H, Hkv, Nq, Nk, delta,
+                                 stream);
+    if (D == 64)
+        return dispatch_bwd<64>(Q, K, V, O, dO, lse, mask, valid_lens, scale, dQ, dK, dV, B, H, Hkv, Nq, Nk, delta,
+                                stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace tsd

@@ -114,6 +114,72 @@ attn_status_t attn_fwd(const void *Q, const void *K, const void *V, int32_t mask
                        seq_k, head_dim, in_dtype, out_dtype, stream);
 }
 
+size_t attn_bwd_workspace_bytes(int32_t batch, int32_t heads, int32_t seq_q)
+{
+    if (batch < 0 || heads < 0 || seq_q < 0) return 0;
+    const size_t n = (size_t)batch * heads * seq_q * sizeof(float);
+    return (n + 255) / 256 * 256;
+}
+
+attn_status_t attn_bwd(const void *Q, const void *K, const void *V, const void *O, const void *dO, const float *lse,
+                       int32_t mask_kind, const int32_t *valid_lens, float scale, void *dQ, void *dK, void *dV,
+                       int32_t batch, int32_t heads, int32_t kv_heads, int32_t seq_q, int32_t seq_k,
+                       int32_t head_dim, int32_t dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    g_last_error[0] = '\0';
+    if (batch < 0 || heads < 0 || seq_q < 0 || seq_k < 0 || head_dim <= 0)
+        return fail(ATTN_EINVAL, "attn_bwd: negative size or head_dim <= 0 (batch=%d heads=%d seq_q=%d seq_k=%d "
+                                 "head_dim=%d)", batch, heads, seq_q, seq_k, head_dim);
+    if (kv_heads <= 0 || (heads > 0 && heads % kv_heads != 0))
+        return fail(ATTN_EINVAL, "attn_bwd: kv_heads must be positive and divide heads (heads=%d kv_heads=%d)", heads,
+                    kv_heads);
+    if (mask_kind < ATTN_MASK_NONE || mask_kind > ATTN_MASK_CAUSAL_PADDING)
+        return fail(ATTN_EINVAL, "attn_bwd: unknown mask_kind %d", mask_kind);
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_EINVAL, "attn_bwd: unknown dtype %d", dtype);
+    if (!isfinite(scale)) return fail(ATTN_EINVAL, "attn_bwd: scale is not finite");
+    if (scale < 0.f) return fail(ATTN_EUNSUPPORTED, "attn_bwd: negative scale");
+    if (dtype != ATTN_BF16) return fail(ATTN_EUNSUPPORTED, "attn_bwd: only bf16 is supported");
+    if (head_dim != 64 && head_dim != 128)
+        return fail(ATTN_EUNSUPPORTED, "attn_bwd: bf16 supports head_dim 64 or 128, got %d", head_dim);
+    const bool causal = mask_kind == ATTN_MASK_CAUSAL || mask_kind == ATTN_MASK_CAUSAL_PADDING;
+    const bool padding = mask_kind == ATTN_MASK_PADDING || mask_kind == ATTN_MASK_CAUSAL_PADDING;
+    if (causal && seq_q != seq_k)
+        return fail(ATTN_EUNSUPPORTED, "attn_bwd: causal mask needs seq_q == seq_k (%d != %d)", seq_q, seq_k);
+    const long long bh = (long long)batch * heads, bhk = (long long)batch * kv_heads;
+    if (bh > kI32Max || bhk > kI32Max) return fail(ATTN_EINVAL, "attn_bwd: batch*heads too large");
+    const size_t nq = (size_t)bh * seq_q * head_dim * 2, nk = (size_t)bhk * seq_k * head_dim * 2;
+    const size_t nl = (size_t)bh * seq_q * sizeof(float);
+    if (nq == 0 && nk == 0) return ATTN_OK;
+    if ((nq && (!Q || !O || !dO || !lse || !dQ)) || (nk && (!K || !V || !dK || !dV)))
+        return fail(ATTN_EINVAL, "attn_bwd: null pointer");
+    if (padding && !valid_lens) return fail(ATTN_EINVAL, "attn_bwd: padding mask needs valid_lens");
+    const size_t need = attn_bwd_workspace_bytes(batch, heads, seq_q);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(ATTN_EINVAL, "attn_bwd: workspace of %zu bytes, need %zu", workspace_bytes, need);
+    const void *a16[] = {Q, K, V, O, dO, dQ, dK, dV};
+    for (const void *p : a16)
+        if (p && !aligned(p, 16)) return fail(ATTN_EINVAL, "attn_bwd: tensors must be 16-byte aligned");
+    if ((lse && !aligned(lse, 4)) || (valid_lens && padding && !aligned(valid_lens, 4)) ||
+        (workspace && !aligned(workspace, 256)))
+        return fail(ATTN_EINVAL, "attn_bwd: lse, valid_lens 4-byte aligned, workspace 256-byte aligned");
+    const void *ins[] = {Q, K, V, O, dO, lse};
+    const size_t in_n[] = {nq, nk, nk, nq, nq, nl};
+    const void *outs[] = {dQ, dK, dV, workspace};
+    const size_t out_n[] = {nq, nk, nk, need};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlaps(outs[i], out_n[i], ins[j], in_n[j]))
+                return fail(ATTN_EINVAL, "attn_bwd: an output or the workspace overlaps an input");
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], out_n[i], outs[j], out_n[j]))
+                return fail(ATTN_EINVAL, "attn_bwd: outputs overlap");
+    }
+    const hipError_t e = tsd::launch_attn_bwd_bf16(Q, K, V, O, dO, lse, mask_kind, valid_lens, scale, dQ, dK, dV, batch,
+                                                   heads, kv_heads, seq_q, seq_k, head_dim, (float *)workspace,
+                                                   (hipStream_t)stream);
+    return from_hip(e, "attn_bwd launch");
+}
+
 static attn_status_t mha_check(int32_t batch, int32_t seq, int32_t d_model, int32_t h, int32_t dtype)
 {
     if (batch < 0 || seq < 0 || d_model <= 0 || h <= 0)

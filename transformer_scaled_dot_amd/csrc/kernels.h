@@ -35,6 +35,13 @@ hipError_t launch_attn_f32(const float *Q, const float *K, const float *V, int m
                            float scale, float *O, int B, int H, int Nq, int Nk, int D, AttnHeads heads,
                            hipStream_t stream);
 
+// bf16 attention backward, head_dim 64 or 128: dQ [B,H,Nq,D], dK and dV [B,Hkv,Nk,D] (bf16) from Q, K, V,
+// the forward's O and per-row log-sum-exp lse ([B,H,Nq] float32) and dO; delta: [B,H,Nq] float32 scratch.
+hipError_t launch_attn_bwd_bf16(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                                const float *lse, int mask, const int32_t *valid_lens, float scale, void *dQ, void *dK,
+                                void *dV, int B, int H, int Hkv, int Nq, int Nk, int D, float *delta,
+                                hipStream_t stream);
+
 // C = A[M,K] * B[K,N] in bf16 with f32 accumulation, bf16 output.
 // Plain epilogue: C row-major [M,N].
 hipError_t launch_gemm_bf16(const void *A, const void *Bm, void *C, int M, int N, int K, hipStream_t stream);
