@@ -143,7 +143,8 @@ TSD_API attn_status_t attn_fwd_ex(const void *Q, const void *K, const void *V, i
  *   dQ         [batch, heads, seq_q, head_dim]     bf16, written
  *   dK, dV     [batch, kv_heads, seq_k, head_dim]  bf16, written
  *   workspace  device scratch of attn_bwd_workspace_bytes(batch, heads,
- *              seq_q) bytes, 256-byte aligned (holds dO_i . O_i per row)
+ *              seq_q) bytes, 256-byte aligned (holds, per query row, dO_i . O_i
+ *              and lse_i in base 2, each head's rows padded to a multiple of 64)
  *
  * Outputs and workspace must not overlap inputs or each other. Supported
  * set: bf16, head_dim 64 or 128 (else ATTN_EUNSUPPORTED); the causal masks

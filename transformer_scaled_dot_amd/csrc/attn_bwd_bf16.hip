@@ -10,7 +10,9 @@
 //   dS_ij = P_ij (dP_ij - D_i),  D_i = dO_i . O_i  (= sum_j P_ij dP_ij: the softmax Jacobian's row term)
 //   dQ_i  = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i
 // Three kernels:
-//   attn_bwd_delta: D_i for every query row (float32, in the caller's workspace);
+//   attn_bwd_delta: per query row, D_i and lse_i * log2(e) (0 for a row without a visible key) into the
+//                   caller's workspace, each head's rows padded to a multiple of 64 with zeros, so that
+//                   the other kernels fetch whole 64-row tiles of them;
 //   attn_bwd_dkdv:  one workgroup per 128 keys of one (batch, K/V head), 32 keys per wave; it walks the
 //                   query tiles (of every query head of the K/V head's group) and keeps dK and dV in
 //                   registers: S = Q K^T and dP = dO V^T with one key per lane, then dV^T += dO^T P and
@@ -37,18 +39,25 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
-// D_i = dO_i . O_i for `rows` rows of D bf16 values; D/8 consecutive lanes per row, 16 bytes each.
+// Per query row (BH heads of Nq rows, padded to Nq_pad): D_i = dO_i . O_i and lse_i * log2(e) (0 where
+// lse_i = -inf), 0 for padding rows. D/8 consecutive lanes per row, 16 bytes each.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const uint16_t *__restrict__ O,
                                                              const uint16_t *__restrict__ dO,
-                                                             float *__restrict__ delta, long long rows)
+                                                             const float *__restrict__ lse, float *__restrict__ lse2,
+                                                             float *__restrict__ delta, long long BH, int Nq,
+                                                             int Nq_pad)
 {
     constexpr int LPR = D / 8;
     const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-    const long long row = t / LPR;
+    const long long prow = t / LPR;  // padded row index
     const int part = (int)(t % LPR);
+    const long long bh = prow / Nq_pad;
+    const int i = (int)(prow % Nq_pad);
+    const bool real = bh < BH && i < Nq;
+    const long long row = bh * Nq + i;
     float acc = 0.f;
-    if (row < rows) {
+    if (real) {
         const u32x4 o = *(const u32x4 *)(O + row * D + part * 8);
         const u32x4 g = *(const u32x4 *)(dO + row * D + part * 8);
 #pragma unroll
@@ -56,7 +65,11 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const uint16_t *__r
     }
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
-    if (row < rows && part == 0) delta[row] = acc;
+    if (bh < BH && part == 0) {
+        delta[prow] = acc;
+        const float l = real ? lse[row] : 0.f;
+        lse2[prow] = isinf(l) ? 0.f : l * kLog2e;
+    }
 }
 
 // Rows of the wave's 32-row block (this lane's row, 8 bf16 of each 16-wide k-step) as B operands; rows at
@@ -129,13 +142,14 @@ struct TileDma {
 template <int D, int MASK>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    const uint16_t *__restrict__ dO, const float *__restrict__ lse, const float *__restrict__ delta,
+    const uint16_t *__restrict__ dO, const float *__restrict__ lse2, const float *__restrict__ delta,
     const int32_t *__restrict__ valid_lens, float c_log2, float scale, uint16_t *__restrict__ dK,
-    uint16_t *__restrict__ dV, int H, int Hkv, int group, int Nq, int Nk, int num_kblocks)
+    uint16_t *__restrict__ dV, int H, int Hkv, int group, int Nq, int Nq_pad, int Nk, int num_kblocks)
 {
     constexpr int DB = D / 32, TILE_B = kBlockN * D * 2;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_B];  // Q slots 0, 1; dO slots 0, 1
-    constexpr int QS0 = 0, QS1 = TILE_B, GS0 = 2 * TILE_B, GS1 = 3 * TILE_B;
+    // Q slots 0, 1; dO slots 0, 1; then per slot the tile's 64 values of lse * log2(e) and of D
+    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_B + 2 * 512];
+    constexpr int QS0 = 0, QS1 = TILE_B, GS0 = 2 * TILE_B, GS1 = 3 * TILE_B, LS0 = 4 * TILE_B, LS1 = LS0 + 512;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
@@ -175,20 +189,25 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
         qh = Q + (size_t)bh * Nq * D;
         gh = dO + (size_t)bh * Nq * D;
     };
-    auto issue = [&](int u, uint32_t qs, uint32_t gs) {
+    auto issue = [&](int u, uint32_t qs, uint32_t gs, uint32_t ls) {
         const uint16_t *qh, *gh;
         int bh, t;
         head_ptrs(u, qh, gh, bh, t);
         issue_tile<D, TileDma<D>::CH>(lds0, qh, t * kBlockN, Nq, qs, dma.voff, dma.drow, wave);
         issue_tile<D, TileDma<D>::CH>(lds0, gh, t * kBlockN, Nq, gs, dma.voff, dma.drow, wave);
+        // the tile's 64 padded rows of lse * log2(e) (wave 0) and of D (wave 1), 16 bytes per lane
+        const size_t r0 = (size_t)bh * Nq_pad + (size_t)t * kBlockN;
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        if (wv < 2 && lane < 16)
+            lds_dma16(lds0 + ls + wv * 256, (wv == 0 ? lse2 : delta) + r0, (uint32_t)lane * 16);
     };
-    if (n > 0) issue(0, QS0, GS0);
+    if (n > 0) issue(0, QS0, GS0, LS0);
     wait_vmcnt0();
     __syncthreads();
     auto step = [&](int u, auto parity) {
         constexpr int P = decltype(parity)::value;
-        constexpr int QS = P ? QS1 : QS0, GS = P ? GS1 : GS0;
-        if (u + 1 < n) issue(u + 1, P ? QS0 : QS1, P ? GS0 : GS1);
+        constexpr int QS = P ? QS1 : QS0, GS = P ? GS1 : GS0, LS = P ? LS1 : LS0;
+        if (u + 1 < n) issue(u + 1, P ? QS0 : QS1, P ? GS0 : GS1, P ? LS0 : LS1);
         const uint16_t *qh, *gh;
         int bh, t;
         head_ptrs(u, qh, gh, bh, t);
@@ -196,26 +215,20 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
         f32x16 s[1][2], dp[1][2];
         scores<D, 1, QS, false>(smem, ad, kreg, s);
         scores<D, 1, GS, false>(smem, ad, vreg, dp);
-        const float *lh = lse + (size_t)bh * Nq, *dh = delta + (size_t)bh * Nq;
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int q4 = t * kBlockN + jb * 32 + g * 8 + hf * 4;
-                float l4[4], d4[4];
+                const int qo = jb * 32 + g * 8 + hf * 4;  // offset of the lane's 4 rows in the tile
+                const f32x4 l4 = *(const f32x4 *)(smem + LS + qo * 4);
+                const f32x4 d4 = *(const f32x4 *)(smem + LS + 256 + qo * 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int qc = min(q4 + e, Nq - 1);
-                    l4[e] = lh[qc];
-                    d4[e] = dh[qc];
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int q = q4 + e, r = g * 4 + e;
+                    const int q = t * kBlockN + qo + e, r = g * 4 + e;
                     const bool vis = q < Nq && key < kv_len && (!mask_causal(MASK) || key <= q);
-                    const float p = vis ? fast_exp2(fmaf(s[0][jb][r], c_log2, -l4[e] * kLog2e)) : 0.f;
-                    s[0][jb][r] = p;
-                    dp[0][jb][r] = p * (dp[0][jb][r] - d4[e]);
+                    const float p = fast_exp2(fmaf(s[0][jb][r], c_log2, -l4[e]));
+                    s[0][jb][r] = vis ? p : 0.f;
+                    dp[0][jb][r] = vis ? p * (dp[0][jb][r] - d4[e]) : 0.f;
                 }
             }
         bf16x8 pb[1][4], sb[1][4];
@@ -239,9 +252,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 template <int D, int MASK>
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    const uint16_t *__restrict__ dO, const float *__restrict__ lse, const float *__restrict__ delta,
+    const uint16_t *__restrict__ dO, const float *__restrict__ lse2, const float *__restrict__ delta,
     const int32_t *__restrict__ valid_lens, float c_log2, float scale, uint16_t *__restrict__ dQ, int H,
-    int Hkv, int group, int Nq, int Nk, int num_qtiles, int BH)
+    int Hkv, int group, int Nq, int Nq_pad, int Nk, int num_qtiles, int BH)
 {
     constexpr int DB = D / 32, TILE_B = kBlockN * D * 2;
     __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_B];  // K slots 0, 1; V slots 0, 1
@@ -268,12 +281,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     bf16x8 qreg[1][D / 16], greg[1][D / 16];
     load_rows_b<D>(Q + (size_t)bh * Nq * D, qrow, Nq, hf, qreg);
     load_rows_b<D>(dO + (size_t)bh * Nq * D, qrow, Nq, hf, greg);
-    const bool qok = qrow < Nq;
-    const float l_row = qok ? lse[(size_t)bh * Nq + qrow] : 0.f;
-    // a row without a visible key (lse = -inf) has no weights and dQ = 0: subtract 0 instead, so that its
-    // masked scores give exp2(-inf) = 0 rather than -inf - (-inf)
-    const float lse2 = isinf(l_row) ? 0.f : l_row * kLog2e;
-    const float d_row = qok ? delta[(size_t)bh * Nq + qrow] : 0.f;
+    // (a row without a visible key has lse * log2(e) stored as 0, so that its masked scores give
+    // exp2(-inf) = 0 rather than -inf - (-inf); padding rows hold 0)
+    const float l2_row = lse2[(size_t)bh * Nq_pad + min(qrow, Nq_pad - 1)];
+    const float d_row = delta[(size_t)bh * Nq_pad + min(qrow, Nq_pad - 1)];
 
     f32x16 dq[1][DB];
 #pragma unroll
@@ -309,7 +320,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
         for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(fmaf(s[0][jb][r], c_log2, -lse2));
+                const float p = fast_exp2(fmaf(s[0][jb][r], c_log2, -l2_row));
                 dp[0][jb][r] = p * (dp[0][jb][r] - d_row);
             }
         bf16x8 sb[1][4];
@@ -328,28 +339,31 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 template <int D, int MASK>
 hipError_t launch_bwd(const void *Q, const void *K, const void *V, const void *O, const void *dO, const float *lse,
                       const int32_t *vl, float scale, void *dQ, void *dK, void *dV, int B, int H, int Hkv, int Nq,
-                      int Nk, float *delta, hipStream_t s)
+                      int Nk, float *work, hipStream_t s)
 {
-    const long long rows = (long long)B * H * Nq;
+    const long long BH = (long long)B * H;
+    const int Nq_pad = (Nq + kBlockN - 1) / kBlockN * kBlockN;
+    const long long prows = BH * Nq_pad;
+    float *lse2 = work, *delta = work + prows;
     const int group = H / Hkv;
     const float c_log2 = scale * kLog2e;
-    if (rows > 0) {
-        const long long threads = rows * (D / 8);
+    if (prows > 0) {
+        const long long threads = prows * (D / 8);
         hipLaunchKernelGGL((attn_bwd_delta_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                           (const uint16_t *)O, (const uint16_t *)dO, delta, rows);
+                           (const uint16_t *)O, (const uint16_t *)dO, lse, lse2, delta, BH, Nq, Nq_pad);
     }
     const int num_kblocks = (Nk + 127) / 128;
     const long long g1 = (long long)num_kblocks * B * Hkv;
     if (g1 > 0)
         hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, MASK>), dim3((unsigned)g1), dim3(256), 0, s, (const uint16_t *)Q,
-                           (const uint16_t *)K, (const uint16_t *)V, (const uint16_t *)dO, lse, delta, vl, c_log2,
-                           scale, (uint16_t *)dK, (uint16_t *)dV, H, Hkv, group, Nq, Nk, num_kblocks);
+                           (const uint16_t *)K, (const uint16_t *)V, (const uint16_t *)dO, lse2, delta, vl, c_log2,
+                           scale, (uint16_t *)dK, (uint16_t *)dV, H, Hkv, group, Nq, Nq_pad, Nk, num_kblocks);
     const int num_qtiles = (Nq + 127) / 128;
     const long long g2 = (long long)num_qtiles * B * H;
     if (g2 > 0)
         hipLaunchKernelGGL((attn_bwd_dq_kernel<D, MASK>), dim3((unsigned)g2), dim3(256), 0, s, (const uint16_t *)Q,
-                           (const uint16_t *)K, (const uint16_t *)V, (const uint16_t *)dO, lse, delta, vl, c_log2,
-                           scale, (uint16_t *)dQ, H, Hkv, group, Nq, Nk, num_qtiles, B * H);
+                           (const uint16_t *)K, (const uint16_t *)V, (const uint16_t *)dO, lse2, delta, vl, c_log2,
+                           scale, (uint16_t *)dQ, H, Hkv, group, Nq, Nq_pad, Nk, num_qtiles, B * H);
     return hipGetLastError();
 }
 

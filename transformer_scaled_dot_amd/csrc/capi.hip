@@ -117,7 +117,8 @@ attn_status_t attn_fwd(const void *Q, const void *K, const void *V, int32_t mask
 size_t attn_bwd_workspace_bytes(int32_t batch, int32_t heads, int32_t seq_q)
 {
     if (batch < 0 || heads < 0 || seq_q < 0) return 0;
-    const size_t n = (size_t)batch * heads * seq_q * sizeof(float);
+    // per query row, padded to whole 64-row tiles: lse * log2(e) and dO_i . O_i, float32
+    const size_t n = 2 * (size_t)batch * heads * (((size_t)seq_q + 63) / 64 * 64) * sizeof(float);
     return (n + 255) / 256 * 256;
 }
 

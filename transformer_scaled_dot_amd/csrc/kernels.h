@@ -36,10 +36,11 @@ hipError_t launch_attn_f32(const float *Q, const float *K, const float *V, int m
                            hipStream_t stream);
 
 // bf16 attention backward, head_dim 64 or 128: dQ [B,H,Nq,D], dK and dV [B,Hkv,Nk,D] (bf16) from Q, K, V,
-// the forward's O and per-row log-sum-exp lse ([B,H,Nq] float32) and dO; delta: [B,H,Nq] float32 scratch.
+// the forward's O and per-row log-sum-exp lse ([B,H,Nq] float32) and dO; work: float32 scratch of
+// 2 * B * H * (Nq rounded up to 64) values.
 hipError_t launch_attn_bwd_bf16(const void *Q, const void *K, const void *V, const void *O, const void *dO,
                                 const float *lse, int mask, const int32_t *valid_lens, float scale, void *dQ, void *dK,
-                                void *dV, int B, int H, int Hkv, int Nq, int Nk, int D, float *delta,
+                                void *dV, int B, int H, int Hkv, int Nq, int Nk, int D, float *work,
                                 hipStream_t stream);
 
 // C = A[M,K] * B[K,N] in bf16 with f32 accumulation, bf16 output.
