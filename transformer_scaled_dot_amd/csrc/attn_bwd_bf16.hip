@@ -13,10 +13,12 @@
 //   attn_bwd_delta: per query row, D_i and lse_i * log2(e) (0 for a row without a visible key) into the
 //                   caller's workspace, each head's rows padded to a multiple of 64 with zeros, so that
 //                   the other kernels fetch whole 64-row tiles of them;
-//   attn_bwd_dkdv:  one workgroup per 128 keys of one (batch, K/V head), 32 keys per wave; it walks the
-//                   query tiles (of every query head of the K/V head's group) and keeps dK and dV in
-//                   registers: S = Q K^T and dP = dO V^T with one key per lane, then dV^T += dO^T P and
-//                   dK^T += Q^T dS with P and dS taken straight from those accumulators;
+//   attn_bwd_dkdv:  one workgroup per 128 keys of one (batch, K/V head): 8 waves, two per SIMD, each
+//                   owning 32 keys and one 32-row half of every query tile; it walks the query tiles (of
+//                   every query head of the K/V head's group) and keeps partial dK and dV in registers:
+//                   S = Q K^T and dP = dO V^T with one key per lane, then dV^T += dO^T P and
+//                   dK^T += Q^T dS with P and dS taken straight from those accumulators; the two halves
+//                   are added through LDS at the end;
 //   attn_bwd_dq:    one workgroup per 128 query rows of one (batch, head), 32 rows per wave; it walks the
 //                   key tiles like the forward: S^T = K Q^T and dP^T = V dO^T with one query per lane, then
 //                   dQ^T += K^T dS^T.
@@ -102,11 +104,10 @@ __device__ __forceinline__ void pack_operands(const f32x16 (&x)[2], bf16x8 (&pb)
 
 // DMA of one 64-row tile (rows r0 .. r0 + 63 of a [n, D] bf16 matrix) into LDS at slot_off, rows at or past
 // n replaced by row n - 1 (their results are masked). voff/drow: this lane's chunk offsets within a tile.
-template <int D, int CH>
+template <int D, int CH, int WAVES>
 __device__ __forceinline__ void issue_tile(uint32_t lds0, const uint16_t *src, int r0, int n, uint32_t slot_off,
                                            const uint32_t (&voff)[CH], const int (&drow)[CH], int wave)
 {
-    constexpr int WAVES = 4;
     const uint16_t *base = src + (size_t)r0 * D;
     const bool tail = r0 + kBlockN > n;
 #pragma unroll
@@ -120,17 +121,18 @@ __device__ __forceinline__ void issue_tile(uint32_t lds0, const uint16_t *src, i
     }
 }
 
-template <int D>
+template <int D, int WAVES>
 struct TileDma {
     static constexpr int CPR = D / 8;
-    static constexpr int CH = kBlockN * CPR / (4 * 64);
+    static constexpr int CH = kBlockN * CPR / (WAVES * 64);
+    static_assert(kBlockN * CPR % (WAVES * 64) == 0, "tile must split evenly over the workgroup");
     uint32_t voff[CH];
     int drow[CH];
     __device__ TileDma(int wave, int lane)
     {
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
-            const int c = (j * 4 + wave) * 64 + lane;
+            const int c = (j * WAVES + wave) * 64 + lane;
             const int r = c / CPR, x = c % CPR;
             drow[j] = r;
             voff[j] = (uint32_t)(r * D + ((x ^ swz<D>(r)) << 3)) * 2;
@@ -138,43 +140,78 @@ struct TileDma {
     }
 };
 
-// dK and dV for 128 keys of one (batch, K/V head).
+// acc^T += T_blk^T P_blk: the two 16-row chunks of 32-row block blk of the tile at OFF, read transposed,
+// times the two B operands packed from a 32 x 32 accumulator whose rows are that block's rows.
+template <int D, int OFF>
+__device__ __forceinline__ void accumulate_block(const uint8_t *lds, const TileAddrs<D> &ad, int blk,
+                                                 const bf16x8 (&pb)[2], f32x16 (&acc)[D / 32])
+{
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl) {
+        const uint32_t c_off = (uint32_t)(2 * blk + cl) * 16 * D * 2;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const uint8_t *p0 = lds + ad.v[db][0] + OFF + c_off;
+            const uint8_t *p1 = lds + ad.v[db][1] + OFF + c_off;
+            const bf16x8 a = lds_tr_pair((const uint16_t *)p0, (const uint16_t *)p1);
+            acc[db] = mfma32x32x16(a, pb[cl], acc[db]);
+        }
+    }
+}
+
+__device__ __forceinline__ void pack_block(const f32x16 &x, bf16x8 (&pb)[2])
+{
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl) {
+        u32x4 w;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = pack_bf16x2(x[cl * 8 + 2 * u], x[cl * 8 + 2 * u + 1]);
+        pb[cl] = __builtin_bit_cast(bf16x8, w);
+    }
+}
+
+// dK and dV for 128 keys of one (batch, K/V head). 8 waves, two per SIMD: wave w owns keys
+// (w % 4) * 32 .. +31 of the block and query rows (w / 4) * 32 .. +31 of every 64-row query tile; the
+// two waves of a key group add their partial dK and dV through LDS at the end.
 template <int D, int MASK>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const uint16_t *__restrict__ dO, const float *__restrict__ lse2, const float *__restrict__ delta,
     const int32_t *__restrict__ valid_lens, float c_log2, float scale, uint16_t *__restrict__ dK,
     uint16_t *__restrict__ dV, int H, int Hkv, int group, int Nq, int Nq_pad, int Nk, int num_kblocks)
 {
-    constexpr int DB = D / 32, TILE_B = kBlockN * D * 2;
-    // Q slots 0, 1; dO slots 0, 1; then per slot the tile's 64 values of lse * log2(e) and of D
-    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_B + 2 * 512];
-    constexpr int QS0 = 0, QS1 = TILE_B, GS0 = 2 * TILE_B, GS1 = 3 * TILE_B, LS0 = 4 * TILE_B, LS1 = LS0 + 512;
+    constexpr int WAVES = 8, DB = D / 32, TILE_B = kBlockN * D * 2;
+    // Q slots 0, 1; dO slots 0, 1; the block's 128 V and K rows (two tiles each, read as B operands); then per slot the
+    // tile's 64 values of lse * log2(e) and of D. After the loop the first 4 tiles hold the partial
+    // accumulators being added.
+    __shared__ __attribute__((aligned(16))) uint8_t smem[8 * TILE_B + 2 * 512];
+    constexpr int QS0 = 0, QS1 = TILE_B, GS0 = 2 * TILE_B, GS1 = 3 * TILE_B, VB = 4 * TILE_B, KB = 6 * TILE_B;
+    constexpr int LS0 = 8 * TILE_B, LS1 = LS0 + 512;
+    static_assert(4 * 64 * 16 * DB * 4 <= 4 * TILE_B, "the reduction area must fit in the tile slots");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
+    const int kg = wave & 3, qh = wave >> 2;
     const int kbk = blockIdx.x % num_kblocks, bk = blockIdx.x / num_kblocks;
     const int b = bk / Hkv, hk = bk % Hkv;
-    const int kwg0 = kbk * 128, key = kwg0 + wave * 32 + l32;
+    const int kwg0 = kbk * 128, key = kwg0 + kg * 32 + l32;
 
     int kv_len = Nk;
     if (mask_padding(MASK)) {
         const int L = valid_lens[b];
         kv_len = L < 0 ? 0 : (L > Nk ? Nk : L);
     }
-    bf16x8 kreg[1][D / 16], vreg[1][D / 16];
-    load_rows_b<D>(K + (size_t)bk * Nk * D, key, Nk, hf, kreg);
-    load_rows_b<D>(V + (size_t)bk * Nk * D, key, Nk, hf, vreg);
 
-    f32x16 dk[1][DB], dv[1][DB];
+    f32x16 dk[DB], dv[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dk[0][i][r] = dv[0][i][r] = 0.f;
+        for (int r = 0; r < 16; ++r) dk[i][r] = dv[i][r] = 0.f;
 
     const TileAddrs<D> ad = tile_addrs<D>(lane);
-    const TileDma<D> dma(wave, lane);
+    const TileDma<D, WAVES> dma(wave, lane);
     const uint32_t lds0 = lds_addr(smem);
+    const uint32_t blk_off = (uint32_t)qh * 32 * D * 2;
     // query tiles that can see one of these keys: causal rows below the first key see none of them
     const int nqt = (Nq + kBlockN - 1) / kBlockN;
     const int t0 = mask_causal(MASK) ? min(kwg0 / kBlockN, nqt) : 0;
@@ -182,25 +219,36 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     const int n = group * per_head;
     const int h0 = hk * group;
 
-    auto head_ptrs = [&](int u, const uint16_t *&qh, const uint16_t *&gh, int &bh, int &t) {
-        const int h = h0 + u / per_head;
+    auto tile_of = [&](int u, int &bh, int &t) {
+        bh = b * H + h0 + u / per_head;
         t = t0 + u % per_head;
-        bh = b * H + h;
-        qh = Q + (size_t)bh * Nq * D;
-        gh = dO + (size_t)bh * Nq * D;
     };
     auto issue = [&](int u, uint32_t qs, uint32_t gs, uint32_t ls) {
-        const uint16_t *qh, *gh;
         int bh, t;
-        head_ptrs(u, qh, gh, bh, t);
-        issue_tile<D, TileDma<D>::CH>(lds0, qh, t * kBlockN, Nq, qs, dma.voff, dma.drow, wave);
-        issue_tile<D, TileDma<D>::CH>(lds0, gh, t * kBlockN, Nq, gs, dma.voff, dma.drow, wave);
+        tile_of(u, bh, t);
+        issue_tile<D, TileDma<D, WAVES>::CH, WAVES>(lds0, Q + (size_t)bh * Nq * D, t * kBlockN, Nq, qs, dma.voff,
+                                                    dma.drow, wave);
+        issue_tile<D, TileDma<D, WAVES>::CH, WAVES>(lds0, dO + (size_t)bh * Nq * D, t * kBlockN, Nq, gs, dma.voff,
+                                                    dma.drow, wave);
         // the tile's 64 padded rows of lse * log2(e) (wave 0) and of D (wave 1), 16 bytes per lane
         const size_t r0 = (size_t)bh * Nq_pad + (size_t)t * kBlockN;
         const int wv = __builtin_amdgcn_readfirstlane(wave);
         if (wv < 2 && lane < 16)
             lds_dma16(lds0 + ls + wv * 256, (wv == 0 ? lse2 : delta) + r0, (uint32_t)lane * 16);
     };
+    // the block's K and V rows (rows past Nk repeat row Nk - 1; those keys are masked)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+        const uint16_t *src = (x == 0 ? K : V) + (size_t)bk * Nk * D;
+        const uint32_t dst = x == 0 ? KB : VB;
+        issue_tile<D, TileDma<D, WAVES>::CH, WAVES>(lds0, src, kwg0, Nk, dst, dma.voff, dma.drow, wave);
+        if (kwg0 + kBlockN < Nk)
+            issue_tile<D, TileDma<D, WAVES>::CH, WAVES>(lds0, src, kwg0 + kBlockN, Nk, dst + TILE_B, dma.voff,
+                                                        dma.drow, wave);
+    }
+    // this wave's 32 K and V rows inside them: B operands read with the same lane addresses as a tile's rows
+    const uint32_t kv_sub = (uint32_t)(kg >> 1) * TILE_B + (uint32_t)(kg & 1) * 32 * D * 2;
+    const uint32_t v_off = VB + kv_sub, k_off = KB + kv_sub;
     if (n > 0) issue(0, QS0, GS0, LS0);
     wait_vmcnt0();
     __syncthreads();
@@ -208,34 +256,40 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
         constexpr int P = decltype(parity)::value;
         constexpr int QS = P ? QS1 : QS0, GS = P ? GS1 : GS0, LS = P ? LS1 : LS0;
         if (u + 1 < n) issue(u + 1, P ? QS0 : QS1, P ? GS0 : GS1, P ? LS0 : LS1);
-        const uint16_t *qh, *gh;
         int bh, t;
-        head_ptrs(u, qh, gh, bh, t);
-        // S = Q K^T and dP = dO V^T: one key per lane, rows = queries jb*32 + (r/4)*8 + hf*4 + r%4
-        f32x16 s[1][2], dp[1][2];
-        scores<D, 1, QS, false>(smem, ad, kreg, s);
-        scores<D, 1, GS, false>(smem, ad, vreg, dp);
+        tile_of(u, bh, t);
+        // S = Q K^T and dP = dO V^T for this wave's 32 query rows: one key per lane
+        f32x16 s, dp;
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
+        for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int qo = jb * 32 + g * 8 + hf * 4;  // offset of the lane's 4 rows in the tile
-                const f32x4 l4 = *(const f32x4 *)(smem + LS + qo * 4);
-                const f32x4 d4 = *(const f32x4 *)(smem + LS + 256 + qo * 4);
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const bf16x8 aq = *(const bf16x8 *)(smem + ad.k[ks] + QS + blk_off);
+            const bf16x8 kb = *(const bf16x8 *)(smem + ad.k[ks] + k_off);
+            const bf16x8 ag = *(const bf16x8 *)(smem + ad.k[ks] + GS + blk_off);
+            const bf16x8 vb = *(const bf16x8 *)(smem + ad.k[ks] + v_off);
+            s = mfma32x32x16(aq, kb, s);
+            dp = mfma32x32x16(ag, vb, dp);
+        }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int q = t * kBlockN + qo + e, r = g * 4 + e;
-                    const bool vis = q < Nq && key < kv_len && (!mask_causal(MASK) || key <= q);
-                    const float p = fast_exp2(fmaf(s[0][jb][r], c_log2, -l4[e]));
-                    s[0][jb][r] = vis ? p : 0.f;
-                    dp[0][jb][r] = vis ? p * (dp[0][jb][r] - d4[e]) : 0.f;
-                }
+        for (int g = 0; g < 4; ++g) {
+            const int qo = qh * 32 + g * 8 + hf * 4;  // offset of the lane's 4 rows in the tile
+            const f32x4 l4 = *(const f32x4 *)(smem + LS + qo * 4);
+            const f32x4 d4 = *(const f32x4 *)(smem + LS + 256 + qo * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int q = t * kBlockN + qo + e, r = g * 4 + e;
+                const bool vis = q < Nq && key < kv_len && (!mask_causal(MASK) || key <= q);
+                const float p = fast_exp2(fmaf(s[r], c_log2, -l4[e]));
+                s[r] = vis ? p : 0.f;
+                dp[r] = vis ? p * (dp[r] - d4[e]) : 0.f;
             }
-        bf16x8 pb[1][4], sb[1][4];
-        pack_operands(s[0], pb);
-        pack_operands(dp[0], sb);
-        accumulate_pv<D, 1, GS, false>(smem, ad, pb, dv);  // dV^T += dO^T P
-        accumulate_pv<D, 1, QS, false>(smem, ad, sb, dk);  // dK^T += Q^T dS
+        }
+        bf16x8 pb[2], sb[2];
+        pack_block(s, pb);
+        pack_block(dp, sb);
+        accumulate_block<D, GS>(smem, ad, qh, pb, dv);  // dV^T += dO^T P
+        accumulate_block<D, QS>(smem, ad, qh, sb, dk);  // dK^T += Q^T dS
         wait_vmcnt0();
         __syncthreads();
     };
@@ -243,9 +297,35 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
         step(u, std::integral_constant<int, 0>());
         if (u + 1 < n) step(u + 1, std::integral_constant<int, 1>());
     }
-    // dV = acc, dK = scale * acc, rows = keys of this (batch, K/V head)
-    store_rows<D, false, kOutBHND, false>(dv[0], 1.f, key, bk, Hkv, Nk, b, hf, dV);
-    store_rows<D, false, kOutBHND, false>(dk[0], 1.f / scale, key, bk, Hkv, Nk, b, hf, dK);
+    // add the second query half's partial sums into the first's, through LDS (16-byte chunks, lanes
+    // contiguous), dK then dV; then the first half stores
+    f32x4 *red = (f32x4 *)smem;
+    auto reduce = [&](f32x16 (&acc)[DB]) {
+        if (qh == 1) {
+#pragma unroll
+            for (int i = 0; i < DB * 4; ++i)
+                red[(kg * DB * 4 + i) * 64 + lane] =
+                    f32x4{acc[i / 4][(i % 4) * 4], acc[i / 4][(i % 4) * 4 + 1], acc[i / 4][(i % 4) * 4 + 2],
+                          acc[i / 4][(i % 4) * 4 + 3]};
+        }
+        __syncthreads();
+        if (qh == 0) {
+#pragma unroll
+            for (int i = 0; i < DB * 4; ++i) {
+                const f32x4 x = red[(kg * DB * 4 + i) * 64 + lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i / 4][(i % 4) * 4 + e] += x[e];
+            }
+        }
+        __syncthreads();
+    };
+    reduce(dk);
+    reduce(dv);
+    if (qh == 0) {
+        // dV = acc, dK = scale * acc, rows = keys of this (batch, K/V head)
+        store_rows<D, false, kOutBHND, false>(dv, 1.f, key, bk, Hkv, Nk, b, hf, dV);
+        store_rows<D, false, kOutBHND, false>(dk, 1.f / scale, key, bk, Hkv, Nk, b, hf, dK);
+    }
 }
 
 // dQ for 128 query rows of one (batch, head).
@@ -293,12 +373,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
         for (int r = 0; r < 16; ++r) dq[0][i][r] = 0.f;
 
     const TileAddrs<D> ad = tile_addrs<D>(lane);
-    const TileDma<D> dma(wave, lane);
+    const TileDma<D, 4> dma(wave, lane);
     const uint32_t lds0 = lds_addr(smem);
     const uint16_t *Kh = K + kvbh * Nk * D, *Vh = V + kvbh * Nk * D;
     if (ntiles > 0) {
-        issue_tile<D, TileDma<D>::CH>(lds0, Kh, 0, kv_end, KS0, dma.voff, dma.drow, wave);
-        issue_tile<D, TileDma<D>::CH>(lds0, Vh, 0, kv_end, VS0, dma.voff, dma.drow, wave);
+        issue_tile<D, TileDma<D, 4>::CH, 4>(lds0, Kh, 0, kv_end, KS0, dma.voff, dma.drow, wave);
+        issue_tile<D, TileDma<D, 4>::CH, 4>(lds0, Vh, 0, kv_end, VS0, dma.voff, dma.drow, wave);
     }
     wait_vmcnt0();
     __syncthreads();
@@ -306,9 +386,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
         constexpr int P = decltype(parity)::value;
         constexpr int KS = P ? KS1 : KS0, VS = P ? VS1 : VS0;
         if (t + 1 < ntiles) {
-            issue_tile<D, TileDma<D>::CH>(lds0, Kh, (t + 1) * kBlockN, kv_end, P ? KS0 : KS1, dma.voff, dma.drow,
+            issue_tile<D, TileDma<D, 4>::CH, 4>(lds0, Kh, (t + 1) * kBlockN, kv_end, P ? KS0 : KS1, dma.voff, dma.drow,
                                           wave);
-            issue_tile<D, TileDma<D>::CH>(lds0, Vh, (t + 1) * kBlockN, kv_end, P ? VS0 : VS1, dma.voff, dma.drow,
+            issue_tile<D, TileDma<D, 4>::CH, 4>(lds0, Vh, (t + 1) * kBlockN, kv_end, P ? VS0 : VS1, dma.voff, dma.drow,
                                           wave);
         }
         // S^T = K Q^T and dP^T = V dO^T: one query per lane, rows = keys
@@ -355,7 +435,7 @@ hipError_t launch_bwd(const void *Q, const void *K, const void *V, const void *O
     const int num_kblocks = (Nk + 127) / 128;
     const long long g1 = (long long)num_kblocks * B * Hkv;
     if (g1 > 0)
-        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, MASK>), dim3((unsigned)g1), dim3(256), 0, s, (const uint16_t *)Q,
+        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, MASK>), dim3((unsigned)g1), dim3(512), 0, s, (const uint16_t *)Q,
                            (const uint16_t *)K, (const uint16_t *)V, (const uint16_t *)dO, lse2, delta, vl, c_log2,
                            scale, (uint16_t *)dK, (uint16_t *)dV, H, Hkv, group, Nq, Nq_pad, Nk, num_kblocks);
     const int num_qtiles = (Nq + 127) / 128;
