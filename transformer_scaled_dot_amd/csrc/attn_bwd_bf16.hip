@@ -19,7 +19,7 @@
 //                   S = Q K^T and dP = dO V^T with one key per lane, then dV^T += dO^T P and
 //                   dK^T += Q^T dS with P and dS taken straight from those accumulators; the two halves
 //                   are added through LDS at the end;
-//   attn_bwd_dq:    one workgroup per 128 query rows of one (batch, head), 32 rows per wave; it walks the
+//   attn_bwd_dq:    one workgroup per 256 query rows of one (batch, head), 32 rows per wave; it walks the
 //                   key tiles like the forward: S^T = K Q^T and dP^T = V dO^T with one query per lane, then
 //                   dQ^T += K^T dS^T.
 // Both main kernels use the forward's tile layout and contractions (attn_tiles.h); Q/dO (dK/dV kernel) or
@@ -328,15 +328,15 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
     }
 }
 
-// dQ for 128 query rows of one (batch, head).
+// dQ for 256 query rows of one (batch, head): 8 waves of 32 rows, two per SIMD.
 template <int D, int MASK>
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const uint16_t *__restrict__ dO, const float *__restrict__ lse2, const float *__restrict__ delta,
     const int32_t *__restrict__ valid_lens, float c_log2, float scale, uint16_t *__restrict__ dQ, int H,
     int Hkv, int group, int Nq, int Nq_pad, int Nk, int num_qtiles, int BH)
 {
-    constexpr int DB = D / 32, TILE_B = kBlockN * D * 2;
+    constexpr int WAVES = 8, ROWS = WAVES * 32, DB = D / 32, TILE_B = kBlockN * D * 2;
     __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_B];  // K slots 0, 1; V slots 0, 1
     constexpr int KS0 = 0, KS1 = TILE_B, VS0 = 2 * TILE_B, VS1 = 3 * TILE_B;
 
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     if (mask_causal(MASK)) qt = num_qtiles - 1 - qt;  // longest first
     const int b = bh / H, h = bh % H;
     const size_t kvbh = (size_t)b * Hkv + h / group;
-    const int q0 = qt * 128, qrow = q0 + wave * 32 + l32;
+    const int q0 = qt * ROWS, qrow = q0 + wave * 32 + l32;
 
     int kv_len = Nk;
     if (mask_padding(MASK)) {
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
         kv_len = L < 0 ? 0 : (L > Nk ? Nk : L);
     }
     int kv_end = kv_len;
-    if (mask_causal(MASK)) kv_end = min(kv_len, q0 + 128);
+    if (mask_causal(MASK)) kv_end = min(kv_len, q0 + ROWS);
     const int ntiles = (kv_end + kBlockN - 1) / kBlockN;
 
     bf16x8 qreg[1][D / 16], greg[1][D / 16];
@@ -373,12 +373,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
         for (int r = 0; r < 16; ++r) dq[0][i][r] = 0.f;
 
     const TileAddrs<D> ad = tile_addrs<D>(lane);
-    const TileDma<D, 4> dma(wave, lane);
+    const TileDma<D, WAVES> dma(wave, lane);
     const uint32_t lds0 = lds_addr(smem);
     const uint16_t *Kh = K + kvbh * Nk * D, *Vh = V + kvbh * Nk * D;
     if (ntiles > 0) {
-        issue_tile<D, TileDma<D, 4>::CH, 4>(lds0, Kh, 0, kv_end, KS0, dma.voff, dma.drow, wave);
-        issue_tile<D, TileDma<D, 4>::CH, 4>(lds0, Vh, 0, kv_end, VS0, dma.voff, dma.drow, wave);
+        issue_tile<D, TileDma<D, WAVES>::CH, WAVES>(lds0, Kh, 0, kv_end, KS0, dma.voff, dma.drow, wave);
+        issue_tile<D, TileDma<D, WAVES>::CH, WAVES>(lds0, Vh, 0, kv_end, VS0, dma.voff, dma.drow, wave);
     }
     wait_vmcnt0();
     __syncthreads();
@@ -386,9 +386,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
         constexpr int P = decltype(parity)::value;
         constexpr int KS = P ? KS1 : KS0, VS = P ? VS1 : VS0;
         if (t + 1 < ntiles) {
-            issue_tile<D, TileDma<D, 4>::CH, 4>(lds0, Kh, (t + 1) * kBlockN, kv_end, P ? KS0 : KS1, dma.voff, dma.drow,
+            issue_tile<D, TileDma<D, WAVES>::CH, WAVES>(lds0, Kh, (t + 1) * kBlockN, kv_end, P ? KS0 : KS1, dma.voff, dma.drow,
                                           wave);
-            issue_tile<D, TileDma<D, 4>::CH, 4>(lds0, Vh, (t + 1) * kBlockN, kv_end, P ? VS0 : VS1, dma.voff, dma.drow,
+            issue_tile<D, TileDma<D, WAVES>::CH, WAVES>(lds0, Vh, (t + 1) * kBlockN, kv_end, P ? VS0 : VS1, dma.voff, dma.drow,
                                           wave);
         }
         // S^T = K Q^T and dP^T = V dO^T: one query per lane, rows = keys
@@ -438,10 +438,10 @@ hipError_t launch_bwd(const void *Q, const void *K, const void *V, const void *O
         hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, MASK>), dim3((unsigned)g1), dim3(512), 0, s, (const uint16_t *)Q,
                            (const uint16_t *)K, (const uint16_t *)V, (const uint16_t *)dO, lse2, delta, vl, c_log2,
                            scale, (uint16_t *)dK, (uint16_t *)dV, H, Hkv, group, Nq, Nq_pad, Nk, num_kblocks);
-    const int num_qtiles = (Nq + 127) / 128;
+    const int num_qtiles = (Nq + 255) / 256;
     const long long g2 = (long long)num_qtiles * B * H;
     if (g2 > 0)
-        hipLaunchKernelGGL((attn_bwd_dq_kernel<D, MASK>), dim3((unsigned)g2), dim3(256), 0, s, (const uint16_t *)Q,
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<D, MASK>), dim3((unsigned)g2), dim3(512), 0, s, (const uint16_t *)Q,
                            (const uint16_t *)K, (const uint16_t *)V, (const uint16_t *)dO, lse2, delta, vl, c_log2,
                            scale, (uint16_t *)dQ, H, Hkv, group, Nq, Nq_pad, Nk, num_qtiles, B * H);
     return hipGetLastError();
