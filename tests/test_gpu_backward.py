@@ -117,3 +117,26 @@ def test_backward_ragged_and_tiny(dev):
 def test_backward_longer(dev):
     """1024 keys: many query tiles per key block and key tiles per query block."""
     run_case(dev, 4400, 1, 2, 1, 1024, 1024, 128, "causal")
+
+
+def test_backward_full_size_sampled_heads(dev):
+    """The causal 4K launch shape (B4 H16 N4096 d128): the backward runs on the whole workload and two of
+    its 64 (batch, head) slices are compared element by element with the oracle (a head's gradients
+    depend only on that head's Q, K, V and dO), within the same per-element bounds."""
+    import transformer_scaled_dot_amd as tsd
+
+    B, H, N, d = 4, 16, 4096, 128
+    q, k, v, g = (synth.normal_tensor(4500 + i, (B, H, N, d)) for i in range(4))
+    Q, K, V, G = q.torch(dev), k.torch(dev), v.torch(dev), g.torch(dev)
+    o, lse = tsd.attn_fwd(Q, K, V, mask="causal", return_lse=True)
+    dq, dk, dv = tsd.attn_bwd(Q, K, V, o, G, lse, mask="causal")
+    torch.cuda.synchronize()
+    scale = 1.0 / np.sqrt(d)
+    for b, h in ((0, 0), (3, 15)):
+        sl = lambda t: t.f32[b:b + 1, h:h + 1].astype(np.float64)
+        got = [x[b:b + 1, h:h + 1].float().cpu().numpy().astype(np.float64) for x in (dq, dk, dv)]
+        ref = oracle.attention_backward(sl(q), sl(k), sl(v), sl(g), mask="causal", scale=scale)
+        _, A = oracle.attention(sl(q), sl(k), sl(v), mask="causal", scale=scale, return_weights=True)
+        tols = bounds(sl(q), sl(k), sl(v), sl(g), A, "causal", None, scale)
+        for what, x, r, t in zip(("dQ", "dK", "dV"), got, ref, tols):
+            check("bwd [4,16,4096,128] causal, head (%d,%d) %s" % (b, h, what), x, r, t)
