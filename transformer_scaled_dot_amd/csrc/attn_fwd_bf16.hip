@@ -51,6 +51,9 @@ constexpr float kRescaleSlack = 8.f;    // log2 units the reference max may lag 
 #define TSD_D128_DESIGN 3
 #endif
 constexpr int kD128Design = TSD_D128_DESIGN;
+#ifndef TSD_HEAD_MAJOR
+#define TSD_HEAD_MAJOR 1
+#endif
 #ifndef TSD_WAVES128
 #define TSD_WAVES128 8
 #endif
@@ -473,6 +476,27 @@ __device__ __forceinline__ int qb2_sched(int w, int j, int G, int num_items)
     return qb2_round_item(w, (j + w) % n_w, G);
 }
 
+// Head-major alternative for grids of whole XCDs (G % 8 == 0, workgroup w on XCD w % 8) when every XCD can
+// take the same number of whole rounds: XCD x runs the items of heads bh = x, x + 8, ... in head order, all
+// query blocks of one head next to each other, so that the M = G / 8 workgroups of an XCD work on one or
+// two heads at a time and share those heads' K/V tiles in the XCD's L2. Workgroup m takes slot m of even
+// rounds and slot M - 1 - m of odd ones (long and short items alternate). Returns the item index
+// (query-block index * BH + bh) or num_items when the workgroup has no j-th item.
+__device__ __forceinline__ int qb2_sched_heads(int w, int j, int G, int BH, int num_qtiles, int num_items)
+{
+    const int M = G / 8, x = w & 7, m = w >> 3;
+    const int rounds = (BH / 8) * num_qtiles / M;
+    if (j >= rounds) return num_items;
+    const int n = j * M + ((j & 1) ? M - 1 - m : m);
+    const int k = n / num_qtiles, q = n - k * num_qtiles;
+    return q * BH + x + 8 * k;
+}
+
+__device__ __forceinline__ bool qb2_heads_schedule(int G, int BH, int num_qtiles)
+{
+    return TSD_HEAD_MAJOR && G % 8 == 0 && BH % 8 == 0 && ((BH / 8) * num_qtiles) % (G / 8) == 0;
+}
+
 template <int MASK>
 __device__ __forceinline__ Qb2Item qb2_item(int p, int num_items, int num_qtiles, int BH, int H, int Nk,
                                             const int32_t *__restrict__ valid_lens, const AttnHeads &hd)
@@ -590,7 +614,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
 
     int k = 0, off = 0;
-    Qb2Item cur = qb2_item<MASK>(qb2_sched(w, 0, G, num_items), num_items, num_qtiles, BH, H, Nk, valid_lens, hd);
+    const bool by_heads = qb2_heads_schedule(G, BH, num_qtiles);
+    auto sched = [&](int j) {
+        return by_heads ? qb2_sched_heads(w, j, G, BH, num_qtiles, num_items) : qb2_sched(w, j, G, num_items);
+    };
+    Qb2Item cur = qb2_item<MASK>(sched(0), num_items, num_qtiles, BH, H, Nk, valid_lens, hd);
     if (!cur.valid) return;
     q_tiles(cur);
     first_tiles(cur, 0);
@@ -617,7 +645,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // arrive while this item's tiles run
         __syncthreads();
         const Qb2Item nxt =
-            qb2_item<MASK>(qb2_sched(w, ++k, G, num_items), num_items, num_qtiles, BH, H, Nk, valid_lens, hd);
+            qb2_item<MASK>(sched(++k), num_items, num_qtiles, BH, H, Nk, valid_lens, hd);
         if (nxt.valid) q_tiles(nxt);
 
         const int qmin_w = cur.q0 + wave * RW, qmax_w = qmin_w + RW - 1;
