@@ -288,3 +288,17 @@ def test_config5_long_context(dev):
     say("C5 bf16 out: %d of %d sampled elements have |O| >= 8" % ((~small).sum(), small.size))
     check("C5 bf16 out, |O| < 8", gotb[small], ref[small], "bf16")
     assert np.abs(gotb - ref).max() <= 2 ** -5 + TOL_BF16_MAX
+
+
+def test_clock_probe_reports_plausible_rate(dev):
+    """The measurement probe (not part of the attention path): a clock between 0.3 and 3 GHz and a matrix
+    rate between 50 TFLOP/s and the published 2.5 PFLOP/s dense bf16 peak scaled to that clock (4 SIMDs per
+    compute unit, 1024 bf16 flops per SIMD cycle)."""
+    import transformer_scaled_dot_amd as tsd
+
+    p = tsd.clock_probe(dev, spin_us=1000)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    ceiling = cus * 4 * 1024 * p["clock_mhz"] * 1e6 / 1e12
+    say("clock probe: %.0f MHz, %.1f TFLOP/s (clock-scaled ceiling %.1f)" % (p["clock_mhz"], p["tflops"], ceiling))
+    assert 300 < p["clock_mhz"] < 3000
+    assert 50 < p["tflops"] <= ceiling * 1.02

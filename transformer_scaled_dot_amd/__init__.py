@@ -247,17 +247,25 @@ def mha_fwd(x, w_qkv, w_o, h: int, out=None, workspace=None):
     return out
 
 
-def clock_probe_mhz(device=None, spin_us: int = 2000) -> float:
-    """Mean shader clock (MHz) over one workgroup per compute unit kept busy with matrix instructions for
-    ``spin_us`` of wall time (measurement support; synchronises the device)."""
+def clock_probe(device=None, spin_us: int = 2000) -> dict:
+    """Shader clock and matrix rate under a pure bf16 MFMA load on pseudo-random operands, one workgroup of
+    four waves per compute unit for ``spin_us`` of wall time (measurement support; synchronises the device).
+    Returns {"clock_mhz": mean shader clock, "tflops": bf16 32x32x16 flops issued / wall time}."""
     import torch
 
     lib = load_library()
     device = torch.device("cuda", 0) if device is None else torch.device(device)
     blocks = torch.cuda.get_device_properties(device).multi_processor_count
-    out = torch.zeros(2 * blocks, dtype=torch.int64, device=device)
+    out = torch.zeros(3 * blocks, dtype=torch.int64, device=device)
     st = lib.attn_clock_probe(ctypes.c_void_p(out.data_ptr()), blocks, int(spin_us), _stream_ptr(device))
     _raise_for(lib, st, "attn_clock_probe")
-    v = out.view(blocks, 2).sum(dim=0).cpu().tolist()
-    return 100.0 * v[0] / max(v[1], 1)
+    v = out.view(blocks, 3).double().cpu()
+    wall_s = float(v[:, 1].max()) / 100e6
+    return {"clock_mhz": 100.0 * float(v[:, 0].sum()) / max(float(v[:, 1].sum()), 1.0),
+            "tflops": 4 * 32 * 32 * 16 * 2 * float(v[:, 2].sum()) / max(wall_s, 1e-9) / 1e12}
+
+
+def clock_probe_mhz(device=None, spin_us: int = 2000) -> float:
+    """Mean shader clock (MHz) of clock_probe."""
+    return clock_probe(device, spin_us)["clock_mhz"]
 

@@ -53,8 +53,9 @@ hipError_t launch_gemm_bf16(const void *A, const void *Bm, void *C, int M, int N
 hipError_t launch_gemm_bf16_qkv_split(const void *X, const void *Wqkv, void *qkv, int batch, int seq, int d_model,
                                       int heads, hipStream_t stream);
 
-// Measurement support: `blocks` workgroups run matrix instructions for spin_us of wall time and write
-// (s_memtime ticks, 100 MHz s_memrealtime ticks) per workgroup to out[2 * blocks].
+// Measurement support: `blocks` workgroups of four waves issue bf16 32x32x16 matrix instructions on
+// pseudo-random operands for spin_us of wall time and write (s_memtime ticks, 100 MHz s_memrealtime ticks,
+// instructions issued per wave) per workgroup to out[3 * blocks].
 hipError_t launch_clock_probe(uint64_t *out, int blocks, int spin_us, hipStream_t stream);
 
 }  // namespace tsd
