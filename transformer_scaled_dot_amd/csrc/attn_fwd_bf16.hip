@@ -480,16 +480,18 @@ __device__ __forceinline__ int qb2_sched(int w, int j, int G, int num_items)
 // take the same number of whole rounds: XCD x runs the items of heads bh = x, x + 8, ... in head order, all
 // query blocks of one head next to each other, so that the M = G / 8 workgroups of an XCD work on one or
 // two heads at a time and share those heads' K/V tiles in the XCD's L2. Workgroup m takes slot m of even
-// rounds and slot M - 1 - m of odd ones (long and short items alternate). Returns the item index
-// (query-block index * BH + bh) or num_items when the workgroup has no j-th item.
-__device__ __forceinline__ int qb2_sched_heads(int w, int j, int G, int BH, int num_qtiles, int num_items)
+// rounds and slot M - 1 - m of odd ones (long and short items alternate). Sets bh and the query-block
+// index of the workgroup's j-th item (item index qt * BH + bh); false when it has none.
+__device__ __forceinline__ bool qb2_sched_heads(int w, int j, int G, int BH, int num_qtiles, int &bh, int &qt)
 {
     const int M = G / 8, x = w & 7, m = w >> 3;
     const int rounds = (BH / 8) * num_qtiles / M;
-    if (j >= rounds) return num_items;
+    if (j >= rounds) return false;
     const int n = j * M + ((j & 1) ? M - 1 - m : m);
-    const int k = n / num_qtiles, q = n - k * num_qtiles;
-    return q * BH + x + 8 * k;
+    const int k = n / num_qtiles;
+    qt = n - k * num_qtiles;
+    bh = x + 8 * k;
+    return true;
 }
 
 __device__ __forceinline__ bool qb2_heads_schedule(int G, int BH, int num_qtiles)
@@ -497,16 +499,16 @@ __device__ __forceinline__ bool qb2_heads_schedule(int G, int BH, int num_qtiles
     return TSD_HEAD_MAJOR && G % 8 == 0 && BH % 8 == 0 && ((BH / 8) * num_qtiles) % (G / 8) == 0;
 }
 
+// The parameters of the item (bh, query block qt of the schedule's order); valid = false: no item.
 template <int MASK>
-__device__ __forceinline__ Qb2Item qb2_item(int p, int num_items, int num_qtiles, int BH, int H, int Nk,
+__device__ __forceinline__ Qb2Item qb2_item(bool valid, int bh, int qt, int num_qtiles, int H, int Nk,
                                             const int32_t *__restrict__ valid_lens, const AttnHeads &hd)
 {
     constexpr int BM = 256;
     Qb2Item it{};
-    it.valid = p < num_items;
+    it.valid = valid;
     if (!it.valid) return it;
-    it.bh = p % BH;
-    int qt = p / BH;
+    it.bh = bh;
     if (mask_causal(MASK)) qt = num_qtiles - 1 - qt;
     it.b = it.bh / H;
     it.kvh = it.b * hd.kv_heads + (it.bh - it.b * H) / hd.group;
@@ -606,19 +608,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             issue(Vh, 0, it.kv_end, VSLOT0 + off * TILE_B);
         }
     };
-    // the item's Q rows (the four waves' 64-row blocks) into the Q slots
+    // the item's Q rows (the four waves' 64-row blocks) into the Q slots, each block through a buffer
+    // descriptor that covers its rows below Nq: rows past Nq (a last partial block) read as zeros
     auto q_tiles = [&](const Qb2Item &it) {
-        const uint16_t *Qh = Q + (size_t)it.bh * Nq * D;
+        const uint16_t *Qh = Q + ((size_t)it.bh * Nq + it.q0) * D;
 #pragma unroll
-        for (int qw = 0; qw < WAVES; ++qw) issue(Qh, it.q0 + qw * RW, Nq, QSLOT + qw * TILE_B);
+        for (int qw = 0; qw < WAVES; ++qw) {
+            const int rows = __builtin_amdgcn_readfirstlane(min(max(Nq - it.q0 - qw * RW, 0), RW));
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(Qh + (size_t)qw * RW * D), (short)0, rows * D * 2, 0x20000);
+#pragma unroll
+            for (int j = 0; j < CH; ++j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void *)(uintptr_t)(lbw + QSLOT + qw * TILE_B + j * WAVES * 1024),
+                    16, voff[j], 0, 0, 0);
+        }
     };
 
     int k = 0, off = 0;
     const bool by_heads = qb2_heads_schedule(G, BH, num_qtiles);
-    auto sched = [&](int j) {
-        return by_heads ? qb2_sched_heads(w, j, G, BH, num_qtiles, num_items) : qb2_sched(w, j, G, num_items);
+    // the workgroup's j-th item
+    auto item = [&](int j) {
+        int bh = 0, qt = 0;
+        bool valid;
+        if (by_heads) {
+            valid = qb2_sched_heads(w, j, G, BH, num_qtiles, bh, qt);
+        } else {
+            const int p = qb2_sched(w, j, G, num_items);
+            valid = p < num_items;
+            qt = p / BH;
+            bh = p - qt * BH;
+        }
+        return qb2_item<MASK>(valid, bh, qt, num_qtiles, H, Nk, valid_lens, hd);
     };
-    Qb2Item cur = qb2_item<MASK>(sched(0), num_items, num_qtiles, BH, H, Nk, valid_lens, hd);
+    Qb2Item cur = item(0);
     if (!cur.valid) return;
     q_tiles(cur);
     first_tiles(cur, 0);
@@ -631,21 +654,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             wait_vmcnt0();
             __syncthreads();
         }
-        // O = 0 and Q^T (this wave's rows, from its Q slot) in the AGPRs the tile loop names
-        u32x4 qv[QB][KS];
+        // O = 0 and Q^T (this wave's rows, from its Q slot) in the AGPRs the tile loop names. The slot offset
+        // is computed here, per item, so that the eight addresses are not held across the tile loop
+        uint32_t wq = QSLOT + wave * TILE_B;
+        asm volatile("" : "+v"(wq));
+        uint32_t qa[KS];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                qv[qb][ks] = *(const u32x4 *)(smem + QSLOT + wave * TILE_B + qb * 32 * D * 2 + ad.k[ks]);
+        for (int ks = 0; ks < KS; ++ks) qa[ks] = kaddr[ks] + wq;
         bf16x8 qreg[QB][KS];
         f32x16 acc[QB][DB];
-        qb2_init(acc, qreg, qv);
+        qb2_init(acc, qreg, qa);
         // every wave has its Q before any wave fetches the next item's Q rows into the Q slots; they
         // arrive while this item's tiles run
         __syncthreads();
-        const Qb2Item nxt =
-            qb2_item<MASK>(sched(++k), num_items, num_qtiles, BH, H, Nk, valid_lens, hd);
+        const Qb2Item nxt = item(++k);
         if (nxt.valid) q_tiles(nxt);
 
         const int qmin_w = cur.q0 + wave * RW, qmax_w = qmin_w + RW - 1;

@@ -686,29 +686,26 @@ def render():
         "// generator for the schedule and the register plan).",
         "",
     ]
-    # O = 0 (each 32 x 32 block by one MFMA of zero operands, 16 AGPRs per instruction) and Q^T into its AGPRs
+    # Q^T read from the wave's Q slot straight into its AGPRs (qa[ks]: LDS address of k-step ks of the first
+    # query block, the second block 32 rows = 8 KiB further) and O = 0 (each 32 x 32 block by one MFMA of zero
+    # operands, 16 AGPRs per instruction) while the reads are in flight
+    qrd = ["ds_read_b128 a[%d:%d], %%[qa%d] offset:%d" % (Q_A + 4 * (qb * KS + ks), Q_A + 4 * (qb * KS + ks) + 3, ks,
+                                                           qb * 32 * D * 2) for qb in range(QB) for ks in range(KS)]
     zero = ["v_mov_b32 v%d, 0" % r for r in range(ZERO_V, ZERO_V + 4)] + ["s_nop 4"]
     zero += ["v_mfma_f32_32x32x16_bf16 a[%d:%d], v[%d:%d], v[%d:%d], 0" % (b, b + 15, ZERO_V, ZERO_V + 3, ZERO_V,
                                                                            ZERO_V + 3) for b in range(O_A, O_A + 128, 16)]
-    qmov = []
-    for qb in range(QB):
-        for ks in range(KS):
-            for w in range(4):
-                qmov.append("v_accvgpr_write_b32 a%d, %%[qv%d_%d]" % (Q_A + 4 * (qb * KS + ks) + w, qb * KS + ks, w))
     lines += [
-        "__device__ __forceinline__ void qb2_init(f32x16 (&o)[2][4], bf16x8 (&q)[2][8], const u32x4 (&qv)[2][8])",
+        "__device__ __forceinline__ void qb2_init(f32x16 (&o)[2][4], bf16x8 (&q)[2][8], const uint32_t (&qa)[8])",
         "{",
         "    asm volatile(",
-        "\n".join('        "%s\\n"' % t for t in zero + qmov + list(O_WAIT)),
+        "\n".join('        "%s\\n"' % t for t in qrd + zero + ["s_waitcnt lgkmcnt(0)"] + list(O_WAIT)),
         "        : " + ",\n          ".join(
             ['"={a[%d:%d]}"(o[%d][%d])' % (O_A + (qb * DB + db) * 16, O_A + (qb * DB + db) * 16 + 15, qb, db)
              for qb in range(QB) for db in range(DB)] +
             ['"={a[%d:%d]}"(q[%d][%d])' % (Q_A + 4 * (qb * KS + ks), Q_A + 4 * (qb * KS + ks) + 3, qb, ks)
              for qb in range(QB) for ks in range(KS)]),
-        "        : " + ",\n          ".join(
-            ['[qv%d_%d] "v"(qv[%d][%d][%d])' % (qb * KS + ks, w, qb, ks, w)
-             for qb in range(QB) for ks in range(KS) for w in range(4)]),
-        "        : " + ", ".join('"v%d"' % r for r in range(ZERO_V, ZERO_V + 4)) + ");",
+        "        : " + ",\n          ".join(['[qa%d] "v"(qa[%d])' % (ks, ks) for ks in range(KS)]),
+        "        : " + ", ".join('"v%d"' % r for r in range(ZERO_V, ZERO_V + 4)) + ", \"memory\");",
         "}",
         "",
     ]
