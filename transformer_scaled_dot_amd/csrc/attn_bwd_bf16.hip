@@ -191,7 +191,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
-    const int kg = wave & 3, qh = wave >> 2;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int kg = wv & 3, qh = wv >> 2;
     const int kbk = blockIdx.x % num_kblocks, bk = blockIdx.x / num_kblocks;
     const int b = bk / Hkv, hk = bk % Hkv;
     const int kwg0 = kbk * 128, key = kwg0 + kg * 32 + l32;
@@ -219,20 +220,21 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
     const int n = group * per_head;
     const int h0 = hk * group;
 
-    auto tile_of = [&](int u, int &bh, int &t) {
-        bh = b * H + h0 + u / per_head;
-        t = t0 + u % per_head;
+    // the tiles in walking order: (query head, tile) = (h0 + u / per_head, t0 + u % per_head), followed by
+    // counters rather than divided out per step
+    auto advance = [&](int &bh, int &t) {
+        if (++t == nqt) {
+            t = t0;
+            ++bh;
+        }
     };
-    auto issue = [&](int u, uint32_t qs, uint32_t gs, uint32_t ls) {
-        int bh, t;
-        tile_of(u, bh, t);
+    auto issue = [&](int bh, int t, uint32_t qs, uint32_t gs, uint32_t ls) {
         issue_tile<D, TileDma<D, WAVES>::CH, WAVES>(lds0, Q + (size_t)bh * Nq * D, t * kBlockN, Nq, qs, dma.voff,
                                                     dma.drow, wave);
         issue_tile<D, TileDma<D, WAVES>::CH, WAVES>(lds0, dO + (size_t)bh * Nq * D, t * kBlockN, Nq, gs, dma.voff,
                                                     dma.drow, wave);
         // the tile's 64 padded rows of lse * log2(e) (wave 0) and of D (wave 1), 16 bytes per lane
         const size_t r0 = (size_t)bh * Nq_pad + (size_t)t * kBlockN;
-        const int wv = __builtin_amdgcn_readfirstlane(wave);
         if (wv < 2 && lane < 16)
             lds_dma16(lds0 + ls + wv * 256, (wv == 0 ? lse2 : delta) + r0, (uint32_t)lane * 16);
     };
@@ -249,15 +251,23 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
     // this wave's 32 K and V rows inside them: B operands read with the same lane addresses as a tile's rows
     const uint32_t kv_sub = (uint32_t)(kg >> 1) * TILE_B + (uint32_t)(kg & 1) * 32 * D * 2;
     const uint32_t v_off = VB + kv_sub, k_off = KB + kv_sub;
-    if (n > 0) issue(0, QS0, GS0, LS0);
+    int t_c = t0;                          // query tile of the next step
+    int bh_f = b * H + h0, t_f = t0;       // (query head, tile) fetched next
+    if (n > 0) {
+        issue(bh_f, t_f, QS0, GS0, LS0);
+        advance(bh_f, t_f);
+    }
     wait_vmcnt0();
     __syncthreads();
     auto step = [&](int u, auto parity) {
         constexpr int P = decltype(parity)::value;
         constexpr int QS = P ? QS1 : QS0, GS = P ? GS1 : GS0, LS = P ? LS1 : LS0;
-        if (u + 1 < n) issue(u + 1, P ? QS0 : QS1, P ? GS0 : GS1, P ? LS0 : LS1);
-        int bh, t;
-        tile_of(u, bh, t);
+        if (u + 1 < n) {
+            issue(bh_f, t_f, P ? QS0 : QS1, P ? GS0 : GS1, P ? LS0 : LS1);
+            advance(bh_f, t_f);
+        }
+        const int t = t_c;
+        if (++t_c == nqt) t_c = t0;
         // S = Q K^T and dP = dO V^T for this wave's 32 query rows: one key per lane
         f32x16 s, dp;
 #pragma unroll
@@ -271,18 +281,37 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
             s = mfma32x32x16(aq, kb, s);
             dp = mfma32x32x16(ag, vb, dp);
         }
+        // every (row, key) pair of the wave's 32 x 32 block visible (the common case): no per-element test
+        const int qlo = t * kBlockN + qh * 32, klast = kwg0 + kg * 32 + 31;
+        const bool all_vis = qlo + 31 < Nq && klast < kv_len && (!mask_causal(MASK) || klast <= qlo);
+        if (all_vis) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int qo = qh * 32 + g * 8 + hf * 4;  // offset of the lane's 4 rows in the tile
-            const f32x4 l4 = *(const f32x4 *)(smem + LS + qo * 4);
-            const f32x4 d4 = *(const f32x4 *)(smem + LS + 256 + qo * 4);
+            for (int g = 0; g < 4; ++g) {
+                const int qo = qh * 32 + g * 8 + hf * 4;  // offset of the lane's 4 rows in the tile
+                const f32x4 l4 = *(const f32x4 *)(smem + LS + qo * 4);
+                const f32x4 d4 = *(const f32x4 *)(smem + LS + 256 + qo * 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int q = t * kBlockN + qo + e, r = g * 4 + e;
-                const bool vis = q < Nq && key < kv_len && (!mask_causal(MASK) || key <= q);
-                const float p = fast_exp2(fmaf(s[r], c_log2, -l4[e]));
-                s[r] = vis ? p : 0.f;
-                dp[r] = vis ? p * (dp[r] - d4[e]) : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    const int r = g * 4 + e;
+                    const float p = fast_exp2(fmaf(s[r], c_log2, -l4[e]));
+                    s[r] = p;
+                    dp[r] = p * (dp[r] - d4[e]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int qo = qh * 32 + g * 8 + hf * 4;
+                const f32x4 l4 = *(const f32x4 *)(smem + LS + qo * 4);
+                const f32x4 d4 = *(const f32x4 *)(smem + LS + 256 + qo * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int q = t * kBlockN + qo + e, r = g * 4 + e;
+                    const bool vis = q < Nq && key < kv_len && (!mask_causal(MASK) || key <= q);
+                    const float p = fast_exp2(fmaf(s[r], c_log2, -l4[e]));
+                    s[r] = vis ? p : 0.f;
+                    dp[r] = vis ? p * (dp[r] - d4[e]) : 0.f;
+                }
             }
         }
         bf16x8 pb[2], sb[2];
@@ -395,7 +424,10 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
         f32x16 s[1][2], dp[1][2];
         scores<D, 1, KS, false>(smem, ad, qreg, s);
         scores<D, 1, VS, false>(smem, ad, greg, dp);
-        mask_scores<MASK>(s[0], t * kBlockN, kv_len, qrow, hf);
+        // a tile whose keys every row of the wave sees needs no mask
+        const int klast = t * kBlockN + kBlockN - 1;
+        if (!(klast < kv_len && (!mask_causal(MASK) || klast <= q0 + __builtin_amdgcn_readfirstlane(wave) * 32)))
+            mask_scores<MASK>(s[0], t * kBlockN, kv_len, qrow, hf);
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
