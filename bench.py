@@ -246,6 +246,8 @@ def main():
                     help="also time the padding, multi-head and 32K workloads, the grouped-heads/log-sum-exp "
                          "variant and the backward pass")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the backward pass at the causal 4K shape (for its kernel trace)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -263,6 +265,12 @@ def main():
     tsd.load_library()
     if args.copy_calibration:
         copy_calibration(dev)
+        return
+    if args.backward_only:
+        rb = bench_backward(dev, max(20, args.steps // 5), 20)
+        print(json.dumps({"backward_causal_b4h16n4096d128": {"ms": round(rb["ms"], 4),
+                                                             "tflops": round(rb["flops"] / rb["ms"] / 1e9, 2)}}),
+              flush=True)
         return
 
     r = bench_attention(dev, 3, args.steps, args.warmup, "causal")
