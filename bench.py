@@ -36,7 +36,8 @@ WORKLOAD = dict(workload="sdpa_bf16_b4_h16_n4096_d128_causal", B=4, H=16, N=4096
                 dtype="bf16", scale="1/sqrt(128)")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_causal_b4h16n4096d128_hbm_traffic.json")
 KERNEL_SOURCES = ["transformer_scaled_dot_amd/csrc/attn_fwd_bf16.hip", "transformer_scaled_dot_amd/csrc/attn_qb2_tile.inc",
-                  "transformer_scaled_dot_amd/csrc/device_common.h", "transformer_scaled_dot_amd/csrc/attn_tiles.h"]
+                  "transformer_scaled_dot_amd/csrc/device_common.h", "transformer_scaled_dot_amd/csrc/attn_tiles.h",
+                  "transformer_scaled_dot_amd/csrc/attn_sched.h"]
 
 
 def kernel_source_hash() -> str:

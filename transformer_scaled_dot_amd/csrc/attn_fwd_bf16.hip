@@ -29,6 +29,7 @@
 //     scalar per lane; it is skipped when no row of the wave changed max.
 //   * Causal: key tiles above a wave's diagonal are skipped, tiles crossing
 //     it are masked; workgroups are issued longest-first.
+#include "attn_sched.h"
 #include "attn_tiles.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -51,9 +52,6 @@ constexpr float kRescaleSlack = 8.f;    // log2 units the reference max may lag 
 #define TSD_D128_DESIGN 3
 #endif
 constexpr int kD128Design = TSD_D128_DESIGN;
-#ifndef TSD_HEAD_MAJOR
-#define TSD_HEAD_MAJOR 1
-#endif
 #ifndef TSD_WAVES128
 #define TSD_WAVES128 8
 #endif
@@ -456,48 +454,6 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2])
 struct Qb2Item {
     int valid, bh, b, kvh, q0, kv_len, kv_end, ntiles;
 };
-
-// Item of workgroup w in round k: even rounds in workgroup order, odd rounds reversed (by groups of 8 when
-// G is a multiple of 8, so that the XCD stays the same).
-__device__ __forceinline__ int qb2_round_item(int w, int k, int G)
-{
-    const int i = (k & 1) ? ((G & 7) == 0 ? (G / 8 - 1 - w / 8) * 8 + (w & 7) : G - 1 - w) : w;
-    return k * G + i;
-}
-
-// The j-th item workgroup w processes (>= num_items: none). A workgroup takes its rounds' items starting
-// from round w mod (its item count), so that item boundaries -- where a workgroup waits for its next
-// item's first tiles -- do not fall at the same time on every CU.
-__device__ __forceinline__ int qb2_sched(int w, int j, int G, int num_items)
-{
-    const int rounds = num_items / G;
-    const int n_w = rounds + (qb2_round_item(w, rounds, G) < num_items ? 1 : 0);
-    if (j >= n_w) return num_items;
-    return qb2_round_item(w, (j + w) % n_w, G);
-}
-
-// Head-major alternative for grids of whole XCDs (G % 8 == 0, workgroup w on XCD w % 8) when every XCD can
-// take the same number of whole rounds: XCD x runs the items of heads bh = x, x + 8, ... in head order, all
-// query blocks of one head next to each other, so that the M = G / 8 workgroups of an XCD work on one or
-// two heads at a time and share those heads' K/V tiles in the XCD's L2. Workgroup m takes slot m of even
-// rounds and slot M - 1 - m of odd ones (long and short items alternate). Sets bh and the query-block
-// index of the workgroup's j-th item (item index qt * BH + bh); false when it has none.
-__device__ __forceinline__ bool qb2_sched_heads(int w, int j, int G, int BH, int num_qtiles, int &bh, int &qt)
-{
-    const int M = G / 8, x = w & 7, m = w >> 3;
-    const int rounds = (BH / 8) * num_qtiles / M;
-    if (j >= rounds) return false;
-    const int n = j * M + ((j & 1) ? M - 1 - m : m);
-    const int k = n / num_qtiles;
-    qt = n - k * num_qtiles;
-    bh = x + 8 * k;
-    return true;
-}
-
-__device__ __forceinline__ bool qb2_heads_schedule(int G, int BH, int num_qtiles)
-{
-    return TSD_HEAD_MAJOR && G % 8 == 0 && BH % 8 == 0 && ((BH / 8) * num_qtiles) % (G / 8) == 0;
-}
 
 // The parameters of the item (bh, query block qt of the schedule's order); valid = false: no item.
 template <int MASK>
