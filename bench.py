@@ -252,7 +252,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        print("bench.py: the benchmark runs on one GPU only; --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch
