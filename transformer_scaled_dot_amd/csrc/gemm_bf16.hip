@@ -9,15 +9,21 @@
 // an accumulator lane holds one output ROW and four consecutive columns per
 // register group: stores are 8 contiguous bytes per lane. The B^T operand is
 // read from the row-major B tile with ds_read_b64_tr_b16, the A^T operand
-// with plain 16-byte LDS reads. Tiles are 128 x BN x 32 with 2 x 2 waves and
-// a double-buffered LDS stage.
+// with plain 16-byte LDS reads. Tiles are 128 x BN x BK with 2 x 2 waves and a double-buffered LDS
+// stage: 128 x 128 x 32 on grids of at least two workgroups per CU, else 128 x 64 x 64 where K allows.
 #include "device_common.h"
 #include "kernels.h"
+
+#include <type_traits>
+
+#ifndef TSD_GEMM_NARROW_BK
+#define TSD_GEMM_NARROW_BK 64
+#endif
 
 namespace tsd {
 namespace {
 
-constexpr int kBM = 128, kBK = 32;
+constexpr int kBM = 128, kBK = 32;  // kBK: the smallest k-step, the granularity K must have
 
 enum Epilogue { kEpiPlain = 0, kEpiQkvSplit = 1 };
 
@@ -25,19 +31,19 @@ struct QkvShape {
     int batch, seq, d_model, heads, dk;
 };
 
-template <int BN, int EPI>
+template <int BN, int BK, int EPI>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ Bm,
                                                         uint16_t *__restrict__ C, int M, int N, int Kd, QkvShape qs)
 {
     constexpr int TM = kBM / 2, TN = BN / 2;  // per-wave tile
     constexpr int MB = TM / 32, NB = TN / 32;
-    constexpr int SA = kBK + 8;    // A row pitch (elements): 16-byte reads of 16 rows hit disjoint banks
+    constexpr int SA = BK + 8;    // A row pitch (elements): 16-byte reads of 16 rows hit disjoint banks
     constexpr int SB = BN + 16;    // B row pitch
-    constexpr int ACH = kBM * kBK / 8 / 256;  // 16-byte chunks per thread
-    constexpr int BCH = kBK * BN / 8 / 256;
+    constexpr int ACH = kBM * BK / 8 / 256;  // 16-byte chunks per thread
+    constexpr int BCH = BK * BN / 8 / 256;
     static_assert(ACH >= 1 && BCH >= 1, "");
     __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * SA];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBK * SB];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BK * SB];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
@@ -52,7 +58,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t *__restri
 #pragma unroll
         for (int i = 0; i < ACH; ++i) {
             const int c = tid + i * 256;
-            const int row = c / (kBK / 8), col = (c % (kBK / 8)) * 8;
+            const int row = c / (BK / 8), col = (c % (BK / 8)) * 8;
             const int m = m0 + row;
             areg[i] = m < M ? *(const u32x4 *)(A + (size_t)m * Kd + k0 + col) : u32x4{0u, 0u, 0u, 0u};
         }
@@ -67,7 +73,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t *__restri
 #pragma unroll
         for (int i = 0; i < ACH; ++i) {
             const int c = tid + i * 256;
-            const int row = c / (kBK / 8), col = (c % (kBK / 8)) * 8;
+            const int row = c / (BK / 8), col = (c % (BK / 8)) * 8;
             *(u32x4 *)(&As[buf][row * SA + col]) = areg[i];
         }
 #pragma unroll
@@ -86,16 +92,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t *__restri
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.f;
 
-    const int nk = Kd / kBK;
+    const int nk = Kd / BK;
     load(0);
     store(0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) load((kt + 1) * kBK);
+        if (kt + 1 < nk) load((kt + 1) * BK);
         const uint16_t *as = As[kt & 1];
         const uint16_t *bs = Bs[kt & 1];
 #pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
+        for (int kk = 0; kk < BK / 16; ++kk) {
             bf16x8 bop[MB];
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
@@ -151,12 +157,19 @@ hipError_t launch(const void *A, const void *Bm, void *C, int M, int N, int K, Q
     const bool wide = (N % 128 == 0) && mt * (N / 128) >= 512;
     const long long grid = mt * (wide ? N / 128 : N / 64);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    auto go = [&](auto bn, auto bk) {
+        hipLaunchKernelGGL((gemm_bf16_kernel<decltype(bn)::value, decltype(bk)::value, EPI>), dim3((unsigned)grid),
+                           dim3(256), 0, stream, (const uint16_t *)A, (const uint16_t *)Bm, (uint16_t *)C, M, N, K, qs);
+    };
+    // narrow grids (fewer workgroups, each waiting on its global loads once per k-step) take deeper k-steps
+    // where K allows: fewer load round trips and barriers, more products between them
+    constexpr int NBK = TSD_GEMM_NARROW_BK;
     if (wide)
-        hipLaunchKernelGGL((gemm_bf16_kernel<128, EPI>), dim3((unsigned)grid), dim3(256), 0, stream,
-                           (const uint16_t *)A, (const uint16_t *)Bm, (uint16_t *)C, M, N, K, qs);
+        go(std::integral_constant<int, 128>(), std::integral_constant<int, 32>());
+    else if (K % NBK == 0)
+        go(std::integral_constant<int, 64>(), std::integral_constant<int, NBK>());
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<64, EPI>), dim3((unsigned)grid), dim3(256), 0, stream,
-                           (const uint16_t *)A, (const uint16_t *)Bm, (uint16_t *)C, M, N, K, qs);
+        go(std::integral_constant<int, 64>(), std::integral_constant<int, 32>());
     return hipGetLastError();
 }
 
