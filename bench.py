@@ -339,6 +339,10 @@ def main():
         rg = bench_grouped_lse(dev, args.steps, max(200, args.warmup // 4))
         extra["C3_gqa_h16_kv4_causal_padding_lse"] = {"ms": round(rg["ms"], 5),
                                                      "tflops": round(rg["flops"] / rg["ms"] / 1e9, 2)}
+        # the fp32 accuracy path at its tiny shape [2,1,5,16]: launch-latency bound, reported in microseconds
+        r1 = bench_attention(dev, 1, args.steps, 100, "none", out_dtype=torch.float32)
+        extra["C1_f32_b2h1n5d16"] = {"us_per_launch": round(r1["ms"] * 1e3, 2),
+                                     "us_median": round(float(np.median(r1["each"])) * 1e3, 2)}
         rb = bench_backward(dev, max(20, args.steps // 5), 20)
         extra["C3_backward_causal_b4h16n4096d128"] = {"ms": round(rb["ms"], 4),
                                                       "tflops": round(rb["flops"] / rb["ms"] / 1e9, 2)}
