@@ -304,3 +304,17 @@ def test_clock_probe_reports_plausible_rate(dev):
     say("clock probe: %.0f MHz, %.1f TFLOP/s (clock-scaled ceiling %.1f)" % (p["clock_mhz"], p["tflops"], ceiling))
     assert 300 < p["clock_mhz"] < 3000
     assert 50 < p["tflops"] <= ceiling * 1.02
+
+
+@pytest.mark.parametrize("mask", ["none", "causal", "padding"])
+def test_d64_eight_wave_launch(dev, mask):
+    """Head_dim 64 on a grid that takes the 8-wave (256-row) workgroups: B2 H16 N2000 (8 query tiles of 256
+    rows per head, 256 workgroups, the last tile ragged), sampled rows and tile edges against the oracle."""
+    B, H, N, d = 2, 16, 2000, 64
+    q, k, v = (synth.normal_tensor(5100 + i, (B, H, N, d)) for i in range(3))
+    vl = np.asarray([1999, 777], dtype=np.int32)
+    got = gpu_attn(dev, q, k, v, mask=mask, vl=vl if mask == "padding" else None).reshape(-1, d)
+    rows = sample_rows(B, H, N, 2048, seed=51, tile=256)
+    ref = oracle.attention_rows_per_head(q.f32, k.f32, v.f32, rows, mask=mask,
+                                         valid_lens=vl if mask == "padding" else None)
+    check("bf16 [2,16,2000,64] %s, 8-wave launch (sampled rows)" % mask, got[rows], ref, "bf16")

@@ -55,10 +55,10 @@ constexpr int kD128Design = TSD_D128_DESIGN;
 #ifndef TSD_WAVES128
 #define TSD_WAVES128 8
 #endif
-// Wavefronts per workgroup of the generic kernel. 128-wide heads: 8 waves
-// (two per SIMD) share one copy of each K/V tile in LDS, which halves the
-// LDS write traffic of the tile loads against two 4-wave workgroups per CU.
-constexpr int kWaves128 = TSD_WAVES128, kWaves64 = 4;
+// Wavefronts per workgroup of the generic kernel for 128-wide heads (design 1): 8 waves (two per SIMD)
+// share one copy of each K/V tile in LDS, which halves the LDS write traffic of the tile loads against
+// two 4-wave workgroups per CU. (64-wide heads choose 4 or 8 per launch.)
+constexpr int kWaves128 = TSD_WAVES128;
 
 // Online softmax of one tile of scores of one query block, base 2 (scale *
 // log2(e) folded into c_log2 > 0, so a masked score -inf gives exactly
@@ -709,35 +709,57 @@ int device_cu_count()
     return n;
 }
 
-template <int D, int MASK, bool OUT_F32, int OLAYOUT>
-hipError_t launch_variant(const void *Q, const void *K, const void *V, const int32_t *valid_lens, float scale,
-                          void *O, int B, int H, int Nq, int Nk, AttnHeads hd, hipStream_t stream)
+// The C++ MFMA kernel (32 * QB query rows per wave, WAVES waves per workgroup) on its grid of query tiles.
+template <int D, int QB, int MASK, bool OUT_F32, int OLAYOUT, int WAVES>
+hipError_t launch_cpp(const void *Q, const void *K, const void *V, const int32_t *valid_lens, float c_log2, void *O,
+                      int B, int H, int Nq, int Nk, AttnHeads hd, hipStream_t stream)
 {
-    // 32 (QB = 1) or 64 (QB = 2) query rows per wave; 64-row waves need the
-    // whole register file: one wave per SIMD, 4 per workgroup
-    constexpr bool QB2ASM = D == 128 && kD128Design == 3;
-    constexpr int QB = (D == 128 && kD128Design >= 2) ? 2 : 1;
-    constexpr int WAVES = QB == 2 ? 4 : (D == 128 ? kWaves128 : kWaves64);
     constexpr int BM = WAVES * 32 * QB;
     const int BH = B * H;
     const int num_qtiles = (Nq + BM - 1) / BM;
     const long long grid = (long long)num_qtiles * BH;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    // exp(x) = exp2(x * log2(e)). The kernel needs c_log2 > 0 so that masked
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QB, MASK, OUT_F32, OLAYOUT, WAVES>), dim3((unsigned)grid),
+                       dim3(WAVES * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
+                       valid_lens, c_log2, O, H, Nq, Nk, num_qtiles, BH, hd);
+    return hipGetLastError();
+}
+
+template <int D, int MASK, bool OUT_F32, int OLAYOUT>
+hipError_t launch_variant(const void *Q, const void *K, const void *V, const int32_t *valid_lens, float scale,
+                          void *O, int B, int H, int Nq, int Nk, AttnHeads hd, hipStream_t stream)
+{
+    // exp(x) = exp2(x * log2(e)). The kernels need c_log2 > 0 so that masked
     // scores (-inf) map to weight 0 without a select; below 1e-30 every
     // visible exp2 argument rounds to 0 anyway, which is the scale = 0 result.
     const float c_log2 = fmaxf(scale * 1.4426950408889634f, 1e-30f);
-    if constexpr (QB2ASM)
+    if constexpr (D == 128 && kD128Design == 3) {
+        // 64 query rows per wave: the whole register file, one wave per SIMD, 4 per workgroup; a persistent
+        // grid of at most one workgroup per CU over 256-row work items
+        const int BH = B * H;
+        const int num_qtiles = (Nq + 255) / 256;
+        const long long grid = (long long)num_qtiles * BH;
+        if (grid <= 0) return hipSuccess;
+        if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL((attn_fwd_qb2_kernel<MASK, OUT_F32, OLAYOUT>),
                            dim3((unsigned)std::min<long long>(grid, device_cu_count())), dim3(256), 0, stream,
                            (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, valid_lens, c_log2, O, H,
                            Nq, Nk, num_qtiles, BH, hd);
-    else
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QB, MASK, OUT_F32, OLAYOUT, WAVES>), dim3((unsigned)grid),
-                           dim3(WAVES * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
-                           valid_lens, c_log2, O, H, Nq, Nk, num_qtiles, BH, hd);
-    return hipGetLastError();
+        return hipGetLastError();
+    } else if constexpr (D == 64) {
+        // 8 waves (256 rows per workgroup) when that grid still gives every CU a workgroup (4.5 % faster at
+        // B4 H8 N2048), else 4 (128 rows: twice the workgroups for small launches)
+        const long long g8 = (long long)((Nq + 255) / 256) * B * H;
+        if (g8 >= device_cu_count())
+            return launch_cpp<D, 1, MASK, OUT_F32, OLAYOUT, 8>(Q, K, V, valid_lens, c_log2, O, B, H, Nq, Nk, hd, stream);
+        return launch_cpp<D, 1, MASK, OUT_F32, OLAYOUT, 4>(Q, K, V, valid_lens, c_log2, O, B, H, Nq, Nk, hd, stream);
+    } else if constexpr (kD128Design == 2) {
+        return launch_cpp<D, 2, MASK, OUT_F32, OLAYOUT, 4>(Q, K, V, valid_lens, c_log2, O, B, H, Nq, Nk, hd, stream);
+    } else {
+        return launch_cpp<D, 1, MASK, OUT_F32, OLAYOUT, kWaves128>(Q, K, V, valid_lens, c_log2, O, B, H, Nq, Nk, hd,
+                                                                   stream);
+    }
 }
 
 template <int D, int MASK>
