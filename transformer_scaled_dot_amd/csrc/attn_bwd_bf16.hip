@@ -193,7 +193,10 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
     const int l32 = lane & 31, hf = lane >> 5;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int kg = wv & 3, qh = wv >> 2;
-    const int kbk = blockIdx.x % num_kblocks, bk = blockIdx.x / num_kblocks;
+    // key block major: every head's first key block, then every head's second, ... With the causal mask
+    // the first blocks see the most query tiles, so the longest workgroups are dispatched first
+    const int BHkv = (int)(gridDim.x / num_kblocks);
+    const int kbk = blockIdx.x / BHkv, bk = blockIdx.x % BHkv;
     const int b = bk / Hkv, hk = bk % Hkv;
     const int kwg0 = kbk * 128, key = kwg0 + kg * 32 + l32;
 
