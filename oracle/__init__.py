@@ -171,10 +171,14 @@ def attention_rows(q, k, v, rows, mask="none", valid_lens=None, scale=None, thre
     return (O, L) if return_lse else O
 
 
-def attention_rows_per_head(q, k, v, rows, mask="none", valid_lens=None, scale=None, threads=0, return_lse=False):
+def attention_rows_per_head(q, k, v, rows, mask="none", valid_lens=None, scale=None, threads=0, return_lse=False,
+                            lib=None):
     """Like :func:`attention_rows`, but ``q, k, v`` may be any arrays that
     index as [b, h] -> [N, d] (e.g. float32 views of huge inputs): only the
-    heads that the rows touch are widened to float64, one head at a time."""
+    heads that the rows touch are widened to float64, one head at a time.
+    Flat row r belongs to batch b, query head h = divmod(r // Nq, H) and
+    query i = r % Nq; it reads K/V head h // (H // H_kv) of batch b and, for
+    the padding masks, valid_lens[b]."""
     rows = np.asarray(rows, dtype=np.int64)
     H, Nq = q.shape[1], q.shape[2]
     grp = H // k.shape[1]
@@ -187,7 +191,7 @@ def attention_rows_per_head(q, k, v, rows, mask="none", valid_lens=None, scale=N
         vl = None if mask not in _USES_VALID_LENS else np.asarray([valid_lens[b]], dtype=np.int32)
         out[sel], lse[sel] = attention_rows(_f64(q[b, h])[None, None], _f64(k[b, h // grp])[None, None],
                                             _f64(v[b, h // grp])[None, None], rows[sel] % Nq, mask=mask,
-                                            valid_lens=vl, scale=scale, threads=threads, return_lse=True)
+                                            valid_lens=vl, scale=scale, threads=threads, return_lse=True, lib=lib)
     return (out, lse) if return_lse else out
 
 

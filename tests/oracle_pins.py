@@ -335,6 +335,29 @@ def pin_row_subset_equals_full(lib):
     assert np.array_equal(Or, O[rows])
 
 
+def pin_rows_per_head_equals_full(lib, mod=None):
+    """The per-head row helper (flat row -> batch, query head, query index; K/V head h // (H / H_kv); the
+    batch's own valid length) gives the same rows, bit for bit, as the full call, for every mask, grouped
+    and plain K/V heads, per-batch valid lengths and float32 views of the inputs. ``mod`` is the module
+    whose helper is checked (the oracle itself by default; altered copies in the planted-mistake test)."""
+    mod = oracle if mod is None else mod
+    B, H, Nq, Nk, d = 2, 4, 9, 11, 8
+    vl = np.asarray([3, 11], dtype=np.int32)
+    q32 = _randn(1450, (B, H, Nq, d)).astype(np.float32)
+    for hkv in (1, 2, 4):
+        k32 = _randn(1451 + hkv, (B, hkv, Nk, d)).astype(np.float32)
+        v32 = _randn(1461 + hkv, (B, hkv, Nk, d)).astype(np.float32)
+        q, k, v = (t.astype(np.float64) for t in (q32, k32, v32))
+        # every row, in an order that visits the heads and batches out of sequence
+        rows = np.asarray([(r * 37) % (B * H * Nq) for r in range(B * H * Nq)], dtype=np.int64)
+        for mask in _ALL_MASKS:
+            O, L = oracle.attention(q, k, v, mask=mask, valid_lens=vl, lib=lib, return_lse=True)
+            Or, Lr = mod.attention_rows_per_head(q32, k32, v32, rows, mask=mask, valid_lens=vl, return_lse=True,
+                                                 lib=lib)
+            assert np.array_equal(Or, O.reshape(-1, d)[rows]), (hkv, mask)
+            assert np.array_equal(Lr, L.reshape(-1)[rows]), (hkv, mask)
+
+
 # --- log-sum-exp of the scores ----------------------------------------------
 
 def pin_lse_hand_example_page1(lib):

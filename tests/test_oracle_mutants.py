@@ -2,11 +2,12 @@
 plausible slip (a dropped term, a wrong sign, index or operand) must be
 caught by at least one pin. The real oracle is never modified."""
 import os
+import types
 
 import pytest
 
 import oracle
-from oracle_pins import PINS
+from oracle_pins import PINS, pin_rows_per_head_equals_full
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
 
@@ -57,3 +58,28 @@ def test_pins_catch_planted_mistake(name, tmp_path):
         except (AssertionError, ValueError, FloatingPointError):
             caught.append(pin.__name__)
     assert caught, "no pin caught the planted mistake %s" % name
+
+
+# mistakes in the Python helper that maps flat rows of huge inputs to their heads (oracle/__init__.py)
+PY_SRC = oracle.__file__
+PY_MUTANTS = {
+    "rows_kv_head_round_robin": ("_f64(k[b, h // grp])", "_f64(k[b, h % grp])"),
+    "rows_first_batch_length_for_all": ("np.asarray([valid_lens[b]], dtype=np.int32)",
+                                        "np.asarray([valid_lens[0]], dtype=np.int32)"),
+    "rows_query_index_from_head": ("rows[sel] % Nq, mask=mask,", "(rows[sel] // H) % Nq, mask=mask,"),
+    "rows_batch_head_swapped": ("b, h = divmod(int(bh), H)", "h, b = divmod(int(bh), B)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_rows_helper_pin_catches_planted_mistake(name):
+    old, new = PY_MUTANTS[name]
+    text = open(PY_SRC, encoding="utf-8").read()
+    assert text.count(old) == 1, "mutation site not found exactly once: %r" % old
+    if name == "rows_batch_head_swapped":
+        new = new.replace("B)", "q.shape[0])")
+    mod = types.ModuleType("oracle_mutant_" + name)
+    mod.__file__ = PY_SRC  # the altered helper still loads the real C oracle
+    exec(compile(text.replace(old, new), PY_SRC, "exec"), mod.__dict__)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        pin_rows_per_head_equals_full(None, mod=mod)
