@@ -112,6 +112,11 @@ def test_backward_ragged_and_tiny(dev):
     for (nq, nk) in [(1, 1), (5, 5), (64, 64), (129, 129)]:
         run_case(dev, 4300 + nq, 1, 2, 1, nq, nk, 64, "causal")
     run_case(dev, 4310, 1, 2, 2, 70, 33, 128, "none", scale=0.3)
+    # scale 0: uniform weights over the visible keys, dQ = dK = 0; masked scores must still get weight 0
+    for d in (64, 128):
+        run_case(dev, 4320 + d, 2, 2, 1, 100, 100, d, "causal", scale=0.0)
+        run_case(dev, 4330 + d, 2, 2, 2, 90, 150, d, "padding", vl=[17, 150], scale=0.0)
+        run_case(dev, 4340 + d, 2, 2, 2, 130, 130, d, "causal_padding", vl=[0, 77], scale=0.0)
 
 
 def test_backward_longer(dev):
@@ -119,10 +124,12 @@ def test_backward_longer(dev):
     run_case(dev, 4400, 1, 2, 1, 1024, 1024, 128, "causal")
 
 
-def test_backward_full_size_sampled_heads(dev):
-    """The causal 4K launch shape (B4 H16 N4096 d128): the backward runs on the whole workload and two of
-    its 64 (batch, head) slices are compared element by element with the oracle (a head's gradients
-    depend only on that head's Q, K, V and dO), within the same per-element bounds."""
+@pytest.mark.timeout(600)
+def test_backward_full_size_eight_heads(dev):
+    """The causal 4K launch shape (B4 H16 N4096 d128): the backward runs on the whole workload and eight of
+    its 64 (batch, head) slices, spread over the batches and heads, are compared element by element with the
+    oracle (a head's gradients depend only on that head's Q, K, V and dO), within the same per-element
+    bounds."""
     import transformer_scaled_dot_amd as tsd
 
     B, H, N, d = 4, 16, 4096, 128
@@ -132,7 +139,7 @@ def test_backward_full_size_sampled_heads(dev):
     dq, dk, dv = tsd.attn_bwd(Q, K, V, o, G, lse, mask="causal")
     torch.cuda.synchronize()
     scale = 1.0 / np.sqrt(d)
-    for b, h in ((0, 0), (3, 15)):
+    for b, h in ((0, 0), (0, 9), (1, 3), (1, 14), (2, 6), (2, 11), (3, 1), (3, 15)):
         sl = lambda t: t.f32[b:b + 1, h:h + 1].astype(np.float64)
         got = [x[b:b + 1, h:h + 1].float().cpu().numpy().astype(np.float64) for x in (dq, dk, dv)]
         ref = oracle.attention_backward(sl(q), sl(k), sl(v), sl(g), mask="causal", scale=scale)

@@ -4,10 +4,11 @@ same seeded inputs, on an MI355X.
 Tolerances (max / mean absolute error against the float64 oracle):
   float32 inputs:                       max <= 1e-5
   bfloat16 inputs, f32 accumulation:    max <= 2e-2 and mean <= 2e-3
-Small and ragged shapes are compared element by element; the full-size
-workloads are compared on sampled query rows that the oracle computes one by
-one (rows are independent, so each sampled row is exact), plus properties
-that hold for every row at any size.
+Every shape, the full-size workloads included, is compared element by
+element with the oracle on the whole output; the long-context workload's
+oracle runs one head at a time (heads are independent). Properties that hold
+for every row at any size (weights summing to one, masked keys never reaching
+the output) are checked besides.
 """
 import math
 
@@ -58,20 +59,6 @@ def check(name, got, ref, dtype):
         assert mx <= TOL_F32, name
     else:
         assert mx <= TOL_BF16_MAX and mean <= TOL_BF16_MEAN, name
-
-
-def sample_rows(B, H, N, count, seed, tile=128):
-    """Flat row indices (b*H + h)*N + i: rows 0, 1, N-1 and both sides of
-    every tile edge of a few heads, plus seeded uniform rows."""
-    rng_rows = (synth.uniform01(seed, count) * (B * H * N)).astype(np.int64) % (B * H * N)
-    heads = (synth.uniform01(seed + 1, 4) * (B * H)).astype(np.int64) % (B * H)
-    edges = []
-    for bh in heads:
-        for e in list(range(0, N, tile)) + [1, N - 1]:
-            for i in (e - 1, e, e + 1):
-                if 0 <= i < N:
-                    edges.append(bh * N + i)
-    return np.unique(np.concatenate([rng_rows, np.asarray(edges, dtype=np.int64)]))
 
 
 # ---------------------------------------------------------------- float32 path
@@ -216,21 +203,75 @@ def test_empty_and_degenerate(dev):
     assert tsd.attn_fwd(z, kk, kk).shape == (1, 1, 0, 64)
 
 
+def oracle_by_heads(q, k, v, mask, vl=None, label="", heads_per_call=None):
+    """The oracle's whole output, computed over groups of (query head, K/V head) pairs of all batches so
+    that only one group's inputs are widened to float64 at a time; prints its progress."""
+    B, H = q.shape[:2]
+    grp = H // k.shape[1]
+    step = heads_per_call or H
+    out = np.empty(q.shape[:3] + (v.shape[3],), dtype=np.float64)
+    for h0 in range(0, H, step):
+        hs = list(range(h0, min(H, h0 + step)))
+        kv = sorted({h // grp for h in hs})
+        # every query head of the group reads its own K/V head: pass one K/V head per query head
+        kk = np.stack([k[:, h // grp] for h in hs], axis=1)
+        vv = np.stack([v[:, h // grp] for h in hs], axis=1)
+        out[:, hs] = oracle.attention(q[:, hs], kk, vv, mask=mask, valid_lens=vl)
+        if step < H:
+            say("%s: oracle heads %d..%d of %d done (K/V heads %s)" % (label, hs[0], hs[-1], H, kv))
+    return out
+
+
 def test_config3_causal_full_size(dev):
-    """B4 H16 N4096 d128 causal, the launch the bench times: sampled rows
-    against the oracle, and every row's weights summing to one (V = 1)."""
+    """B4 H16 N4096 d128 causal, the launch the bench times: every output element against the oracle, and
+    every row's weights summing to one (V = 1)."""
     q, k, v, _ = synth.attn_inputs(3)
-    B, H, N, d = q.shape
-    got = gpu_attn(dev, q, k, v, mask="causal").reshape(-1, d)
-    rows = sample_rows(B, H, N, 4096, seed=30)
-    say("C3: %d sampled rows" % rows.size)
-    ref = oracle.attention_rows_per_head(q.f32, k.f32, v.f32, rows, mask="causal")
-    check("C3 bf16 [4,16,4096,128] causal (sampled rows)", got[rows], ref, "bf16")
+    got = gpu_attn(dev, q, k, v, mask="causal")
+    ref = oracle_by_heads(q.f32, k.f32, v.f32, "causal")
+    check("C3 bf16 [4,16,4096,128] causal (every element)", got, ref, "bf16")
+    del got, ref
     ones = synth.Tensor(synth.f32_to_bf16_bits(np.ones(v.shape, np.float32)), "bf16", v.shape)
     o1 = gpu_attn(dev, q, k, ones, mask="causal", out_dtype="f32")
     err = np.abs(o1 - 1.0)
     say("C3 V=1: max |O-1| %.3e" % err.max())
     assert err.max() <= 4e-3
+
+
+def test_reference_max_moves_d128(dev):
+    """The 128-wide-head kernel keeps a per-row reference maximum that it moves (rescaling the partial
+    output and sum) only when a tile's maximum exceeds it by more than 2^8 in the exponent. Keys whose
+    scores rise from tile to tile (each 64-key tile's keys carry a growing component along the queries'
+    common direction) and a large scale make that move happen on most rows and tiles; the count is taken on
+    the CPU from the scores, and every element is compared with the oracle."""
+    B, H, N, d = 1, 4, 1024, 128
+    scale = 0.3
+    z = [synth.normal_f64(6100 + i, B * H * N * d).reshape(B, H, N, d) for i in range(3)]
+    u = np.ones(d) / np.sqrt(d)
+    tile = (np.arange(N) // 64).astype(np.float64)
+    qf = z[0] + 1.5 * u
+    kf = z[1] + (4.0 * tile)[None, None, :, None] * u
+    mk = lambda a: synth.Tensor(synth.f32_to_bf16_bits(a.astype(np.float32)), "bf16", a.shape)
+    q, k, v = mk(qf), mk(kf), mk(z[2])
+    # how often a tile's maximum (log2 units) exceeds the row's last reference by more than 8
+    moves = 0
+    for h in range(H):
+        S = q.f64[0, h] @ k.f64[0, h].T * scale * np.log2(np.e)
+        for mask in ("none", "causal"):
+            Sm = np.where(np.tril(np.ones((N, N), bool)), S, -np.inf) if mask == "causal" else S
+            tmax = Sm.reshape(N, N // 64, 64).max(axis=2)
+            ref = tmax[:, 0].copy()
+            for t in range(1, N // 64):
+                up = tmax[:, t] > ref + 8
+                moves += int(up.sum())
+                ref[up] = tmax[up, t]
+    say("reference moves in the inputs (rows x tiles, both masks): %d" % moves)
+    assert moves > 15000
+    for mask in ("none", "causal"):
+        for out in ("bf16", "f32"):
+            got = gpu_attn(dev, q, k, v, mask=mask, scale=scale, out_dtype=out)
+            ref = oracle.attention(q.f64, k.f64, v.f64, mask=mask, scale=scale)
+            check("bf16 [1,4,1024,128] %s scale %.2f rising tile maxima, out %s" % (mask, scale, out), got, ref,
+                  "bf16")
 
 
 def test_config4_mha_full(dev):
@@ -272,33 +313,41 @@ def test_mha_identity_projection_hand_example(dev, golden_dir):
     check("mha identity projections", got, oracle.mha(x.f64, wqkv.f64, wo.f64, h), "bf16")
 
 
+def bf16_half_ulp(x):
+    """Half a unit in the last place of bfloat16 (8 significant bits) at |x|: the most that rounding a
+    value of that size to the bf16 output can change it."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return 2.0 ** (e - 8)
+
+
+@pytest.mark.timeout(900)
 def test_config5_long_context(dev):
-    """B1 H32 N32768 d128 causal, inputs x2: sampled rows. With a float32
-    output the full tolerance applies to every sampled element; with a bf16
-    output, elements with |O| >= 8 carry up to 2^-5 of output rounding alone,
-    so they are reported separately."""
+    """B1 H32 N32768 d128 causal, inputs x2: every output element against the oracle (run one head at a
+    time). The float32 output carries no output rounding: every element is held to the tolerance. A bf16
+    output adds its own representation error on top of the arithmetic's, up to half a unit in the last
+    place of |O| (2^-7 for 2 <= |O| < 4, 2^-6 for 4 <= |O| < 8, values these x2 inputs reach), so each
+    bf16-output element is held to the tolerance plus that half unit, and the mean to the mean tolerance."""
     q, k, v, _ = synth.attn_inputs(5)
-    B, H, N, d = q.shape
-    rows = sample_rows(B, H, N, 4096, seed=50)
-    say("C5: %d sampled rows" % rows.size)
-    ref = oracle.attention_rows_per_head(q.f32, k.f32, v.f32, rows, mask="causal")
-    got = gpu_attn(dev, q, k, v, mask="causal", out_dtype="f32").reshape(-1, d)
-    check("C5 bf16 [1,32,32768,128] x2 causal, f32 out (sampled rows)", got[rows], ref, "bf16")
+    got = gpu_attn(dev, q, k, v, mask="causal", out_dtype="f32")
+    gotb = gpu_attn(dev, q, k, v, mask="causal")
+    ref = oracle_by_heads(q.f32, k.f32, v.f32, "causal", label="C5", heads_per_call=2)
+    check("C5 bf16 [1,32,32768,128] x2 causal, f32 out (every element)", got, ref, "bf16")
     del got
-    gotb = gpu_attn(dev, q, k, v, mask="causal").reshape(-1, d)[rows]
-    small = np.abs(ref) < 8
-    say("C5 bf16 out: %d of %d sampled elements have |O| >= 8" % ((~small).sum(), small.size))
-    check("C5 bf16 out, |O| < 8", gotb[small], ref[small], "bf16")
-    assert np.abs(gotb - ref).max() <= 2 ** -5 + TOL_BF16_MAX
+    err = np.abs(gotb - ref)
+    tol = TOL_BF16_MAX + bf16_half_ulp(ref)
+    say("C5 bf16 out: max abs err %.3e, mean %.3e, worst err / (tolerance + half unit) %.3f"
+        % (float(err.max()), float(err.mean()), float((err / tol).max())))
+    assert np.all(np.isfinite(gotb))
+    assert np.all(err <= tol) and float(err.mean()) <= TOL_BF16_MEAN
 
 
 def test_clock_probe_reports_plausible_rate(dev):
     """The measurement probe (not part of the attention path): a clock between 0.3 and 3 GHz and a matrix
     rate between 50 TFLOP/s and the published 2.5 PFLOP/s dense bf16 peak scaled to that clock (4 SIMDs per
     compute unit, 1024 bf16 flops per SIMD cycle)."""
-    import transformer_scaled_dot_amd as tsd
+    from transformer_scaled_dot_amd.probe import clock_probe
 
-    p = tsd.clock_probe(dev, spin_us=1000)
+    p = clock_probe(dev, spin_us=1000)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     ceiling = cus * 4 * 1024 * p["clock_mhz"] * 1e6 / 1e12
     say("clock probe: %.0f MHz, %.1f TFLOP/s (clock-scaled ceiling %.1f)" % (p["clock_mhz"], p["tflops"], ceiling))
@@ -306,15 +355,33 @@ def test_clock_probe_reports_plausible_rate(dev):
     assert 50 < p["tflops"] <= ceiling * 1.02
 
 
-@pytest.mark.parametrize("mask", ["none", "causal", "padding"])
+@pytest.mark.parametrize("mask", ["none", "causal", "padding", "causal_padding"])
 def test_d64_eight_wave_launch(dev, mask):
     """Head_dim 64 on a grid that takes the 8-wave (256-row) workgroups: B2 H16 N2000 (8 query tiles of 256
-    rows per head, 256 workgroups, the last tile ragged), sampled rows and tile edges against the oracle."""
+    rows per head, 256 workgroups, the last tile ragged), every element against the oracle."""
     B, H, N, d = 2, 16, 2000, 64
     q, k, v = (synth.normal_tensor(5100 + i, (B, H, N, d)) for i in range(3))
     vl = np.asarray([1999, 777], dtype=np.int32)
-    got = gpu_attn(dev, q, k, v, mask=mask, vl=vl if mask == "padding" else None).reshape(-1, d)
-    rows = sample_rows(B, H, N, 2048, seed=51, tile=256)
-    ref = oracle.attention_rows_per_head(q.f32, k.f32, v.f32, rows, mask=mask,
-                                         valid_lens=vl if mask == "padding" else None)
-    check("bf16 [2,16,2000,64] %s, 8-wave launch (sampled rows)" % mask, got[rows], ref, "bf16")
+    pad = mask in ("padding", "causal_padding")
+    got = gpu_attn(dev, q, k, v, mask=mask, vl=vl if pad else None)
+    ref = oracle.attention(q.f64, k.f64, v.f64, mask=mask, valid_lens=vl if pad else None)
+    check("bf16 [2,16,2000,64] %s, 8-wave launch" % mask, got, ref, "bf16")
+
+
+def test_d64_eight_wave_grouped_lse(dev):
+    """The 8-wave d64 workgroups with grouped K/V heads (16 query heads over 4) and the log-sum-exp."""
+    import transformer_scaled_dot_amd as tsd
+
+    B, H, Hkv, N, d = 2, 16, 4, 2000, 64
+    q = synth.normal_tensor(5200, (B, H, N, d))
+    k, v = (synth.normal_tensor(5201 + i, (B, Hkv, N, d)) for i in range(2))
+    vl = np.asarray([2000, 1234], dtype=np.int32)
+    o, lse = tsd.attn_fwd(q.torch(dev), k.torch(dev), v.torch(dev), mask="causal_padding",
+                          valid_lens=torch.from_numpy(vl).to(dev), return_lse=True)
+    torch.cuda.synchronize()
+    ref, rl = oracle.attention(q.f64, k.f64, v.f64, mask="causal_padding", valid_lens=vl, return_lse=True)
+    check("bf16 [2,16/4,2000,64] causal_padding, 8-wave launch", o.float().cpu().numpy().astype(np.float64), ref,
+          "bf16")
+    err = np.abs(lse.cpu().numpy().astype(np.float64) - rl)
+    say("  lse max abs err %.3e" % err.max())
+    assert err.max() <= 2.0 ** -8 + 1e-4

@@ -425,8 +425,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
         }
         // S^T = K Q^T and dP^T = V dO^T: one query per lane, rows = keys
         f32x16 s[1][2], dp[1][2];
-        scores<D, 1, KS, false>(smem, ad, qreg, s);
-        scores<D, 1, VS, false>(smem, ad, greg, dp);
+        scores<D, 1, KS>(smem, ad, qreg, s);
+        scores<D, 1, VS>(smem, ad, greg, dp);
         // a tile whose keys every row of the wave sees needs no mask
         const int klast = t * kBlockN + kBlockN - 1;
         if (!(klast < kv_len && (!mask_causal(MASK) || klast <= q0 + __builtin_amdgcn_readfirstlane(wave) * 32)))
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
             }
         bf16x8 sb[1][4];
         pack_operands(dp[0], sb);
-        accumulate_pv<D, 1, KS, false>(smem, ad, sb, dq);  // dQ^T += K^T dS^T
+        accumulate_pv<D, 1, KS>(smem, ad, sb, dq);  // dQ^T += K^T dS^T
         wait_vmcnt0();
         __syncthreads();
     };
@@ -461,7 +461,9 @@ hipError_t launch_bwd(const void *Q, const void *K, const void *V, const void *O
     const long long prows = BH * Nq_pad;
     float *lse2 = work, *delta = work + prows;
     const int group = H / Hkv;
-    const float c_log2 = scale * kLog2e;
+    // scale = 0 must still send masked scores (-inf) to weight 0: -inf * 0 would be NaN in the dQ kernel's
+    // exponent, so the factor is held above 0 (every score below 1e-30 in magnitude then weighs as 0 does)
+    const float c_log2 = fmaxf(scale * kLog2e, 1e-30f);
     if (prows > 0) {
         const long long threads = prows * (D / 8);
         hipLaunchKernelGGL((attn_bwd_delta_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
