@@ -1,12 +1,13 @@
 """Throughput of the attention forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--extra]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-s S] [--no-cpu-baseline] [--extra]
 
 One step = one attn_fwd launch over the causal workload B=4, H=16, N=4096,
 d=128 in bf16 (inputs already resident in HBM; two buffer sets alternate so
-the 256 MB Infinity Cache cannot hold a step's whole working set). The
-default warmup (about half a second of launches) lets the GPU clock settle
-at its sustained value under this load before the timed steps. Prints
+the 256 MB Infinity Cache cannot hold a step's whole working set). Before
+the W warmup steps, untimed launches run for S seconds (default 0.75) so
+that the GPU clock settles at its sustained value under this load; exactly K
+steps are then timed. Prints
 ONE JSON line with TFLOP/s (FLOPs counted as 4*B*H*N_q*N_k*d, halved for the
 causal mask), the kernel's roofline position, and the CPU oracle timed on a
 bounded sample of the same workload.
@@ -66,6 +67,25 @@ def hbm_traffic_per_launch():
     return t.get("bytes_per_launch")
 
 
+def settle_clock(fn, seconds):
+    """Untimed launches, back to back, until ``seconds`` of wall time have
+    passed (checked at a device synchronisation every 64 launches): the GPU
+    clock ramps up for a few hundred milliseconds under a sustained matrix
+    load, so without this the first timed launches run at a lower clock.
+    Returns (launches issued, wall seconds spent)."""
+    import torch
+
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(64):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n, time.perf_counter() - t0
+
+
 def time_launches(fn, nsteps, warmup, per_launch=False):
     """Warm up, then time exactly nsteps launches between two device
     synchronisations with HIP events on the launching (current) stream.
@@ -91,7 +111,7 @@ def time_launches(fn, nsteps, warmup, per_launch=False):
     return ev[0].elapsed_time(ev[-1]) / nsteps, wall, each
 
 
-def bench_attention(dev, cfg_id, nsteps, warmup, mask, sets=2, out_dtype=None):
+def bench_attention(dev, cfg_id, nsteps, warmup, mask, sets=2, out_dtype=None, settle_s=0.0):
     import torch
 
     import synth
@@ -110,6 +130,7 @@ def bench_attention(dev, cfg_id, nsteps, warmup, mask, sets=2, out_dtype=None):
         qq, kk, vv, oo = bufs[i % sets]
         tsd.attn_fwd(qq, kk, vv, mask=mask, valid_lens=vl_t, out=oo, out_dtype=oo.dtype)
 
+    settled = settle_clock(step, settle_s) if settle_s > 0 else (0, 0.0)
     ms, wall, _ = time_launches(step, nsteps, warmup)
     # a second pass with an event between launches for the per-launch spread (the events could add a
     # little between launches, so the mean above comes from a pass without them)
@@ -118,10 +139,10 @@ def bench_attention(dev, cfg_id, nsteps, warmup, mask, sets=2, out_dtype=None):
         flops = attn_flops(B, H, N, N, d, False)
     else:
         flops = attn_flops(B, H, N, N, d, mask == "causal")
-    return dict(ms=ms, wall=wall, flops=flops, shape=(B, H, N, d), valid_lens=vl, each=each)
+    return dict(ms=ms, wall=wall, flops=flops, shape=(B, H, N, d), valid_lens=vl, each=each, settled=settled)
 
 
-def bench_mha(dev, nsteps, warmup, sets=4):
+def bench_mha(dev, nsteps, warmup, sets=4, settle_s=0.0):
     import torch
 
     import synth
@@ -138,13 +159,15 @@ def bench_mha(dev, nsteps, warmup, sets=4):
         xx, ww, wwo, oo, ws = bufs[i % sets]
         tsd.mha_fwd(xx, ww, wwo, h, out=oo, workspace=ws)
 
+    if settle_s > 0:
+        settle_clock(step, settle_s)
     ms, wall, _ = time_launches(step, nsteps, warmup)
     dk = dm // h
     flops = 8.0 * B * N * dm * dm + 4.0 * B * h * N * N * dk
     return dict(ms=ms, wall=wall, flops=flops)
 
 
-def bench_grouped_lse(dev, nsteps, warmup, sets=2):
+def bench_grouped_lse(dev, nsteps, warmup, sets=2, settle_s=0.0):
     """The causal 4K workload with 4 K/V heads for its 16 query heads, the causal-and-padding mask (every
     valid length = N, so the work is the causal work) and the per-row log-sum-exp written out."""
     import torch
@@ -165,11 +188,13 @@ def bench_grouped_lse(dev, nsteps, warmup, sets=2):
         q, k, v, o, lse = bufs[i % sets]
         tsd.attn_fwd(q, k, v, mask="causal_padding", valid_lens=vl, out=o, lse=lse)
 
+    if settle_s > 0:
+        settle_clock(step, settle_s)
     ms, _, _ = time_launches(step, nsteps, warmup)
     return dict(ms=ms, flops=attn_flops(B, H, N, N, d, True))
 
 
-def bench_backward(dev, nsteps, warmup, sets=2):
+def bench_backward(dev, nsteps, warmup, sets=2, settle_s=0.0):
     """The backward pass at the causal 4K shape (B4 H16 N4096 d128): dQ, dK, dV from the forward's O and
     log-sum-exp and a synthetic output gradient. FLOPs: the five N x N x d products of the chain rule
     (S recomputed, dP, dV, dK, dQ), halved for causal, i.e. 2.5 times the forward's."""
@@ -190,8 +215,34 @@ def bench_backward(dev, nsteps, warmup, sets=2):
         q, k, v, g, o, lse, ws = bufs[i % sets]
         tsd.attn_bwd(q, k, v, o, g, lse, mask="causal", workspace=ws)
 
+    if settle_s > 0:
+        settle_clock(step, settle_s)
     ms, _, _ = time_launches(step, nsteps, warmup)
     return dict(ms=ms, flops=2.5 * attn_flops(B, H, N, N, d, True))
+
+
+def bench_one(dev, which, nsteps, warmup, settle_s):
+    """One of the other workloads, timed like the benchmark line (settle, warmup, timed steps)."""
+    if which == "padding":
+        r2 = bench_attention(dev, 2, nsteps, warmup, "padding", sets=16, settle_s=settle_s)
+        B2, H2, N2, d2 = r2["shape"]
+        L = r2["valid_lens"].astype(np.float64)
+        alg_flops = 4.0 * H2 * d2 * N2 * L.sum()
+        hbm = 2.0 * B2 * H2 * N2 * d2 * 2 + 2.0 * H2 * d2 * 2 * L.sum()  # Q, O + valid K, V rows
+        return {"ms": round(r2["ms"], 5), "tflops_metric": round(r2["flops"] / r2["ms"] / 1e9, 2),
+                "tflops_valid_keys": round(alg_flops / r2["ms"] / 1e9, 2),
+                "hbm_gbs_algorithmic": round(hbm / r2["ms"] / 1e6, 1),
+                "hbm_frac": round(hbm / r2["ms"] / 1e6 / PEAK_HBM_GBS, 4), "algorithmic_bytes": int(hbm)}
+    if which == "mha":
+        r4 = bench_mha(dev, nsteps, warmup, settle_s=settle_s)
+        return {"ms": round(r4["ms"], 5), "tflops": round(r4["flops"] / r4["ms"] / 1e9, 2)}
+    if which == "causal32k":
+        r5 = bench_attention(dev, 5, max(5, nsteps // 20), 5, "causal", sets=1, settle_s=settle_s)
+        return {"ms": round(r5["ms"], 4), "tflops": round(r5["flops"] / r5["ms"] / 1e9, 2)}
+    if which == "backward":
+        rb = bench_backward(dev, max(20, nsteps // 5), 20, settle_s=settle_s)
+        return {"ms": round(rb["ms"], 4), "tflops": round(rb["flops"] / rb["ms"] / 1e9, 2)}
+    raise ValueError(which)
 
 
 def cpu_baseline(target_s=15.0):
@@ -239,16 +290,19 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
-    # ~0.5 s of back-to-back launches: the GPU clock ramps up for a few hundred
-    # ms under this load, and the figure of interest is the sustained rate
-    ap.add_argument("--warmup", type=int, default=1500)
+    ap.add_argument("--warmup", type=int, default=20)
+    # the GPU clock ramps up for a few hundred ms under this load and the figure of interest is the sustained
+    # rate: untimed launches run for this long before the warmup steps (reported as "clock_settle")
+    ap.add_argument("--settle-s", type=float, default=0.75)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", action="store_true",
                     help="also time the padding, multi-head and 32K workloads, the grouped-heads/log-sum-exp "
                          "variant and the backward pass")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--backward-only", action="store_true",
-                    help="time only the backward pass at the causal 4K shape (for its kernel trace)")
+    ap.add_argument("--only", choices=["padding", "mha", "causal32k", "backward"],
+                    help="time only one other workload (for its kernel trace and counters): the padding workload "
+                         "B8 H8 N512 d64, the multi-head layer B4 N2048 d_model 512 h8, the causal B1 H32 N32768 "
+                         "d128 workload, or the backward pass at the causal 4K shape")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -267,14 +321,11 @@ def main():
     if args.copy_calibration:
         copy_calibration(dev)
         return
-    if args.backward_only:
-        rb = bench_backward(dev, max(20, args.steps // 5), 20)
-        print(json.dumps({"backward_causal_b4h16n4096d128": {"ms": round(rb["ms"], 4),
-                                                             "tflops": round(rb["flops"] / rb["ms"] / 1e9, 2)}}),
-              flush=True)
+    if args.only:
+        print(json.dumps({args.only: bench_one(dev, args.only, args.steps, args.warmup, args.settle_s)}), flush=True)
         return
 
-    r = bench_attention(dev, 3, args.steps, args.warmup, "causal")
+    r = bench_attention(dev, 3, args.steps, args.warmup, "causal", settle_s=args.settle_s)
     tflops = r["flops"] / (r["ms"] * 1e-3) / 1e12
     B, H, N, d = r["shape"]
     out = {
@@ -309,43 +360,33 @@ def main():
             "launch_ms_min": round(float(np.min(r["each"])), 5),
         },
         "wall_s_timed_region": round(r["wall"], 4),
+        "clock_settle": {"seconds": round(r["settled"][1], 3), "launches": r["settled"][0],
+                         "note": "untimed launches of the same step before the warmup steps, so that the timed "
+                                 "steps run at the clock the GPU sustains under this load"},
     }
     # right after the timed launches: every SIMD issuing only bf16 MFMAs on pseudo-random operands. Its clock
     # and rate are the practical matrix ceiling of this chip (the power limit holds the clock well under the
     # 2.4 GHz the published peak assumes); the roofline's peak stays the published one.
-    probe = tsd.clock_probe(dev)
+    from transformer_scaled_dot_amd.probe import clock_probe
+
+    probe = clock_probe(dev)
     out["sclk_mhz_after"] = round(probe["clock_mhz"], 0)
     out["mfma_only_probe"] = {"tflops": round(probe["tflops"], 1), "clock_mhz": round(probe["clock_mhz"], 0),
                                "operands": "pseudo-random bf16, uniform in [-2, 2)",
                                "value_over_probe": round(tflops / probe["tflops"], 4)}
     if args.extra:
         extra = {}
-        r2 = bench_attention(dev, 2, args.steps, args.warmup, "padding", sets=16)
-        B2, H2, N2, d2 = r2["shape"]
-        L = r2["valid_lens"].astype(np.float64)
-        alg_flops = 4.0 * H2 * d2 * N2 * L.sum()
-        hbm = 2.0 * B2 * H2 * N2 * d2 * 2 + 2.0 * H2 * d2 * 2 * L.sum()  # Q, O + valid K, V rows
-        extra["C2_padding_b8h8n512d64"] = {
-            "ms": round(r2["ms"], 5), "tflops_metric": round(r2["flops"] / r2["ms"] / 1e9, 2),
-            "tflops_valid_keys": round(alg_flops / r2["ms"] / 1e9, 2),
-            "hbm_gbs_algorithmic": round(hbm / r2["ms"] / 1e6, 1),
-            "hbm_frac": round(hbm / r2["ms"] / 1e6 / PEAK_HBM_GBS, 4)}
-        r4 = bench_mha(dev, args.steps, args.warmup)
-        extra["C4_mha_b4n2048dm512h8"] = {"ms": round(r4["ms"], 5),
-                                          "tflops": round(r4["flops"] / r4["ms"] / 1e9, 2)}
-        r5 = bench_attention(dev, 5, max(5, args.steps // 20), 5, "causal", sets=1)
-        extra["C5_causal_b1h32n32768d128"] = {"ms": round(r5["ms"], 4),
-                                              "tflops": round(r5["flops"] / r5["ms"] / 1e9, 2)}
-        rg = bench_grouped_lse(dev, args.steps, max(200, args.warmup // 4))
+        extra["C2_padding_b8h8n512d64"] = bench_one(dev, "padding", args.steps, args.warmup, 0.2)
+        extra["C4_mha_b4n2048dm512h8"] = bench_one(dev, "mha", args.steps, args.warmup, 0.2)
+        extra["C5_causal_b1h32n32768d128"] = bench_one(dev, "causal32k", args.steps, args.warmup, 0.3)
+        rg = bench_grouped_lse(dev, args.steps, args.warmup, settle_s=0.3)
         extra["C3_gqa_h16_kv4_causal_padding_lse"] = {"ms": round(rg["ms"], 5),
                                                      "tflops": round(rg["flops"] / rg["ms"] / 1e9, 2)}
         # the fp32 accuracy path at its tiny shape [2,1,5,16]: launch-latency bound, reported in microseconds
         r1 = bench_attention(dev, 1, args.steps, 100, "none", out_dtype=torch.float32)
         extra["C1_f32_b2h1n5d16"] = {"us_per_launch": round(r1["ms"] * 1e3, 2),
                                      "us_median": round(float(np.median(r1["each"])) * 1e3, 2)}
-        rb = bench_backward(dev, max(20, args.steps // 5), 20)
-        extra["C3_backward_causal_b4h16n4096d128"] = {"ms": round(rb["ms"], 4),
-                                                      "tflops": round(rb["flops"] / rb["ms"] / 1e9, 2)}
+        extra["C3_backward_causal_b4h16n4096d128"] = bench_one(dev, "backward", args.steps, args.warmup, 0.3)
         out["extra"] = extra
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
