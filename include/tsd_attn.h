@@ -192,27 +192,6 @@ TSD_API attn_status_t mha_fwd(const void *X, const void *W_qkv, const void *W_o,
                       int32_t seq, int32_t d_model, int32_t dtype, void *workspace, size_t workspace_bytes,
                       void *stream);
 
-/*
- * attn_clock_probe -- measurement support, not part of the attention path:
- * the shader clock and matrix-instruction rate the GPU sustains under a
- * pure matrix load. One workgroup of four waves (one per SIMD) per compute
- * unit issues back-to-back bf16 32x32x16 MFMAs (32768 flops each) on
- * pseudo-random operands, uniform in [-2, 2), for spin_us microseconds of
- * wall time, and records, per workgroup, the shader-clock ticks (s_memtime),
- * the 100 MHz wall-clock ticks (s_memrealtime) and the MFMAs each wave
- * issued: mean MHz = 100 * sum(ticks) / sum(wall ticks); rate = 4 waves *
- * 32768 * sum(MFMAs) / wall time. (With operands of zero the chip clocks
- * far higher: the rate with data is the practical matrix ceiling.)
- *
- *   out      device uint64 [3 * blocks], 8-byte aligned: (ticks, wall
- *            ticks, MFMAs per wave) per workgroup; written by the kernel
- *   blocks   1 .. 65536 workgroups (use the compute-unit count)
- *   spin_us  1 .. 100000
- *   stream   HIP stream (null: the default stream)
- * Errors: ATTN_EINVAL for a null or misaligned out or a count out of range.
- */
-TSD_API attn_status_t attn_clock_probe(uint64_t *out, int32_t blocks, int32_t spin_us, void *stream);
-
 /* Static description of a status code. */
 TSD_API const char *attn_status_string(int32_t status);
 

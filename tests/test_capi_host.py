@@ -114,6 +114,75 @@ def test_attn_fwd_empty_is_ok_without_gpu(lib):
     assert call_attn(lib, B=0) == 0
 
 
+GB = 1 << 28  # spacing of the fake buffers below: no two overlap at the sizes used
+
+
+def call_bwd(lib, Q=FAKE, K=FAKE + GB, V=FAKE + 2 * GB, O=FAKE + 3 * GB, dO=FAKE + 4 * GB, lse=FAKE + 5 * GB, mask=0,
+             vl=0, scale=0.125, dQ=FAKE + 6 * GB, dK=FAKE + 7 * GB, dV=FAKE + 8 * GB, B=1, H=4, Hkv=2, Nq=8, Nk=8,
+             d=64, dt=BF16, ws=FAKE + 9 * GB, wsb=1 << 20):
+    P = ctypes.c_void_p
+    return lib.attn_bwd(P(Q), P(K), P(V), P(O), P(dO), P(lse), mask, P(vl), ctypes.c_float(scale), P(dQ), P(dK),
+                        P(dV), B, H, Hkv, Nq, Nk, d, dt, P(ws), ctypes.c_size_t(wsb), P(0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), EINVAL),                           # negative size
+    (dict(Nk=-3), EINVAL),
+    (dict(d=0), EINVAL),                            # head_dim <= 0
+    (dict(Hkv=0), EINVAL),                          # kv_heads not positive
+    (dict(Hkv=3), EINVAL),                          # does not divide H = 4
+    (dict(mask=-1), EINVAL),                        # unknown mask kind
+    (dict(mask=4), EINVAL),
+    (dict(dt=7), EINVAL),                           # unknown dtype
+    (dict(scale=float("nan")), EINVAL),             # scale not finite
+    (dict(scale=float("-inf")), EINVAL),
+    (dict(scale=-0.5), EUNSUP),                     # negative scale
+    (dict(dt=F32), EUNSUP),                         # only bf16
+    (dict(d=32), EUNSUP),                           # head_dim 64 or 128
+    (dict(mask=1, Nq=8, Nk=9), EUNSUP),             # causal needs seq_q == seq_k
+    (dict(mask=3, vl=FAKE + 10 * GB, Nq=9, Nk=8), EUNSUP),
+    (dict(Q=0), EINVAL),                            # null pointers on the query side
+    (dict(O=0), EINVAL),
+    (dict(dO=0), EINVAL),
+    (dict(lse=0), EINVAL),
+    (dict(dQ=0), EINVAL),
+    (dict(K=0), EINVAL),                            # and on the key side
+    (dict(V=0), EINVAL),
+    (dict(dK=0), EINVAL),
+    (dict(dV=0), EINVAL),
+    (dict(mask=2, vl=0), EINVAL),                   # padding needs valid_lens
+    (dict(mask=3, vl=0), EINVAL),
+    (dict(ws=0), EINVAL),                           # workspace missing
+    (dict(wsb=255), EINVAL),                        # workspace too small (needs 2 * 4 * 64 * 4 bytes)
+    (dict(Q=FAKE + 8), EINVAL),                     # tensors 16-byte aligned
+    (dict(dV=FAKE + 8 * GB + 4), EINVAL),
+    (dict(lse=FAKE + 5 * GB + 2), EINVAL),          # lse 4-byte aligned
+    (dict(mask=2, vl=FAKE + 10 * GB + 1), EINVAL),  # valid_lens 4-byte aligned
+    (dict(ws=FAKE + 9 * GB + 16), EINVAL),          # workspace 256-byte aligned
+    (dict(dQ=FAKE), EINVAL),                        # an output overlaps an input
+    (dict(dK=FAKE + 5 * GB), EINVAL),               # dK over lse
+    (dict(ws=FAKE + 3 * GB), EINVAL),               # the workspace over O
+    (dict(dK=FAKE + 6 * GB), EINVAL),               # outputs overlap each other
+    (dict(ws=FAKE + 8 * GB), EINVAL),               # the workspace over dV
+])
+def test_attn_bwd_rejects(lib, kw, status):
+    assert call_bwd(lib, **kw) == status
+    assert lib.attn_last_error() != b""
+
+
+def test_attn_bwd_empty_is_ok_without_gpu(lib):
+    assert call_bwd(lib, Nq=0, Nk=0) == 0
+    assert call_bwd(lib, B=0, Q=0, K=0, V=0, O=0, dO=0, lse=0, dQ=0, dK=0, dV=0, ws=0, wsb=0) == 0
+
+
+def test_attn_bwd_workspace_bytes(lib):
+    # lse * log2(e) and D per query row, float32, rows padded to whole 64-row tiles, rounded up to 256 bytes
+    assert lib.attn_bwd_workspace_bytes(4, 16, 4096) == 2 * 4 * 16 * 4096 * 4
+    assert lib.attn_bwd_workspace_bytes(1, 3, 65) == 2 * 3 * 128 * 4
+    assert lib.attn_bwd_workspace_bytes(1, 1, 1) == 512
+    assert lib.attn_bwd_workspace_bytes(-1, 1, 1) == 0
+
+
 def call_mha(lib, X=FAKE, W=FAKE + (1 << 28), Wo=FAKE + (2 << 28), h=8, O=FAKE + (3 << 28), B=1, N=16, dm=512,
              dt=BF16, ws=FAKE + (4 << 28), wsb=1 << 27):
     P = ctypes.c_void_p
@@ -154,6 +223,10 @@ def test_binding_refuses_cpu_tensors(lib):
 
 
 @pytest.mark.parametrize("args", [(0, 256, 1000), (8, 0, 1000), (8, 65537, 1000), (8, 256, 0), (8, 256, 100001)])
-def test_clock_probe_rejects(lib, args):
+def test_clock_probe_rejects(args):
+    """The benchmark's clock probe lives in its own library, not in the attention library's exports."""
+    from transformer_scaled_dot_amd import probe
+
     ptr, blocks, spin = args
-    assert lib.attn_clock_probe(ctypes.c_void_p(ptr), blocks, spin, None) == EINVAL
+    assert probe._load().tsd_probe_clock(ctypes.c_void_p(ptr), blocks, spin, None) == 1
+    assert not hasattr(tsd.load_library(), "attn_clock_probe")

@@ -27,7 +27,7 @@ MASK_KINDS = {"none": 0, "causal": 1, "padding": 2, "causal_padding": 3}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_bwd_workspace_bytes", "mha_workspace_bytes", "mha_fwd",
-           "attn_clock_probe", "attn_status_string", "attn_last_error")
+           "attn_status_string", "attn_last_error")
 
 _lib = None
 
@@ -63,8 +63,6 @@ def load_library():
     lib.mha_workspace_bytes.restype = ctypes.c_size_t
     lib.mha_fwd.argtypes = [P, P, P, I32, P, I32, I32, I32, I32, P, ctypes.c_size_t, P]
     lib.mha_fwd.restype = ctypes.c_int
-    lib.attn_clock_probe.argtypes = [P, I32, I32, P]
-    lib.attn_clock_probe.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [I32]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
@@ -245,27 +243,3 @@ def mha_fwd(x, w_qkv, w_o, h: int, out=None, workspace=None):
                      ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream_ptr(x.device))
     _raise_for(lib, st, "mha_fwd")
     return out
-
-
-def clock_probe(device=None, spin_us: int = 2000) -> dict:
-    """Shader clock and matrix rate under a pure bf16 MFMA load on pseudo-random operands, one workgroup of
-    four waves per compute unit for ``spin_us`` of wall time (measurement support; synchronises the device).
-    Returns {"clock_mhz": mean shader clock, "tflops": bf16 32x32x16 flops issued / wall time}."""
-    import torch
-
-    lib = load_library()
-    device = torch.device("cuda", 0) if device is None else torch.device(device)
-    blocks = torch.cuda.get_device_properties(device).multi_processor_count
-    out = torch.zeros(3 * blocks, dtype=torch.int64, device=device)
-    st = lib.attn_clock_probe(ctypes.c_void_p(out.data_ptr()), blocks, int(spin_us), _stream_ptr(device))
-    _raise_for(lib, st, "attn_clock_probe")
-    v = out.view(blocks, 3).double().cpu()
-    wall_s = float(v[:, 1].max()) / 100e6
-    return {"clock_mhz": 100.0 * float(v[:, 0].sum()) / max(float(v[:, 1].sum()), 1.0),
-            "tflops": 4 * 32 * 32 * 16 * 2 * float(v[:, 2].sum()) / max(wall_s, 1e-9) / 1e12}
-
-
-def clock_probe_mhz(device=None, spin_us: int = 2000) -> float:
-    """Mean shader clock (MHz) of clock_probe."""
-    return clock_probe(device, spin_us)["clock_mhz"]
-

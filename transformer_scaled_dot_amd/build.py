@@ -20,7 +20,10 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtsd_attn.so")
-SOURCES = ["attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "attn_fwd_f32.hip", "gemm_bf16.hip", "clock_probe.hip", "capi.hip"]
+SOURCES = ["attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "attn_fwd_f32.hip", "gemm_bf16.hip", "capi.hip"]
+# the benchmark's clock probe: a library of its own, outside the attention library and its C ABI
+PROBE_LIB = os.path.join(HERE, "libtsd_probe.so")
+PROBE_SOURCES = [os.path.join("probe", "clock_probe.hip")]
 ARCH = "gfx950"
 
 
@@ -37,7 +40,7 @@ COMMON_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    obj = os.path.join(BUILD_DIR, os.path.splitext(os.path.basename(src))[0] + ".o")
     cmd = [hipcc()] + COMMON_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -45,19 +48,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libtsd_attn.so next to this file."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, out: str) -> str:
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libtsd_attn.so (and the benchmark's libtsd_probe.so) next to this file."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(4, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

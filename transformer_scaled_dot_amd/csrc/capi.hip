@@ -241,16 +241,6 @@ attn_status_t mha_fwd(const void *X, const void *W_qkv, const void *W_o, int32_t
     return from_hip(e, "mha_fwd output GEMM");
 }
 
-attn_status_t attn_clock_probe(uint64_t *out, int32_t blocks, int32_t spin_us, void *stream)
-{
-    g_last_error[0] = '\0';
-    if (!out) return fail(ATTN_EINVAL, "attn_clock_probe: null pointer");
-    if (blocks < 1 || blocks > 65536 || spin_us < 1 || spin_us > 100000)
-        return fail(ATTN_EINVAL, "attn_clock_probe: blocks %d or spin_us %d out of range", blocks, spin_us);
-    if (!aligned(out, 8)) return fail(ATTN_EINVAL, "attn_clock_probe: out must be 8-byte aligned");
-    return from_hip(tsd::launch_clock_probe(out, blocks, spin_us, (hipStream_t)stream), "attn_clock_probe");
-}
-
 const char *attn_status_string(int32_t status)
 {
     switch (status) {
