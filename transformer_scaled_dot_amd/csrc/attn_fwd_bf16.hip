@@ -45,20 +45,6 @@ namespace tsd {
 namespace {
 
 constexpr float kRescaleSlack = 8.f;    // log2 units the reference max may lag the true max
-// Kernel design for 128-wide heads: 1 = 32 rows per wave, software
-// pipelined; 2 = 64 rows per wave (inline-asm MFMA, O in AGPRs, one wave
-// per SIMD); 3 = 64 rows per wave with the hand-scheduled tile step.
-#ifndef TSD_D128_DESIGN
-#define TSD_D128_DESIGN 3
-#endif
-constexpr int kD128Design = TSD_D128_DESIGN;
-#ifndef TSD_WAVES128
-#define TSD_WAVES128 8
-#endif
-// Wavefronts per workgroup of the generic kernel for 128-wide heads (design 1): 8 waves (two per SIMD)
-// share one copy of each K/V tile in LDS, which halves the LDS write traffic of the tile loads against
-// two 4-wave workgroups per CU. (64-wide heads choose 4 or 8 per launch.)
-constexpr int kWaves128 = TSD_WAVES128;
 
 // Online softmax of one tile of scores of one query block, base 2 (scale *
 // log2(e) folded into c_log2 > 0, so a masked score -inf gives exactly
@@ -163,15 +149,11 @@ __device__ __forceinline__ void store_rows_bf16_staged(const u32x8 (&pk)[4], int
     asm volatile("" ::: "memory");
 }
 
-// Occupancy: 128-wide heads with two query blocks per wave need the whole
-// register file (one wave per SIMD); otherwise two waves share a SIMD.
+// The C++ kernel (64-wide heads): one query block of 32 rows per wave, two waves per SIMD.
 template <int D, int QB>
 struct AttnTraits {
-    static constexpr int kWavesPerEU = QB == 2 ? 1 : 2;
-    // S(t+1)/softmax(t) overlap needs a second score buffer: only with one query block
-    static constexpr bool kPipelined = QB == 1;
-    // two query blocks: O accumulators pinned in AGPRs, scores in VGPRs (inline-asm MFMA)
-    static constexpr bool kAsm = QB == 2;
+    static constexpr int kWavesPerEU = 2;
+    static constexpr bool kPipelined = QB == 1;  // S(t+1)/softmax(t) overlap: a second score buffer
 };
 
 template <int D, int QB, int MASK, bool OUT_F32, int OLAYOUT, int WAVES>
@@ -181,7 +163,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
     const int32_t *__restrict__ valid_lens, float c_log2, void *__restrict__ Out, int H, int Nq, int Nk,
     int num_qtiles, int BH, AttnHeads hd)
 {
-    constexpr bool ASM = AttnTraits<D, QB>::kAsm;
+    static_assert(QB == 1, "one query block per wave");
     constexpr int RW = QB * 32;        // query rows per wave
     constexpr int BM = WAVES * RW;     // query rows per workgroup
     constexpr int KS = D / 16;         // k-steps of the Q K^T contraction
@@ -236,11 +218,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
         }
     }
 
-    if constexpr (ASM) {
-        static_assert(KS == 8, "");
-        agpr_write_fence_16(qreg);  // Q^T lives in AGPRs for the whole kernel
-    }
-
     f32x16 acc[QB][DB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -248,7 +225,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
         for (int i = 0; i < DB; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[qb][i][r] = 0.f;
-    if constexpr (ASM) valu_fence_a8(acc);
     float mc_run[QB], l_run[QB];  // running (scaled, base-2) reference max and row sum
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -312,15 +288,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
             upd = upd || u;
         }
         if (__builtin_amdgcn_ballot_w64(upd)) {
-            if constexpr (ASM) mfma_fence_a8(acc);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                 for (int i = 0; i < DB; ++i)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[qb][i][r] *= alpha[qb];
-            if constexpr (ASM) valu_fence_a8(acc);
-        }
+                }
     };
 
     if constexpr (AttnTraits<D, QB>::kPipelined) {
@@ -334,7 +308,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
             __syncthreads();
             if (ntiles > 1) issue(Kh, 1, KSLOT1);
             issue(Vh, 0, VSLOT0);
-            if (ntiles_w > 0) scores<D, QB, KSLOT0, ASM>(smem, ad, qreg, sa);
+            if (ntiles_w > 0) scores<D, QB, KSLOT0>(smem, ad, qreg, sa);
             wait_vmcnt0();
             __syncthreads();
         }
@@ -349,14 +323,14 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
                 prepare(t, cur, mref);
                 bf16x8 pb[QB][4];
                 if (t + 1 < ntiles_w) {
-                    scores<D, QB, KNEXT, ASM>(smem, ad, qreg, nxt);
+                    scores<D, QB, KNEXT>(smem, ad, qreg, nxt);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) softmax_exp(cur[qb], pb[qb], mref[qb], c_log2, l_run[qb]);
-                    accumulate_pv<D, QB, VCUR, ASM>(smem, ad, pb, acc);
+                    accumulate_pv<D, QB, VCUR>(smem, ad, pb, acc);
                 } else {
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) softmax_exp(cur[qb], pb[qb], mref[qb], c_log2, l_run[qb]);
-                    accumulate_pv<D, QB, VCUR, ASM>(smem, ad, pb, acc);
+                    accumulate_pv<D, QB, VCUR>(smem, ad, pb, acc);
                 }
             }
             wait_vmcnt0();
@@ -383,14 +357,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
             }
             if (t < ntiles_w) {
                 f32x16 cur[QB][2];
-                scores<D, QB, P ? KSLOT1 : KSLOT0, ASM>(smem, ad, qreg, cur);
+                scores<D, QB, P ? KSLOT1 : KSLOT0>(smem, ad, qreg, cur);
                 float mref[QB];
                 prepare(t, cur, mref);
                 bf16x8 pb[QB][4];
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) softmax_exp(cur[qb], pb[qb], mref[qb], c_log2, l_run[qb]);
-                if constexpr (ASM) valu_fence_v8(pb);
-                accumulate_pv<D, QB, P ? VSLOT1 : VSLOT0, ASM>(smem, ad, pb, acc);
+                accumulate_pv<D, QB, P ? VSLOT1 : VSLOT0>(smem, ad, pb, acc);
             }
             wait_vmcnt0();
             __syncthreads();
@@ -402,7 +375,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
     }
 
     // ---- epilogue: O = O_acc / l (0 for a row with no visible key) ----
-    if constexpr (ASM) mfma_fence_a8(acc);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) store_rows<D, OUT_F32, OLAYOUT>(acc[qb], l_run[qb], qrow[qb], bh, H, Nq, b, hf, Out);
     if (hd.lse) {
@@ -695,20 +667,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 }
 
-// Compute units of the current device (cached per device): the persistent grid's size.
-int device_cu_count()
-{
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cache[dev].load(std::memory_order_relaxed);
-    if (n <= 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cache[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 // The C++ MFMA kernel (32 * QB query rows per wave, WAVES waves per workgroup) on its grid of query tiles.
 template <int D, int QB, int MASK, bool OUT_F32, int OLAYOUT, int WAVES>
 hipError_t launch_cpp(const void *Q, const void *K, const void *V, const int32_t *valid_lens, float c_log2, void *O,
@@ -734,7 +692,7 @@ hipError_t launch_variant(const void *Q, const void *K, const void *V, const int
     // scores (-inf) map to weight 0 without a select; below 1e-30 every
     // visible exp2 argument rounds to 0 anyway, which is the scale = 0 result.
     const float c_log2 = fmaxf(scale * 1.4426950408889634f, 1e-30f);
-    if constexpr (D == 128 && kD128Design == 3) {
+    if constexpr (D == 128) {
         // 64 query rows per wave: the whole register file, one wave per SIMD, 4 per workgroup; a persistent
         // grid of at most one workgroup per CU over 256-row work items
         const int BH = B * H;
@@ -747,18 +705,14 @@ hipError_t launch_variant(const void *Q, const void *K, const void *V, const int
                            (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, valid_lens, c_log2, O, H,
                            Nq, Nk, num_qtiles, BH, hd);
         return hipGetLastError();
-    } else if constexpr (D == 64) {
+    } else {
+        static_assert(D == 64, "head_dim 64 or 128");
         // 8 waves (256 rows per workgroup) when that grid still gives every CU a workgroup (4.5 % faster at
         // B4 H8 N2048), else 4 (128 rows: twice the workgroups for small launches)
         const long long g8 = (long long)((Nq + 255) / 256) * B * H;
         if (g8 >= device_cu_count())
             return launch_cpp<D, 1, MASK, OUT_F32, OLAYOUT, 8>(Q, K, V, valid_lens, c_log2, O, B, H, Nq, Nk, hd, stream);
         return launch_cpp<D, 1, MASK, OUT_F32, OLAYOUT, 4>(Q, K, V, valid_lens, c_log2, O, B, H, Nq, Nk, hd, stream);
-    } else if constexpr (kD128Design == 2) {
-        return launch_cpp<D, 2, MASK, OUT_F32, OLAYOUT, 4>(Q, K, V, valid_lens, c_log2, O, B, H, Nq, Nk, hd, stream);
-    } else {
-        return launch_cpp<D, 1, MASK, OUT_F32, OLAYOUT, kWaves128>(Q, K, V, valid_lens, c_log2, O, B, H, Nq, Nk, hd,
-                                                                   stream);
     }
 }
 
@@ -791,6 +745,20 @@ hipError_t dispatch_mask(const void *Q, const void *K, const void *V, int mask, 
 }
 
 }  // namespace
+
+// Compute units of the current device (cached per device): the persistent grid's size.
+int device_cu_count()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 hipError_t launch_attn_bf16(const void *Q, const void *K, const void *V, int mask, const int32_t *valid_lens,
                             float scale, void *O, int out_f32, int out_layout, int B, int H, int Nq, int Nk, int D,

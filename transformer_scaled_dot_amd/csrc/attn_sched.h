@@ -17,10 +17,6 @@
 #endif
 #endif
 
-#ifndef TSD_HEAD_MAJOR
-#define TSD_HEAD_MAJOR 1
-#endif
-
 namespace tsd {
 
 // Item of workgroup w in round k: even rounds in workgroup order, odd rounds reversed (by groups of 8 when
@@ -62,7 +58,7 @@ TSD_HD bool qb2_sched_heads(int w, int j, int G, int BH, int num_qtiles, int &bh
 
 TSD_HD bool qb2_heads_schedule(int G, int BH, int num_qtiles)
 {
-    return TSD_HEAD_MAJOR && G % 8 == 0 && BH % 8 == 0 && ((BH / 8) * num_qtiles) % (G / 8) == 0;
+    return G % 8 == 0 && BH % 8 == 0 && ((BH / 8) * num_qtiles) % (G / 8) == 0;
 }
 
 }  // namespace tsd

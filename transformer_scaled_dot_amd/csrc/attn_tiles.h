@@ -65,31 +65,11 @@ __device__ __forceinline__ TileAddrs<D> tile_addrs(int lane)
 // S^T = K Q^T for one 64-key tile and QB blocks of 32 queries: s[qb][jb]
 // holds keys jb*32.. of query block qb. KOFF: byte offset of the K tile in
 // LDS (compile-time, folded into immediates).
-template <int D, int QB, int KOFF, bool ASM>
+template <int D, int QB, int KOFF>
 __device__ __forceinline__ void scores(const uint8_t *lds, const TileAddrs<D> &ad, const bf16x8 (&qreg)[QB][D / 16],
                                        f32x16 (&s)[QB][2])
 {
     constexpr int KS = D / 16;
-    if constexpr (ASM) {
-        static_assert(QB == 2, "the asm path holds two query blocks");
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 k0 = *(const bf16x8 *)(lds + ad.k[ks] + KOFF);
-            const bf16x8 k1 = *(const bf16x8 *)(lds + ad.k[ks] + KOFF + 32 * D * 2);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                if (ks == 0) {
-                    mfma_zero_vgpr_ba(s[qb][0], k0, qreg[qb][ks]);
-                    mfma_zero_vgpr_ba(s[qb][1], k1, qreg[qb][ks]);
-                } else {
-                    mfma_acc_vgpr_ba(s[qb][0], k0, qreg[qb][ks]);
-                    mfma_acc_vgpr_ba(s[qb][1], k1, qreg[qb][ks]);
-                }
-            }
-        }
-        mfma_fence_v4(s[0][0], s[0][1], s[1][0], s[1][1]);
-        return;
-    }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -128,7 +108,7 @@ __device__ __forceinline__ void mask_scores(f32x16 (&s)[2], int k0, int kv_len, 
 // c*16 + (t/4)*8 + hf*4 + t%4, the order in which the S accumulator holds
 // the keys; a transposed read of rows c*16 + hf*4 + (0..3) (+8) gives
 // exactly those 8 keys per column.
-template <int D, int QB, int VOFF, bool ASM>
+template <int D, int QB, int VOFF>
 __device__ __forceinline__ void accumulate_pv(const uint8_t *lds, const TileAddrs<D> &ad, const bf16x8 (&pb)[QB][4],
                                               f32x16 (&acc)[QB][D / 32])
 {
@@ -140,12 +120,7 @@ __device__ __forceinline__ void accumulate_pv(const uint8_t *lds, const TileAddr
             const uint8_t *p1 = lds + ad.v[db][1] + VOFF + c * 16 * D * 2;
             const bf16x8 a = lds_tr_pair((const uint16_t *)p0, (const uint16_t *)p1);
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                if constexpr (ASM)
-                    mfma_acc_agpr(acc[qb][db], a, pb[qb][c]);
-                else
-                    acc[qb][db] = mfma32x32x16(a, pb[qb][c], acc[qb][db]);
-            }
+            for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32x32x16(a, pb[qb][c], acc[qb][db]);
         }
     }
 }

@@ -35,68 +35,13 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b,
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// The same MFMA as inline asm with the register file pinned: accumulators in
-// AGPRs ("a") or VGPRs ("v"). Kernels that need more than the 256
-// architectural VGPRs use these to keep output accumulators and resident
-// operands in AGPRs while scores stay in VGPRs for the VALU. The compiler's
-// hazard recognizer does not look inside inline asm, so:
-//  - each asm MFMA starts with 4 wait states, which covers any VALU or
-//    v_accvgpr_* write of its operands just before it (the MFMA pipe is
-//    busy with the previous MFMA for far longer, so this costs no time);
-//  - results are read only after the explicit fences below.
-__device__ __forceinline__ void mfma_acc_agpr(f32x16 &acc, const bf16x8 &a, const bf16x8 &b)
-{
-    asm("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
-// B operand taken from AGPRs (an operand that stays resident for the whole
-// kernel, kept out of the VGPR budget).
-__device__ __forceinline__ void mfma_acc_vgpr_ba(f32x16 &acc, const bf16x8 &a, const bf16x8 &b)
-{
-    asm("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
-}
-
-__device__ __forceinline__ void mfma_zero_vgpr_ba(f32x16 &acc, const bf16x8 &a, const bf16x8 &b)
-{
-    asm("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
-}
-
-// >= 19 wait states after a 16-pass MFMA wrote these accumulators, before
-// anything else reads or writes them.
-__device__ __forceinline__ void mfma_fence_v4(f32x16 &a, f32x16 &b, f32x16 &c, f32x16 &d)
-{
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
-}
-
+// >= 19 wait states after a 16-pass MFMA wrote these AGPR accumulators (inline asm outside the compiler's
+// hazard tracking), before anything else reads or writes them.
 __device__ __forceinline__ void mfma_fence_a8(f32x16 (&x)[2][4])
 {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4"
                  : "+a"(x[0][0]), "+a"(x[0][1]), "+a"(x[0][2]), "+a"(x[0][3]), "+a"(x[1][0]), "+a"(x[1][1]),
                    "+a"(x[1][2]), "+a"(x[1][3]));
-}
-
-// >= 2 wait states after VALU (or accvgpr) writes, before an MFMA reads.
-__device__ __forceinline__ void valu_fence_a8(f32x16 (&x)[2][4])
-{
-    asm volatile("s_nop 1"
-                 : "+a"(x[0][0]), "+a"(x[0][1]), "+a"(x[0][2]), "+a"(x[0][3]), "+a"(x[1][0]), "+a"(x[1][1]),
-                   "+a"(x[1][2]), "+a"(x[1][3]));
-}
-
-// >= 4 wait states after operands were moved into AGPRs.
-__device__ __forceinline__ void agpr_write_fence_16(bf16x8 (&x)[2][8])
-{
-    asm volatile("s_nop 3"
-                 : "+a"(x[0][0]), "+a"(x[0][1]), "+a"(x[0][2]), "+a"(x[0][3]), "+a"(x[0][4]), "+a"(x[0][5]),
-                   "+a"(x[0][6]), "+a"(x[0][7]), "+a"(x[1][0]), "+a"(x[1][1]), "+a"(x[1][2]), "+a"(x[1][3]),
-                   "+a"(x[1][4]), "+a"(x[1][5]), "+a"(x[1][6]), "+a"(x[1][7]));
-}
-
-__device__ __forceinline__ void valu_fence_v8(bf16x8 (&x)[2][4])
-{
-    asm volatile("s_nop 1"
-                 : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]), "+v"(x[1][0]), "+v"(x[1][1]),
-                   "+v"(x[1][2]), "+v"(x[1][3]));
 }
 
 // Two transposed 4x4 reads make one 8-element MFMA operand.

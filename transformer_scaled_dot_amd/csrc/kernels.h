@@ -43,6 +43,9 @@ hipError_t launch_attn_bwd_bf16(const void *Q, const void *K, const void *V, con
                                 void *dV, int B, int H, int Hkv, int Nq, int Nk, int D, float *work,
                                 hipStream_t stream);
 
+// Compute units of the current device (cached per device): the size of persistent grids.
+int device_cu_count();
+
 // C = A[M,K] * B[K,N] in bf16 with f32 accumulation, bf16 output.
 // Plain epilogue: C row-major [M,N].
 hipError_t launch_gemm_bf16(const void *A, const void *Bm, void *C, int M, int N, int K, hipStream_t stream);
@@ -53,9 +56,5 @@ hipError_t launch_gemm_bf16(const void *A, const void *Bm, void *C, int M, int N
 hipError_t launch_gemm_bf16_qkv_split(const void *X, const void *Wqkv, void *qkv, int batch, int seq, int d_model,
                                       int heads, hipStream_t stream);
 
-// Measurement support: `blocks` workgroups of four waves issue bf16 32x32x16 matrix instructions on
-// pseudo-random operands for spin_us of wall time and write (s_memtime ticks, 100 MHz s_memrealtime ticks,
-// instructions issued per wave) per workgroup to out[3 * blocks].
-hipError_t launch_clock_probe(uint64_t *out, int blocks, int spin_us, hipStream_t stream);
 
 }  // namespace tsd
