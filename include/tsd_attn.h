@@ -161,6 +161,30 @@ TSD_API attn_status_t attn_bwd(const void *Q, const void *K, const void *V, cons
 TSD_API size_t attn_bwd_workspace_bytes(int32_t batch, int32_t heads, int32_t seq_q);
 
 /*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * or training loops, harnesses that forbid allocation). Same arguments,
+ * results, supported set and errors as attn_bwd, minus the workspace: the
+ * per-row terms go to a scratch array the library holds in each GPU's
+ * memory from load until the process ends, attn_bwd_noalloc_max_scratch_bytes()
+ * bytes (8 MiB), i.e. batch * heads * (seq_q rounded up to 64) <= 2^20 rows
+ * (the B1 H32 N32768 workload exactly); larger sizes return ATTN_EINVAL
+ * before any HIP call. The call allocates nothing (no hipMalloc, no
+ * allocating library routine) and does not synchronise. Every call on a
+ * GPU shares that GPU's one scratch array: calls that overlap in time on
+ * one GPU (other streams, other threads) race and must be serialised by
+ * the caller; calls on one stream are ordered and safe. Nothing carries
+ * over between calls (each writes every scratch value it reads).
+ */
+TSD_API attn_status_t attn_bwd_noalloc(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                               const float *lse, int32_t mask_kind, const int32_t *valid_lens, float scale,
+                               void *dQ, void *dK, void *dV, int32_t batch, int32_t heads, int32_t kv_heads,
+                               int32_t seq_q, int32_t seq_k, int32_t head_dim, int32_t dtype, void *stream);
+
+/* attn_bwd_noalloc_max_scratch_bytes -- the size of attn_bwd_noalloc's scratch array (8 MiB). */
+TSD_API size_t attn_bwd_noalloc_max_scratch_bytes(void);
+
+/*
  * mha_workspace_bytes -- device workspace mha_fwd needs for these sizes:
  * Q, K, V split into heads ([3, batch, h, seq, d_model/h]) plus the
  * concatenated head outputs ([batch, seq, d_model]), in bf16. Returns 0

@@ -9,6 +9,7 @@ built, or a tensor is not on the GPU, the call raises.
     attn_fwd(q, k, v, mask="none"|"causal"|"padding"|"causal_padding",
              valid_lens=None, scale=None, out_dtype=None, return_lse=False)
              -> o  (or (o, lse))
+    attn_bwd(q, k, v, o, do, lse, mask=..., valid_lens=None, scale=None) -> (dq, dk, dv)
     mha_fwd(x, w_qkv, w_o, h) -> y
 """
 from __future__ import annotations
@@ -26,8 +27,9 @@ ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 MASK_KINDS = {"none": 0, "causal": 1, "padding": 2, "causal_padding": 3}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
-EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_bwd_workspace_bytes", "mha_workspace_bytes", "mha_fwd",
-           "attn_status_string", "attn_last_error")
+EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_noalloc",
+           "attn_bwd_noalloc_max_scratch_bytes", "mha_workspace_bytes", "mha_fwd", "attn_status_string",
+           "attn_last_error")
 
 _lib = None
 
@@ -59,6 +61,11 @@ def load_library():
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd_workspace_bytes.argtypes = [I32, I32, I32]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_bwd_noalloc.argtypes = [P, P, P, P, P, P, I32, P, ctypes.c_float, P, P, P, I32, I32, I32, I32, I32, I32,
+                                     I32, P]
+    lib.attn_bwd_noalloc.restype = ctypes.c_int
+    lib.attn_bwd_noalloc_max_scratch_bytes.argtypes = []
+    lib.attn_bwd_noalloc_max_scratch_bytes.restype = ctypes.c_size_t
     lib.mha_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.mha_workspace_bytes.restype = ctypes.c_size_t
     lib.mha_fwd.argtypes = [P, P, P, I32, P, I32, I32, I32, I32, P, ctypes.c_size_t, P]

@@ -7,6 +7,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 namespace {
@@ -122,12 +124,17 @@ size_t attn_bwd_workspace_bytes(int32_t batch, int32_t heads, int32_t seq_q)
     return (n + 255) / 256 * 256;
 }
 
-attn_status_t attn_bwd(const void *Q, const void *K, const void *V, const void *O, const void *dO, const float *lse,
-                       int32_t mask_kind, const int32_t *valid_lens, float scale, void *dQ, void *dK, void *dV,
-                       int32_t batch, int32_t heads, int32_t kv_heads, int32_t seq_q, int32_t seq_k,
-                       int32_t head_dim, int32_t dtype, void *workspace, size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Every argument check of attn_bwd except the workspace's (done on the host, before any HIP call).
+attn_status_t bwd_check(const void *Q, const void *K, const void *V, const void *O, const void *dO, const float *lse,
+                        int32_t mask_kind, const int32_t *valid_lens, float scale, void *dQ, void *dK, void *dV,
+                        int32_t batch, int32_t heads, int32_t kv_heads, int32_t seq_q, int32_t seq_k,
+                        int32_t head_dim, int32_t dtype, bool *empty)
 {
-    g_last_error[0] = '\0';
+    *empty = false;
     if (batch < 0 || heads < 0 || seq_q < 0 || seq_k < 0 || head_dim <= 0)
         return fail(ATTN_EINVAL, "attn_bwd: negative size or head_dim <= 0 (batch=%d heads=%d seq_q=%d seq_k=%d "
                                  "head_dim=%d)", batch, heads, seq_q, seq_k, head_dim);
@@ -150,35 +157,118 @@ attn_status_t attn_bwd(const void *Q, const void *K, const void *V, const void *
     if (bh > kI32Max || bhk > kI32Max) return fail(ATTN_EINVAL, "attn_bwd: batch*heads too large");
     const size_t nq = (size_t)bh * seq_q * head_dim * 2, nk = (size_t)bhk * seq_k * head_dim * 2;
     const size_t nl = (size_t)bh * seq_q * sizeof(float);
-    if (nq == 0 && nk == 0) return ATTN_OK;
+    if (nq == 0 && nk == 0) {
+        *empty = true;
+        return ATTN_OK;
+    }
     if ((nq && (!Q || !O || !dO || !lse || !dQ)) || (nk && (!K || !V || !dK || !dV)))
         return fail(ATTN_EINVAL, "attn_bwd: null pointer");
     if (padding && !valid_lens) return fail(ATTN_EINVAL, "attn_bwd: padding mask needs valid_lens");
-    const size_t need = attn_bwd_workspace_bytes(batch, heads, seq_q);
-    if (need && (!workspace || workspace_bytes < need))
-        return fail(ATTN_EINVAL, "attn_bwd: workspace of %zu bytes, need %zu", workspace_bytes, need);
     const void *a16[] = {Q, K, V, O, dO, dQ, dK, dV};
     for (const void *p : a16)
         if (p && !aligned(p, 16)) return fail(ATTN_EINVAL, "attn_bwd: tensors must be 16-byte aligned");
-    if ((lse && !aligned(lse, 4)) || (valid_lens && padding && !aligned(valid_lens, 4)) ||
-        (workspace && !aligned(workspace, 256)))
-        return fail(ATTN_EINVAL, "attn_bwd: lse, valid_lens 4-byte aligned, workspace 256-byte aligned");
+    if ((lse && !aligned(lse, 4)) || (valid_lens && padding && !aligned(valid_lens, 4)))
+        return fail(ATTN_EINVAL, "attn_bwd: lse and valid_lens must be 4-byte aligned");
     const void *ins[] = {Q, K, V, O, dO, lse};
     const size_t in_n[] = {nq, nk, nk, nq, nq, nl};
-    const void *outs[] = {dQ, dK, dV, workspace};
-    const size_t out_n[] = {nq, nk, nk, need};
-    for (int i = 0; i < 4; ++i) {
+    const void *outs[] = {dQ, dK, dV};
+    const size_t out_n[] = {nq, nk, nk};
+    for (int i = 0; i < 3; ++i) {
         for (int j = 0; j < 6; ++j)
             if (overlaps(outs[i], out_n[i], ins[j], in_n[j]))
-                return fail(ATTN_EINVAL, "attn_bwd: an output or the workspace overlaps an input");
-        for (int j = i + 1; j < 4; ++j)
-            if (overlaps(outs[i], out_n[i], outs[j], out_n[j]))
-                return fail(ATTN_EINVAL, "attn_bwd: outputs overlap");
+                return fail(ATTN_EINVAL, "attn_bwd: an output overlaps an input");
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], out_n[i], outs[j], out_n[j])) return fail(ATTN_EINVAL, "attn_bwd: outputs overlap");
     }
+    return ATTN_OK;
+}
+
+// Scratch of attn_bwd_noalloc: the per-row terms of one call (dO_i . O_i and lse_i in base 2), in a
+// file-scope device array that every GPU the library runs on holds until the process ends. Host code uses
+// the per-device address that hipGetSymbolAddress returns, never the array's name.
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of the scratch array, looked up once per device (with that device current).
+attn_status_t device_scratch(void **out)
+{
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ATTN_EHIP, "attn_bwd_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_EINVAL, "attn_bwd_noalloc: device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t g = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (g != hipSuccess || !p)
+            return fail(ATTN_EHIP, "attn_bwd_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(g));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_bwd(const void *Q, const void *K, const void *V, const void *O, const void *dO, const float *lse,
+                       int32_t mask_kind, const int32_t *valid_lens, float scale, void *dQ, void *dK, void *dV,
+                       int32_t batch, int32_t heads, int32_t kv_heads, int32_t seq_q, int32_t seq_k,
+                       int32_t head_dim, int32_t dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    g_last_error[0] = '\0';
+    bool empty = false;
+    const attn_status_t st = bwd_check(Q, K, V, O, dO, lse, mask_kind, valid_lens, scale, dQ, dK, dV, batch, heads,
+                                       kv_heads, seq_q, seq_k, head_dim, dtype, &empty);
+    if (st != ATTN_OK || empty) return st;
+    const size_t need = attn_bwd_workspace_bytes(batch, heads, seq_q);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(ATTN_EINVAL, "attn_bwd: workspace of %zu bytes, need %zu", workspace_bytes, need);
+    if (workspace && !aligned(workspace, 256)) return fail(ATTN_EINVAL, "attn_bwd: workspace must be 256-byte aligned");
+    const size_t nq = (size_t)batch * heads * seq_q * head_dim * 2, nk = (size_t)batch * kv_heads * seq_k * head_dim * 2;
+    const size_t nl = (size_t)batch * heads * seq_q * sizeof(float);
+    const void *bufs[] = {Q, K, V, O, dO, lse, dQ, dK, dV};
+    const size_t buf_n[] = {nq, nk, nk, nq, nq, nl, nq, nk, nk};
+    for (int j = 0; j < 9; ++j)
+        if (overlaps(workspace, need, bufs[j], buf_n[j]))
+            return fail(ATTN_EINVAL, "attn_bwd: the workspace overlaps an input or an output");
     const hipError_t e = tsd::launch_attn_bwd_bf16(Q, K, V, O, dO, lse, mask_kind, valid_lens, scale, dQ, dK, dV, batch,
                                                    heads, kv_heads, seq_q, seq_k, head_dim, (float *)workspace,
                                                    (hipStream_t)stream);
     return from_hip(e, "attn_bwd launch");
+}
+
+size_t attn_bwd_noalloc_max_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+attn_status_t attn_bwd_noalloc(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                               const float *lse, int32_t mask_kind, const int32_t *valid_lens, float scale, void *dQ,
+                               void *dK, void *dV, int32_t batch, int32_t heads, int32_t kv_heads, int32_t seq_q,
+                               int32_t seq_k, int32_t head_dim, int32_t dtype, void *stream)
+{
+    g_last_error[0] = '\0';
+    bool empty = false;
+    const attn_status_t st = bwd_check(Q, K, V, O, dO, lse, mask_kind, valid_lens, scale, dQ, dK, dV, batch, heads,
+                                       kv_heads, seq_q, seq_k, head_dim, dtype, &empty);
+    if (st != ATTN_OK || empty) return st;
+    const size_t need = attn_bwd_workspace_bytes(batch, heads, seq_q);
+    if (need > kNoAllocScratchBytes)
+        return fail(ATTN_EINVAL, "attn_bwd_noalloc: these sizes need %zu bytes of scratch, more than the %zu the "
+                                 "library holds (batch * heads * seq_q rounded up to 64 must stay <= %zu)",
+                    need, kNoAllocScratchBytes, kNoAllocScratchBytes / 8);
+    void *ws = nullptr;
+    const attn_status_t sst = device_scratch(&ws);
+    if (sst != ATTN_OK) return sst;
+    // every scratch value a call reads is first written by that call (its row-term kernel covers every padded
+    // row), so nothing needs clearing between calls
+    const hipError_t e = tsd::launch_attn_bwd_bf16(Q, K, V, O, dO, lse, mask_kind, valid_lens, scale, dQ, dK, dV, batch,
+                                                   heads, kv_heads, seq_q, seq_k, head_dim, (float *)ws,
+                                                   (hipStream_t)stream);
+    return from_hip(e, "attn_bwd_noalloc launch");
 }
 
 static attn_status_t mha_check(int32_t batch, int32_t seq, int32_t d_model, int32_t h, int32_t dtype)
