@@ -127,6 +127,30 @@ TSD_API attn_status_t attn_fwd_ex(const void *Q, const void *K, const void *V, i
                           int32_t in_dtype, int32_t out_dtype, void *stream);
 
 /*
+ * attn_weights -- the attention weights themselves, A = softmax(scale Q K^T
+ * + M) row by row, for short key sequences: the second result of the
+ * pages' attention functions (the "attention-mechanism" page, section
+ * 最小实现, returns (output, A); "多模态大模型学习笔记（十四）" section 2.3
+ * returns the weights too). The attention kernels never form A (at long
+ * sequences it is the n x n matrix that tiling avoids, "Self-Attention
+ * 机制" section 瓶颈); this call computes it where it is small.
+ *
+ *   Q          [batch, heads, seq_q, head_dim]      dtype
+ *   K          [batch, kv_heads, seq_k, head_dim]   dtype (grouped heads as in attn_fwd_ex)
+ *   mask_kind, valid_lens, scale: as for attn_fwd_ex
+ *   A          device float32 [batch, heads, seq_q, seq_k], 4-byte aligned, written;
+ *              masked weights are exactly 0, each row with a visible key sums to 1
+ *              (rounding aside), a row without one is all zeros
+ *   dtype      ATTN_BF16 or ATTN_F32; scores and softmax in float32
+ *
+ * Supported set: seq_k <= 1024, head_dim 1..256 (else ATTN_EUNSUPPORTED);
+ * the causal masks need seq_q == seq_k. Errors as for attn_fwd.
+ */
+TSD_API attn_status_t attn_weights(const void *Q, const void *K, int32_t mask_kind, const int32_t *valid_lens,
+                           float scale, float *A, int32_t batch, int32_t heads, int32_t kv_heads, int32_t seq_q,
+                           int32_t seq_k, int32_t head_dim, int32_t dtype, void *stream);
+
+/*
  * attn_bwd -- gradients of attn_fwd_ex's O with respect to Q, K and V.
  * The pages give no backward algorithm; this is the chain rule through
  * the forward stages ("04. Self-Attention", section 四), the weights

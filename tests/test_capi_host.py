@@ -114,6 +114,40 @@ def test_attn_fwd_empty_is_ok_without_gpu(lib):
     assert call_attn(lib, B=0) == 0
 
 
+def call_weights(lib, Q=FAKE, K=FAKE + (1 << 28), mask=0, vl=0, scale=0.125, A=FAKE + (2 << 28), B=1, H=2, Hkv=2,
+                 Nq=8, Nk=8, d=64, dt=BF16):
+    P = ctypes.c_void_p
+    return lib.attn_weights(P(Q), P(K), mask, P(vl), ctypes.c_float(scale), P(A), B, H, Hkv, Nq, Nk, d, dt, P(0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), EINVAL),
+    (dict(d=0), EINVAL),
+    (dict(Hkv=3), EINVAL),
+    (dict(mask=5), EINVAL),
+    (dict(dt=9), EINVAL),
+    (dict(scale=float("nan")), EINVAL),
+    (dict(Q=0), EINVAL),
+    (dict(A=0), EINVAL),
+    (dict(mask=2, vl=0), EINVAL),
+    (dict(A=FAKE + (2 << 28) + 2), EINVAL),       # A not 4-byte aligned
+    (dict(A=FAKE), EINVAL),                       # A overlaps Q
+    (dict(Q=FAKE + 1), EINVAL),                   # bf16 Q not 2-byte aligned
+    (dict(scale=-1.0), EUNSUP),
+    (dict(Nk=1025, Nq=8), EUNSUP),                # only short key sequences
+    (dict(d=257), EUNSUP),
+    (dict(mask=1, Nq=8, Nk=9), EUNSUP),
+])
+def test_attn_weights_rejects(lib, kw, status):
+    assert call_weights(lib, **kw) == status
+    assert lib.attn_last_error() != b""
+
+
+def test_attn_weights_empty_is_ok_without_gpu(lib):
+    assert call_weights(lib, Nq=0) == 0
+    assert call_weights(lib, Nk=0, Q=0, K=0, A=0) == 0
+
+
 GB = 1 << 28  # spacing of the fake buffers below: no two overlap at the sizes used
 
 

@@ -9,6 +9,7 @@ built, or a tensor is not on the GPU, the call raises.
     attn_fwd(q, k, v, mask="none"|"causal"|"padding"|"causal_padding",
              valid_lens=None, scale=None, out_dtype=None, return_lse=False)
              -> o  (or (o, lse))
+    attn_weights(q, k, mask=..., valid_lens=None, scale=None) -> A  (Nk <= 1024)
     attn_bwd(q, k, v, o, do, lse, mask=..., valid_lens=None, scale=None) -> (dq, dk, dv)
     mha_fwd(x, w_qkv, w_o, h) -> y
 """
@@ -18,7 +19,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["attn_fwd", "attn_bwd", "mha_fwd", "mha_workspace_bytes", "library_path", "load_library", "AttnError"]
+__all__ = ["attn_fwd", "attn_weights", "attn_bwd", "mha_fwd", "mha_workspace_bytes", "library_path", "load_library", "AttnError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtsd_attn.so")
@@ -27,7 +28,7 @@ ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 MASK_KINDS = {"none": 0, "causal": 1, "padding": 2, "causal_padding": 3}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
-EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_noalloc",
+EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_weights", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_noalloc",
            "attn_bwd_noalloc_max_scratch_bytes", "mha_workspace_bytes", "mha_fwd", "attn_status_string",
            "attn_last_error")
 
@@ -59,6 +60,8 @@ def load_library():
     lib.attn_bwd.argtypes = [P, P, P, P, P, P, I32, P, ctypes.c_float, P, P, P, I32, I32, I32, I32, I32, I32, I32,
                              P, ctypes.c_size_t, P]
     lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_weights.argtypes = [P, P, I32, P, ctypes.c_float, P, I32, I32, I32, I32, I32, I32, I32, P]
+    lib.attn_weights.restype = ctypes.c_int
     lib.attn_bwd_workspace_bytes.argtypes = [I32, I32, I32]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_noalloc.argtypes = [P, P, P, P, P, P, I32, P, ctypes.c_float, P, P, P, I32, I32, I32, I32, I32, I32,
@@ -167,6 +170,35 @@ def attn_fwd(q, k, v, mask: str = "none", valid_lens=None, scale: float | None =
                          B, H, Hkv, Nq, Nk, d, _dtype_code(q), _dtype_code(out), _stream_ptr(q.device))
     _raise_for(lib, st, "attn_fwd")
     return (out, lse) if lse is not None else out
+
+
+def attn_weights(q, k, mask: str = "none", valid_lens=None, scale: float | None = None):
+    """The attention weights A = softmax(q k^T * scale + M), float32 [B, H, Nq, Nk], for short key
+    sequences (Nk <= 1024): the pages' second result of attention. q [B,H,Nq,d], k [B,H_kv,Nk,d] (bf16 or
+    float32); masks, valid_lens and scale as for attn_fwd. Enqueued on the current stream."""
+    import torch
+
+    lib = load_library()
+    if mask not in MASK_KINDS:
+        raise ValueError("mask must be one of %s" % sorted(MASK_KINDS))
+    _check_gpu(q, k, valid_lens)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k must be 4-D [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d or k.dtype != q.dtype:
+        raise ValueError("k must be [B, H_kv, Nk, d] with q's dtype")
+    uses_lens = mask in ("padding", "causal_padding")
+    if uses_lens and (valid_lens is None or valid_lens.dtype != torch.int32 or tuple(valid_lens.shape) != (B,)):
+        raise ValueError("%s mask needs valid_lens: int32 GPU tensor of shape [B]" % mask)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    a = torch.empty((B, H, Nq, Nk), dtype=torch.float32, device=q.device)
+    P = ctypes.c_void_p
+    st = lib.attn_weights(P(q.data_ptr()), P(k.data_ptr()), MASK_KINDS[mask],
+                          P(valid_lens.data_ptr() if uses_lens else 0), ctypes.c_float(scale), P(a.data_ptr()), B, H,
+                          Hkv, Nq, Nk, d, _dtype_code(q), _stream_ptr(q.device))
+    _raise_for(lib, st, "attn_weights")
+    return a
 
 
 def attn_bwd(q, k, v, o, do, lse, mask: str = "none", valid_lens=None, scale: float | None = None, workspace=None):

@@ -20,7 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtsd_attn.so")
-SOURCES = ["attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "attn_fwd_f32.hip", "gemm_bf16.hip", "capi.hip"]
+SOURCES = ["attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "attn_fwd_f32.hip", "attn_weights.hip", "gemm_bf16.hip",
+           "capi.hip"]
 # the benchmark's clock probe: a library of its own, outside the attention library and its C ABI
 PROBE_LIB = os.path.join(HERE, "libtsd_probe.so")
 PROBE_SOURCES = [os.path.join("probe", "clock_probe.hip")]

@@ -116,6 +116,46 @@ attn_status_t attn_fwd(const void *Q, const void *K, const void *V, int32_t mask
                        seq_k, head_dim, in_dtype, out_dtype, stream);
 }
 
+attn_status_t attn_weights(const void *Q, const void *K, int32_t mask_kind, const int32_t *valid_lens, float scale,
+                           float *A, int32_t batch, int32_t heads, int32_t kv_heads, int32_t seq_q, int32_t seq_k,
+                           int32_t head_dim, int32_t dtype, void *stream)
+{
+    g_last_error[0] = '\0';
+    if (batch < 0 || heads < 0 || seq_q < 0 || seq_k < 0 || head_dim <= 0)
+        return fail(ATTN_EINVAL, "attn_weights: negative size or head_dim <= 0");
+    if (kv_heads <= 0 || (heads > 0 && heads % kv_heads != 0))
+        return fail(ATTN_EINVAL, "attn_weights: kv_heads must be positive and divide heads (heads=%d kv_heads=%d)",
+                    heads, kv_heads);
+    if (mask_kind < ATTN_MASK_NONE || mask_kind > ATTN_MASK_CAUSAL_PADDING)
+        return fail(ATTN_EINVAL, "attn_weights: unknown mask_kind %d", mask_kind);
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_EINVAL, "attn_weights: unknown dtype %d", dtype);
+    if (!isfinite(scale)) return fail(ATTN_EINVAL, "attn_weights: scale is not finite");
+    if (scale < 0.f) return fail(ATTN_EUNSUPPORTED, "attn_weights: negative scale");
+    if (head_dim > 256) return fail(ATTN_EUNSUPPORTED, "attn_weights: head_dim %d > 256", head_dim);
+    if (seq_k > tsd::kAttnWeightsMaxKeys)
+        return fail(ATTN_EUNSUPPORTED, "attn_weights: seq_k %d > %d (the weights are formed only for short key "
+                                       "sequences)", seq_k, tsd::kAttnWeightsMaxKeys);
+    const bool causal = mask_kind == ATTN_MASK_CAUSAL || mask_kind == ATTN_MASK_CAUSAL_PADDING;
+    const bool padding = mask_kind == ATTN_MASK_PADDING || mask_kind == ATTN_MASK_CAUSAL_PADDING;
+    if (causal && seq_q != seq_k)
+        return fail(ATTN_EUNSUPPORTED, "attn_weights: causal mask needs seq_q == seq_k (%d != %d)", seq_q, seq_k);
+    const long long bh = (long long)batch * heads;
+    if (bh > kI32Max) return fail(ATTN_EINVAL, "attn_weights: batch*heads too large");
+    const size_t eb = dtype_bytes(dtype);
+    const size_t nq = (size_t)bh * seq_q * head_dim * eb, nk = (size_t)batch * kv_heads * seq_k * head_dim * eb;
+    const size_t na = (size_t)bh * seq_q * seq_k * sizeof(float);
+    if (na == 0) return ATTN_OK;  // no weight to write
+    if (!Q || !K || !A) return fail(ATTN_EINVAL, "attn_weights: null Q, K or A");
+    if (padding && !valid_lens) return fail(ATTN_EINVAL, "attn_weights: padding mask needs valid_lens");
+    if (!aligned(Q, eb) || !aligned(K, eb) || !aligned(A, 4) || (padding && !aligned(valid_lens, 4)))
+        return fail(ATTN_EINVAL, "attn_weights: misaligned pointer");
+    if (overlaps(A, na, Q, nq) || overlaps(A, na, K, nk)) return fail(ATTN_EINVAL, "attn_weights: A overlaps Q or K");
+    const tsd::AttnHeads hd{kv_heads, heads > 0 ? heads / kv_heads : 1, nullptr};
+    return from_hip(tsd::launch_attn_weights(Q, K, mask_kind, valid_lens, scale, A, dtype == ATTN_BF16, batch, heads,
+                                             seq_q, seq_k, head_dim, hd, (hipStream_t)stream),
+                    "attn_weights launch");
+}
+
 size_t attn_bwd_workspace_bytes(int32_t batch, int32_t heads, int32_t seq_q)
 {
     if (batch < 0 || heads < 0 || seq_q < 0) return 0;

@@ -43,6 +43,13 @@ hipError_t launch_attn_bwd_bf16(const void *Q, const void *K, const void *V, con
                                 void *dV, int B, int H, int Hkv, int Nq, int Nk, int D, float *work,
                                 hipStream_t stream);
 
+// The attention weights A = softmax(Q K^T * scale + M) as float32 [B,H,Nq,Nk], for Nk <= kAttnWeightsMaxKeys;
+// Q [B,H,Nq,D] and K [B,Hkv,Nk,D] bf16 (bf16 = 1) or float32, D in 1..256.
+constexpr int kAttnWeightsMaxKeys = 1024;
+hipError_t launch_attn_weights(const void *Q, const void *K, int mask, const int32_t *valid_lens, float scale,
+                               float *A, int bf16, int B, int H, int Nq, int Nk, int D, AttnHeads heads,
+                               hipStream_t stream);
+
 // Compute units of the current device (cached per device): the size of persistent grids.
 int device_cu_count();
 
