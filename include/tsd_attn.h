@@ -240,6 +240,47 @@ TSD_API attn_status_t mha_fwd(const void *X, const void *W_qkv, const void *W_o,
                       int32_t seq, int32_t d_model, int32_t dtype, void *workspace, size_t workspace_bytes,
                       void *stream);
 
+/*
+ * mha_cross_workspace_bytes -- device workspace mha_cross_fwd needs: Q split
+ * into heads ([batch, h, seq_q, d_k]), K and V split into heads ([2, batch,
+ * h, seq_kv, d_k]) and the concatenated head outputs ([batch, seq_q,
+ * d_model]), bf16. Returns 0 for sizes mha_cross_fwd would reject.
+ */
+TSD_API size_t mha_cross_workspace_bytes(int32_t batch, int32_t seq_q, int32_t seq_kv, int32_t d_model, int32_t h,
+                                 int32_t dtype);
+
+/*
+ * mha_cross_fwd -- multi-head cross-attention layer, no bias: the queries
+ * come from one sequence, the keys and values from another
+ * ("多模态大模型学习笔记（十四）" section 4: in the decoder's cross-attention
+ * Q is the decoder's, K and V the encoder's; "Transformer 详解" section
+ * 编码器、解码器与因果掩码). Q = Xq W_Q, [K | V] = Xkv [W_K | W_V], heads
+ * split and concatenated as in mha_fwd, Y = C W_o.
+ *
+ *   Xq       [batch, seq_q, d_model]        dtype
+ *   Xkv      [batch, seq_kv, d_model]       dtype (may be NULL when seq_kv = 0)
+ *   W_qkv    [d_model, 3*d_model]           the same weight layout as mha_fwd
+ *   W_o      [d_model, d_model]
+ *   h        number of heads; d_k = d_model / h; scale 1/sqrt(d_k)
+ *   mask_kind ATTN_MASK_NONE, or ATTN_MASK_PADDING with valid_lens (device
+ *            int32 [batch]): keys j >= valid_lens[b] of the key sequence are
+ *            hidden (clamped to [0, seq_kv]); a row without a visible key is 0.
+ *            The causal masks are defined for self-attention only:
+ *            ATTN_EUNSUPPORTED.
+ *   O        [batch, seq_q, d_model]        dtype
+ *   workspace, workspace_bytes: device scratch of at least
+ *            mha_cross_workspace_bytes(...) bytes, 256-byte aligned.
+ *
+ * Runs four kernels on `stream`: the query projection and the key/value
+ * projection (both writing the head-split layout), attention (writing the
+ * concatenated layout), the output projection. Intermediates are bf16.
+ * Supported set and errors as for mha_fwd.
+ */
+TSD_API attn_status_t mha_cross_fwd(const void *Xq, const void *Xkv, const void *W_qkv, const void *W_o, int32_t h,
+                            int32_t mask_kind, const int32_t *valid_lens, void *O, int32_t batch, int32_t seq_q,
+                            int32_t seq_kv, int32_t d_model, int32_t dtype, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 TSD_API const char *attn_status_string(int32_t status);
 

@@ -77,6 +77,8 @@ def _load(path: str | None = None):
         lib.oracle_attn_bwd.restype = ctypes.c_int
         lib.oracle_mha.argtypes = [P, P, P, I64, I64, I64, I64, P, ctypes.c_int]
         lib.oracle_mha.restype = ctypes.c_int
+        lib.oracle_mha_cross.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_int, P, P, ctypes.c_int]
+        lib.oracle_mha_cross.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _libs[path] = lib
@@ -206,4 +208,29 @@ def mha(x, w_qkv, w_o, h, threads=0, lib=None):
     rc = _load(lib).oracle_mha(_ptr(x), _ptr(w_qkv), _ptr(w_o), B, N, dm, int(h), _ptr(Y), int(threads))
     if rc < 0:
         raise ValueError("oracle_mha rejected its arguments")
+    return Y
+
+
+def mha_cross(xq, xkv, w_qkv, w_o, h, mask="none", valid_lens=None, threads=0, lib=None):
+    """Multi-head cross-attention layer: queries from xq [B,Nq,d_model], keys and values from xkv
+    [B,Nkv,d_model], Q = xq W_Q and [K | V] = xkv [W_K | W_V] with W_qkv = [W_Q | W_K | W_V], heads split
+    as in :func:`mha`, mask "none" or "padding" (keys j >= valid_lens[b] hidden), Y = concat . W_o."""
+    xq, xkv, w_qkv, w_o = _f64(xq), _f64(xkv), _f64(w_qkv), _f64(w_o)
+    B, Nq, dm = xq.shape
+    if xkv.ndim != 3 or xkv.shape[0] != B or xkv.shape[2] != dm:
+        raise ValueError("xkv must be [B, Nkv, d_model]")
+    if w_qkv.shape != (dm, 3 * dm) or w_o.shape != (dm, dm) or dm % h:
+        raise ValueError("bad mha shapes")
+    if mask not in ("none", "padding"):
+        raise ValueError("cross-attention masks: none or padding")
+    vl = None
+    if mask == "padding":
+        vl = np.ascontiguousarray(valid_lens, dtype=np.int32)
+        if vl.shape != (B,):
+            raise ValueError("valid_lens must be [B]")
+    Y = np.zeros((B, Nq, dm), dtype=np.float64)
+    rc = _load(lib).oracle_mha_cross(_ptr(xq), _ptr(xkv), _ptr(w_qkv), _ptr(w_o), B, Nq, xkv.shape[1], dm, int(h),
+                                     MASK[mask], _ptr(vl), _ptr(Y), int(threads))
+    if rc < 0:
+        raise ValueError("oracle_mha_cross rejected its arguments")
     return Y

@@ -366,3 +366,71 @@ int oracle_mha(const double *X, const double *Wqkv, const double *Wo, int64_t B,
     free(P); free(C); free(Qh); free(Kh); free(Vh);
     return used;
 }
+
+/*
+ * Multi-head cross-attention layer without bias: the queries come from one
+ * sequence and the keys and values from another ("多模态大模型学习笔记（十四）"
+ * section 4: in the decoder's cross-attention Q is the decoder's and K, V
+ * the encoder's; "Transformer 详解" section 编码器、解码器与因果掩码), with
+ * the same weights and head split as oracle_mha:
+ *   Q = Xq W_Q,  [K | V] = Xkv [W_K | W_V],  W_qkv = [W_Q | W_K | W_V]
+ *   head i: columns [i*d_k, (i+1)*d_k) of Q, K and V, scale 1/sqrt(d_k)
+ *   mask: none, or padding of the key sequence (keys j >= valid_lens[b])
+ *   C[:, i*d_k:(i+1)*d_k] = head_i ;  Y = C W_o
+ * Xq [B,Nq,d_model], Xkv [B,Nkv,d_model], Y [B,Nq,d_model]; no intermediate
+ * rounding.
+ */
+int oracle_mha_cross(const double *Xq, const double *Xkv, const double *Wqkv, const double *Wo, int64_t B,
+                     int64_t Nq, int64_t Nkv, int64_t d_model, int64_t h, int mask_kind, const int32_t *valid_lens,
+                     double *Y, int nthreads)
+{
+    if (B < 0 || Nq < 0 || Nkv < 0 || d_model <= 0 || h <= 0 || d_model % h) return -1;
+    if (mask_kind != ORACLE_MASK_NONE && mask_kind != ORACLE_MASK_PADDING) return -1;
+    if (mask_kind == ORACLE_MASK_PADDING && !valid_lens && B > 0) return -1;
+    int used = set_threads(nthreads);
+    const int64_t dk = d_model / h, Mq = B * Nq, Mk = B * Nkv, W3 = 3 * d_model;
+    const size_t nq = (size_t)(Mq * d_model > 0 ? Mq * d_model : 1), nk = (size_t)(Mk * d_model > 0 ? Mk * d_model : 1);
+    double *Wq = (double *)malloc(sizeof(double) * (size_t)(d_model * d_model));
+    double *Wkv = (double *)malloc(sizeof(double) * (size_t)(d_model * 2 * d_model));
+    double *Pq = (double *)malloc(sizeof(double) * nq), *Pkv = (double *)malloc(sizeof(double) * 2 * nk);
+    double *Qh = (double *)malloc(sizeof(double) * nq), *Oh = (double *)malloc(sizeof(double) * nq);
+    double *C = (double *)malloc(sizeof(double) * nq);
+    double *Kh = (double *)malloc(sizeof(double) * nk), *Vh = (double *)malloc(sizeof(double) * nk);
+    if (!Wq || !Wkv || !Pq || !Pkv || !Qh || !Oh || !C || !Kh || !Vh) {
+        free(Wq); free(Wkv); free(Pq); free(Pkv); free(Qh); free(Oh); free(C); free(Kh); free(Vh);
+        return -1;
+    }
+    /* the weight's column blocks: W_Q, and W_K | W_V side by side */
+    for (int64_t r = 0; r < d_model; ++r) {
+        for (int64_t c = 0; c < d_model; ++c) Wq[r * d_model + c] = Wqkv[r * W3 + c];
+        for (int64_t c = 0; c < 2 * d_model; ++c) Wkv[r * 2 * d_model + c] = Wqkv[r * W3 + d_model + c];
+    }
+    matmul_f64(Xq, Wq, Pq, Mq, d_model, d_model);
+    matmul_f64(Xkv, Wkv, Pkv, Mk, d_model, 2 * d_model);
+
+    /* split into heads: [B,N,h,dk] -> [B,h,N,dk] */
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t hh = 0; hh < h; ++hh)
+            for (int64_t c = 0; c < dk; ++c) {
+                for (int64_t t = 0; t < Nq; ++t)
+                    Qh[((b * h + hh) * Nq + t) * dk + c] = Pq[(b * Nq + t) * d_model + hh * dk + c];
+                for (int64_t t = 0; t < Nkv; ++t) {
+                    Kh[((b * h + hh) * Nkv + t) * dk + c] = Pkv[(b * Nkv + t) * 2 * d_model + hh * dk + c];
+                    Vh[((b * h + hh) * Nkv + t) * dk + c] = Pkv[(b * Nkv + t) * 2 * d_model + d_model + hh * dk + c];
+                }
+            }
+
+    oracle_attn(Qh, Kh, Vh, B, h, h, Nq, Nkv, dk, dk, mask_kind, valid_lens, 1.0 / sqrt((double)dk), Oh, NULL, NULL,
+                nthreads);
+
+    /* concat: [B,h,Nq,dk] -> [B,Nq,h*dk] */
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t hh = 0; hh < h; ++hh)
+            for (int64_t t = 0; t < Nq; ++t)
+                for (int64_t c = 0; c < dk; ++c)
+                    C[(b * Nq + t) * d_model + hh * dk + c] = Oh[((b * h + hh) * Nq + t) * dk + c];
+    matmul_f64(C, Wo, Y, Mq, d_model, d_model);
+
+    free(Wq); free(Wkv); free(Pq); free(Pkv); free(Qh); free(Oh); free(C); free(Kh); free(Vh);
+    return used;
+}

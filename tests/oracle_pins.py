@@ -317,6 +317,53 @@ def pin_mha_identity_projections_split_heads(lib):
         np.testing.assert_allclose(Y[:, :, i * dk:(i + 1) * dk], Oi, atol=1e-14, rtol=0)
 
 
+def pin_mha_cross_matches_torch_float64(lib):
+    """The cross-attention layer against torch float64 ops: Q from the query sequence through W_Q, K and V
+    from the other sequence through W_K and W_V ("多模态大模型学习笔记（十四）" section 4), heads split and
+    concatenated as in the self-attention layer, keys past each batch's valid length hidden."""
+    import torch
+    import torch.nn.functional as F
+
+    for (B, Nq, Nkv, dm, h) in [(2, 5, 9, 16, 4), (1, 7, 3, 12, 3), (2, 4, 4, 8, 1)]:
+        xq = _randn(1500 + dm, (B, Nq, dm))
+        xkv = _randn(1501 + dm, (B, Nkv, dm))
+        wqkv = _randn(1502 + dm, (dm, 3 * dm), np.sqrt(1.0 / dm))
+        wo = _randn(1503 + dm, (dm, dm), np.sqrt(1.0 / dm))
+        vl = np.asarray([Nkv, max(1, Nkv // 2)][:B], dtype=np.int32)
+        Xq, Xkv, Wqkv, Wo = map(torch.from_numpy, (xq, xkv, wqkv, wo))
+        dk = dm // h
+        qh = (Xq @ Wqkv[:, :dm]).reshape(B, Nq, h, dk).transpose(1, 2)
+        kh = (Xkv @ Wqkv[:, dm:2 * dm]).reshape(B, Nkv, h, dk).transpose(1, 2)
+        vh = (Xkv @ Wqkv[:, 2 * dm:]).reshape(B, Nkv, h, dk).transpose(1, 2)
+        for mask in ("none", "padding"):
+            keep = None
+            if mask == "padding":
+                keep = torch.from_numpy(np.arange(Nkv)[None, :] < vl[:, None])[:, None, None, :]
+            ctx = F.scaled_dot_product_attention(qh, kh, vh, attn_mask=keep).transpose(1, 2).reshape(B, Nq, dm)
+            Y = oracle.mha_cross(xq, xkv, wqkv, wo, h, mask=mask, valid_lens=vl, lib=lib)
+            np.testing.assert_allclose(Y, (ctx @ Wo).numpy(), atol=1e-12, rtol=0)
+
+
+def pin_mha_cross_reduces_to_self_attention(lib):
+    """With the query and key sequences the same and no mask, the cross-attention layer is the multi-head
+    self-attention layer; with W_QKV = [I | I | I] and W_O = I, head i is attention of the i-th column
+    block of the queries over the i-th block of the other sequence."""
+    B, N, dm, h = 2, 6, 12, 3
+    x = _randn(1510, (B, N, dm))
+    wqkv = _randn(1511, (dm, 3 * dm), np.sqrt(1.0 / dm))
+    wo = _randn(1512, (dm, dm), np.sqrt(1.0 / dm))
+    np.testing.assert_allclose(oracle.mha_cross(x, x, wqkv, wo, h, lib=lib), oracle.mha(x, wqkv, wo, h, lib=lib),
+                               atol=1e-13, rtol=0)
+    xkv = _randn(1513, (B, 4, dm))
+    I = np.eye(dm)
+    Y = oracle.mha_cross(x, xkv, np.concatenate([I, I, I], axis=1), I, h, lib=lib)
+    dk = dm // h
+    for i in range(h):
+        qi, ki = x[:, :, i * dk:(i + 1) * dk][:, None], xkv[:, :, i * dk:(i + 1) * dk][:, None]
+        np.testing.assert_allclose(Y[:, :, i * dk:(i + 1) * dk], oracle.attention(qi, ki, ki, lib=lib)[:, 0],
+                                   atol=1e-14, rtol=0)
+
+
 def pin_row_subset_equals_full(lib):
     """Output rows computed one by one equal the same rows of the full call
     (the full-size GPU checks rely on this)."""

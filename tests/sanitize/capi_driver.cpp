@@ -76,6 +76,16 @@ int main()
     EXPECT(mha_fwd(fake(0), fake(1), fake(2), 7, fake(3), 1, 16, 512, 1, fake(4), mws, nullptr), ATTN_EINVAL);
     EXPECT(mha_fwd(fake(0), fake(1), fake(2), 8, fake(3), 1, 16, 512, 1, fake(4), mws - 2, nullptr), ATTN_EINVAL);
     EXPECT(mha_fwd(fake(0), fake(1), fake(2), 8, fake(3), 0, 16, 512, 1, fake(4), mws, nullptr), ATTN_OK);
+    // mha_cross_fwd
+    const size_t cws = mha_cross_workspace_bytes(2, 16, 24, 512, 8, 1);
+    EXPECT(mha_cross_fwd(fake(0), fake(1), fake(2), fake(3), 8, 2, vl, fake(4), 2, 16, 24, 512, 1, fake(5), cws,
+                         nullptr), ATTN_EHIP);
+    EXPECT(mha_cross_fwd(fake(0), fake(1), fake(2), fake(3), 8, 1, nullptr, fake(4), 2, 16, 24, 512, 1, fake(5), cws,
+                         nullptr), ATTN_EUNSUPPORTED);
+    EXPECT(mha_cross_fwd(fake(0), fake(1), fake(2), fake(3), 8, 0, nullptr, fake(4), 2, 16, 24, 512, 1, fake(5),
+                         cws - 1, nullptr), ATTN_EINVAL);
+    EXPECT(mha_cross_fwd(fake(0), nullptr, fake(2), fake(3), 8, 0, nullptr, fake(4), 2, 16, 0, 512, 1, fake(5), cws,
+                         nullptr), ATTN_EHIP);
     for (int st = -1; st < 5; ++st)
         if (!attn_status_string(st) || !strlen(attn_status_string(st))) ++fails;
     if (fails) return 1;

@@ -30,6 +30,10 @@ hipError_t launch_gemm_bf16_qkv_split(const void *, const void *, void *, int, i
 {
     return hipErrorNoDevice;
 }
+hipError_t launch_gemm_bf16_heads(const void *, const void *, int, void *, int, int, int, int, int, hipStream_t)
+{
+    return hipErrorNoDevice;
+}
 int device_cu_count() { return 256; }
 
 }  // namespace tsd

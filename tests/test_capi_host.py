@@ -239,6 +239,41 @@ def test_mha_fwd_rejects(lib, kw, status):
     assert call_mha(lib, **kw) == status
 
 
+def call_cross(lib, Xq=FAKE, Xkv=FAKE + (1 << 28), W=FAKE + (2 << 28), Wo=FAKE + (3 << 28), h=8, mask=0, vl=0,
+               O=FAKE + (4 << 28), B=2, Nq=16, Nkv=24, dm=512, dt=BF16, ws=FAKE + (5 << 28), wsb=1 << 27):
+    P = ctypes.c_void_p
+    return lib.mha_cross_fwd(P(Xq), P(Xkv), P(W), P(Wo), h, mask, P(vl), P(O), B, Nq, Nkv, dm, dt, P(ws),
+                             ctypes.c_size_t(wsb), P(0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Xq=0), EINVAL),
+    (dict(Xkv=0), EINVAL),
+    (dict(ws=0), EINVAL),
+    (dict(h=7), EINVAL),
+    (dict(Nkv=-1), EINVAL),
+    (dict(mask=2, vl=0), EINVAL),                  # padding needs valid_lens
+    (dict(mask=5), EINVAL),
+    (dict(wsb=100), EINVAL),
+    (dict(O=FAKE), EINVAL),                        # output aliases Xq
+    (dict(ws=FAKE + (1 << 28)), EINVAL),           # workspace over Xkv
+    (dict(mask=1), EUNSUP),                        # causal is for self-attention only
+    (dict(mask=3, vl=FAKE + (6 << 28)), EUNSUP),
+    (dict(dt=F32), EUNSUP),
+    (dict(h=16), EUNSUP),                          # d_k = 32
+])
+def test_mha_cross_fwd_rejects(lib, kw, status):
+    assert call_cross(lib, **kw) == status
+    assert lib.attn_last_error() != b""
+
+
+def test_mha_cross_workspace_bytes(lib):
+    assert lib.mha_cross_workspace_bytes(4, 2048, 512, 512, 8, BF16) == (2 * 4 * 2048 + 2 * 4 * 512) * 512 * 2
+    assert lib.mha_cross_workspace_bytes(1, 4, 4, 512, 7, BF16) == 0
+    assert lib.mha_cross_workspace_bytes(1, 4, -1, 512, 8, BF16) == 0
+    assert call_cross(lib, Nq=0) == 0  # no output row: nothing to do
+
+
 def test_mha_workspace_bytes(lib):
     assert lib.mha_workspace_bytes(4, 2048, 512, 8, BF16) == 4 * 4 * 2048 * 512 * 2
     assert lib.mha_workspace_bytes(4, 2048, 512, 7, BF16) == 0

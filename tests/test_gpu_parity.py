@@ -385,3 +385,38 @@ def test_d64_eight_wave_grouped_lse(dev):
     err = np.abs(lse.cpu().numpy().astype(np.float64) - rl)
     say("  lse max abs err %.3e" % err.max())
     assert err.max() <= 2.0 ** -8 + 1e-4
+
+
+@pytest.mark.parametrize("B,Nq,Nkv,dm,h,mask", [(2, 77, 130, 256, 4, "none"), (2, 200, 64, 512, 8, "padding"),
+                                                 (1, 33, 300, 768, 6, "padding"), (3, 130, 130, 128, 1, "none"),
+                                                 (2, 64, 1, 256, 2, "none")])
+def test_mha_cross_layer(dev, B, Nq, Nkv, dm, h, mask):
+    """The cross-attention layer (queries from one sequence, keys and values from another) against the
+    oracle, every element: head widths 64 and 128, ragged lengths on both sides, a single key, and the
+    key padding mask with one batch's keys cut to a third."""
+    import transformer_scaled_dot_amd as tsd
+
+    xq = synth.normal_tensor(5300 + Nq, (B, Nq, dm))
+    xkv = synth.normal_tensor(5301 + Nkv, (B, Nkv, dm))
+    _, wqkv, wo = synth.mha_inputs(4, B=1, N=1, d_model=dm)
+    vl = np.asarray([Nkv, max(1, Nkv // 3), Nkv][:B], dtype=np.int32)
+    vl_t = torch.from_numpy(vl).to(dev) if mask == "padding" else None
+    y = tsd.mha_cross_fwd(xq.torch(dev), xkv.torch(dev), wqkv.torch(dev), wo.torch(dev), h, mask=mask,
+                          valid_lens=vl_t)
+    torch.cuda.synchronize()
+    got = y.float().cpu().numpy().astype(np.float64)
+    ref = oracle.mha_cross(xq.f64, xkv.f64, wqkv.f64, wo.f64, h, mask=mask, valid_lens=vl)
+    check("mha cross [%d,%d<-%d,%d] h%d %s" % (B, Nq, Nkv, dm, h, mask), got, ref, "bf16")
+
+
+def test_mha_cross_equals_self_layer(dev):
+    """With the same sequence on both sides and no mask, the cross layer computes the self-attention
+    layer (the same kernels: bit for bit)."""
+    import transformer_scaled_dot_amd as tsd
+
+    x, wqkv, wo = synth.mha_inputs(4, B=2, N=300, d_model=512)
+    X, W, Wo = x.torch(dev), wqkv.torch(dev), wo.torch(dev)
+    y1 = tsd.mha_fwd(X, W, Wo, 8)
+    y2 = tsd.mha_cross_fwd(X, X, W, Wo, 8)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)

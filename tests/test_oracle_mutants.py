@@ -27,7 +27,10 @@ MUTANTS = {
                                        "int64_t src = (b * N + t) * W3 + c * h + hh;"),
     "mha_heads_interleaved_on_concat": ("C[(b * N + t) * d_model + hh * dk + c]",
                                         "C[(b * N + t) * d_model + c * h + hh]"),
-    "mha_scale_by_d_model": ("1.0 / sqrt((double)dk)", "1.0 / sqrt((double)d_model)"),
+    "mha_scale_by_d_model": ("ORACLE_MASK_NONE, NULL, 1.0 / sqrt((double)dk), Oh,",
+                             "ORACLE_MASK_NONE, NULL, 1.0 / sqrt((double)d_model), Oh,"),
+    "cross_scale_by_d_model": ("mask_kind, valid_lens, 1.0 / sqrt((double)dk), Oh,",
+                               "mask_kind, valid_lens, 1.0 / sqrt((double)d_model), Oh,"),
     "causal_padding_either_rule": ("return j <= i && j < valid_len;", "return j <= i || j < valid_len;"),
     "causal_padding_ignores_lengths": ("return mask_kind == ORACLE_MASK_PADDING || mask_kind == ORACLE_MASK_CAUSAL_PADDING;",
                                        "return mask_kind == ORACLE_MASK_PADDING;"),
@@ -40,6 +43,14 @@ MUTANTS = {
     "bwd_dv_weighted_by_da": ("dVbh[j * dv + c] += a[j] * g[c];", "dVbh[j * dv + c] += da[j] * g[c];"),
     "bwd_group_first_head_only": ("for (int64_t h = hk * group; h < (hk + 1) * group; ++h) {",
                                   "for (int64_t h = hk * group; h < hk * group + 1; ++h) {"),
+    "cross_queries_from_key_sequence": ("matmul_f64(Xq, Wq, Pq, Mq, d_model, d_model);",
+                                        "matmul_f64(Xkv, Wq, Pq, Mq, d_model, d_model);"),
+    "cross_k_v_swapped": ("Vh[((b * h + hh) * Nkv + t) * dk + c] = Pkv[(b * Nkv + t) * 2 * d_model + d_model + hh * dk + c];",
+                          "Vh[((b * h + hh) * Nkv + t) * dk + c] = Pkv[(b * Nkv + t) * 2 * d_model + hh * dk + c];"),
+    "cross_padding_ignored": ("oracle_attn(Qh, Kh, Vh, B, h, h, Nq, Nkv, dk, dk, mask_kind, valid_lens,",
+                              "oracle_attn(Qh, Kh, Vh, B, h, h, Nq, Nkv, dk, dk, ORACLE_MASK_NONE, valid_lens,"),
+    "cross_w_k_block_from_w_q": ("Wkv[r * 2 * d_model + c] = Wqkv[r * W3 + d_model + c];",
+                                 "Wkv[r * 2 * d_model + c] = Wqkv[r * W3 + c];"),
 }
 
 

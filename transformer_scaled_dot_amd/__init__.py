@@ -19,7 +19,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["attn_fwd", "attn_weights", "attn_bwd", "mha_fwd", "mha_workspace_bytes", "library_path", "load_library", "AttnError"]
+__all__ = ["attn_fwd", "attn_weights", "attn_bwd", "mha_fwd", "mha_cross_fwd", "mha_workspace_bytes", "library_path", "load_library", "AttnError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtsd_attn.so")
@@ -29,7 +29,8 @@ MASK_KINDS = {"none": 0, "causal": 1, "padding": 2, "causal_padding": 3}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_weights", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_noalloc",
-           "attn_bwd_noalloc_max_scratch_bytes", "mha_workspace_bytes", "mha_fwd", "attn_status_string",
+           "attn_bwd_noalloc_max_scratch_bytes", "mha_workspace_bytes", "mha_fwd", "mha_cross_workspace_bytes",
+           "mha_cross_fwd", "attn_status_string",
            "attn_last_error")
 
 _lib = None
@@ -73,6 +74,10 @@ def load_library():
     lib.mha_workspace_bytes.restype = ctypes.c_size_t
     lib.mha_fwd.argtypes = [P, P, P, I32, P, I32, I32, I32, I32, P, ctypes.c_size_t, P]
     lib.mha_fwd.restype = ctypes.c_int
+    lib.mha_cross_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
+    lib.mha_cross_workspace_bytes.restype = ctypes.c_size_t
+    lib.mha_cross_fwd.argtypes = [P, P, P, P, I32, I32, P, P, I32, I32, I32, I32, I32, P, ctypes.c_size_t, P]
+    lib.mha_cross_fwd.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [I32]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
@@ -281,4 +286,36 @@ def mha_fwd(x, w_qkv, w_o, h: int, out=None, workspace=None):
                      _dtype_code(x), ctypes.c_void_p(workspace.data_ptr()),
                      ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream_ptr(x.device))
     _raise_for(lib, st, "mha_fwd")
+    return out
+
+
+def mha_cross_fwd(xq, xkv, w_qkv, w_o, h: int, mask: str = "none", valid_lens=None, out=None, workspace=None):
+    """Multi-head cross-attention layer: queries from xq [B, Nq, d_model], keys and values from xkv
+    [B, Nkv, d_model], the weights of mha_fwd (W_qkv [d_model, 3 d_model] = [W_Q | W_K | W_V], W_o);
+    mask "none" or "padding" (keys j >= valid_lens[b] of xkv hidden). Returns [B, Nq, d_model]."""
+    import torch
+
+    lib = load_library()
+    if mask not in ("none", "padding"):
+        raise ValueError("cross-attention masks: none or padding")
+    _check_gpu(xq, xkv, w_qkv, w_o, valid_lens, out, workspace)
+    if xq.dim() != 3 or xkv.dim() != 3 or xkv.shape[0] != xq.shape[0] or xkv.shape[2] != xq.shape[2]:
+        raise ValueError("xq [B, Nq, d_model] and xkv [B, Nkv, d_model] expected")
+    B, Nq, dm = xq.shape
+    Nkv = xkv.shape[1]
+    if tuple(w_qkv.shape) != (dm, 3 * dm) or tuple(w_o.shape) != (dm, dm):
+        raise ValueError("w_qkv must be [d_model, 3 d_model] and w_o [d_model, d_model]")
+    if mask == "padding" and (valid_lens is None or valid_lens.dtype != torch.int32 or tuple(valid_lens.shape) != (B,)):
+        raise ValueError("padding mask needs valid_lens: int32 GPU tensor of shape [B]")
+    need = int(lib.mha_cross_workspace_bytes(B, Nq, Nkv, dm, int(h), _dtype_code(xq)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=xq.device)
+    if out is None:
+        out = torch.empty((B, Nq, dm), dtype=xq.dtype, device=xq.device)
+    P = ctypes.c_void_p
+    st = lib.mha_cross_fwd(P(xq.data_ptr()), P(xkv.data_ptr()), P(w_qkv.data_ptr()), P(w_o.data_ptr()), int(h),
+                           MASK_KINDS[mask], P(valid_lens.data_ptr() if mask == "padding" else 0), P(out.data_ptr()),
+                           B, Nq, Nkv, dm, _dtype_code(xq), P(workspace.data_ptr()),
+                           ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream_ptr(xq.device))
+    _raise_for(lib, st, "mha_cross_fwd")
     return out

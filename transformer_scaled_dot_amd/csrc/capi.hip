@@ -371,6 +371,72 @@ attn_status_t mha_fwd(const void *X, const void *W_qkv, const void *W_o, int32_t
     return from_hip(e, "mha_fwd output GEMM");
 }
 
+size_t mha_cross_workspace_bytes(int32_t batch, int32_t seq_q, int32_t seq_kv, int32_t d_model, int32_t h,
+                                 int32_t dtype)
+{
+    char saved[sizeof g_last_error];
+    snprintf(saved, sizeof saved, "%s", g_last_error);
+    const attn_status_t st = seq_kv < 0 ? ATTN_EINVAL : mha_check(batch, seq_q, d_model, h, dtype);
+    const attn_status_t st2 = st == ATTN_OK ? mha_check(batch, seq_kv, d_model, h, dtype) : st;
+    snprintf(g_last_error, sizeof g_last_error, "%s", saved);
+    if (st2 != ATTN_OK) return 0;
+    const size_t tq = (size_t)batch * seq_q * d_model, tk = (size_t)batch * seq_kv * d_model;
+    return (2 * tq + 2 * tk) * 2;  // q and k, v split into heads + concatenated head outputs, bf16
+}
+
+attn_status_t mha_cross_fwd(const void *Xq, const void *Xkv, const void *W_qkv, const void *W_o, int32_t h,
+                            int32_t mask_kind, const int32_t *valid_lens, void *O, int32_t batch, int32_t seq_q,
+                            int32_t seq_kv, int32_t d_model, int32_t dtype, void *workspace, size_t workspace_bytes,
+                            void *stream)
+{
+    g_last_error[0] = '\0';
+    if (seq_kv < 0) return fail(ATTN_EINVAL, "mha_cross_fwd: negative seq_kv");
+    attn_status_t st = mha_check(batch, seq_q, d_model, h, dtype);
+    if (st != ATTN_OK) return st;
+    if (mask_kind != ATTN_MASK_NONE && mask_kind != ATTN_MASK_PADDING)
+        return fail(mask_kind == ATTN_MASK_CAUSAL || mask_kind == ATTN_MASK_CAUSAL_PADDING ? ATTN_EUNSUPPORTED
+                                                                                            : ATTN_EINVAL,
+                    "mha_cross_fwd: mask_kind must be none or padding (got %d)", mask_kind);
+    if ((long long)batch * seq_kv > kI32Max) return fail(ATTN_EINVAL, "mha_cross_fwd: batch*seq_kv too large");
+    const size_t tq = (size_t)batch * seq_q * d_model, tk = (size_t)batch * seq_kv * d_model;
+    if (tq == 0) return ATTN_OK;  // no output row
+    const bool padding = mask_kind == ATTN_MASK_PADDING;
+    if (!Xq || !W_qkv || !W_o || !O || !workspace || (tk && !Xkv))
+        return fail(ATTN_EINVAL, "mha_cross_fwd: null pointer");
+    if (padding && !valid_lens) return fail(ATTN_EINVAL, "mha_cross_fwd: padding mask needs valid_lens");
+    const size_t need = mha_cross_workspace_bytes(batch, seq_q, seq_kv, d_model, h, dtype);
+    if (workspace_bytes < need)
+        return fail(ATTN_EINVAL, "mha_cross_fwd: workspace of %zu bytes, need %zu", workspace_bytes, need);
+    if (!aligned(Xq, 16) || (Xkv && !aligned(Xkv, 16)) || !aligned(W_qkv, 16) || !aligned(W_o, 16) ||
+        !aligned(O, 16) || !aligned(workspace, 256) || (padding && !aligned(valid_lens, 4)))
+        return fail(ATTN_EINVAL, "mha_cross_fwd: tensors must be 16-byte aligned, workspace 256-byte aligned");
+    const size_t wb = (size_t)d_model * d_model * 2;
+    const void *ins[] = {Xq, Xkv, W_qkv, W_o};
+    const size_t in_n[] = {tq * 2, tk * 2, 3 * wb, wb};
+    for (int j = 0; j < 4; ++j)
+        if (overlaps(O, tq * 2, ins[j], in_n[j]) || overlaps(workspace, need, ins[j], in_n[j]))
+            return fail(ATTN_EINVAL, "mha_cross_fwd: output or workspace overlaps an input");
+    if (overlaps(workspace, need, O, tq * 2)) return fail(ATTN_EINVAL, "mha_cross_fwd: workspace overlaps O");
+
+    hipStream_t s = (hipStream_t)stream;
+    const int dk = d_model / h;
+    uint16_t *qh = (uint16_t *)workspace;  // [batch][h][seq_q][dk]
+    uint16_t *kvh = qh + tq;               // [2][batch][h][seq_kv][dk]
+    uint16_t *ctx = kvh + 2 * tk;          // [batch][seq_q][h*dk]
+    hipError_t e = tsd::launch_gemm_bf16_heads(Xq, W_qkv, 3 * d_model, qh, batch, seq_q, d_model, d_model, h, s);
+    if (e != hipSuccess) return from_hip(e, "mha_cross_fwd query projection GEMM");
+    if (tk) {
+        e = tsd::launch_gemm_bf16_heads(Xkv, (const uint16_t *)W_qkv + d_model, 3 * d_model, kvh, batch, seq_kv,
+                                        2 * d_model, d_model, h, s);
+        if (e != hipSuccess) return from_hip(e, "mha_cross_fwd key/value projection GEMM");
+    }
+    e = tsd::launch_attn_bf16(qh, kvh, kvh + tk, mask_kind, valid_lens, 1.0f / sqrtf((float)dk), ctx, 0, tsd::kOutBNHD,
+                              batch, h, seq_q, seq_kv, dk, tsd::AttnHeads{h, 1, nullptr}, s);
+    if (e != hipSuccess) return from_hip(e, "mha_cross_fwd attention");
+    e = tsd::launch_gemm_bf16(ctx, W_o, O, batch * seq_q, d_model, d_model, s);
+    return from_hip(e, "mha_cross_fwd output GEMM");
+}
+
 const char *attn_status_string(int32_t status)
 {
     switch (status) {

@@ -54,7 +54,7 @@ __device__ __forceinline__ uint32_t gsw(int r, int e)
 template <int BM, int BN, int WM, int WN, int STAGES, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(const uint16_t *__restrict__ A,
                                                                 const uint16_t *__restrict__ Bm,
-                                                                uint16_t *__restrict__ C, int M, int N, int Kd,
+                                                                uint16_t *__restrict__ C, int M, int N, int Kd, int ldb,
                                                                 int tiles_n, int xcd_chunk, QkvShape qs)
 {
     constexpr int NW = WM * WN;
@@ -93,13 +93,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(const uint16_t 
     for (int j = 0; j < B_DMA; ++j) {
         const int blk = j * NW + wave, r = blk * B_RPK + lane / B_CPR, cp = lane % B_CPR;
         const int c = cp ^ swz<BN>(r);
-        b_off[j] = (uint32_t)r * (uint32_t)N * 2u + (uint32_t)c * 16u;
+        b_off[j] = (uint32_t)r * (uint32_t)ldb * 2u + (uint32_t)c * 16u;
     }
     const uint32_t lds0 = lds_addr(smem);
     const uint32_t lwave = __builtin_amdgcn_readfirstlane(lds0 + wave * 1024);
     const uint16_t *Ab = A + (size_t)m0 * Kd, *Bb = Bm + n0;
     auto fetch = [&](int kt, int buf) {
-        const uint16_t *ak = Ab + kt * kGBK, *bk = Bb + (size_t)kt * kGBK * N;
+        const uint16_t *ak = Ab + kt * kGBK, *bk = Bb + (size_t)kt * kGBK * ldb;
 #pragma unroll
         for (int j = 0; j < A_DMA; ++j) lds_dma16(lwave + buf * STAGE + j * NW * 1024, ak, a_off[j]);
 #pragma unroll
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(const uint16_t 
             bf16x8 aop[NB], bop[MB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-                aop[nb] = lds_tr_pair((const uint16_t *)(st + (rb[nb][0] ^ 0) + kk * 16 * BN * 2),
+                aop[nb] = lds_tr_pair((const uint16_t *)(st + rb[nb][0] + kk * 16 * BN * 2),
                                       (const uint16_t *)(st + rb[nb][1] + kk * 16 * BN * 2));
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
@@ -203,7 +203,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(const uint16_t 
 }
 
 template <int EPI>
-hipError_t launch(const void *A, const void *Bm, void *C, int M, int N, int K, QkvShape qs, hipStream_t stream)
+hipError_t launch(const void *A, const void *Bm, int ldb, void *C, int M, int N, int K, QkvShape qs,
+                  hipStream_t stream)
 {
     if (M <= 0) return hipSuccess;
     const int cus = device_cu_count();
@@ -214,8 +215,8 @@ hipError_t launch(const void *A, const void *Bm, void *C, int M, int N, int K, Q
         if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         const int chunk = grid % 8 == 0 ? (int)(grid / 8) : 0;
         hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, ST, EPI>), dim3((unsigned)grid), dim3(WM * WN * 64), 0,
-                           stream, (const uint16_t *)A, (const uint16_t *)Bm, (uint16_t *)C, M, N, K, (int)tiles_n,
-                           chunk, qs);
+                           stream, (const uint16_t *)A, (const uint16_t *)Bm, (uint16_t *)C, M, N, K, ldb,
+                           (int)tiles_n, chunk, qs);
         return hipGetLastError();
     };
     using I = std::integral_constant<int, 0>;
@@ -235,16 +236,23 @@ hipError_t launch(const void *A, const void *Bm, void *C, int M, int N, int K, Q
 hipError_t launch_gemm_bf16(const void *A, const void *Bm, void *C, int M, int N, int K, hipStream_t stream)
 {
     if (N % 64 != 0 || K % kGBK != 0) return hipErrorInvalidValue;
-    return launch<kEpiPlain>(A, Bm, C, M, N, K, QkvShape{0, 1, 1, 1, 1}, stream);
+    return launch<kEpiPlain>(A, Bm, N, C, M, N, K, QkvShape{0, 1, 1, 1, 1}, stream);
+}
+
+hipError_t launch_gemm_bf16_heads(const void *X, const void *W, int ldw, void *out, int batch, int seq, int n_cols,
+                                  int d_model, int heads, hipStream_t stream)
+{
+    if (d_model % 64 != 0 || d_model % heads != 0 || (d_model / heads) % 64 != 0 || n_cols % d_model != 0 ||
+        ldw < n_cols || ldw % 8 != 0)
+        return hipErrorInvalidValue;
+    const QkvShape qs{batch, seq, d_model, heads, d_model / heads};
+    return launch<kEpiQkvSplit>(X, W, ldw, out, batch * seq, n_cols, d_model, qs, stream);
 }
 
 hipError_t launch_gemm_bf16_qkv_split(const void *X, const void *Wqkv, void *qkv, int batch, int seq, int d_model,
                                       int heads, hipStream_t stream)
 {
-    const int N = 3 * d_model;
-    if (d_model % 64 != 0 || d_model % heads != 0 || (d_model / heads) % 64 != 0) return hipErrorInvalidValue;
-    const QkvShape qs{batch, seq, d_model, heads, d_model / heads};
-    return launch<kEpiQkvSplit>(X, Wqkv, qkv, batch * seq, N, d_model, qs, stream);
+    return launch_gemm_bf16_heads(X, Wqkv, 3 * d_model, qkv, batch, seq, 3 * d_model, d_model, heads, stream);
 }
 
 }  // namespace tsd

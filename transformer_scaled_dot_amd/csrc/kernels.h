@@ -63,5 +63,11 @@ hipError_t launch_gemm_bf16(const void *A, const void *Bm, void *C, int M, int N
 hipError_t launch_gemm_bf16_qkv_split(const void *X, const void *Wqkv, void *qkv, int batch, int seq, int d_model,
                                       int heads, hipStream_t stream);
 
+// The same head-split epilogue for the columns [0, n_cols) of a weight with row stride ldw (W may point into
+// a wider matrix): out[which][b][head][t][c] with which = n / d_model, so n_cols = d_model gives Q alone
+// and n_cols = 2 d_model (W at the W_K block) gives K and V.
+hipError_t launch_gemm_bf16_heads(const void *X, const void *W, int ldw, void *out, int batch, int seq, int n_cols,
+                                  int d_model, int heads, hipStream_t stream);
+
 
 }  // namespace tsd
