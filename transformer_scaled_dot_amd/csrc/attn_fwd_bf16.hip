@@ -153,10 +153,12 @@ __device__ __forceinline__ void store_rows_bf16_staged(const u32x8 (&pk)[4], int
 template <int D, int QB>
 struct AttnTraits {
     static constexpr int kWavesPerEU = 2;
-    static constexpr bool kPipelined = QB == 1;  // S(t+1)/softmax(t) overlap: a second score buffer
 };
 
-template <int D, int QB, int MASK, bool OUT_F32, int OLAYOUT, int WAVES>
+// KSPLIT = 2: the workgroup's waves form two sets of WAVES / 2, each set running the same query rows over
+// one half of the key tiles (for grids too small to give every SIMD two waves otherwise); the halves' online
+// softmax states (reference max, sum, partial output) are merged through LDS at the end.
+template <int D, int QB, int MASK, bool OUT_F32, int OLAYOUT, int WAVES, int KSPLIT>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
     AttnTraits<D, QB>::kWavesPerEU, AttnTraits<D, QB>::kWavesPerEU))) void attn_fwd_bf16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
@@ -164,20 +166,25 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
     int num_qtiles, int BH, AttnHeads hd)
 {
     static_assert(QB == 1, "one query block per wave");
+    static_assert(KSPLIT == 1 || KSPLIT == 2, "one or two key halves");
+    constexpr int RB = WAVES / KSPLIT; // waves per key half = 32-row blocks per workgroup
     constexpr int RW = QB * 32;        // query rows per wave
-    constexpr int BM = WAVES * RW;     // query rows per workgroup
+    constexpr int BM = RB * RW;        // query rows per workgroup
     constexpr int KS = D / 16;         // k-steps of the Q K^T contraction
     constexpr int DB = D / 32;         // 32-row blocks of O^T
     constexpr int TILE_B = kBlockN * D * 2;                     // bytes of one K (or V) tile
     constexpr int CPR = D / 8;                                  // 16-byte chunks per row
-    constexpr int CH = kBlockN * CPR / (WAVES * 64);            // DMA chunks per lane per tensor per tile
-    static_assert(kBlockN * CPR % (WAVES * 64) == 0, "tile must split evenly over the workgroup");
+    constexpr int CH = kBlockN * CPR / (RB * 64);               // DMA chunks per lane per tensor per tile
+    static_assert(kBlockN * CPR % (RB * 64) == 0, "tile must split evenly over the waves of a key half");
     static_assert(4 * TILE_B <= 65536, "LDS offsets must fit instruction immediates");
-    // LDS bytes: [K slot 0 | K slot 1 | V slot 0 | V slot 1]; tile i uses slot i % 2
-    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_B];
+    // LDS bytes, per key half: [K slot 0 | K slot 1 | V slot 0 | V slot 1]; tile i uses slot i % 2
+    constexpr int HALF_B = 4 * TILE_B;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[KSPLIT * HALF_B];
     constexpr int KSLOT0 = 0, KSLOT1 = TILE_B, VSLOT0 = 2 * TILE_B, VSLOT1 = 3 * TILE_B;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // kh: the wave's key half; wave: its 32-row block within the workgroup
+    const int kh = __builtin_amdgcn_readfirstlane((tid >> 6) / RB), wave = (tid >> 6) % RB;
     const int l32 = lane & 31, hf = lane >> 5;
 
     // q-tile-major order: the q-tiles of one head are BH ids apart, which
@@ -232,7 +239,26 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
         l_run[qb] = 0.f;
     }
 
-    const TileAddrs<D> ad = tile_addrs<D>(lane);
+    TileAddrs<D> ad = tile_addrs<D>(lane);
+    if constexpr (KSPLIT > 1) {
+        // the second key half's slots: its base folded into the address registers (slot offsets stay
+        // instruction immediates)
+        const uint32_t hb = (uint32_t)__builtin_amdgcn_readfirstlane(kh * HALF_B);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint32_t x = ad.k[ks] + hb;
+            asm volatile("" : "+v"(x));
+            ad.k[ks] = x;
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                uint32_t x = ad.v[db][h2] + hb;
+                asm volatile("" : "+v"(x));
+                ad.v[db][h2] = x;
+            }
+    }
 
     // DMA j of this wave fills the 64 consecutive LDS chunks
     // [(j*WAVES + wave)*64, +64) of a tile; lane i fetches the global chunk
@@ -244,7 +270,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
     int drow[CH];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-        const int c = (j * WAVES + wave) * 64 + lane;
+        const int c = (j * RB + wave) * 64 + lane;
         const int r = c / CPR, x = c % CPR;
         drow[j] = r;
         voff[j] = (uint32_t)(r * D + ((x ^ swz<D>(r)) << 3)) * 2;
@@ -260,7 +286,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
                 const int r = min(drow[j], kv_end - 1 - k0);
                 off = off - (uint32_t)(drow[j] - r) * (D * 2);
             }
-            lds_dma16(__builtin_amdgcn_readfirstlane(lds0 + slot_off + (j * WAVES + wave) * 1024), base, off);
+            lds_dma16(__builtin_amdgcn_readfirstlane(lds0 + kh * HALF_B + slot_off + (j * RB + wave) * 1024), base,
+                      off);
         }
     };
 
@@ -297,18 +324,25 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
                 }
     };
 
-    if constexpr (AttnTraits<D, QB>::kPipelined) {
+    // This wave's key half: tiles [tb, te) of the workgroup's ntiles (all of them without a split); nsteps
+    // steps for every wave (the halves differ by at most one tile), each ending in the same barrier.
+    const int nt0 = KSPLIT == 1 ? ntiles : (ntiles + 1) / 2;
+    const int tb = kh == 0 ? 0 : nt0, te = kh == 0 ? nt0 : ntiles;
+    const int nh = te - tb;                                  // tiles this half fetches
+    const int nwh = min(max(ntiles_w - tb, 0), nh);           // tiles of the half this wave computes
+    const int nsteps = nt0;
+    {
         // Software pipeline: iteration t reads K(t+1) and V(t) from LDS while
         // the DMA fills K(t+2) and V(t+1); the MFMAs of S(t+1) are issued in
-        // the same basic block as the exponentials of S(t).
+        // the same basic block as the exponentials of S(t). (t: the tile's index within the half.)
         f32x16 sa[QB][2], sb[QB][2];
-        if (ntiles > 0) {
-            issue(Kh, 0, KSLOT0);
+        if (nsteps > 0) {
+            if (nh > 0) issue(Kh, tb, KSLOT0);
             wait_vmcnt0();
             __syncthreads();
-            if (ntiles > 1) issue(Kh, 1, KSLOT1);
-            issue(Vh, 0, VSLOT0);
-            if (ntiles_w > 0) scores<D, QB, KSLOT0>(smem, ad, qreg, sa);
+            if (nh > 1) issue(Kh, tb + 1, KSLOT1);
+            if (nh > 0) issue(Vh, tb, VSLOT0);
+            if (nwh > 0) scores<D, QB, KSLOT0>(smem, ad, qreg, sa);
             wait_vmcnt0();
             __syncthreads();
         }
@@ -316,13 +350,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
             constexpr int P = decltype(parity)::value;  // t % 2
             constexpr int KNEXT = P ? KSLOT0 : KSLOT1;  // K(t+1) lives in slot (t+1)%2
             constexpr int VCUR = P ? VSLOT1 : VSLOT0;   // V(t) in slot t%2
-            if (t + 2 < ntiles) issue(Kh, t + 2, P ? KSLOT1 : KSLOT0);
-            if (t + 1 < ntiles) issue(Vh, t + 1, P ? VSLOT0 : VSLOT1);
-            if (t < ntiles_w) {
+            if (t + 2 < nh) issue(Kh, tb + t + 2, P ? KSLOT1 : KSLOT0);
+            if (t + 1 < nh) issue(Vh, tb + t + 1, P ? VSLOT0 : VSLOT1);
+            if (t < nwh) {
                 float mref[QB];
-                prepare(t, cur, mref);
+                prepare(tb + t, cur, mref);
                 bf16x8 pb[QB][4];
-                if (t + 1 < ntiles_w) {
+                if (t + 1 < nwh) {
                     scores<D, QB, KNEXT>(smem, ad, qreg, nxt);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) softmax_exp(cur[qb], pb[qb], mref[qb], c_log2, l_run[qb]);
@@ -336,42 +370,39 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
             wait_vmcnt0();
             __syncthreads();
         };
-        for (int t = 0; t < ntiles; t += 2) {
+        for (int t = 0; t < nsteps; t += 2) {
             step(t, std::integral_constant<int, 0>(), sa, sb);
-            if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>(), sb, sa);
+            if (t + 1 < nsteps) step(t + 1, std::integral_constant<int, 1>(), sb, sa);
         }
-    } else {
-        // Plain double buffering: iteration t computes tile t from slot t%2
-        // while the DMA fills slot (t+1)%2 with tile t+1.
-        if (ntiles > 0) {
-            issue(Kh, 0, KSLOT0);
-            issue(Vh, 0, VSLOT0);
-        }
-        wait_vmcnt0();
-        __syncthreads();
-        auto step = [&](int t, auto parity) {
-            constexpr int P = decltype(parity)::value;  // t % 2
-            if (t + 1 < ntiles) {
-                issue(Kh, t + 1, P ? KSLOT0 : KSLOT1);
-                issue(Vh, t + 1, P ? VSLOT0 : VSLOT1);
-            }
-            if (t < ntiles_w) {
-                f32x16 cur[QB][2];
-                scores<D, QB, P ? KSLOT1 : KSLOT0>(smem, ad, qreg, cur);
-                float mref[QB];
-                prepare(t, cur, mref);
-                bf16x8 pb[QB][4];
+    }
+
+    if constexpr (KSPLIT > 1) {
+        // Merge the halves, row by row (lane by lane: both halves hold the same rows and output columns in
+        // the same lanes). With references m_a, m_b: m = max, each half scaled by exp2(m_x - m) (0 for a half
+        // without a visible key), O = O_a s_a + O_b s_b, l = l_a s_a + l_b s_b. The second half's state goes
+        // through LDS (the tile slots are free: the last step ended in a barrier).
+        constexpr int NV = DB * 16 + 2;
+        float *part = (float *)smem + wave * (NV * 64);
+        if (kh == 1) {
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) softmax_exp(cur[qb], pb[qb], mref[qb], c_log2, l_run[qb]);
-                accumulate_pv<D, QB, P ? VSLOT1 : VSLOT0>(smem, ad, pb, acc);
-            }
-            wait_vmcnt0();
-            __syncthreads();
-        };
-        for (int t = 0; t < ntiles; t += 2) {
-            step(t, std::integral_constant<int, 0>());
-            if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>());
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) part[(db * 16 + r) * 64 + lane] = acc[0][db][r];
+            part[(NV - 2) * 64 + lane] = mc_run[0];
+            part[(NV - 1) * 64 + lane] = l_run[0];
         }
+        __syncthreads();
+        if (kh == 1) return;
+        const float mb = part[(NV - 2) * 64 + lane], lb = part[(NV - 1) * 64 + lane];
+        const float m = fmaxf(mc_run[0], mb);
+        const float sa = mc_run[0] == -INFINITY ? 0.f : fast_exp2(mc_run[0] - m);
+        const float sb = mb == -INFINITY ? 0.f : fast_exp2(mb - m);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[0][db][r] = acc[0][db][r] * sa + part[(db * 16 + r) * 64 + lane] * sb;
+        l_run[0] = l_run[0] * sa + lb * sb;
+        mc_run[0] = m;
     }
 
     // ---- epilogue: O = O_acc / l (0 for a row with no visible key) ----
@@ -668,17 +699,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // The C++ MFMA kernel (32 * QB query rows per wave, WAVES waves per workgroup) on its grid of query tiles.
-template <int D, int QB, int MASK, bool OUT_F32, int OLAYOUT, int WAVES>
+template <int D, int QB, int MASK, bool OUT_F32, int OLAYOUT, int WAVES, int KSPLIT = 1>
 hipError_t launch_cpp(const void *Q, const void *K, const void *V, const int32_t *valid_lens, float c_log2, void *O,
                       int B, int H, int Nq, int Nk, AttnHeads hd, hipStream_t stream)
 {
-    constexpr int BM = WAVES * 32 * QB;
+    constexpr int BM = WAVES / KSPLIT * 32 * QB;
     const int BH = B * H;
     const int num_qtiles = (Nq + BM - 1) / BM;
     const long long grid = (long long)num_qtiles * BH;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QB, MASK, OUT_F32, OLAYOUT, WAVES>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, QB, MASK, OUT_F32, OLAYOUT, WAVES, KSPLIT>), dim3((unsigned)grid),
                        dim3(WAVES * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
                        valid_lens, c_log2, O, H, Nq, Nk, num_qtiles, BH, hd);
     return hipGetLastError();
@@ -708,10 +739,15 @@ hipError_t launch_variant(const void *Q, const void *K, const void *V, const int
     } else {
         static_assert(D == 64, "head_dim 64 or 128");
         // 8 waves (256 rows per workgroup) when that grid still gives every CU a workgroup (4.5 % faster at
-        // B4 H8 N2048), else 4 (128 rows: twice the workgroups for small launches)
-        const long long g8 = (long long)((Nq + 255) / 256) * B * H;
-        if (g8 >= device_cu_count())
+        // B4 H8 N2048); else 4 waves of 128 rows, which give every SIMD two waves when their grid has more
+        // workgroups than CUs; smaller grids split each workgroup's keys over two sets of 4 waves
+        const int cus = device_cu_count();
+        const long long g8 = (long long)((Nq + 255) / 256) * B * H, g4 = (long long)((Nq + 127) / 128) * B * H;
+        if (g8 >= cus)
             return launch_cpp<D, 1, MASK, OUT_F32, OLAYOUT, 8>(Q, K, V, valid_lens, c_log2, O, B, H, Nq, Nk, hd, stream);
+        if (g4 <= cus)
+            return launch_cpp<D, 1, MASK, OUT_F32, OLAYOUT, 8, 2>(Q, K, V, valid_lens, c_log2, O, B, H, Nq, Nk, hd,
+                                                                 stream);
         return launch_cpp<D, 1, MASK, OUT_F32, OLAYOUT, 4>(Q, K, V, valid_lens, c_log2, O, B, H, Nq, Nk, hd, stream);
     }
 }
