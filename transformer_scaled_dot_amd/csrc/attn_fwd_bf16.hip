@@ -356,16 +356,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
                 float mref[QB];
                 prepare(tb + t, cur, mref);
                 bf16x8 pb[QB][4];
-                if (t + 1 < nwh) {
-                    scores<D, QB, KNEXT>(smem, ad, qreg, nxt);
+                // S(t+1) also on the wave's last tile (one set of MFMAs whose result is never read): a
+                // branch here would leave the compiler two versions of the O accumulator to reconcile
+                scores<D, QB, KNEXT>(smem, ad, qreg, nxt);
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) softmax_exp(cur[qb], pb[qb], mref[qb], c_log2, l_run[qb]);
-                    accumulate_pv<D, QB, VCUR>(smem, ad, pb, acc);
-                } else {
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) softmax_exp(cur[qb], pb[qb], mref[qb], c_log2, l_run[qb]);
-                    accumulate_pv<D, QB, VCUR>(smem, ad, pb, acc);
-                }
+                for (int qb = 0; qb < QB; ++qb) softmax_exp(cur[qb], pb[qb], mref[qb], c_log2, l_run[qb]);
+                accumulate_pv<D, QB, VCUR>(smem, ad, pb, acc);
             }
             wait_vmcnt0();
             __syncthreads();
