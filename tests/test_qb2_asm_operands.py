@@ -159,8 +159,9 @@ def test_step_slots():
         kr, vr, _, _ = _slots(last)
         assert kr == set() and vr == {P}
     for off in (0, 1):
-        kr, vr, kw, vw = _slots(g.first_tile(off))
-        assert kr == {off} and not vr and not kw and not vw
+        for turn in (False, True):
+            kr, vr, kw, vw = _slots(g.first_tile(off, turn))
+            assert kr == {off} and not vr and not kw and not vw
     # step 0 fetches K(2) into the slot S(0) reads K(0) from: a barrier must separate them
     body = g.loop_body()
     assert "s_barrier" in body[body.index("L_first_done_%=:"):body.index("L_top_%=:")]
@@ -333,6 +334,9 @@ class _ScalarModel:
                 assert -(1 << 31) <= v < (1 << 31), "signed overflow: %s" % ln
                 self.put(a[0], v)
                 self.scc = None
+            elif op == "s_mul_i32":
+                self.put(a[0], _s32(self.val(a[1])) * _s32(self.val(a[2])))
+                self.scc = None
             elif op == "s_lshl_b32":
                 self.put(a[0], self.val(a[1]) << self.val(a[2]))
                 self.scc = None
@@ -365,10 +369,13 @@ class _ScalarModel:
 
 
 def test_loop_scalar_control_model():
-    """For items of every tile count, wave extent, masked tile and diagonal tile: step t issues the four
-    loads of K(t+2) into K slot (t+off)%2 and of V(t+1) into the other V slot, each with the descriptor of
-    that tile of the stream (this item's tiles, then the next item's; its size the bytes below that
-    item's kv_end, never negative), and takes the path its tile calls for."""
+    """For items of every tile count, wave extent, masked tile and diagonal tile, with and without the turn
+    from a previous item: step t issues the four loads of K(t+2) into K slot (t+off)%2 and of V(t+1) into
+    the other V slot, each with the descriptor of that tile of the stream (this item's tiles, then the next
+    item's; its size the bytes below that item's kv_end, never negative), and takes the path its tile calls
+    for; the next item's Q rows are fetched into the Q slots, block qw through a descriptor of the rows below
+    N_q (min(64, max(0, nqr - 64 qw)) rows; nothing when nqr = 0), right after the barrier behind S(0) in
+    items of fewer than five tiles, else at step nt - 5 + qw."""
     g = _gen()
     body = g.loop_body()
     rng = np.random.default_rng(11)
@@ -384,7 +391,13 @@ def test_loop_scalar_control_model():
         # bases with low words near a 4 GiB boundary, so that the carries into the high word happen
         bases = {k: int(rng.integers(1, 1 << 16)) << 32 | (M32 + 1 - TILE * int(rng.integers(1, 6)))
                  for k in ("kh", "vh", "nkh", "nvh")}
-        ops = {"t": 0, "nt": nt, "ntw": ntw, "tm": tm, "dg": dg, "off": off, "kve": kve, "nkve": nkve, "lbw": 0}
+        nqr = int(rng.choice([0, int(rng.integers(1, 300))]))
+        nq = int(rng.integers(1, 1 << 16)) << 32 | (M32 + 1 - TILE * int(rng.integers(1, 6)))
+        tn = int(rng.integers(0, 2))
+        ops = {"t": 0, "nt": nt, "ntw": ntw, "tm": tm, "dg": dg, "off": off, "kve": kve, "nkve": nkve, "lbw": 0,
+               "tn": tn, "qsb": 4 * TB, "ostr": 256,
+               "obl": int(rng.integers(0, M32)), "obh": int(rng.integers(0, 1 << 16)),
+               "onb": int(rng.integers(0, 1 << 20)), "nql": nq & M32, "nqh": nq >> 32, "nqr": nqr}
         for k, b in bases.items():
             ops[k + "l"], ops[k + "h"] = b & M32, b >> 32
         m = _ScalarModel(body, ops, rng)
@@ -393,7 +406,15 @@ def test_loop_scalar_control_model():
         assert not m.steps[0]                      # the barrier after S(0): nothing fetched before it
         steps, paths = m.steps[1:], m.paths[:-1]
         assert len(steps) == nt, (case, ops)
-
+        # the next item's Q rows into the Q slots: items of fewer than five tiles fetch them right after
+        # that barrier (with step 0's loads), longer ones block qw at step nt - 5 + qw
+        qload = lambda x: x[4] >= g.QSLOT
+        got = [(t, x) for t, st in enumerate(steps) for x in st if qload(x)] + [(nt, x) for x in m.loads if qload(x)]
+        want_q = [(0 if nt < 5 else nt - 5 + qw,
+                   (g.SREG if nt >= 5 else g.KRES, nq + qw * TB, min(64, max(0, nqr - 64 * qw)) * 256, 0x20000,
+                    g.QSLOT + qw * TB + j * 4096)) for qw in range(4) for j in range(4)] if nqr > 0 else []
+        assert got == want_q, (case, ops)
+        steps = [[x for x in st if not qload(x)] for st in steps]
         def desc(h, x):
             if x < nt:
                 return bases[h] + x * TILE, max(0, kve * 256 - x * TILE)
@@ -472,3 +493,182 @@ def test_row_sum_product_gives_each_lane_its_query_sum():
         for l in range(64):
             for i in range(4):
                 np.testing.assert_allclose(Dm[4 * (l // 16) + i, l % 16], P[l % 32].sum(), rtol=1e-12)
+
+
+# --------------------------------------------------------------------------------------------------
+# The turn between two items, executed per lane on a model: the finished item's O (fp32, in the AGPR
+# layout of the 32 x 32 products) must reach global memory as bf16(O / l) at row (wave row), column d,
+# through the staging area of the wave and nothing else, for both output layouts and partial row blocks.
+
+def _bf16_bits(x):
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint32)
+
+
+def _run_vector(prog, O, inv, ops, lds, out, touched, v, acc, sreg):
+    """Executes the vector, LDS and store instructions of a turn program for 64 lanes (scalar
+    instructions: the few that compute addresses). O[k][r]: lane values of AGPR O_A + 16 k + r."""
+    g = _gen()
+    lanes = np.arange(64, dtype=np.int64)
+    cleared = set()
+
+    def reg(x):
+        x = x.strip()
+        if x.startswith("%["):
+            val = ops[x[2:-1]]
+            return np.broadcast_to(np.asarray(val, dtype=np.int64) & M32, (64,)).copy()
+        if re.fullmatch(r"v\d+", x):
+            return v[int(x[1:])].copy()
+        if re.fullmatch(r"s\d+", x):
+            return np.full(64, sreg[int(x[1:])], dtype=np.int64)
+        return np.full(64, int(x, 0) & M32, dtype=np.int64)
+
+    def sval(x):
+        x = x.strip()
+        if x.startswith("%["):
+            return ops[x[2:-1]] & M32
+        if re.fullmatch(r"s\d+", x):
+            return sreg[int(x[1:])]
+        return int(x, 0) & M32
+
+    def vrange(x):
+        m = re.fullmatch(r"[va]\[(\d+):(\d+)\]", x.strip())
+        return range(int(m.group(1)), int(m.group(2)) + 1)
+
+    for t in prog:
+        op, _, args = t.partition(" ")
+        a = [x.strip() for x in args.split(",")] if args else []
+        if op in ("s_waitcnt", "s_nop"):
+            continue
+        if op.startswith("s_"):
+            if a[0] in ("s80", "s81", "s82", "s83", "s88", "s89", "s90", "s91") and op == "s_mov_b32":
+                continue                              # buffer descriptors: the model checks offsets against onb
+            x = {"s_mov_b32": lambda: sval(a[1]), "s_lshl_b32": lambda: sval(a[1]) << sval(a[2]),
+                 "s_add_u32": lambda: sval(a[1]) + sval(a[2]),
+                 "s_mul_i32": lambda: sval(a[1]) * sval(a[2])}[op]()
+            sreg[int(a[0][1:])] = x & M32
+            continue
+        if op == "v_mfma_f32_32x32x16_bf16":
+            # O cleared by a product of zero operands: only after every read of that block
+            m = re.fullmatch(r"a\[(\d+):(\d+)\]", a[0])
+            k = (int(m.group(1)) - g.O_A) // 16
+            assert a[1] == a[2] == "v[%d:%d]" % (g.TURN_ZERO_V, g.TURN_ZERO_V + 3) and a[3] == "0", t
+            assert k not in cleared
+            cleared.add(k)
+            O[k][:] = np.nan                          # any later read of the block would show in the output
+            continue
+        d = int(a[0][1:]) if re.fullmatch(r"v\d+", a[0]) else None
+        if op == "v_add_u32":
+            v[d] = (reg(a[1]) + reg(a[2])) & M32
+        elif op == "v_mov_b32":
+            v[d] = reg(a[1])
+        elif op == "v_mbcnt_lo_u32_b32":
+            v[d] = np.minimum(lanes, 32) + reg(a[2])
+        elif op == "v_mbcnt_hi_u32_b32":
+            v[d] = np.maximum(lanes - 32, 0) + reg(a[2])
+        elif op == "v_and_b32":
+            v[d] = reg(a[1]) & reg(a[2])
+        elif op == "v_xor_b32":
+            v[d] = reg(a[1]) ^ reg(a[2])
+        elif op == "v_lshrrev_b32":
+            v[d] = reg(a[2]) >> reg(a[1])
+        elif op == "v_lshlrev_b32":
+            v[d] = (reg(a[2]) << reg(a[1])) & M32
+        elif op == "v_lshl_add_u32":
+            v[d] = ((reg(a[1]) << reg(a[2])) + reg(a[3])) & M32
+        elif op == "v_mul_u32_u24":
+            v[d] = ((reg(a[1]) & 0xFFFFFF) * (reg(a[2]) & 0xFFFFFF)) & M32
+        elif op == "v_mad_u32_u24":
+            v[d] = ((reg(a[1]) & 0xFFFFFF) * (reg(a[2]) & 0xFFFFFF) + reg(a[3])) & M32
+        elif op == "v_accvgpr_read_b32":
+            k, r = divmod(int(a[1][1:]) - g.O_A, 16)
+            v[d] = O[k][r].astype(np.float32).view(np.uint32).astype(np.int64)
+        elif op == "v_mul_f32":
+            qb = int(re.match(r"%\[inv(\d)\]", a[2]).group(1))
+            x = reg(a[1]).astype(np.uint32).view(np.float32) * np.float32(inv[qb])
+            v[d] = x.astype(np.float32).view(np.uint32).astype(np.int64)
+        elif op == "v_cvt_pk_bf16_f32":
+            lo = _bf16_bits(reg(a[1]).astype(np.uint32).view(np.float32))
+            hi = _bf16_bits(reg(a[2]).astype(np.uint32).view(np.float32))
+            v[d] = (lo | (hi << 16)).astype(np.int64)
+        elif op == "ds_write_b64":
+            m = re.search(r"offset:(\d+)", t)
+            addr = reg(a[0]) + (int(m.group(1)) if m else 0)
+            src = list(vrange(a[1].split()[0]))
+            for ln in range(64):
+                for i, rr in enumerate(src):
+                    lds[addr[ln] + 4 * i:addr[ln] + 4 * i + 4] = np.frombuffer(
+                        np.uint32(v[rr][ln]).tobytes(), dtype=np.uint8)
+            touched[0], touched[1] = min(touched[0], int(addr.min())), max(touched[1], int(addr.max()) + 8)
+        elif op == "ds_read_b128":
+            dst = list(vrange(a[0]))
+            m = re.search(r"offset:(\d+)", t)
+            addr = reg(a[1].split()[0]) + (int(m.group(1)) if m else 0)
+            vals = [np.array([int(np.frombuffer(lds[addr[ln] + 4 * i:addr[ln] + 4 * i + 4].tobytes(),
+                                                dtype=np.uint32)[0]) for ln in range(64)], dtype=np.int64)
+                    for i in range(4)]
+            for i, rr in enumerate(dst):
+                (v if a[0].startswith("v") else acc)[rr] = vals[i]
+            if a[0].startswith("v"):                  # the Q rows' reads are not the output's
+                touched[0], touched[1] = min(touched[0], int(addr.min())), max(touched[1], int(addr.max()) + 16)
+        elif op == "buffer_store_dwordx4":
+            src = list(vrange(a[0]))
+            data = v if a[0].startswith("v") else acc
+            voff = reg(a[1])
+            for ln in range(64):
+                o = int(voff[ln])
+                if o + 16 <= ops["onb"]:
+                    for i, rr in enumerate(src):
+                        out[o + 4 * i:o + 4 * i + 4] = np.frombuffer(np.uint32(data[rr][ln]).tobytes(),
+                                                                      dtype=np.uint8)
+                else:
+                    assert o >= ops["onb"], "a store straddles the end of the rows"
+        else:
+            pytest.fail("no model for %s" % t)
+    return cleared
+
+
+def _run_turn(g, off, O, inv, ops, lds_size, out_bytes):
+    """The turn on the model. Returns the output bytes (unwritten: 0xEE) and the LDS range the output rows
+    went through."""
+    pre, lead, items, _ = g.turn_work(off)
+    v, acc, sreg = {}, {}, {}
+    lds = np.zeros(lds_size, dtype=np.uint8)
+    out = np.full(out_bytes, 0xEE, dtype=np.uint8)
+    touched = [1 << 40, -1]
+    cleared = _run_vector(list(pre) + list(lead) + [x for it in items for x in it["ins"]], O, inv, ops, lds, out,
+                          touched, v, acc, sreg)
+    assert cleared == set(range(8)), "O not cleared block by block"
+    return out, touched
+
+
+@pytest.mark.parametrize("layout,nrows,off", [("bhnd", 64, 0), ("bhnd", 64, 1), ("bnhd", 64, 0), ("bnhd", 64, 1),
+                                              ("bhnd", 37, 1), ("bnhd", 5, 0), ("bhnd", 0, 1)])
+def test_turn_writes_previous_item_rows(layout, nrows, off):
+    """The turn packs the finished item's O (the AGPR layout of the 32 x 32 products) as bf16(O / l) into the
+    wave's Q slot and stores the rows from there: every row below the descriptor's end reaches memory at row * stride + column * 2, nothing else is
+    written, and the rows go through the wave's own Q slot only."""
+    g = _gen()
+    rng = np.random.default_rng(5)
+    H, wave = 3, 2
+    stride = 256 if layout == "bhnd" else H * 256
+    qsb = 4 * TB + wave * TB
+    onb = (nrows - 1) * stride + 256 if nrows > 0 else 0
+    O = rng.standard_normal((8, 16, 64)).astype(np.float32) * 3
+    inv = (np.float32(0.37), np.float32(1.9))
+    ops = {"wq": 4 * TB + wave * TB, "qsb": qsb, "ostr": stride, "onb": onb, **{"ka%d" % ks: 0 for ks in range(8)}}
+    out, touched = _run_turn(g, off, O.copy(), inv, ops, 10 * TB, 64 * stride + 256)
+    assert touched[0] >= qsb and touched[1] <= qsb + TB, "output rows outside the wave's Q slot"
+    want = np.full(64 * stride + 256, 0xEE, dtype=np.uint8)
+    for k in range(8):
+        qb, db = divmod(k, 4)
+        for r in range(16):
+            for ln in range(64):
+                l32, hf = ln % 32, ln // 32
+                q, dcol = qb * 32 + l32, db * 32 + (r // 4) * 8 + hf * 4 + r % 4
+                if q >= nrows:
+                    continue
+                b = int(_bf16_bits(np.float32(O[k][r][ln]) * inv[qb]))
+                o = q * stride + dcol * 2
+                want[o:o + 2] = np.frombuffer(np.uint16(b).tobytes(), dtype=np.uint8)
+    assert np.array_equal(out, want)

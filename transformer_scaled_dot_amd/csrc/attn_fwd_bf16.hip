@@ -501,7 +501,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     static_assert(kBlockN * CPR % (WAVES * 64) == 0, "tile must split evenly over the workgroup");
     // K0 K1 V0 V1 (the tile loop's slots), then the Q rows of the four waves (the next item's while the
     // current item's loop runs its last tiles)
-    __shared__ __attribute__((aligned(16))) uint8_t smem[10 * TILE_B];
+    __shared__ __attribute__((aligned(256))) uint8_t smem[10 * TILE_B];
     constexpr int KSLOT0 = 0, KSLOT1 = TILE_B, VSLOT0 = 2 * TILE_B, VSLOT1 = 3 * TILE_B, QSLOT = 4 * TILE_B;
     constexpr int STAGE = 8 * TILE_B;  // 8 KiB per wave for the output rows (bf16 output)
 
@@ -596,35 +596,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         return qb2_item<MASK>(valid, bh, qt, num_qtiles, H, Nk, valid_lens, hd);
     };
-    Qb2Item cur = item(0);
-    if (!cur.valid) return;
-    q_tiles(cur);
-    first_tiles(cur, 0);
-    bool fetched = true;  // this item's first tiles were fetched outside a tile loop: wait for them
-    for (;;) {
-        // Every fetch into the Q and K/V slots is cooperative. When the tile loop streamed this item's first
-        // tiles, its last step waited for all of them (and for the Q rows issued before it) and ended with a
-        // barrier; otherwise wait here, then barrier, so that every wave sees the whole tiles.
-        if (fetched) {
-            wait_vmcnt0();
-            __syncthreads();
-        }
-        // O = 0 and Q^T (this wave's rows, from its Q slot) in the AGPRs the tile loop names. The slot offset
-        // is computed here, per item, so that the eight addresses are not held across the tile loop
+    // Q^T of this wave's rows from its Q slot into the AGPRs the tile loop names, and O = 0. The slot offset
+    // is computed here so that the eight addresses are not held across the tile loop
+    bf16x8 qreg[QB][KS];
+    f32x16 acc[QB][DB];
+    auto q_init = [&]() {
         uint32_t wq = QSLOT + wave * TILE_B;
         asm volatile("" : "+v"(wq));
         uint32_t qa[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qa[ks] = kaddr[ks] + wq;
-        bf16x8 qreg[QB][KS];
-        f32x16 acc[QB][DB];
         qb2_init(acc, qreg, qa);
-        // every wave has its Q before any wave fetches the next item's Q rows into the Q slots; they
-        // arrive while this item's tiles run
-        __syncthreads();
+    };
+    Qb2Item cur = item(0);
+    if (!cur.valid) return;
+    q_tiles(cur);
+    first_tiles(cur, 0);
+    wait_vmcnt0();
+    __syncthreads();
+    q_init();
+    // bf16 output: the tile loop of each later item starts with the turn, which packs the previous item's
+    // output rows while the new item's first scores are computed (turn = 1); the parameters of those rows
+    constexpr int OSTRIDE = (OLAYOUT == kOutBHND ? D : 0) * 2;  // BNHD: H * D * 2, below
+    const uint32_t ostride = OSTRIDE ? OSTRIDE : (uint32_t)H * D * 2;
+    int32_t turn = 0;
+    float inv[QB] = {0.f, 0.f};
+    uint64_t ob = 0;
+    uint32_t ob_bytes = 0;
+    for (;;) {
         const Qb2Item nxt = item(++k);
-        if (nxt.valid) q_tiles(nxt);
-
         const int qmin_w = cur.q0 + wave * RW, qmax_w = qmin_w + RW - 1;
         int32_t lim[QB];
 #pragma unroll
@@ -650,45 +650,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const uint64_t kh = (uint64_t)(K + (size_t)cur.kvh * Nk * D), vh = (uint64_t)(V + (size_t)cur.kvh * Nk * D);
         const Qb2Item &nn = nxt.valid ? nxt : cur;  // a valid address even when there is no next item
         const uint64_t nkh = (uint64_t)(K + (size_t)nn.kvh * Nk * D), nvh = (uint64_t)(V + (size_t)nn.kvh * Nk * D);
+        // the next item's Q rows, fetched into the Q slots by the loop once every wave has read this item's
+        const uint64_t nq = (uint64_t)(Q + ((size_t)nn.bh * Nq + nn.q0) * D);
+        const int nq_rows = nxt.valid ? Nq - nxt.q0 : 0;
         float l_run[QB] = {0.f, 0.f}, mc0 = -INFINITY, mc1 = -INFINITY;
         qb2_loop(acc, qreg, kaddr, vaddr, voff, lim[0], lim[1], c_log2, l_run[0], l_run[1], mc0, mc1,
                  u(0), u(cur.ntiles), u(ntiles_w), u(t_mask), u(cur.kv_end), u((uint32_t)kh),
                  u((uint32_t)(kh >> 32)), u((uint32_t)vh), u((uint32_t)(vh >> 32)), lbw, u(off),
                  u((uint32_t)nkh), u((uint32_t)(nkh >> 32)), u((uint32_t)nvh), u((uint32_t)(nvh >> 32)),
-                 u(nxt.valid ? nxt.kv_end : 0), u(t_diag));
-
-        // The loop's last steps fetched the next item's K(0), K(1), V(0) into the slots of parity
-        // (off + ntiles) % 2 and ended with a barrier after they (and the next Q rows) had arrived. With
-        // fewer than two tiles it did not (K(0) of the next item would have been due before this item's
-        // first step): fetch them here.
-        // the row sums come from an MFMA over all 64 lanes: each lane holds its row's whole sum. bf16 output:
-        // O / l packed straight from the O registers, before anything else needs registers
-        u32x8 pk[QB][DB];
-        if constexpr (!OUT_F32) {
-            float inv[QB];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) inv[qb] = l_run[qb] > 0.f ? __builtin_amdgcn_rcpf(l_run[qb]) : 0.f;
-            qb2_out_bf16(acc, inv[0], inv[1], pk);
-        }
-        const int off_next = (off + cur.ntiles) & 1;
-        fetched = cur.ntiles < 2;
-        if (nxt.valid && fetched) first_tiles(nxt, off_next);
-        if constexpr (OUT_F32) mfma_fence_a8(acc);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            if constexpr (OUT_F32) {
-                store_rows<D, OUT_F32, OLAYOUT, false>(acc[qb], l_run[qb], cur.q0 + wave * RW + qb * 32 + l32, cur.bh,
-                                                       H, Nq, cur.b, hf, Out);
-            } else {
-                store_rows_bf16_staged<OLAYOUT>(pk[qb], cur.q0 + wave * RW + qb * 32, cur.bh, H, Nq, cur.b, lane,
-                                                smem + STAGE + wave * 8192, Out);
-            }
-        }
+                 u(nxt.valid ? nxt.kv_end : 0), u(t_diag), u(turn), inv[0], inv[1], u((uint32_t)ob),
+                 u((uint32_t)(ob >> 32)), u(ob_bytes), u(ostride), u(QSLOT + wave * TILE_B),
+                 u(lds0 + QSLOT + wave * TILE_B), u((uint32_t)nq), u((uint32_t)(nq >> 32)), u(nq_rows));
         if (hd.lse) {
             store_lse(hd.lse, l_run[0], mc0, cur.q0 + wave * RW + l32, cur.bh, Nq, hf);
             store_lse(hd.lse, l_run[1], mc1, cur.q0 + wave * RW + 32 + l32, cur.bh, Nq, hf);
         }
+        // the row sums come from an MFMA over all 64 lanes: each lane holds its row's whole sum
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) inv[qb] = l_run[qb] > 0.f ? __builtin_amdgcn_rcpf(l_run[qb]) : 0.f;
+        if constexpr (OUT_F32) {
+            mfma_fence_a8(acc);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                store_rows<D, OUT_F32, OLAYOUT, false>(acc[qb], l_run[qb], cur.q0 + wave * RW + qb * 32 + l32, cur.bh,
+                                                       H, Nq, cur.b, hf, Out);
+        } else if (!nxt.valid) {
+            // the last item's rows: O / l packed straight from the O registers, then staged and stored
+            u32x8 pk[QB][DB];
+            qb2_out_bf16(acc, inv[0], inv[1], pk);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                store_rows_bf16_staged<OLAYOUT>(pk[qb], cur.q0 + wave * RW + qb * 32, cur.bh, H, Nq, cur.b, lane,
+                                                smem + STAGE + wave * 8192, Out);
+        } else {
+            // this item's rows, written by the next item's turn: the wave's 64 rows from row0, those below Nq
+            const int row0 = cur.q0 + wave * RW;
+            const size_t first = OLAYOUT == kOutBHND ? ((size_t)cur.bh * Nq + row0) * D
+                                                     : (((size_t)cur.b * Nq + row0) * H + cur.bh % H) * D;
+            const int nrows = min(RW, Nq - row0);
+            ob = (uint64_t)((uint16_t *)Out + first);
+            ob_bytes = nrows > 0 ? (uint32_t)(nrows - 1) * ostride + D * 2 : 0u;
+            turn = 1;
+        }
         if (!nxt.valid) break;
+        // The loop's last steps fetched the next item's K(0), K(1), V(0) into the slots of parity
+        // (off + ntiles) % 2 and ended with a barrier after they (and the next Q rows) had arrived. With
+        // fewer than two tiles it did not (K(0) of the next item would have been due before this item's
+        // first step): fetch them here and wait for them (and for the Q rows).
+        const int off_next = (off + cur.ntiles) & 1;
+        if (cur.ntiles < 2) {
+            first_tiles(nxt, off_next);
+            wait_vmcnt0();
+            __syncthreads();
+        }
+        if constexpr (OUT_F32) q_init();
         cur = nxt;
         off = off_next;
     }

@@ -78,7 +78,7 @@ def s_reg(buf, qb, jb, r):
 
 
 def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mref1]"), mx=("%[mx0]", "%[mx1]"),
-        dma_ins=(), ref_upd=False, diag=False):
+        dma_ins=(), ref_upd=False, diag=False, pre=(), lead=(), extra_items=(), extra_mfma=()):
     """Instruction list of one block.
 
     x_buf: S buffer holding S(t) (exp + P.V part), y_buf: buffer receiving the
@@ -88,6 +88,11 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
     scores (after their row max and after this block's row sums); diag: the new scores are those of the
     wave's causal diagonal tile (its first key is the wave's first row; tile start * 64 in s89): mask
     them (keys past each row's own) before their row max.
+    pre: instructions placed before the block's first operand reads (which then do not wait for the LDS
+    reads in pre: the first MFMA's operand wait covers them, LDS returning in order); lead: instructions
+    placed behind the first operand reads, before the first MFMA; extra_items: further work (dicts as the
+    softmax items: ins, name, after) filled into the MFMA shadows after the block's own, in order;
+    extra_mfma: MFMAs issued after the block's own, each after the extra items it names under "needs".
     The block ends without waiting for its last MFMAs: code that reads O or
     the new scores next must wait 24 wait states first (O_WAIT)."""
     koff = kslot * TILE_B
@@ -122,6 +127,7 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
                 ls = ar(LSUM_A + 4 * qb, 4)
                 mfma.append(dict(op=None, kind="SUM", qb=qb, c=c,
                                  text="v_mfma_f32_16x16x32_bf16 %s, %s, %s, %s" % (ls, ar(ONES_A, 4), pop, ls)))
+    mfma += [dict(f, op=None, kind="X") for f in extra_mfma]
     first_use, last_use = {}, {}
     for m, f in enumerate(mfma):
         if f["op"] is None:
@@ -199,12 +205,15 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
             items.append(dict(ins=ref_check(qb), deadline=len(mfma) + 8, ready=s_last + 4, p=None,
                               name="ref q%d" % qb, after=["max q%d" % qb]))
 
+    for n, it in enumerate(extra_items):
+        items.append(dict(it, deadline=len(mfma) + 1000, ready=it.get("ready", 0), p=None))
+
     def cost(t):
         if t.startswith("v_exp"):
             return EXP_CYC
         return ISSUE_CYC
 
-    out = ["s_waitcnt lgkmcnt(0)"]
+    out = list(pre) if pre else ["s_waitcnt lgkmcnt(0)"]
     issued, pos, p_done = [], {}, {}
     waited = [-1]       # LDS reads up to this index are known complete (LDS returns in order)
     queue = [dict(it, k=0, order=n) for n, it in enumerate(items)]
@@ -257,6 +266,7 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
     prog = {"c": 0, "e": 0}
 
     emit_reads(0)
+    out += list(lead)
     for m, f in enumerate(mfma):
         if f["kind"] in ("PV", "SUM"):
             p = P0 + 4 * (f["qb"] * 4 + f["c"])
@@ -273,6 +283,13 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
             gap = sum(1 for t in out[p_done[p] + 1:] if not t.startswith("s_waitcnt"))
             if gap < 2:
                 out.append("s_nop %d" % (1 - gap))
+        for name in f.get("needs", ()):
+            def force_named(it):
+                for a_ in it.get("after", ()):
+                    force_named(by_name[a_])
+                while it["k"] < len(it["ins"]):
+                    emit(it)
+            force_named(by_name[name])
         if f["op"] is not None and pos[f["op"]] > waited[0]:
             # wait once for this operand and for those of the next MFMAs already read (they have had
             # at least as long to arrive), rather than once per operand
@@ -497,18 +514,154 @@ def rescale():
     return o + ["s_nop 1"]
 
 
-def first_tile(off):
+# ---------------------------------------------------------------------------
+# The turn between two items of a workgroup: the finished item's output O / l is packed to bf16 while the new
+# item's Q rows go from the wave's Q slot into the Q AGPRs and its first scores S(0) are computed, so that the
+# matrix pipe keeps working across the item boundary. The packed rows are written into the wave's Q slot (its Q
+# rows have been read by then: LDS executes a wave's operations in order), 64 rows of 256 bytes with their 16-byte
+# chunks XOR-swizzled by row, read back as whole rows and stored (non-temporal: the output is not read again,
+# so it should not push the K/V tiles other workgroups share out of the L2). O is cleared by MFMAs of zero
+# operands. Registers of the turn (free while S(0) is computed: the other score buffer, P, the V staging and the
+# exp temporaries):
+TURN_ZERO_V = 176       # v[176:179] = 0: operands of the MFMAs that clear O
+TURN_WB_V = 180         # the lane's write address for chunk 0 (chunk c: XOR c << 4; row block qb: + 8 KiB)
+TURN_RB_V = 181         # v[181:184]: the lane's read addresses for rows 4 j + (lane >> 4), j = 0..3
+TURN_SB_V = 185         # the lane's byte offset in its output row group (row (lane >> 4), chunk lane & 15)
+TURN_T_V = (186, 187)   # address temporaries (of the set-up)
+TURN_L_V = 188          # v188 lane id, v189 lane & 15, v190 lane >> 4, v191 scratch
+TURN_QA_V = 192         # v[192:199]: LDS addresses of the new Q rows, one per k-step
+OUT_RES = KRES          # s[80:83]: the output rows' buffer descriptor (the K stream's is set after the turn)
+
+
+def zero_o(k):
+    return "v_mfma_f32_32x32x16_bf16 a[%d:%d], v[%d:%d], v[%d:%d], 0" % (
+        O_A + 16 * k, O_A + 16 * k + 15, TURN_ZERO_V, TURN_ZERO_V + 3, TURN_ZERO_V, TURN_ZERO_V + 3)
+
+
+def turn_work(off):
+    """(pre, lead, items, zero MFMAs) of the turn for an item whose first scores go to buffer `off`: the finished
+    item's packed rows go to the other score buffer (8 registers per 32 x 32 block of O, as qb2_out_bf16
+    packs them), the pack temporaries alternate between the two halves of P."""
+    pkb = S_BUF[1 - off]
+    L, T0, T1 = TURN_L_V, TURN_T_V[0], TURN_T_V[1]
+    pre = ["v_add_u32 v%d, %%[wq], %%[ka%d]" % (TURN_QA_V + ks, ks) for ks in range(KS)]
+    pre += ["ds_read_b128 a[%d:%d], v%d offset:%d" % (Q_A + 4 * (qb * KS + ks), Q_A + 4 * (qb * KS + ks) + 3,
+                                                      TURN_QA_V + ks, qb * 32 * D * 2)
+            for qb in range(QB) for ks in range(KS)]
+    pre += ["s_mov_b32 s%d, %%[obl]" % OUT_RES, "s_mov_b32 s%d, %%[obh]" % (OUT_RES + 1),
+            "s_mov_b32 s%d, %%[onb]" % (OUT_RES + 2), "s_mov_b32 s%d, %s" % (OUT_RES + 3, BUF_WORD3)]
+    pre += ["v_mov_b32 v%d, 0" % r for r in range(TURN_ZERO_V, TURN_ZERO_V + 4)]
+    pre += ["v_mbcnt_lo_u32_b32 v%d, -1, 0" % L, "v_mbcnt_hi_u32_b32 v%d, -1, v%d" % (L, L),
+            "v_and_b32 v%d, 15, v%d" % (L + 1, L), "v_lshrrev_b32 v%d, 4, v%d" % (L + 2, L)]
+    # write address: slot + (lane & 31) * 256 + (lane >> 5) * 8 + ((lane & 15) << 4); the slot is 256-byte
+    # aligned, so bits 4..7 hold lane & 15 and chunk c is that address XOR (c << 4)
+    pre += ["v_and_b32 v%d, 31, v%d" % (T0, L), "v_lshlrev_b32 v%d, 8, v%d" % (T0, T0),
+            "v_lshrrev_b32 v%d, 5, v%d" % (T1, L), "v_lshl_add_u32 v%d, v%d, 3, v%d" % (T0, T1, T0),
+            "v_lshl_add_u32 v%d, v%d, 4, v%d" % (T0, L + 1, T0), "v_add_u32 v%d, %%[qsb], v%d" % (TURN_WB_V, T0)]
+    # read address of row group j: row r = 4 j + (lane >> 4), chunk (lane & 15) XOR r
+    for j in range(4):
+        pre += ["v_add_u32 v%d, %d, v%d" % (T0, 4 * j, L + 2), "v_xor_b32 v%d, v%d, v%d" % (T1, T0, L + 1),
+                "v_lshlrev_b32 v%d, 4, v%d" % (T1, T1), "v_lshl_add_u32 v%d, v%d, 8, v%d" % (T0, T0, T1),
+                "v_add_u32 v%d, %%[qsb], v%d" % (TURN_RB_V + j, T0)]
+    pre += ["v_mul_u32_u24 v%d, %%[ostr], v%d" % (T0, L + 2),
+            "v_lshl_add_u32 v%d, v%d, 4, v%d" % (TURN_SB_V, L + 1, T0)]
+
+    packs = []
+    for k in range(QB * DB):
+        qb, t, pk = k // DB, P0 + 16 * (k % 2), pkb + 8 * k
+        ins = ["v_accvgpr_read_b32 v%d, a%d" % (t + r, O_A + 16 * k + r) for r in range(16)]
+        ins += ["v_mul_f32 v%d, v%d, %%[inv%d]" % (t + r, t + r, qb) for r in range(16)]
+        ins += ["v_cvt_pk_bf16_f32 v%d, v%d, v%d" % (pk + j, t + 2 * j, t + 2 * j + 1) for j in range(8)]
+        packs.append(ins)
+    # block 0 is packed ahead of the first MFMA (while the Q and first K reads are in flight)
+    lead = packs[0]
+    items = [dict(ins=packs[k], name="pack %d" % k, after=["pack %d" % (k - 2)] if k >= 3 else [])
+             for k in range(1, QB * DB)]
+    # one 32-row block at a time: its packed registers into the slot, and (direct) read back as whole rows
+    # into the same registers, then stored. Addresses of the writes and the stores' offsets: the exp
+    # temporaries (block 0; free once the Q reads are issued), then the K operand registers (block 1; free
+    # once the last S(0) MFMA has issued, four MFMAs before: ready)
+    for qb in range(QB):
+        tmp = [TMP + i for i in range(8)] if qb == 0 else list(range(KST, KST + 16))
+        ready = 0 if qb == 0 else 32 + 4
+        rows = pkb + 32 * qb
+        w = []
+        for c in range(16):
+            db, rg = c // 4, c % 4
+            src = rows + 8 * db + 2 * rg
+            a = tmp[c % len(tmp)]
+            w += ["v_xor_b32 v%d, 0x%x, v%d" % (a, c << 4, TURN_WB_V),
+                  "ds_write_b64 v%d, v[%d:%d] offset:%d" % (a, src, src + 1, qb * 32 * 256)]
+        after = ["pack %d" % k for k in range(qb * DB, (qb + 1) * DB) if k > 0]
+        after += ["store 0"] if qb else []
+        items.append(dict(ins=w, name="write %d" % qb, after=after, ready=ready))
+        rd = ["ds_read_b128 v[%d:%d], v%d offset:%d" % (rows + 4 * i, rows + 4 * i + 3, TURN_RB_V + (i & 3),
+                                                        (2 * qb + (i >> 2)) * 4096) for i in range(8)]
+        items.append(dict(ins=rd, name="read %d" % qb, after=["write %d" % qb], ready=ready))
+        st = ["s_waitcnt lgkmcnt(0)"]
+        for i in range(8):
+            a = tmp[i]
+            st += ["v_mad_u32_u24 v%d, %d, %%[ostr], v%d" % (a, qb * 32 + 4 * i, TURN_SB_V),
+                   "buffer_store_dwordx4 v[%d:%d], v%d, s[%d:%d], 0 offen nt" % (rows + 4 * i, rows + 4 * i + 3, a,
+                                                                                OUT_RES, OUT_RES + 3)]
+            if i % 2 == 1:
+                # the row block's four 32 x 32 blocks of O are cleared between its stores
+                st.append(zero_o(qb * DB + i // 2))
+        items.append(dict(ins=st, name="store %d" % qb, after=["read %d" % qb], ready=ready))
+    # priority (the scheduler takes ready items in list order): block 0's packing, its staging, the first
+    # block of qb 1 packed while block 0's rows come back from LDS, its stores, then the rest
+    by = {it["name"]: it for it in items}
+    order = ["pack 1", "pack 2", "pack 3", "write 0", "read 0", "pack 4", "store 0", "pack 5", "pack 6", "pack 7",
+             "write 1", "read 1", "store 1"]
+    by["store 0"]["after"] = ["read 0", "pack 4"]
+    items = [by[n] for n in order]
+    return pre, lead, items, []
+
+
+def first_tile(off, turn=False):
     """S(0) of the wave, its mask where needed, its reference (O and l are still 0: no rescale). Tiles of
-    the item take the slots and score buffers of parity (t + off) % 2: K(0) is in K slot off."""
-    tag = "f%d" % off
-    o = ["s_cmp_le_i32 %[ntw], 0", "s_cbranch_scc1 L_first_done_%="]
+    the item take the slots and score buffers of parity (t + off) % 2: K(0) is in K slot off.
+    turn: also the turn (the finished item's output, the new Q rows, O cleared), in the MFMA shadows of
+    S(0), or on its own when the wave has no tile."""
+    tag = ("t%d" if turn else "f%d") % off
+    kw = {}
+    if turn:
+        pre, lead, items, zero = turn_work(off)
+        kw = dict(pre=pre, lead=lead, extra_items=items, extra_mfma=zero)
+    o = ["s_cmp_le_i32 %[ntw], 0", "s_cbranch_scc1 " + ("L_%s_only_%%=" % tag if turn else "L_first_done_%=")]
     o += gen(x_buf=1 - off, y_buf=off, kslot=off, vslot=off, do_s=True, do_pv=False, do_max=True,
-             mx=("v%d" % MX_V[0], "v%d" % MX_V[1]))
+             mx=("v%d" % MX_V[0], "v%d" % MX_V[1]), **kw)
     o += ["s_mov_b32 s%d, 0" % SREG, "s_cmp_eq_u32 %[dg], 0", "s_cbranch_scc1 L_%s_mask_%%=" % tag,
           "s_cmp_lt_i32 s%d, %%[tm]" % SREG, "s_cbranch_scc1 L_%s_ref_%%=" % tag, "L_%s_mask_%%=:" % tag]
     o += mask_tile("s%d" % SREG, off)
     o += ["L_%s_ref_%%=:" % tag] + full_ref() + ["s_branch L_first_done_%="]
+    if turn:
+        o += ["L_%s_only_%%=:" % tag]
+        o += gen(x_buf=1 - off, y_buf=off, kslot=off, vslot=off, do_s=False, do_pv=False, do_max=False, **kw)
+        o += ["s_branch L_first_done_%="]
     return o
+
+
+QSLOT = 4 * TILE_B      # LDS offset of the Q slots (four 64-row blocks)
+
+
+def q_next_dma():
+    """The next item's Q rows into the Q slots when this item has fewer than five tiles (else the general
+    steps fetch them block by block, q_block_dma), issued once every wave has its own Q rows (after the barrier
+    that follows S(0)): its four 64-row blocks, a quarter of each by every wave (the K/V tiles' DMA offsets),
+    through descriptors covering each block's rows below N_q (rows past it read as zeros). nqr = the rows from
+    the next item's first row to N_q; 0: no next item."""
+    o = ["s_cmp_le_i32 %[nqr], 0", "s_cbranch_scc1 L_qdma_done_%=", "s_cmp_ge_i32 %[nt], 5",
+         "s_cbranch_scc1 L_qdma_done_%="]
+    for qw in range(4):
+        o += ["s_add_u32 s%d, %%[nql], %d" % (KRES, qw * TILE_B), "s_addc_u32 s%d, %%[nqh], 0" % (KRES + 1),
+              "s_sub_i32 s%d, %%[nqr], %d" % (KRES + 2, 64 * qw), "s_max_i32 s%d, s%d, 0" % (KRES + 2, KRES + 2),
+              "s_min_i32 s%d, s%d, 64" % (KRES + 2, KRES + 2), "s_lshl_b32 s%d, s%d, 8" % (KRES + 2, KRES + 2),
+              "s_mov_b32 s%d, %s" % (KRES + 3, BUF_WORD3)]
+        for j in range(4):
+            o += ["s_add_u32 m0, %%[lbw], %d" % (QSLOT + qw * TILE_B + j * 4096), "s_nop 0",
+                  "buffer_load_dwordx4 %%[vo%d], s[%d:%d], 0 offen nt lds" % (j, KRES, KRES + 3)]
+    return o + ["L_qdma_done_%=:"]
 
 
 def stream_res(res, x, base_lo, base_hi, nbase_lo, nbase_hi):
@@ -553,12 +706,15 @@ def iteration(parity):
     uf = "s[%d:%d], s[%d:%d]" % (UFLAG[0], UFLAG[0] + 1, UFLAG[1], UFLAG[1] + 1)
     full = lambda **kw: gen(x_buf=P, y_buf=1 - P, kslot=1 - P, vslot=P, do_s=True, do_pv=True, do_max=True,
                             mref=mref, mx=mx, dma_ins=groups, ref_upd=True, **kw)
-    # common step
-    o = ["s_cmp_lt_i32 %%[t], s%d" % TF_S, "s_cbranch_scc0 L_slow_%s_%%=" % tag]
+    # common step (t < tf); the steps nt - 5 .. that fetch the next item's Q rows take a copy of it, out of line
+    o = ["s_cmp_lt_i32 %%[t], s%d" % TF_S, "s_cbranch_scc0 L_slow_%s_%%=" % tag,
+         "s_add_i32 s%d, %%[t], 5" % SREG, "s_cmp_ge_i32 s%d, %%[nt]" % SREG, "s_cbranch_scc1 L_qst_%s_%%=" % tag]
     o += res_advance_fast(KRES) + res_advance_fast(VRES)
     o += full()
     o += ["s_or_b64 vcc, %s" % uf, "s_cbranch_vccnz L_move_%s_%%=" % tag,
           "L_after_%s_%%=:" % tag, "s_waitcnt vmcnt(0)", "s_barrier"]
+    tails = ["L_qst_%s_%%=:" % tag] + res_advance_fast(KRES) + res_advance_fast(VRES) + full()
+    tails += ["s_or_b64 vcc, %s" % uf, "s_cbranch_vccnz L_move_%s_%%=" % tag, "s_branch L_after_%s_%%=" % tag]
     # general step: descriptors to K(t+2) and V(t+1) of the stream (past this item's last tile, the next
     # item's first tiles, so that they are in their slots when this item ends)
     ool = ["L_slow_%s_%%=:" % tag, "s_cmp_ge_i32 %[t], %[nt]", "s_cbranch_scc1 L_end_%="]
@@ -592,7 +748,35 @@ def iteration(parity):
     for g in groups:
         ool += g
     ool += ["s_branch L_after_%s_%%=" % tag]
+    ool += tails
+    ool = [x.replace("L_after_%s_%%=" % tag, "L_qchk_%s_%%=" % tag) if "branch" in x else x for x in ool]
+    ool += q_block_dma(tag)
+    o += ["L_cont_%s_%%=:" % tag]
     return o, ool
+
+
+def q_block_dma(tag):
+    """End of a step that is not a plain common one: in items of five or more tiles, the steps nt - 5 .. nt - 2
+    each fetch one
+    64-row block of the next item's Q rows (block t - nt + 5) into its Q slot, behind the step's own K/V
+    fetches, and end by waiting for all but those four loads: the block has until the next step's end to
+    arrive, and the last one is in before this item's loop ends. Every wave fetches a quarter of each block,
+    so every Q slot is complete once all waves have passed that barrier."""
+    qw, t = UFLAG[0], UFLAG[0] + 1
+    o = ["L_qchk_%s_%%=:" % tag, "s_sub_i32 s%d, %%[t], %%[nt]" % qw, "s_add_i32 s%d, s%d, 5" % (qw, qw),
+         "s_cmp_lt_u32 s%d, 4" % qw, "s_cbranch_scc0 L_after_%s_%%=" % tag,
+         "s_cmp_lt_i32 %[nt], 5", "s_cbranch_scc1 L_after_%s_%%=" % tag,
+         "s_cmp_le_i32 %[nqr], 0", "s_cbranch_scc1 L_after_%s_%%=" % tag]
+    o += ["s_lshl_b32 s%d, s%d, 14" % (t, qw), "s_add_u32 s%d, %%[nql], s%d" % (SREG, t),
+          "s_addc_u32 s%d, %%[nqh], 0" % (SREG + 1), "s_lshl_b32 s%d, s%d, 6" % (t, qw),
+          "s_sub_i32 s%d, %%[nqr], s%d" % (SREG + 2, t), "s_max_i32 s%d, s%d, 0" % (SREG + 2, SREG + 2),
+          "s_min_i32 s%d, s%d, 64" % (SREG + 2, SREG + 2), "s_lshl_b32 s%d, s%d, 8" % (SREG + 2, SREG + 2),
+          "s_mov_b32 s%d, %s" % (SREG + 3, BUF_WORD3),
+          "s_lshl_b32 s%d, s%d, 14" % (t, qw), "s_add_u32 s%d, s%d, %%[lbw]" % (t, t)]
+    for j in range(4):
+        o += ["s_add_u32 m0, s%d, %d" % (t, QSLOT + j * 4096), "s_nop 0",
+              "buffer_load_dwordx4 %%[vo%d], s[%d:%d], 0 offen nt lds" % (j, SREG, SREG + 3)]
+    return o + ["s_waitcnt vmcnt(4)", "s_barrier", "s_branch L_cont_%s_%%=" % tag]
 
 
 def ones_pattern():
@@ -608,11 +792,15 @@ def loop_body():
     o += ["v_accvgpr_write_b32 a%d, v0" % (ONES_A + i) for i in range(4)]
     o += ["v_accvgpr_write_b32 a%d, 0" % (LSUM_A + i) for i in range(4 * QB)]
     o += ["s_nop 3", "s_lshl_b32 s%d, %%[nkve], 8" % NKVB_S, "v_mov_b32 v%d, 0xff800000" % NINF_V]
-    # S(0) with the item's parity
-    o += ["s_cmp_eq_u32 %[off], 0", "s_cbranch_scc0 L_first1_%="] + first_tile(0)
+    # S(0) with the item's parity, with the turn from the previous item (tn != 0) or without
+    o += ["s_cmp_eq_u32 %[tn], 0", "s_cbranch_scc1 L_plain_%="]
+    o += ["s_cmp_eq_u32 %[off], 0", "s_cbranch_scc0 L_turn1_%="] + first_tile(0, True)
+    o += ["L_turn1_%=:"] + first_tile(1, True)
+    o += ["L_plain_%=:", "s_cmp_eq_u32 %[off], 0", "s_cbranch_scc0 L_first1_%="] + first_tile(0)
     o += ["L_first1_%=:"] + first_tile(1) + ["L_first_done_%=:"]
-    # step 0 fetches K(2) into the slot K(0) came from: no wave may still be reading K(0)
-    o += ["s_barrier"]
+    # step 0 fetches K(2) into the slot K(0) came from, and the next item's Q rows go where this item's were
+    # read from: no wave may still be reading either
+    o += ["s_barrier"] + q_next_dma()
     # descriptors one tile behind: each step first moves them to K(t+2) and V(t+1) of the stream
     o += stream_res(KRES, 1, "%[khl]", "%[khh]", "%[nkhl]", "%[nkhh]")
     o += stream_res(VRES, 0, "%[vhl]", "%[vhh]", "%[nvhl]", "%[nvhh]")
@@ -635,14 +823,18 @@ def loop_body():
 
 def render_loop():
     body = loop_body()
-    outs = (o_binding() + ['[l0] "+v"(l0)', '[l1] "+v"(l1)', '[mc0] "+v"(mc0)', '[mc1] "+v"(mc1)', '[t] "+s"(t)'])
-    ins = (q_binding() + ka_binding() + va_binding() +
+    # Q^T is read and written: the turn loads the new item's rows into the same AGPRs
+    outs = (o_binding() + ['"+' + b[1:] for b in q_binding()] +
+            ['[l0] "+v"(l0)', '[l1] "+v"(l1)', '[mc0] "+v"(mc0)', '[mc1] "+v"(mc1)', '[t] "+s"(t)'])
+    ins = (ka_binding() + va_binding() +
            ['[vo%d] "v"(vo[%d])' % (j, j) for j in range(4)] +
            ['[lim0] "v"(lim0)', '[lim1] "v"(lim1)', '[c] "s"(c_log2)', '[nt] "s"(ntiles)', '[ntw] "s"(ntiles_w)',
             '[tm] "s"(t_mask)', '[kve] "s"(kv_end)', '[khl] "s"(kh_lo)', '[khh] "s"(kh_hi)',
             '[vhl] "s"(vh_lo)', '[vhh] "s"(vh_hi)', '[lbw] "s"(lbw)', '[off] "s"(off)', '[nkhl] "s"(nkh_lo)',
             '[nkhh] "s"(nkh_hi)', '[nvhl] "s"(nvh_lo)', '[nvhh] "s"(nvh_hi)', '[nkve] "s"(nkv_end)',
-            '[dg] "s"(t_diag)'])
+            '[dg] "s"(t_diag)', '[tn] "s"(turn)', '[inv0] "v"(inv0)', '[inv1] "v"(inv1)', '[obl] "s"(ob_lo)',
+            '[obh] "s"(ob_hi)', '[onb] "s"(ob_bytes)', '[ostr] "s"(ob_stride)',
+            '[wq] "s"(qslot)', '[qsb] "s"(qslot_lds)', '[nql] "s"(nq_lo)', '[nqh] "s"(nq_hi)', '[nqr] "s"(nq_rows)'])
     clob = (['"a%d"' % r for r in range(LSUM_A, ONES_A + 4)] + ['"v%d"' % r for r in LOOP_CLOB_V] +
             ['"s%d"' % r for r in LOOP_CLOB_S] +
             ['"vcc"', '"m0"', '"scc"', '"memory"'])
@@ -656,7 +848,14 @@ def render_loop():
         "// tiles (K(0), K(1), V(0) of the item given by nkh/nvh/nkv_end; nkv_end = 0: none). t_diag: the",
         "// wave's causal diagonal tile, masked inside its step (else out of range; t_mask then covers it).",
         "// K and V are read through range-checked buffer descriptors: rows at or past kv_end are not read.",
-        "__device__ __forceinline__ void qb2_loop(f32x16 (&o)[2][4], const bf16x8 (&q)[2][8], const uint32_t (&ka)[8],",
+        "// turn != 0: before S(0), the item's Q rows are read from the wave's Q slot (qslot: its offset from the",
+        "// K operand addresses; qslot_lds: its LDS address, 256-byte aligned) into q, and o (the previous item's",
+        "// output, unnormalised) is packed as O / l (inv0, inv1: 1 / l of the wave's two row blocks) in bf16 into",
+        "// that slot and stored from there to the rows of the buffer descriptor (ob_lo, ob_hi, ob_bytes), row r of",
+        "// the wave at byte r * ob_stride; o is then cleared. turn == 0: q and o (= 0) are given. The next item's Q rows (nq_rows rows from address nq, 0: none) are fetched into the Q slots",
+        "// after the barrier behind S(0) (items of fewer than five tiles) or one 64-row block per step at steps",
+        "// nt - 5 .. nt - 2.",
+        "__device__ __forceinline__ void qb2_loop(f32x16 (&o)[2][4], bf16x8 (&q)[2][8], const uint32_t (&ka)[8],",
         "                                         const uint32_t (&va)[4][2], const uint32_t (&vo)[4],",
         "                                         int32_t lim0, int32_t lim1, float c_log2,",
         "                                         float &l0, float &l1, float &mc0, float &mc1,",
@@ -664,7 +863,10 @@ def render_loop():
         "                                         int32_t kv_end, uint32_t kh_lo, uint32_t kh_hi,",
         "                                         uint32_t vh_lo, uint32_t vh_hi, uint32_t lbw, int32_t off,",
         "                                         uint32_t nkh_lo, uint32_t nkh_hi, uint32_t nvh_lo, uint32_t nvh_hi,",
-        "                                         int32_t nkv_end, int32_t t_diag)",
+        "                                         int32_t nkv_end, int32_t t_diag, int32_t turn, float inv0,",
+        "                                         float inv1, uint32_t ob_lo, uint32_t ob_hi, uint32_t ob_bytes,",
+        "                                         uint32_t ob_stride, uint32_t qslot, uint32_t qslot_lds,",
+        "                                         uint32_t nq_lo, uint32_t nq_hi, int32_t nq_rows)",
         "{",
         "#pragma clang diagnostic push",
         "#pragma clang diagnostic ignored \"-Winline-asm\"",
