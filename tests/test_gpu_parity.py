@@ -152,14 +152,15 @@ def test_causal_future_keys_never_reach_output(dev):
     assert np.array_equal(o1[:, :, 0], v.f64[:, :, 0])
 
 
-def test_d128_item_transitions_padding(dev):
-    """More (256-row query block, head) items than CUs, so that every workgroup of the 128-wide-head
-    kernel runs several items back to back, with key counts of 0, 1, under one tile, exactly one tile and
-    several tiles (the next item's first tiles are fetched by the previous item's tile loop, or separately
-    after items of fewer than two tiles). Keys at or past valid_len hold NaN: they are never fetched, so
-    they never reach an output."""
+@pytest.mark.parametrize("d", [128, 64])
+def test_item_transitions_padding(dev, d):
+    """More (256-row query block, head) items than CUs, so that every workgroup of the persistent kernel (both
+    head widths) runs several items back to back, with key counts of 0, 1, under one tile, exactly one tile
+    and several tiles (the next item's first tiles are fetched by the previous item's tile loop, or separately
+    after items of fewer than two tiles). Keys at or past valid_len hold NaN: they are never fetched, so they
+    never reach an output."""
     B, H, N = 8, 40, 260
-    q, k, v, _ = synth.attn_inputs(2, B=B, H=H, N=N, d=128)
+    q, k, v, _ = synth.attn_inputs(2, B=B, H=H, N=N, d=d)
     vl = np.asarray([0, 1, 63, 64, 65, 128, 260, 17], dtype=np.int32)
     kr, vr = k.raw.copy(), v.raw.copy()
     for b in range(B):
@@ -170,19 +171,22 @@ def test_d128_item_transitions_padding(dev):
     assert np.all(got[0] == 0.0)
     heads = [1, 7, 20, 39]  # the oracle on a few heads of every batch (all heads are independent)
     ref = oracle.attention(q.f64[:, heads], k.f64[:, heads], v.f64[:, heads], mask="padding", valid_lens=vl)
-    check("bf16 [8,40,260,128] padding, valid_lens %s, heads %s" % (vl.tolist(), heads), got[:, heads], ref, "bf16")
+    check("bf16 [8,40,260,%d] padding, valid_lens %s, heads %s" % (d, vl.tolist(), heads), got[:, heads], ref, "bf16")
 
 
-@pytest.mark.parametrize("N", [40, 70, 300])
-def test_d128_item_transitions_causal(dev, N):
-    """Causal, 128-wide heads, B*H = 320 heads: at N = 40 every item has one key tile (all next-item tiles
-    fetched after the item), at 70 two, at 300 a mix of 4 and 5."""
+@pytest.mark.parametrize("d,N,out", [(128, 40, "bf16"), (128, 70, "bf16"), (128, 300, "bf16"), (64, 40, "bf16"),
+                                     (64, 70, "bf16"), (64, 300, "bf16"), (64, 300, "f32"), (64, 1100, "bf16")])
+def test_item_transitions_causal(dev, d, N, out):
+    """Causal, B*H = 320 heads (several items per workgroup of the persistent kernel): at N = 40 every item
+    has one key tile (all next-item tiles fetched after the item), at 70 two, at 300 a mix of 4 and 5; at
+    1100 items of up to 17 tiles (the next item's Q rows fetched block by block in the last steps)."""
     B, H = 4, 80
-    q, k, v, _ = synth.attn_inputs(3, B=B, H=H, N=N, d=128)
-    got = gpu_attn(dev, q, k, v, mask="causal")
+    q, k, v, _ = synth.attn_inputs(3, B=B, H=H, N=N, d=d)
+    got = gpu_attn(dev, q, k, v, mask="causal", out_dtype=out)
     heads = [0, 33, 79]
     ref = oracle.attention(q.f64[:, heads], k.f64[:, heads], v.f64[:, heads], mask="causal")
-    check("bf16 [4,80,%d,128] causal, heads %s" % (N, heads), got[:, heads], ref, "bf16")
+    # bf16 inputs and products: the bf16 bound also for a float32 output
+    check("%s out [4,80,%d,%d] causal, heads %s" % (out, N, d, heads), got[:, heads], ref, "bf16")
 
 
 def test_empty_and_degenerate(dev):
@@ -285,8 +289,11 @@ def test_config4_mha_full(dev):
 
 
 @pytest.mark.parametrize("B,N,dm,h", [(1, 96, 128, 2), (2, 77, 256, 2), (1, 130, 512, 8), (3, 33, 256, 4),
-                                      (1, 300, 768, 6)])
+                                      (1, 300, 768, 6), (8, 1100, 512, 8)])
 def test_mha_shapes(dev, B, N, dm, h):
+    """The multi-head layer against the oracle, every element; [8,1100,512] h8 has 320 items of 256 rows (more
+    than CUs: the persistent attention kernel, several items per workgroup, concat layout, a ragged last
+    block)."""
     import transformer_scaled_dot_amd as tsd
 
     x, wqkv, wo = synth.mha_inputs(4, B=B, N=N, d_model=dm)
@@ -357,19 +364,20 @@ def test_clock_probe_reports_plausible_rate(dev):
 
 @pytest.mark.parametrize("mask", ["none", "causal", "padding", "causal_padding"])
 def test_d64_eight_wave_launch(dev, mask):
-    """Head_dim 64 on a grid that takes the 8-wave (256-row) workgroups: B2 H16 N2000 (8 query tiles of 256
-    rows per head, 256 workgroups, the last tile ragged), every element against the oracle."""
+    """Head_dim 64 on a grid of 256-row items that covers every CU (the persistent kernel, one item per
+    workgroup): B2 H16 N2000 (8 query tiles of 256 rows per head, the last tile ragged), every element against
+    the oracle."""
     B, H, N, d = 2, 16, 2000, 64
     q, k, v = (synth.normal_tensor(5100 + i, (B, H, N, d)) for i in range(3))
     vl = np.asarray([1999, 777], dtype=np.int32)
     pad = mask in ("padding", "causal_padding")
     got = gpu_attn(dev, q, k, v, mask=mask, vl=vl if pad else None)
     ref = oracle.attention(q.f64, k.f64, v.f64, mask=mask, valid_lens=vl if pad else None)
-    check("bf16 [2,16,2000,64] %s, 8-wave launch" % mask, got, ref, "bf16")
+    check("bf16 [2,16,2000,64] %s, persistent launch" % mask, got, ref, "bf16")
 
 
 def test_d64_eight_wave_grouped_lse(dev):
-    """The 8-wave d64 workgroups with grouped K/V heads (16 query heads over 4) and the log-sum-exp."""
+    """The persistent d64 launch with grouped K/V heads (16 query heads over 4) and the log-sum-exp."""
     import transformer_scaled_dot_amd as tsd
 
     B, H, Hkv, N, d = 2, 16, 4, 2000, 64
@@ -380,7 +388,7 @@ def test_d64_eight_wave_grouped_lse(dev):
                           valid_lens=torch.from_numpy(vl).to(dev), return_lse=True)
     torch.cuda.synchronize()
     ref, rl = oracle.attention(q.f64, k.f64, v.f64, mask="causal_padding", valid_lens=vl, return_lse=True)
-    check("bf16 [2,16/4,2000,64] causal_padding, 8-wave launch", o.float().cpu().numpy().astype(np.float64), ref,
+    check("bf16 [2,16/4,2000,64] causal_padding, persistent launch", o.float().cpu().numpy().astype(np.float64), ref,
           "bf16")
     err = np.abs(lse.cpu().numpy().astype(np.float64) - rl)
     say("  lse max abs err %.3e" % err.max())

@@ -27,17 +27,23 @@ CSRC = os.path.join(ROOT, "transformer_scaled_dot_amd", "csrc")
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
-def _gen():
+def _gen(d=128):
     spec = importlib.util.spec_from_file_location("gen_qb2_tile", os.path.join(CSRC, "gen_qb2_tile.py"))
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
+    mod.configure(d)
     return mod
 
 
-def test_include_matches_generator():
-    g = _gen()
-    with open(os.path.join(CSRC, "attn_qb2_tile.inc"), encoding="utf-8") as f:
-        assert f.read() == g.render(), "attn_qb2_tile.inc is stale: rerun gen_qb2_tile.py"
+HEAD_DIMS = (128, 64)
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_include_matches_generator(d):
+    g = _gen(d)
+    name = g.OUTPUTS[d]
+    with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+        assert f.read() == g.render(), "%s is stale: rerun gen_qb2_tile.py" % name
 
 
 def _template_regex(line):
@@ -82,8 +88,9 @@ def device_asm(tmp_path_factory):
         return f.read()
 
 
-def test_loop_operands_outside_fixed_registers(device_asm):
-    g = _gen()
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_loop_operands_outside_fixed_registers(device_asm, d):
+    g = _gen(d)
     tmpl = [ln for ln in g.loop_body()]
     pats = [_template_regex(ln) for ln in tmpl]
     fixed_v = set(g.LOOP_CLOB_V)
@@ -122,10 +129,7 @@ def test_loop_operands_outside_fixed_registers(device_asm):
 # LDS slot protocol of the generated loop: which slot each step reads and which one its fetches write,
 # and (as a model) which tile sits in each slot when it is read, across the items a workgroup runs.
 
-TB = 64 * 128 * 2
-
-
-def _slots(ins):
+def _slots(ins, TB=64 * 128 * 2):
     kr, vr, kw, vw = set(), set(), set(), set()
     for t in ins:
         m = re.match(r"ds_read_b128 v\[\d+:\d+\], %\[ka\d\] offset:(\d+)", t)
@@ -141,8 +145,10 @@ def _slots(ins):
     return kr, vr, kw, vw
 
 
-def test_step_slots():
-    g = _gen()
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_step_slots(d):
+    g = _gen(d)
+    _slots_d = lambda ins: _slots(ins, g.TILE_B)
     for P in (0, 1):
         o, ool = g.iteration(P)
         common = o[o.index("s_cbranch_scc0 L_slow_p%d_%%=" % P):]
@@ -150,17 +156,17 @@ def test_step_slots():
         last = ool[ool.index("L_last_p%d_%%=:" % P):ool.index("L_nocomp_p%d_%%=:" % P)]
         noc = ool[ool.index("L_nocomp_p%d_%%=:" % P):]
         for part in (common, general, last, noc):
-            kr, vr, kw, vw = _slots(part)
+            kr, vr, kw, vw = _slots_d(part)
             assert kw == {P} and vw == {1 - P}   # K(t+2) -> K slot P, V(t+1) -> V slot 1-P
             assert not (kr & kw) and not (vr & vw)
         for part in (common, general):
-            kr, vr, _, _ = _slots(part)
+            kr, vr, _, _ = _slots_d(part)
             assert kr == {1 - P} and vr == {P}   # S(t+1) reads K(t+1), P.V reads V(t)
-        kr, vr, _, _ = _slots(last)
+        kr, vr, _, _ = _slots_d(last)
         assert kr == set() and vr == {P}
     for off in (0, 1):
         for turn in (False, True):
-            kr, vr, kw, vw = _slots(g.first_tile(off, turn))
+            kr, vr, kw, vw = _slots_d(g.first_tile(off, turn))
             assert kr == {off} and not vr and not kw and not vw
     # step 0 fetches K(2) into the slot S(0) reads K(0) from: a barrier must separate them
     body = g.loop_body()
@@ -213,16 +219,17 @@ def test_item_stream_model():
         _run_items([int(x) for x in rng.choice([0, 1, 2, 3, 4, 5, 8], size=int(rng.integers(1, 7)))])
 
 
-def test_diagonal_step_slots_and_mask():
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_diagonal_step_slots_and_mask(d):
     """The step that masks the wave's causal diagonal tile inside its block uses the same slots as the
     plain step, and its mask hides exactly the keys past each row: with the tile starting at the wave's
     first row, lane (l32, hf) of query block qb holds row qb*32 + l32 and, in score register r of key
     block jb, key jb*32 + (r//4)*8 + hf*4 + r%4."""
-    g = _gen()
+    g = _gen(d)
     for P in (0, 1):
         _, ool = g.iteration(P)
         diag = ool[ool.index("L_diag_p%d_%%=:" % P):ool.index("L_last_p%d_%%=:" % P)]
-        kr, vr, kw, vw = _slots(diag)
+        kr, vr, kw, vw = _slots(diag, g.TILE_B)
         assert kr == {1 - P} and vr == {P} and kw == {P} and vw == {1 - P}
     for buf in (0, 1):
         for qb in range(2):
@@ -368,7 +375,8 @@ class _ScalarModel:
         pytest.fail("fell off the end of the loop")
 
 
-def test_loop_scalar_control_model():
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_loop_scalar_control_model(d):
     """For items of every tile count, wave extent, masked tile and diagonal tile, with and without the turn
     from a previous item: step t issues the four loads of K(t+2) into K slot (t+off)%2 and of V(t+1) into
     the other V slot, each with the descriptor of that tile of the stream (this item's tiles, then the next
@@ -376,10 +384,11 @@ def test_loop_scalar_control_model():
     for; the next item's Q rows are fetched into the Q slots, block qw through a descriptor of the rows below
     N_q (min(64, max(0, nqr - 64 qw)) rows; nothing when nqr = 0), right after the barrier behind S(0) in
     items of fewer than five tiles, else at step nt - 5 + qw."""
-    g = _gen()
+    g = _gen(d)
+    TB, RB, CH = g.TILE_B, g.ROWB, g.CH
     body = g.loop_body()
     rng = np.random.default_rng(11)
-    TILE, BIG = 0x4000, 0x7FFFFFFF
+    TILE, BIG = TB, 0x7FFFFFFF
     for case in range(3000):
         kve = int(rng.integers(0, 64 * 7))
         nt = (kve + 63) // 64
@@ -395,7 +404,7 @@ def test_loop_scalar_control_model():
         nq = int(rng.integers(1, 1 << 16)) << 32 | (M32 + 1 - TILE * int(rng.integers(1, 6)))
         tn = int(rng.integers(0, 2))
         ops = {"t": 0, "nt": nt, "ntw": ntw, "tm": tm, "dg": dg, "off": off, "kve": kve, "nkve": nkve, "lbw": 0,
-               "tn": tn, "qsb": 4 * TB, "ostr": 256,
+               "tn": tn, "qsb": 4 * TB, "ostr": RB,
                "obl": int(rng.integers(0, M32)), "obh": int(rng.integers(0, 1 << 16)),
                "onb": int(rng.integers(0, 1 << 20)), "nql": nq & M32, "nqh": nq >> 32, "nqr": nqr}
         for k, b in bases.items():
@@ -411,19 +420,19 @@ def test_loop_scalar_control_model():
         qload = lambda x: x[4] >= g.QSLOT
         got = [(t, x) for t, st in enumerate(steps) for x in st if qload(x)] + [(nt, x) for x in m.loads if qload(x)]
         want_q = [(0 if nt < 5 else nt - 5 + qw,
-                   (g.SREG if nt >= 5 else g.KRES, nq + qw * TB, min(64, max(0, nqr - 64 * qw)) * 256, 0x20000,
-                    g.QSLOT + qw * TB + j * 4096)) for qw in range(4) for j in range(4)] if nqr > 0 else []
+                   (g.SREG if nt >= 5 else g.KRES, nq + qw * TB, min(64, max(0, nqr - 64 * qw)) * RB, 0x20000,
+                    g.QSLOT + qw * TB + j * 4096)) for qw in range(4) for j in range(CH)] if nqr > 0 else []
         assert got == want_q, (case, ops)
         steps = [[x for x in st if not qload(x)] for st in steps]
         def desc(h, x):
             if x < nt:
-                return bases[h] + x * TILE, max(0, kve * 256 - x * TILE)
-            return bases["n" + h] + (x - nt) * TILE, max(0, nkve * 256 - (x - nt) * TILE)
+                return bases[h] + x * TILE, max(0, kve * RB - x * TILE)
+            return bases["n" + h] + (x - nt) * TILE, max(0, nkve * RB - (x - nt) * TILE)
 
         for t in range(nt):
             P = (t + off) % 2
-            want = [(g.KRES,) + desc("kh", t + 2) + (0x20000, P * TB + j * 4096) for j in range(4)]
-            want += [(g.VRES,) + desc("vh", t + 1) + (0x20000, 2 * TB + (1 - P) * TB + j * 4096) for j in range(4)]
+            want = [(g.KRES,) + desc("kh", t + 2) + (0x20000, P * TB + j * 4096) for j in range(CH)]
+            want += [(g.VRES,) + desc("vh", t + 1) + (0x20000, 2 * TB + (1 - P) * TB + j * 4096) for j in range(CH)]
             assert sorted(steps[t]) == sorted(want), (case, ops, t)
             p = paths[t] - {"move"}
             if t >= ntw:
@@ -638,30 +647,32 @@ def _run_turn(g, off, O, inv, ops, lds_size, out_bytes):
     touched = [1 << 40, -1]
     cleared = _run_vector(list(pre) + list(lead) + [x for it in items for x in it["ins"]], O, inv, ops, lds, out,
                           touched, v, acc, sreg)
-    assert cleared == set(range(8)), "O not cleared block by block"
+    assert cleared == set(range(2 * g.DB)), "O not cleared block by block"
     return out, touched
 
 
+@pytest.mark.parametrize("d", HEAD_DIMS)
 @pytest.mark.parametrize("layout,nrows,off", [("bhnd", 64, 0), ("bhnd", 64, 1), ("bnhd", 64, 0), ("bnhd", 64, 1),
                                               ("bhnd", 37, 1), ("bnhd", 5, 0), ("bhnd", 0, 1)])
-def test_turn_writes_previous_item_rows(layout, nrows, off):
+def test_turn_writes_previous_item_rows(layout, nrows, off, d):
     """The turn packs the finished item's O (the AGPR layout of the 32 x 32 products) as bf16(O / l) into the
     wave's Q slot and stores the rows from there: every row below the descriptor's end reaches memory at row * stride + column * 2, nothing else is
     written, and the rows go through the wave's own Q slot only."""
-    g = _gen()
+    g = _gen(d)
+    TB, RB, DB = g.TILE_B, g.ROWB, g.DB
     rng = np.random.default_rng(5)
     H, wave = 3, 2
-    stride = 256 if layout == "bhnd" else H * 256
+    stride = RB if layout == "bhnd" else H * RB
     qsb = 4 * TB + wave * TB
-    onb = (nrows - 1) * stride + 256 if nrows > 0 else 0
-    O = rng.standard_normal((8, 16, 64)).astype(np.float32) * 3
+    onb = (nrows - 1) * stride + RB if nrows > 0 else 0
+    O = rng.standard_normal((2 * DB, 16, 64)).astype(np.float32) * 3
     inv = (np.float32(0.37), np.float32(1.9))
-    ops = {"wq": 4 * TB + wave * TB, "qsb": qsb, "ostr": stride, "onb": onb, **{"ka%d" % ks: 0 for ks in range(8)}}
-    out, touched = _run_turn(g, off, O.copy(), inv, ops, 10 * TB, 64 * stride + 256)
+    ops = {"wq": 4 * TB + wave * TB, "qsb": qsb, "ostr": stride, "onb": onb, **{"ka%d" % ks: 0 for ks in range(g.KS)}}
+    out, touched = _run_turn(g, off, O.copy(), inv, ops, 10 * TB, 64 * stride + RB)
     assert touched[0] >= qsb and touched[1] <= qsb + TB, "output rows outside the wave's Q slot"
-    want = np.full(64 * stride + 256, 0xEE, dtype=np.uint8)
-    for k in range(8):
-        qb, db = divmod(k, 4)
+    want = np.full(64 * stride + RB, 0xEE, dtype=np.uint8)
+    for k in range(2 * DB):
+        qb, db = divmod(k, DB)
         for r in range(16):
             for ln in range(64):
                 l32, hf = ln % 32, ln // 32

@@ -107,30 +107,29 @@ __device__ __forceinline__ void store_lse(float *__restrict__ lse, float l, floa
         lse[(size_t)bh * Nq + qrow] = l > 0.f ? (mc + log2f(l)) * 0.69314718055994531f : -INFINITY;
 }
 
-// O = O_acc / l for one block of 32 query rows, as bf16, staged through an 8 KiB LDS area of the wave so
-// that every store writes whole 256-byte rows (four rows per instruction) instead of 16 bytes per row.
-// l_tot: the row's whole sum. The stores go through a buffer descriptor that covers exactly the block's
-// rows below Nq, so rows past Nq are dropped by the range check (no per-row branch). The area's 16-byte
-// chunks are XOR-swizzled by row so that both the 8-byte writes and the 16-byte reads spread over the
-// banks.
+// O = O_acc / l for one block of 32 query rows, as bf16, staged through a 32-row LDS area of the wave (32 * D * 2
+// bytes) so that every store writes whole rows (64 / (D / 8) rows per instruction) instead of 16 bytes per row.
+// The stores go through a buffer descriptor that covers exactly the block's rows below Nq, so rows past Nq are
+// dropped by the range check (no per-row branch). The area's 16-byte chunks are XOR-swizzled by row so that both
+// the 8-byte writes and the 16-byte reads spread over the banks.
 // pk[db] holds the block's 16 values of the lane, already divided by the row sum, as bf16 pairs.
-template <int OLAYOUT>
-__device__ __forceinline__ void store_rows_bf16_staged(const u32x8 (&pk)[4], int row0, int bh, int H, int Nq, int b,
-                                                       int lane, uint8_t *stage, void *__restrict__ Out)
+template <int D, int OLAYOUT>
+__device__ __forceinline__ void store_rows_bf16_staged(const u32x8 (&pk)[D / 32], int row0, int bh, int H, int Nq,
+                                                       int b, int lane, uint8_t *stage, void *__restrict__ Out)
 {
-    constexpr int D = 128;
+    constexpr int CPR = D / 8, RPR = 64 / CPR, ROWB = D * 2;
     // computed here rather than kept from the kernel's start: the lane-dependent addresses would otherwise
     // be hoisted out of the workgroup's item loop and held across the tile loop, which has no registers
     // to spare
     asm volatile("" : "+v"(lane));
     const int l32 = lane & 31, hf = lane >> 5;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
             const int c = db * 4 + rg;
             const u32x2 v = {pk[db][rg * 2], pk[db][rg * 2 + 1]};
-            *(u32x2 *)(stage + l32 * 256 + ((c ^ (l32 & 15)) << 4) + hf * 8) = v;
+            *(u32x2 *)(stage + l32 * ROWB + ((c ^ (l32 & (CPR - 1))) << 4) + hf * 8) = v;
         }
     // the wave's LDS operations complete in order: keep the compiler from moving the reads up
     asm volatile("" ::: "memory");
@@ -141,9 +140,9 @@ __device__ __forceinline__ void store_rows_bf16_staged(const u32x8 (&pk)[4], int
     const int nbytes = nrows > 0 ? (nrows - 1) * stride + D * 2 : 0;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((uint16_t *)Out + first, (short)0, nbytes, 0x20000);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = i * 4 + (lane >> 4), cc = lane & 15;
-        const u32x4 d = *(const u32x4 *)(stage + r * 256 + ((cc ^ (r & 15)) << 4));
+    for (int i = 0; i < 32 / RPR; ++i) {
+        const int r = i * RPR + lane / CPR, cc = lane % CPR;
+        const u32x4 d = *(const u32x4 *)(stage + r * ROWB + ((cc ^ (r & (CPR - 1))) << 4));
         __builtin_amdgcn_raw_buffer_store_b128(d, rs, r * stride + cc * 16, 0, 0);
     }
     asm volatile("" ::: "memory");
@@ -411,6 +410,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(
 }
 
 #include "attn_qb2_tile.inc"
+#include "attn_qb2_tile_d64.inc"
 
 // Row max of one query block's 64 scores of a tile (both half-waves).
 __device__ __forceinline__ float tile_max(const f32x16 (&s)[2])
@@ -424,7 +424,7 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2])
 }
 
 // ---------------------------------------------------------------------------
-// 128-wide heads, 64 query rows per wave (two blocks of 32), 4 waves per
+// 128- and 64-wide heads, 64 query rows per wave (two blocks of 32), 4 waves per
 // workgroup, one wave per SIMD. Every K or V operand read from LDS feeds two
 // MFMAs, which halves the LDS bytes per MFMA against 32-row waves. The whole
 // tile loop of a wave -- S(t+1) MFMAs, the exponentials of S(t), the
@@ -444,8 +444,8 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2])
 // loop's fetches run on past the item's last tile into the next item's first
 // K/V tiles (tiles take slots of parity (t + off) % 2, off carried from item
 // to item). Outputs go out as whole rows through an LDS staging area.
-// LDS: K0 K1 V0 V1, the four waves' Q rows, 8 KiB of staging per wave
-// (160 KiB).
+// LDS: K0 K1 V0 V1, the four waves' Q rows, 32 rows of staging per wave
+// (160 KiB for 128-wide heads, 80 KiB for 64-wide ones).
 //
 // Registers: O, Q^T, the row sums and an all-ones operand in AGPRs, the two
 // score buffers, P and the operand staging in VGPRs, at the physical
@@ -487,13 +487,13 @@ __device__ __forceinline__ Qb2Item qb2_item(bool valid, int bh, int qt, int num_
     return it;
 }
 
-template <int MASK, bool OUT_F32, int OLAYOUT>
+template <int D, int MASK, bool OUT_F32, int OLAYOUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_fwd_qb2_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const int32_t *__restrict__ valid_lens, float c_log2, void *__restrict__ Out, int H, int Nq, int Nk,
     int num_qtiles, int BH, AttnHeads hd)
 {
-    constexpr int D = 128, QB = 2, WAVES = 4, RW = 64;
+    constexpr int QB = 2, WAVES = 4, RW = 64;
     constexpr int KS = D / 16, DB = D / 32;
     constexpr int TILE_B = kBlockN * D * 2;
     constexpr int CPR = D / 8;
@@ -501,9 +501,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     static_assert(kBlockN * CPR % (WAVES * 64) == 0, "tile must split evenly over the workgroup");
     // K0 K1 V0 V1 (the tile loop's slots), then the Q rows of the four waves (the next item's while the
     // current item's loop runs its last tiles)
-    __shared__ __attribute__((aligned(256))) uint8_t smem[10 * TILE_B];
+    constexpr int STAGE_W = 32 * D * 2;  // per wave: 32 output rows (the last item's epilogue)
+    __shared__ __attribute__((aligned(256))) uint8_t smem[8 * TILE_B + WAVES * STAGE_W];
     constexpr int KSLOT0 = 0, KSLOT1 = TILE_B, VSLOT0 = 2 * TILE_B, VSLOT1 = 3 * TILE_B, QSLOT = 4 * TILE_B;
-    constexpr int STAGE = 8 * TILE_B;  // 8 KiB per wave for the output rows (bf16 output)
+    constexpr int STAGE = 8 * TILE_B;  // the waves' output staging areas (bf16 output)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
@@ -542,9 +543,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const uint16_t *base = mat + (size_t)r_base * D;
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
-            // voff[j] = lane's tile row * 256 + its (swizzled) chunk's byte offset in the row
-            const int row = min(r0 + (int)(voff[j] >> 8), r_end - 1);
-            const uint32_t off = (voff[j] & 255u) + (uint32_t)(row - r_base) * (D * 2);
+            // voff[j] = lane's tile row * (D * 2) + its (swizzled) chunk's byte offset in the row
+            const int row = min(r0 + (int)(voff[j] / (D * 2)), r_end - 1);
+            const uint32_t off = (voff[j] % (D * 2)) + (uint32_t)(row - r_base) * (D * 2);
             lds_dma16(lbw + slot_off + j * WAVES * 1024, base, off);
         }
     };
@@ -573,10 +574,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const __amdgpu_buffer_rsrc_t rs =
                 __builtin_amdgcn_make_buffer_rsrc((void *)(Qh + (size_t)qw * RW * D), (short)0, rows * D * 2, 0x20000);
 #pragma unroll
-            for (int j = 0; j < CH; ++j)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (__attribute__((address_space(3))) void *)(uintptr_t)(lbw + QSLOT + qw * TILE_B + j * WAVES * 1024),
-                    16, voff[j], 0, 0, 0);
+            for (int j = 0; j < CH; ++j) lds_dma16_rsrc(rs, lbw + QSLOT + qw * TILE_B + j * WAVES * 1024, voff[j]);
         }
     };
 
@@ -596,25 +594,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         return qb2_item<MASK>(valid, bh, qt, num_qtiles, H, Nk, valid_lens, hd);
     };
-    // Q^T of this wave's rows from its Q slot into the AGPRs the tile loop names, and O = 0. The slot offset
-    // is computed here so that the eight addresses are not held across the tile loop
+    // Q^T of this wave's rows from its Q slot into the AGPRs the tile loop names, and O = 0 (qb2_init; the slot
+    // offset is computed there so that the KS addresses are not held across the tile loop)
     bf16x8 qreg[QB][KS];
     f32x16 acc[QB][DB];
-    auto q_init = [&]() {
-        uint32_t wq = QSLOT + wave * TILE_B;
-        asm volatile("" : "+v"(wq));
-        uint32_t qa[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qa[ks] = kaddr[ks] + wq;
-        qb2_init(acc, qreg, qa);
-    };
     Qb2Item cur = item(0);
     if (!cur.valid) return;
     q_tiles(cur);
     first_tiles(cur, 0);
     wait_vmcnt0();
     __syncthreads();
-    q_init();
+    {
+        uint32_t wq = QSLOT + wave * TILE_B;
+        asm volatile("" : "+v"(wq));
+        uint32_t qa[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qa[ks] = kaddr[ks] + wq;
+        if constexpr (D == 128) qb2_init(acc, qreg, qa);
+        else qb2_init_d64(acc, qreg, qa);
+    }
     // bf16 output: the tile loop of each later item starts with the turn, which packs the previous item's
     // output rows while the new item's first scores are computed (turn = 1); the parameters of those rows
     constexpr int OSTRIDE = (OLAYOUT == kOutBHND ? D : 0) * 2;  // BNHD: H * D * 2, below
@@ -654,7 +652,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const uint64_t nq = (uint64_t)(Q + ((size_t)nn.bh * Nq + nn.q0) * D);
         const int nq_rows = nxt.valid ? Nq - nxt.q0 : 0;
         float l_run[QB] = {0.f, 0.f}, mc0 = -INFINITY, mc1 = -INFINITY;
-        qb2_loop(acc, qreg, kaddr, vaddr, voff, lim[0], lim[1], c_log2, l_run[0], l_run[1], mc0, mc1,
+        if constexpr (D == 128)
+            qb2_loop(acc, qreg, kaddr, vaddr, voff, lim[0], lim[1], c_log2, l_run[0], l_run[1], mc0, mc1,
+                 u(0), u(cur.ntiles), u(ntiles_w), u(t_mask), u(cur.kv_end), u((uint32_t)kh),
+                 u((uint32_t)(kh >> 32)), u((uint32_t)vh), u((uint32_t)(vh >> 32)), lbw, u(off),
+                 u((uint32_t)nkh), u((uint32_t)(nkh >> 32)), u((uint32_t)nvh), u((uint32_t)(nvh >> 32)),
+                 u(nxt.valid ? nxt.kv_end : 0), u(t_diag), u(turn), inv[0], inv[1], u((uint32_t)ob),
+                 u((uint32_t)(ob >> 32)), u(ob_bytes), u(ostride), u(QSLOT + wave * TILE_B),
+                 u(lds0 + QSLOT + wave * TILE_B), u((uint32_t)nq), u((uint32_t)(nq >> 32)), u(nq_rows));
+        else
+            qb2_loop_d64(acc, qreg, kaddr, vaddr, voff, lim[0], lim[1], c_log2, l_run[0], l_run[1], mc0, mc1,
                  u(0), u(cur.ntiles), u(ntiles_w), u(t_mask), u(cur.kv_end), u((uint32_t)kh),
                  u((uint32_t)(kh >> 32)), u((uint32_t)vh), u((uint32_t)(vh >> 32)), lbw, u(off),
                  u((uint32_t)nkh), u((uint32_t)(nkh >> 32)), u((uint32_t)nvh), u((uint32_t)(nvh >> 32)),
@@ -677,11 +684,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         } else if (!nxt.valid) {
             // the last item's rows: O / l packed straight from the O registers, then staged and stored
             u32x8 pk[QB][DB];
-            qb2_out_bf16(acc, inv[0], inv[1], pk);
+            if constexpr (D == 128) qb2_out_bf16(acc, inv[0], inv[1], pk);
+            else qb2_out_bf16_d64(acc, inv[0], inv[1], pk);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
-                store_rows_bf16_staged<OLAYOUT>(pk[qb], cur.q0 + wave * RW + qb * 32, cur.bh, H, Nq, cur.b, lane,
-                                                smem + STAGE + wave * 8192, Out);
+                store_rows_bf16_staged<D, OLAYOUT>(pk[qb], cur.q0 + wave * RW + qb * 32, cur.bh, H, Nq, cur.b, lane,
+                                                   smem + STAGE + wave * STAGE_W, Out);
         } else {
             // this item's rows, written by the next item's turn: the wave's 64 rows from row0, those below Nq
             const int row0 = cur.q0 + wave * RW;
@@ -703,7 +711,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             wait_vmcnt0();
             __syncthreads();
         }
-        if constexpr (OUT_F32) q_init();
+        if constexpr (OUT_F32) {
+            uint32_t wq = QSLOT + wave * TILE_B;
+            asm volatile("" : "+v"(wq));
+            uint32_t qa[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qa[ks] = kaddr[ks] + wq;
+            if constexpr (D == 128) qb2_init(acc, qreg, qa);
+            else qb2_init_d64(acc, qreg, qa);
+        }
         cur = nxt;
         off = off_next;
     }
@@ -742,20 +758,26 @@ hipError_t launch_variant(const void *Q, const void *K, const void *V, const int
         const long long grid = (long long)num_qtiles * BH;
         if (grid <= 0) return hipSuccess;
         if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((attn_fwd_qb2_kernel<MASK, OUT_F32, OLAYOUT>),
+        hipLaunchKernelGGL((attn_fwd_qb2_kernel<D, MASK, OUT_F32, OLAYOUT>),
                            dim3((unsigned)std::min<long long>(grid, device_cu_count())), dim3(256), 0, stream,
                            (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, valid_lens, c_log2, O, H,
                            Nq, Nk, num_qtiles, BH, hd);
         return hipGetLastError();
     } else {
         static_assert(D == 64, "head_dim 64 or 128");
-        // 8 waves (256 rows per workgroup) when that grid still gives every CU a workgroup (4.5 % faster at
-        // B4 H8 N2048); else 4 waves of 128 rows, which give every SIMD two waves when their grid has more
-        // workgroups than CUs; smaller grids split each workgroup's keys over two sets of 4 waves
+        // smaller grids: the C++ kernel with 4 waves of 128 rows, which give every SIMD two waves when their
+        // grid has more workgroups than CUs; smaller still, each workgroup's keys split over two sets of 4 waves
         const int cus = device_cu_count();
         const long long g8 = (long long)((Nq + 255) / 256) * B * H, g4 = (long long)((Nq + 127) / 128) * B * H;
-        if (g8 >= cus)
-            return launch_cpp<D, 1, MASK, OUT_F32, OLAYOUT, 8>(Q, K, V, valid_lens, c_log2, O, B, H, Nq, Nk, hd, stream);
+        if (g8 >= cus) {
+            // 256-row work items cover every CU: the persistent kernel with the generated tile loop (64 rows per
+            // wave, one wave per SIMD), as for 128-wide heads
+            if (g8 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+            hipLaunchKernelGGL((attn_fwd_qb2_kernel<D, MASK, OUT_F32, OLAYOUT>), dim3((unsigned)cus), dim3(256), 0,
+                               stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, valid_lens,
+                               c_log2, O, H, Nq, Nk, (Nq + 255) / 256, B * H, hd);
+            return hipGetLastError();
+        }
         if (g4 <= cus)
             return launch_cpp<D, 1, MASK, OUT_F32, OLAYOUT, 8, 2>(Q, K, V, valid_lens, c_log2, O, B, H, Nq, Nk, hd,
                                                                  stream);

@@ -44,6 +44,11 @@ __device__ __forceinline__ void mfma_fence_a8(f32x16 (&x)[2][4])
                    "+a"(x[1][2]), "+a"(x[1][3]));
 }
 
+__device__ __forceinline__ void mfma_fence_a8(f32x16 (&x)[2][2])
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+a"(x[0][0]), "+a"(x[0][1]), "+a"(x[1][0]), "+a"(x[1][1]));
+}
+
 // Two transposed 4x4 reads make one 8-element MFMA operand.
 __device__ __forceinline__ bf16x8 lds_tr_pair(const uint16_t *lo, const uint16_t *hi)
 {
@@ -111,6 +116,13 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds, const void *base, uint32
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// 16 bytes per lane from a range-checked buffer (byte offset voff) into LDS at lds + 16 * lane.
+__device__ __forceinline__ void lds_dma16_rsrc(__amdgpu_buffer_rsrc_t rs, uint32_t lds, uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(uintptr_t)lds, 16, voff, 0,
+                                             0, 0);
 }
 
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // s_waitcnt vmcnt(0)

@@ -39,15 +39,33 @@ only after three further MFMAs (or 24 wait states) behind the last MFMA that
 wrote it. The loop ends with 24 wait states so that O is complete when C++
 code next reads it.
 
-Run:  python gen_qb2_tile.py  (writes attn_qb2_tile.inc next to this file)
+Run:  python gen_qb2_tile.py  (writes attn_qb2_tile.inc for 128-wide heads and attn_qb2_tile_d64.inc for
+64-wide ones next to this file)
 """
 from __future__ import annotations
 
 import math
 import os
 
-D, KS, DB, QB = 128, 8, 4, 2
-TILE_B = 64 * D * 2
+QB = 2                 # query blocks of 32 rows per wave
+
+
+def configure(d):
+    """Head width of the generated code (128 or 64): sets the module's shape constants."""
+    global D, KS, DB, TILE_B, CH, TSH, RSH, ROWB, CPR, QSLOT, SUFFIX
+    assert d in (64, 128)
+    D, KS, DB = d, d // 16, d // 32
+    TILE_B = 64 * D * 2            # bytes of a 64-row K, V or Q tile
+    CH = TILE_B // 4096            # 1 KiB DMA instructions per tile and wave (4 waves)
+    TSH = TILE_B.bit_length() - 1  # log2 of the tile bytes
+    ROWB = D * 2                   # bytes of a row
+    RSH = ROWB.bit_length() - 1
+    CPR = D // 8                   # 16-byte chunks per row
+    QSLOT = 4 * TILE_B             # LDS offset of the Q slots (four 64-row blocks)
+    SUFFIX = "" if D == 128 else "_d%d" % D
+
+
+configure(128)
 S_BUF = (0, 64)
 P0, KST, VST, TMP, MXT = 128, 160, 176, 192, 200
 MXT_Q = ((200, 201), (217, 218))   # row-max temporaries of qb 0 and qb 1
@@ -100,7 +118,7 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
 
     mfma = []
     if do_s:
-        for i in range(32):
+        for i in range(4 * KS):
             ks, jb, qb = i // 4, (i // 2) % 2, i % 2
             kop = ks * 2 + jb
             dst = S_BUF[y_buf] + (qb * 2 + jb) * 16
@@ -109,8 +127,8 @@ def gen(x_buf, y_buf, kslot, vslot, do_s, do_pv, do_max, mref=("%[mref0]", "%[mr
                              text="v_mfma_f32_32x32x16_bf16 %s, %s, %s, %s" % (
                                  vr(dst, 16), vr(KST + 4 * (kop % NKS), 4), ar(Q_A + 4 * (qb * KS + ks), 4), src_c)))
     if do_pv:
-        for j in range(32):
-            c, db, qb = j // 8, (j // 2) % 4, j % 2
+        for j in range(8 * DB):
+            c, db, qb = j // (2 * DB), (j // 2) % DB, j % 2
             vop = c * DB + db
             acc = O_A + (qb * DB + db) * 16
             pop = vr(P0 + 4 * (qb * 4 + c), 4)
@@ -393,19 +411,19 @@ def tile_res(res, tile_sreg, base_lo, base_hi):
     """Buffer descriptor of one K or V tile of the head: base = head + tile * 16 KiB, size = the bytes of
     the tile's rows below kv_end (0 past the end), so that rows past kv_end read as out of range and
     never touch memory."""
-    return ["s_lshl_b32 s%d, %s, 14" % (SREG + 1, tile_sreg),
+    return ["s_lshl_b32 s%d, %s, %d" % (SREG + 1, tile_sreg, TSH),
             "s_add_u32 s%d, %s, s%d" % (res, base_lo, SREG + 1),
             "s_addc_u32 s%d, %s, 0" % (res + 1, base_hi),
-            "s_lshl_b32 s%d, %%[kve], 8" % (res + 2),
+            "s_lshl_b32 s%d, %%[kve], %d" % (res + 2, RSH),
             "s_sub_i32 s%d, s%d, s%d" % (res + 2, res + 2, SREG + 1),
             "s_max_i32 s%d, s%d, 0" % (res + 2, res + 2),
             "s_mov_b32 s%d, %s" % (res + 3, BUF_WORD3)]
 
 
 def dma_groups(res, slot_off):
-    """The four loads of one tile (each 64 lanes x 16 B into 1 KiB of LDS at M0), one group each."""
+    """The CH loads of one tile (each 64 lanes x 16 B into 1 KiB of LDS at M0), one group each."""
     return [["s_add_u32 m0, %%[lbw], %d" % (slot_off + j * 4096),
-             "buffer_load_dwordx4 %%[vo%d], s[%d:%d], 0 offen lds" % (j, res, res + 3)] for j in range(4)]
+             "buffer_load_dwordx4 %%[vo%d], s[%d:%d], 0 offen lds" % (j, res, res + 3)] for j in range(CH)]
 
 
 def step_dma(parity):
@@ -470,9 +488,9 @@ def max_chain(buf, qb, dst):
 
 
 def res_advance(res):
-    """Move a tile descriptor on by one tile (16 KiB); the size stays clamped at 0."""
-    return ["s_add_u32 s%d, s%d, 0x4000" % (res, res), "s_addc_u32 s%d, s%d, 0" % (res + 1, res + 1),
-            "s_sub_i32 s%d, s%d, 0x4000" % (res + 2, res + 2), "s_max_i32 s%d, s%d, 0" % (res + 2, res + 2)]
+    """Move a tile descriptor on by one tile; the size stays clamped at 0."""
+    return ["s_add_u32 s%d, s%d, 0x%x" % (res, res, TILE_B), "s_addc_u32 s%d, s%d, 0" % (res + 1, res + 1),
+            "s_sub_i32 s%d, s%d, 0x%x" % (res + 2, res + 2, TILE_B), "s_max_i32 s%d, s%d, 0" % (res + 2, res + 2)]
 
 
 def mask_tile(tile_sreg, buf):
@@ -506,8 +524,8 @@ def rescale():
         o += ["v_accvgpr_read_b32 v%d, a%d" % (P0, a), "v_mul_f32 v%d, v%d, v%d" % (P0, P0, ALPHA_V[qb]),
               "v_accvgpr_write_b32 a%d, v%d" % (a, P0)]
     for qb in range(QB):
-        for r in range(64):
-            a = O_A + qb * 64 + r
+        for r in range(16 * DB):
+            a = O_A + qb * 16 * DB + r
             t = P0 + (r % 16)
             o += ["v_accvgpr_read_b32 v%d, a%d" % (t, a), "v_mul_f32 v%d, v%d, v%d" % (t, t, ALPHA_V[qb]),
                   "v_accvgpr_write_b32 a%d, v%d" % (a, t)]
@@ -541,9 +559,14 @@ def zero_o(k):
 def turn_work(off):
     """(pre, lead, items, zero MFMAs) of the turn for an item whose first scores go to buffer `off`: the finished
     item's packed rows go to the other score buffer (8 registers per 32 x 32 block of O, as qb2_out_bf16
-    packs them), the pack temporaries alternate between the two halves of P."""
+    packs them), the pack temporaries alternate between the two halves of P. In the slot a row is ROWB bytes of
+    CPR 16-byte chunks, chunk c of row r at chunk position c XOR (r mod CPR); one 16-byte read per lane covers
+    RPR = 64 / CPR rows (row i RPR + lane / CPR, chunk lane mod CPR), whose positions repeat every NPAT reads."""
     pkb = S_BUF[1 - off]
     L, T0, T1 = TURN_L_V, TURN_T_V[0], TURN_T_V[1]
+    RPR = 64 // CPR
+    NPAT = max(CPR // RPR, 1)
+    NRD = 32 // RPR                   # reads (and stores) per 32-row block
     pre = ["v_add_u32 v%d, %%[wq], %%[ka%d]" % (TURN_QA_V + ks, ks) for ks in range(KS)]
     pre += ["ds_read_b128 a[%d:%d], v%d offset:%d" % (Q_A + 4 * (qb * KS + ks), Q_A + 4 * (qb * KS + ks) + 3,
                                                       TURN_QA_V + ks, qb * 32 * D * 2)
@@ -551,17 +574,19 @@ def turn_work(off):
     pre += ["s_mov_b32 s%d, %%[obl]" % OUT_RES, "s_mov_b32 s%d, %%[obh]" % (OUT_RES + 1),
             "s_mov_b32 s%d, %%[onb]" % (OUT_RES + 2), "s_mov_b32 s%d, %s" % (OUT_RES + 3, BUF_WORD3)]
     pre += ["v_mov_b32 v%d, 0" % r for r in range(TURN_ZERO_V, TURN_ZERO_V + 4)]
+    # lane id, lane mod CPR (chunk of a read), lane / CPR (row of a read)
     pre += ["v_mbcnt_lo_u32_b32 v%d, -1, 0" % L, "v_mbcnt_hi_u32_b32 v%d, -1, v%d" % (L, L),
-            "v_and_b32 v%d, 15, v%d" % (L + 1, L), "v_lshrrev_b32 v%d, 4, v%d" % (L + 2, L)]
-    # write address: slot + (lane & 31) * 256 + (lane >> 5) * 8 + ((lane & 15) << 4); the slot is 256-byte
-    # aligned, so bits 4..7 hold lane & 15 and chunk c is that address XOR (c << 4)
-    pre += ["v_and_b32 v%d, 31, v%d" % (T0, L), "v_lshlrev_b32 v%d, 8, v%d" % (T0, T0),
+            "v_and_b32 v%d, %d, v%d" % (L + 1, CPR - 1, L), "v_lshrrev_b32 v%d, %d, v%d" % (L + 2, CPR.bit_length() - 1, L)]
+    # write address: slot + (lane & 31) * ROWB + (lane >> 5) * 8 + (((lane & 31) mod CPR) << 4); the slot is
+    # 256-byte aligned, so the chunk bits hold (lane & 31) mod CPR and chunk c is that address XOR (c << 4)
+    pre += ["v_and_b32 v%d, 31, v%d" % (T0, L), "v_lshlrev_b32 v%d, %d, v%d" % (T0, RSH, T0),
             "v_lshrrev_b32 v%d, 5, v%d" % (T1, L), "v_lshl_add_u32 v%d, v%d, 3, v%d" % (T0, T1, T0),
             "v_lshl_add_u32 v%d, v%d, 4, v%d" % (T0, L + 1, T0), "v_add_u32 v%d, %%[qsb], v%d" % (TURN_WB_V, T0)]
-    # read address of row group j: row r = 4 j + (lane >> 4), chunk (lane & 15) XOR r
-    for j in range(4):
-        pre += ["v_add_u32 v%d, %d, v%d" % (T0, 4 * j, L + 2), "v_xor_b32 v%d, v%d, v%d" % (T1, T0, L + 1),
-                "v_lshlrev_b32 v%d, 4, v%d" % (T1, T1), "v_lshl_add_u32 v%d, v%d, 8, v%d" % (T0, T0, T1),
+    # read address of pattern j: row r = j RPR + lane / CPR, chunk (lane mod CPR) XOR (r mod CPR)
+    for j in range(NPAT):
+        pre += ["v_add_u32 v%d, %d, v%d" % (T0, RPR * j, L + 2), "v_and_b32 v%d, %d, v%d" % (T1, CPR - 1, T0),
+                "v_xor_b32 v%d, v%d, v%d" % (T1, T1, L + 1),
+                "v_lshlrev_b32 v%d, 4, v%d" % (T1, T1), "v_lshl_add_u32 v%d, v%d, %d, v%d" % (T0, T0, RSH, T1),
                 "v_add_u32 v%d, %%[qsb], v%d" % (TURN_RB_V + j, T0)]
     pre += ["v_mul_u32_u24 v%d, %%[ostr], v%d" % (T0, L + 2),
             "v_lshl_add_u32 v%d, v%d, 4, v%d" % (TURN_SB_V, L + 1, T0)]
@@ -577,43 +602,43 @@ def turn_work(off):
     lead = packs[0]
     items = [dict(ins=packs[k], name="pack %d" % k, after=["pack %d" % (k - 2)] if k >= 3 else [])
              for k in range(1, QB * DB)]
-    # one 32-row block at a time: its packed registers into the slot, and (direct) read back as whole rows
-    # into the same registers, then stored. Addresses of the writes and the stores' offsets: the exp
-    # temporaries (block 0; free once the Q reads are issued), then the K operand registers (block 1; free
-    # once the last S(0) MFMA has issued, four MFMAs before: ready)
+    # one 32-row block at a time: its packed registers into the slot, read back as whole rows into the same
+    # registers (LDS executes a wave's operations in order), then stored. Addresses of the writes and the
+    # stores' offsets: the exp temporaries (block 0; free once the Q reads are issued), then the K operand
+    # registers (block 1; free once the last S(0) MFMA has issued, four MFMAs before: ready)
     for qb in range(QB):
         tmp = [TMP + i for i in range(8)] if qb == 0 else list(range(KST, KST + 16))
-        ready = 0 if qb == 0 else 32 + 4
-        rows = pkb + 32 * qb
+        ready = 0 if qb == 0 else 4 * KS + 4
+        rows = pkb + 8 * DB * qb          # the row block's packed registers (8 per 32 x 32 block)
         w = []
-        for c in range(16):
+        for c in range(CPR):
             db, rg = c // 4, c % 4
             src = rows + 8 * db + 2 * rg
             a = tmp[c % len(tmp)]
             w += ["v_xor_b32 v%d, 0x%x, v%d" % (a, c << 4, TURN_WB_V),
-                  "ds_write_b64 v%d, v[%d:%d] offset:%d" % (a, src, src + 1, qb * 32 * 256)]
+                  "ds_write_b64 v%d, v[%d:%d] offset:%d" % (a, src, src + 1, qb * 32 * ROWB)]
         after = ["pack %d" % k for k in range(qb * DB, (qb + 1) * DB) if k > 0]
         after += ["store 0"] if qb else []
         items.append(dict(ins=w, name="write %d" % qb, after=after, ready=ready))
-        rd = ["ds_read_b128 v[%d:%d], v%d offset:%d" % (rows + 4 * i, rows + 4 * i + 3, TURN_RB_V + (i & 3),
-                                                        (2 * qb + (i >> 2)) * 4096) for i in range(8)]
+        rd = ["ds_read_b128 v[%d:%d], v%d offset:%d" % (rows + 4 * i, rows + 4 * i + 3, TURN_RB_V + (i % NPAT),
+                                                        (qb * NRD + i) // NPAT * NPAT * 1024) for i in range(NRD)]
         items.append(dict(ins=rd, name="read %d" % qb, after=["write %d" % qb], ready=ready))
         st = ["s_waitcnt lgkmcnt(0)"]
-        for i in range(8):
+        for i in range(NRD):
             a = tmp[i]
-            st += ["v_mad_u32_u24 v%d, %d, %%[ostr], v%d" % (a, qb * 32 + 4 * i, TURN_SB_V),
+            st += ["v_mad_u32_u24 v%d, %d, %%[ostr], v%d" % (a, qb * 32 + RPR * i, TURN_SB_V),
                    "buffer_store_dwordx4 v[%d:%d], v%d, s[%d:%d], 0 offen nt" % (rows + 4 * i, rows + 4 * i + 3, a,
                                                                                 OUT_RES, OUT_RES + 3)]
-            if i % 2 == 1:
-                # the row block's four 32 x 32 blocks of O are cleared between its stores
-                st.append(zero_o(qb * DB + i // 2))
+            if (i + 1) % (NRD // DB) == 0:
+                # the row block's 32 x 32 blocks of O are cleared between its stores
+                st.append(zero_o(qb * DB + i // (NRD // DB)))
         items.append(dict(ins=st, name="store %d" % qb, after=["read %d" % qb], ready=ready))
     # priority (the scheduler takes ready items in list order): block 0's packing, its staging, the first
     # block of qb 1 packed while block 0's rows come back from LDS, its stores, then the rest
     by = {it["name"]: it for it in items}
-    order = ["pack 1", "pack 2", "pack 3", "write 0", "read 0", "pack 4", "store 0", "pack 5", "pack 6", "pack 7",
-             "write 1", "read 1", "store 1"]
-    by["store 0"]["after"] = ["read 0", "pack 4"]
+    order = (["pack %d" % k for k in range(1, DB)] + ["write 0", "read 0", "pack %d" % DB, "store 0"] +
+             ["pack %d" % k for k in range(DB + 1, 2 * DB)] + ["write 1", "read 1", "store 1"])
+    by["store 0"]["after"] = ["read 0", "pack %d" % DB]
     items = [by[n] for n in order]
     return pre, lead, items, []
 
@@ -642,9 +667,6 @@ def first_tile(off, turn=False):
     return o
 
 
-QSLOT = 4 * TILE_B      # LDS offset of the Q slots (four 64-row blocks)
-
-
 def q_next_dma():
     """The next item's Q rows into the Q slots when this item has fewer than five tiles (else the general
     steps fetch them block by block, q_block_dma), issued once every wave has its own Q rows (after the barrier
@@ -656,9 +678,9 @@ def q_next_dma():
     for qw in range(4):
         o += ["s_add_u32 s%d, %%[nql], %d" % (KRES, qw * TILE_B), "s_addc_u32 s%d, %%[nqh], 0" % (KRES + 1),
               "s_sub_i32 s%d, %%[nqr], %d" % (KRES + 2, 64 * qw), "s_max_i32 s%d, s%d, 0" % (KRES + 2, KRES + 2),
-              "s_min_i32 s%d, s%d, 64" % (KRES + 2, KRES + 2), "s_lshl_b32 s%d, s%d, 8" % (KRES + 2, KRES + 2),
+              "s_min_i32 s%d, s%d, 64" % (KRES + 2, KRES + 2), "s_lshl_b32 s%d, s%d, %d" % (KRES + 2, KRES + 2, RSH),
               "s_mov_b32 s%d, %s" % (KRES + 3, BUF_WORD3)]
-        for j in range(4):
+        for j in range(CH):
             o += ["s_add_u32 m0, %%[lbw], %d" % (QSLOT + qw * TILE_B + j * 4096), "s_nop 0",
                   "buffer_load_dwordx4 %%[vo%d], s[%d:%d], 0 offen nt lds" % (j, KRES, KRES + 3)]
     return o + ["L_qdma_done_%=:"]
@@ -676,10 +698,10 @@ def stream_res(res, x, base_lo, base_hi, nbase_lo, nbase_hi):
 
 def next_res(res, tile_sreg, base_lo, base_hi):
     """Descriptor of tile (tile_sreg) of the next item (size from its kv_end: 0 when there is none)."""
-    return ["s_lshl_b32 s%d, %s, 14" % (SREG + 1, tile_sreg),
+    return ["s_lshl_b32 s%d, %s, %d" % (SREG + 1, tile_sreg, TSH),
             "s_add_u32 s%d, %s, s%d" % (res, base_lo, SREG + 1),
             "s_addc_u32 s%d, %s, 0" % (res + 1, base_hi),
-            "s_lshl_b32 s%d, %%[nkve], 8" % (res + 2),
+            "s_lshl_b32 s%d, %%[nkve], %d" % (res + 2, RSH),
             "s_sub_i32 s%d, s%d, s%d" % (res + 2, res + 2, SREG + 1),
             "s_max_i32 s%d, s%d, 0" % (res + 2, res + 2),
             "s_mov_b32 s%d, %s" % (res + 3, BUF_WORD3)]
@@ -687,8 +709,8 @@ def next_res(res, tile_sreg, base_lo, base_hi):
 
 def res_advance_fast(res):
     """res_advance while the tile stays below the item's last (the size cannot reach 0)."""
-    return ["s_add_u32 s%d, s%d, 0x4000" % (res, res), "s_addc_u32 s%d, s%d, 0" % (res + 1, res + 1),
-            "s_sub_i32 s%d, s%d, 0x4000" % (res + 2, res + 2)]
+    return ["s_add_u32 s%d, s%d, 0x%x" % (res, res, TILE_B), "s_addc_u32 s%d, s%d, 0" % (res + 1, res + 1),
+            "s_sub_i32 s%d, s%d, 0x%x" % (res + 2, res + 2, TILE_B)]
 
 
 def iteration(parity):
@@ -767,16 +789,16 @@ def q_block_dma(tag):
          "s_cmp_lt_u32 s%d, 4" % qw, "s_cbranch_scc0 L_after_%s_%%=" % tag,
          "s_cmp_lt_i32 %[nt], 5", "s_cbranch_scc1 L_after_%s_%%=" % tag,
          "s_cmp_le_i32 %[nqr], 0", "s_cbranch_scc1 L_after_%s_%%=" % tag]
-    o += ["s_lshl_b32 s%d, s%d, 14" % (t, qw), "s_add_u32 s%d, %%[nql], s%d" % (SREG, t),
+    o += ["s_lshl_b32 s%d, s%d, %d" % (t, qw, TSH), "s_add_u32 s%d, %%[nql], s%d" % (SREG, t),
           "s_addc_u32 s%d, %%[nqh], 0" % (SREG + 1), "s_lshl_b32 s%d, s%d, 6" % (t, qw),
           "s_sub_i32 s%d, %%[nqr], s%d" % (SREG + 2, t), "s_max_i32 s%d, s%d, 0" % (SREG + 2, SREG + 2),
-          "s_min_i32 s%d, s%d, 64" % (SREG + 2, SREG + 2), "s_lshl_b32 s%d, s%d, 8" % (SREG + 2, SREG + 2),
+          "s_min_i32 s%d, s%d, 64" % (SREG + 2, SREG + 2), "s_lshl_b32 s%d, s%d, %d" % (SREG + 2, SREG + 2, RSH),
           "s_mov_b32 s%d, %s" % (SREG + 3, BUF_WORD3),
-          "s_lshl_b32 s%d, s%d, 14" % (t, qw), "s_add_u32 s%d, s%d, %%[lbw]" % (t, t)]
-    for j in range(4):
+          "s_lshl_b32 s%d, s%d, %d" % (t, qw, TSH), "s_add_u32 s%d, s%d, %%[lbw]" % (t, t)]
+    for j in range(CH):
         o += ["s_add_u32 m0, s%d, %d" % (t, QSLOT + j * 4096), "s_nop 0",
               "buffer_load_dwordx4 %%[vo%d], s[%d:%d], 0 offen nt lds" % (j, SREG, SREG + 3)]
-    return o + ["s_waitcnt vmcnt(4)", "s_barrier", "s_branch L_cont_%s_%%=" % tag]
+    return o + ["s_waitcnt vmcnt(%d)" % CH, "s_barrier", "s_branch L_cont_%s_%%=" % tag]
 
 
 def ones_pattern():
@@ -791,7 +813,7 @@ def loop_body():
     o = ones_pattern()
     o += ["v_accvgpr_write_b32 a%d, v0" % (ONES_A + i) for i in range(4)]
     o += ["v_accvgpr_write_b32 a%d, 0" % (LSUM_A + i) for i in range(4 * QB)]
-    o += ["s_nop 3", "s_lshl_b32 s%d, %%[nkve], 8" % NKVB_S, "v_mov_b32 v%d, 0xff800000" % NINF_V]
+    o += ["s_nop 3", "s_lshl_b32 s%d, %%[nkve], %d" % (NKVB_S, RSH), "v_mov_b32 v%d, 0xff800000" % NINF_V]
     # S(0) with the item's parity, with the turn from the previous item (tn != 0) or without
     o += ["s_cmp_eq_u32 %[tn], 0", "s_cbranch_scc1 L_plain_%="]
     o += ["s_cmp_eq_u32 %[off], 0", "s_cbranch_scc0 L_turn1_%="] + first_tile(0, True)
@@ -827,7 +849,7 @@ def render_loop():
     outs = (o_binding() + ['"+' + b[1:] for b in q_binding()] +
             ['[l0] "+v"(l0)', '[l1] "+v"(l1)', '[mc0] "+v"(mc0)', '[mc1] "+v"(mc1)', '[t] "+s"(t)'])
     ins = (ka_binding() + va_binding() +
-           ['[vo%d] "v"(vo[%d])' % (j, j) for j in range(4)] +
+           ['[vo%d] "v"(vo[%d])' % (j, j) for j in range(CH)] +
            ['[lim0] "v"(lim0)', '[lim1] "v"(lim1)', '[c] "s"(c_log2)', '[nt] "s"(ntiles)', '[ntw] "s"(ntiles_w)',
             '[tm] "s"(t_mask)', '[kve] "s"(kv_end)', '[khl] "s"(kh_lo)', '[khh] "s"(kh_hi)',
             '[vhl] "s"(vh_lo)', '[vhh] "s"(vh_hi)', '[lbw] "s"(lbw)', '[off] "s"(off)', '[nkhl] "s"(nkh_lo)',
@@ -855,8 +877,9 @@ def render_loop():
         "// the wave at byte r * ob_stride; o is then cleared. turn == 0: q and o (= 0) are given. The next item's Q rows (nq_rows rows from address nq, 0: none) are fetched into the Q slots",
         "// after the barrier behind S(0) (items of fewer than five tiles) or one 64-row block per step at steps",
         "// nt - 5 .. nt - 2.",
-        "__device__ __forceinline__ void qb2_loop(f32x16 (&o)[2][4], bf16x8 (&q)[2][8], const uint32_t (&ka)[8],",
-        "                                         const uint32_t (&va)[4][2], const uint32_t (&vo)[4],",
+        "__device__ __forceinline__ void qb2_loop%s(f32x16 (&o)[2][%d], bf16x8 (&q)[2][%d], const uint32_t (&ka)[%d],"
+        % (SUFFIX, DB, KS, KS),
+        "                                         const uint32_t (&va)[%d][2], const uint32_t (&vo)[%d]," % (DB, CH),
         "                                         int32_t lim0, int32_t lim1, float c_log2,",
         "                                         float &l0, float &l1, float &mc0, float &mc1,",
         "                                         int32_t t, int32_t ntiles, int32_t ntiles_w, int32_t t_mask,",
@@ -884,20 +907,22 @@ def render_loop():
 def render():
     lines = [
         "// Generated by gen_qb2_tile.py; edit the generator, not this file.",
-        "// Tile steps of the 64-rows-per-wave kernel for 128-wide heads (see the",
+        "// Tile steps of the 64-rows-per-wave kernel for %d-wide heads (see the" % D,
         "// generator for the schedule and the register plan).",
         "",
     ]
     # Q^T read from the wave's Q slot straight into its AGPRs (qa[ks]: LDS address of k-step ks of the first
-    # query block, the second block 32 rows = 8 KiB further) and O = 0 (each 32 x 32 block by one MFMA of zero
+    # query block, the second block 32 rows further) and O = 0 (each 32 x 32 block by one MFMA of zero
     # operands, 16 AGPRs per instruction) while the reads are in flight
     qrd = ["ds_read_b128 a[%d:%d], %%[qa%d] offset:%d" % (Q_A + 4 * (qb * KS + ks), Q_A + 4 * (qb * KS + ks) + 3, ks,
                                                            qb * 32 * D * 2) for qb in range(QB) for ks in range(KS)]
     zero = ["v_mov_b32 v%d, 0" % r for r in range(ZERO_V, ZERO_V + 4)] + ["s_nop 4"]
     zero += ["v_mfma_f32_32x32x16_bf16 a[%d:%d], v[%d:%d], v[%d:%d], 0" % (b, b + 15, ZERO_V, ZERO_V + 3, ZERO_V,
-                                                                           ZERO_V + 3) for b in range(O_A, O_A + 128, 16)]
+                                                                           ZERO_V + 3)
+             for b in range(O_A, O_A + 16 * QB * DB, 16)]
     lines += [
-        "__device__ __forceinline__ void qb2_init(f32x16 (&o)[2][4], bf16x8 (&q)[2][8], const uint32_t (&qa)[8])",
+        "__device__ __forceinline__ void qb2_init%s(f32x16 (&o)[2][%d], bf16x8 (&q)[2][%d], const uint32_t (&qa)[%d])"
+        % (SUFFIX, DB, KS, KS),
         "{",
         "    asm volatile(",
         "\n".join('        "%s\\n"' % t for t in qrd + zero + ["s_waitcnt lgkmcnt(0)"] + list(O_WAIT)),
@@ -938,8 +963,8 @@ def render_out_bf16():
     inps += ['[inv0] "v"(inv0)', '[inv1] "v"(inv1)']
     clob = ['"v%d"' % r for r in list(range(OUT_TMP_V, OUT_TMP_V + 32)) + [OUT_INV_V, OUT_INV_V + 1]]
     return [
-        "__device__ __forceinline__ void qb2_out_bf16(const f32x16 (&o)[2][4], float inv0, float inv1,",
-        "                                             u32x8 (&pk)[2][4])",
+        "__device__ __forceinline__ void qb2_out_bf16%s(const f32x16 (&o)[2][%d], float inv0, float inv1," % (SUFFIX, DB),
+        "                                             u32x8 (&pk)[2][%d])" % DB,
         "{",
         "    asm volatile(",
         "\n".join('        "%s\\n"' % t for t in ins),
@@ -951,9 +976,15 @@ def render_out_bf16():
     ]
 
 
+OUTPUTS = {128: "attn_qb2_tile.inc", 64: "attn_qb2_tile_d64.inc"}
+
+
 if __name__ == "__main__":
     here = os.path.dirname(os.path.abspath(__file__))
-    text = render()
-    with open(os.path.join(here, "attn_qb2_tile.inc"), "w", encoding="utf-8") as f:
-        f.write(text)
-    print("wrote attn_qb2_tile.inc")
+    for d, name in OUTPUTS.items():
+        configure(d)
+        text = render()
+        with open(os.path.join(here, name), "w", encoding="utf-8") as f:
+            f.write(text)
+        print("wrote", name)
+    configure(128)
