@@ -41,11 +41,36 @@ KERNEL_SOURCES = ["transformer_scaled_dot_amd/csrc/attn_fwd_bf16.hip", "transfor
                   "transformer_scaled_dot_amd/csrc/attn_sched.h"]
 
 
+def strip_comments(src: str) -> str:
+    """C/C++ source without its comments, whitespace runs folded to one space: what the
+    compiler sees, so that editing a comment does not count as changing the kernel."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -10,9 +10,17 @@
 // Online Softmax): when the running max moves from m to m', the partial
 // sum and the partial output are rescaled by e^{m - m'}.
 //
-// Work decomposition (one workgroup = WAVES wavefronts of QB*32 query rows
-// each, all of one head; by default QB = 1 and two waves share each SIMD,
-// 8 waves per workgroup for 128-wide heads, 4 for 64-wide ones):
+// Two kernels, one tile design:
+//   * attn_fwd_qb2_kernel (128-wide heads; 64-wide ones when the grid of
+//     256-row items covers every CU): persistent, one workgroup per CU of 4
+//     wavefronts (one per SIMD) of 64 query rows; each workgroup runs a fixed
+//     list of 256-row items, head-major per XCD. Its tile loop is one
+//     generated inline-asm statement (gen_qb2_tile.py).
+//   * attn_fwd_bf16_kernel (64-wide heads on smaller grids): C++ with MFMA
+//     builtins, 32 query rows per wave and two waves per SIMD; 4 waves of
+//     one 128-row block, or 8 waves that split the block's key tiles in two
+//     halves when even the 4-wave grid leaves CUs idle.
+// Shared by both:
 //   * Q^T stays in registers as the B operand of v_mfma_f32_32x32x16_bf16.
 //   * K and V tiles (64 keys) go HBM -> LDS by DMA (no staging registers),
 //     double buffered, while the previous tile is computed.
@@ -28,7 +36,8 @@
 //   * O^T also has one query per lane, so the e^{m - m'} rescale is one
 //     scalar per lane; it is skipped when no row of the wave changed max.
 //   * Causal: key tiles above a wave's diagonal are skipped, tiles crossing
-//     it are masked; workgroups are issued longest-first.
+//     it are masked; long and short items alternate so that every
+//     workgroup gets the same number of tile steps.
 #include "attn_sched.h"
 #include "attn_tiles.h"
 #include "device_common.h"
