@@ -178,3 +178,68 @@ def test_causal_grouped_full_size(dev):
     ref, rl = oracle.attention(q.f64, k.f64, v.f64, mask="causal_padding", valid_lens=vl, return_lse=True)
     check_out("bf16 [4,16/4,4096,128] causal_padding (every element)", got, ref, "bf16")
     check_lse("bf16 [4,16/4,4096,128] causal_padding (every row)", lse, rl, "bf16")
+
+
+@pytest.mark.parametrize("case", ["padding_d64", "causal_d128", "mha"])
+def test_graph_replay_matches_eager(dev, case):
+    """The attention and multi-head calls captured into a HIP graph (torch.cuda.CUDAGraph, as bench.py times
+    its launch-bound workloads): three replays, each preceded by clearing the outputs and an eager launch of
+    another shape and followed by a synchronisation, each give bitwise the outputs of the same calls run
+    eagerly."""
+    import transformer_scaled_dot_amd as tsd
+
+    sets = []
+    if case == "mha":
+        B, N, dm, h = 2, 256, 256, 4
+        for s in range(2):
+            x = synth.normal_tensor(700 + s, (B, N, dm), "bf16").torch(dev)
+            wq = (synth.normal_tensor(710 + s, (dm, 3 * dm), "bf16").torch(dev).float() / dm ** 0.5).to(torch.bfloat16)
+            wo = (synth.normal_tensor(720 + s, (dm, dm), "bf16").torch(dev).float() / dm ** 0.5).to(torch.bfloat16)
+            ws = torch.empty(int(tsd.load_library().mha_workspace_bytes(B, N, dm, h, 1)), dtype=torch.uint8, device=dev)
+            sets.append((x, wq, wo, ws, torch.empty((B, N, dm), dtype=torch.bfloat16, device=dev)))
+
+        def call(i):
+            x, wq, wo, ws, o = sets[i]
+            tsd.mha_fwd(x, wq, wo, h, out=o, workspace=ws)
+    else:
+        if case == "padding_d64":
+            B, H, N, d, mask, vl = 2, 4, 300, 64, "padding", [200, 300]
+        else:
+            B, H, N, d, mask, vl = 1, 2, 500, 128, "causal", None
+        vl_t = torch.tensor(vl, dtype=torch.int32, device=dev) if vl else None
+        for s in range(2):
+            q, k, v = inputs(730 + 3 * s, B, H, H, N, N, d)
+            sets.append((q.torch(dev), k.torch(dev), v.torch(dev),
+                         torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)))
+
+        def call(i):
+            q, k, v, o = sets[i]
+            tsd.attn_fwd(q, k, v, mask=mask, valid_lens=vl_t, out=o)
+
+    outs = [st[-1] for st in sets]
+    for i in range(len(sets)):
+        call(i)
+    torch.cuda.synchronize()
+    want = [o.clone() for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(len(sets)):
+            call(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(len(sets)):
+            call(i)
+    oq, ok_, ov = inputs(760, 1, 2, 2, 130, 130, 64)
+    for rep in range(3):
+        say("graph replay", case, rep)
+        for o in outs:
+            o.zero_()
+        tsd.attn_fwd(oq.torch(dev), ok_.torch(dev), ov.torch(dev), mask="causal")
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for j, (o, w) in enumerate(zip(outs, want)):
+            assert torch.equal(o, w), "replay %d, set %d differs from the eager result" % (rep, j)
