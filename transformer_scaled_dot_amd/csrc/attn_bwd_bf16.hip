@@ -9,19 +9,18 @@
 //   dP_ij = dO_i . v_j
 //   dS_ij = P_ij (dP_ij - D_i),  D_i = dO_i . O_i  (= sum_j P_ij dP_ij: the softmax Jacobian's row term)
 //   dQ_i  = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i
-// Three kernels:
-//   attn_bwd_delta: per query row, D_i and lse_i * log2(e) (0 for a row without a visible key) into the
-//                   caller's workspace, each head's rows padded to a multiple of 64 with zeros, so that
-//                   the other kernels fetch whole 64-row tiles of them;
+// Two kernels, dQ first:
+//   attn_bwd_dq:    one workgroup per 256 query rows of one (batch, head), 32 rows per wave; it walks the
+//                   key tiles like the forward: S^T = K Q^T and dP^T = V dO^T with one query per lane, then
+//                   dQ^T += K^T dS^T. It also writes the row terms D_i and lse_i * log2(e) (0 for a row
+//                   without a visible key) into the caller's workspace, each head's rows padded to a multiple
+//                   of 64 with zeros, so that the dK/dV kernel fetches whole 64-row tiles of them;
 //   attn_bwd_dkdv:  one workgroup per 128 keys of one (batch, K/V head): 8 waves, two per SIMD, each
 //                   owning 32 keys and one 32-row half of every query tile; it walks the query tiles (of
 //                   every query head of the K/V head's group) and keeps partial dK and dV in registers:
 //                   S = Q K^T and dP = dO V^T with one key per lane, then dV^T += dO^T P and
 //                   dK^T += Q^T dS with P and dS taken straight from those accumulators; the two halves
-//                   are added through LDS at the end;
-//   attn_bwd_dq:    one workgroup per 256 query rows of one (batch, head), 32 rows per wave; it walks the
-//                   key tiles like the forward: S^T = K Q^T and dP^T = V dO^T with one query per lane, then
-//                   dQ^T += K^T dS^T.
+//                   are added through LDS at the end.
 // Both main kernels use the forward's tile layout and contractions (attn_tiles.h); Q/dO (dK/dV kernel) or
 // K/V (dQ kernel) tiles of 64 rows go to LDS by DMA, double buffered. P and dS are rounded to bf16 for the
 // MFMAs, products accumulate in float32.
@@ -40,39 +39,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
-
-// Per query row (BH heads of Nq rows, padded to Nq_pad): D_i = dO_i . O_i and lse_i * log2(e) (0 where
-// lse_i = -inf), 0 for padding rows. D/8 consecutive lanes per row, 16 bytes each.
-template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const uint16_t *__restrict__ O,
-                                                             const uint16_t *__restrict__ dO,
-                                                             const float *__restrict__ lse, float *__restrict__ lse2,
-                                                             float *__restrict__ delta, long long BH, int Nq,
-                                                             int Nq_pad)
-{
-    constexpr int LPR = D / 8;
-    const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-    const long long prow = t / LPR;  // padded row index
-    const int part = (int)(t % LPR);
-    const long long bh = prow / Nq_pad;
-    const int i = (int)(prow % Nq_pad);
-    const bool real = bh < BH && i < Nq;
-    const long long row = bh * Nq + i;
-    float acc = 0.f;
-    if (real) {
-        const u32x4 o = *(const u32x4 *)(O + row * D + part * 8);
-        const u32x4 g = *(const u32x4 *)(dO + row * D + part * 8);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) acc += bf16_lo(o[w]) * bf16_lo(g[w]) + bf16_hi(o[w]) * bf16_hi(g[w]);
-    }
-#pragma unroll
-    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
-    if (bh < BH && part == 0) {
-        delta[prow] = acc;
-        const float l = real ? lse[row] : 0.f;
-        lse2[prow] = isinf(l) ? 0.f : l * kLog2e;
-    }
-}
 
 // Rows of the wave's 32-row block (this lane's row, 8 bf16 of each 16-wide k-step) as B operands; rows at
 // or past n read as zero.
@@ -364,9 +330,10 @@ __global__ __launch_bounds__(512) void attn_bwd_dkdv_kernel(
 template <int D, int MASK>
 __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    const uint16_t *__restrict__ dO, const float *__restrict__ lse2, const float *__restrict__ delta,
-    const int32_t *__restrict__ valid_lens, float c_log2, float scale, uint16_t *__restrict__ dQ, int H,
-    int Hkv, int group, int Nq, int Nq_pad, int Nk, int num_qtiles, int BH)
+    const uint16_t *__restrict__ O, const uint16_t *__restrict__ dO, const float *__restrict__ lse,
+    float *__restrict__ lse2, float *__restrict__ delta, const int32_t *__restrict__ valid_lens, float c_log2,
+    float scale, uint16_t *__restrict__ dQ, int H, int Hkv, int group, int Nq, int Nq_pad, int Nk, int num_qtiles,
+    int BH)
 {
     constexpr int WAVES = 8, ROWS = WAVES * 32, DB = D / 32, TILE_B = kBlockN * D * 2;
     __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_B];  // K slots 0, 1; V slots 0, 1
@@ -393,10 +360,31 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
     bf16x8 qreg[1][D / 16], greg[1][D / 16];
     load_rows_b<D>(Q + (size_t)bh * Nq * D, qrow, Nq, hf, qreg);
     load_rows_b<D>(dO + (size_t)bh * Nq * D, qrow, Nq, hf, greg);
-    // (a row without a visible key has lse * log2(e) stored as 0, so that its masked scores give
-    // exp2(-inf) = 0 rather than -inf - (-inf); padding rows hold 0)
-    const float l2_row = lse2[(size_t)bh * Nq_pad + min(qrow, Nq_pad - 1)];
-    const float d_row = delta[(size_t)bh * Nq_pad + min(qrow, Nq_pad - 1)];
+    // The row terms: D_i = dO_i . O_i (this lane's half of every 16-wide k-step, plus the other half from the
+    // lane 32 away, which holds the same row) and lse_i * log2(e), 0 for a row without a visible key, so that
+    // its masked scores give exp2(-inf) = 0 rather than -inf - (-inf). They go to the workspace for the dK/dV
+    // kernel, which runs after this one, with zeros for the rows from Nq up to Nq_pad.
+    float d_row, l2_row = 0.f;
+    {
+        float acc = 0.f;
+        if (qrow < Nq) {
+            const uint16_t *orow = O + ((size_t)bh * Nq + qrow) * D + hf * 8;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const u32x4 o = *(const u32x4 *)(orow + ks * 16);
+                const u32x4 g = __builtin_bit_cast(u32x4, greg[0][ks]);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) acc += bf16_lo(o[w]) * bf16_lo(g[w]) + bf16_hi(o[w]) * bf16_hi(g[w]);
+            }
+            const float l = lse[(size_t)bh * Nq + qrow];
+            l2_row = isinf(l) ? 0.f : l * kLog2e;
+        }
+        d_row = half_swap_sum(acc);
+        if (hf == 0 && qrow < Nq_pad) {
+            delta[(size_t)bh * Nq_pad + qrow] = d_row;
+            lse2[(size_t)bh * Nq_pad + qrow] = l2_row;
+        }
+    }
 
     f32x16 dq[1][DB];
 #pragma unroll
@@ -458,29 +446,25 @@ hipError_t launch_bwd(const void *Q, const void *K, const void *V, const void *O
 {
     const long long BH = (long long)B * H;
     const int Nq_pad = (Nq + kBlockN - 1) / kBlockN * kBlockN;
-    const long long prows = BH * Nq_pad;
-    float *lse2 = work, *delta = work + prows;
+    float *lse2 = work, *delta = work + BH * Nq_pad;
     const int group = H / Hkv;
     // scale = 0 must still send masked scores (-inf) to weight 0: -inf * 0 would be NaN in the dQ kernel's
     // exponent, so the factor is held above 0 (every score below 1e-30 in magnitude then weighs as 0 does)
     const float c_log2 = fmaxf(scale * kLog2e, 1e-30f);
-    if (prows > 0) {
-        const long long threads = prows * (D / 8);
-        hipLaunchKernelGGL((attn_bwd_delta_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                           (const uint16_t *)O, (const uint16_t *)dO, lse, lse2, delta, BH, Nq, Nq_pad);
-    }
+    // dQ first: it also writes the row terms the dK/dV kernel reads
+    const int num_qtiles = (Nq + 255) / 256;
+    const long long g2 = (long long)num_qtiles * B * H;
+    if (g2 > 0)
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<D, MASK>), dim3((unsigned)g2), dim3(512), 0, s, (const uint16_t *)Q,
+                           (const uint16_t *)K, (const uint16_t *)V, (const uint16_t *)O, (const uint16_t *)dO, lse,
+                           lse2, delta, vl, c_log2, scale, (uint16_t *)dQ, H, Hkv, group, Nq, Nq_pad, Nk, num_qtiles,
+                           B * H);
     const int num_kblocks = (Nk + 127) / 128;
     const long long g1 = (long long)num_kblocks * B * Hkv;
     if (g1 > 0)
         hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, MASK>), dim3((unsigned)g1), dim3(512), 0, s, (const uint16_t *)Q,
                            (const uint16_t *)K, (const uint16_t *)V, (const uint16_t *)dO, lse2, delta, vl, c_log2,
                            scale, (uint16_t *)dK, (uint16_t *)dV, H, Hkv, group, Nq, Nq_pad, Nk, num_kblocks);
-    const int num_qtiles = (Nq + 255) / 256;
-    const long long g2 = (long long)num_qtiles * B * H;
-    if (g2 > 0)
-        hipLaunchKernelGGL((attn_bwd_dq_kernel<D, MASK>), dim3((unsigned)g2), dim3(512), 0, s, (const uint16_t *)Q,
-                           (const uint16_t *)K, (const uint16_t *)V, (const uint16_t *)dO, lse2, delta, vl, c_log2,
-                           scale, (uint16_t *)dQ, H, Hkv, group, Nq, Nq_pad, Nk, num_qtiles, B * H);
     return hipGetLastError();
 }
 
