@@ -34,6 +34,10 @@
  *    returns, and never synchronises: work is enqueued on `stream`
  *    (a hipStream_t; NULL = the default stream) and the call returns at
  *    once. Buffers must stay alive until the stream has passed the work.
+ *  - A call enqueues kernel launches only (no memset, copy or host
+ *    callback), so it can be captured into a HIP graph on `stream` and
+ *    replayed; a replay reads and writes the buffers the captured call
+ *    named (attn_fwd and mha_fwd replays are tested against eager calls).
  *  - Tensors are dense, row-major, and 16-byte aligned. Outputs must not
  *    overlap inputs.
  *  - Errors are reported only through the return code; nothing aborts and
