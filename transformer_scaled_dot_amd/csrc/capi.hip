@@ -303,8 +303,8 @@ attn_status_t attn_bwd_noalloc(const void *Q, const void *K, const void *V, cons
     void *ws = nullptr;
     const attn_status_t sst = device_scratch(&ws);
     if (sst != ATTN_OK) return sst;
-    // every scratch value a call reads is first written by that call (its row-term kernel covers every padded
-    // row), so nothing needs clearing between calls
+    // every scratch value a call reads is first written by that call (its dQ kernel writes the row terms of
+    // every padded row before the dK/dV kernel reads them), so nothing needs clearing between calls
     const hipError_t e = tsd::launch_attn_bwd_bf16(Q, K, V, O, dO, lse, mask_kind, valid_lens, scale, dQ, dK, dV, batch,
                                                    heads, kv_heads, seq_q, seq_k, head_dim, (float *)ws,
                                                    (hipStream_t)stream);
